@@ -1,0 +1,155 @@
+"""Python binding of libqmoe, the gfx950 FP4 weight-only MoE expert path.
+
+Argument marshalling only: every step runs in the HIP kernels of libqmoe.so
+(built in-tree by fp4_weight_only_amd.build).  PyTorch supplies device memory
+and the current stream; tensors are passed by data_ptr().  Importing this
+package raises ImportError when the library is not built: there is no CPU
+fallback.
+
+The functions carry the names of the C entry points declared in
+include/qmoe.h and raise QmoeError on any status other than QMOE_OK.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqmoe.so")
+
+QMOE_OK, QMOE_EINVAL, QMOE_EUNSUPPORTED, QMOE_EALIGN, QMOE_EWORKSPACE, QMOE_ELAUNCH = range(6)
+QMOE_FMT_NVFP4, QMOE_FMT_MXFP4 = 0, 1
+QMOE_PATH_AUTO, QMOE_PATH_GEMV, QMOE_PATH_GROUPED = 0, 1, 2
+GEMV_MAX_ROWS = 64
+
+EXPORTS = ("qmoe_route_topk", "qmoe_fp4_gemv_fc1_swiglu", "qmoe_fp4_gemv_fc2", "qmoe_finalize",
+           "qmoe_dequant_fp4", "qmoe_status_str")
+
+
+class QmoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {lib.qmoe_status_str(status).decode()}")
+
+
+class Fp4WeightsC(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("gscale", ctypes.c_void_p),
+                ("E", ctypes.c_int32), ("K", ctypes.c_int32), ("N", ctypes.c_int32), ("fmt", ctypes.c_int32)]
+
+
+class SwigluC(ctypes.Structure):
+    _fields_ = [("alpha", ctypes.c_float), ("beta", ctypes.c_float), ("limit", ctypes.c_float)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built (run: python -m fp4_weight_only_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)
+    W = ctypes.POINTER(Fp4WeightsC)
+    sig = {
+        "qmoe_route_topk": [P, I32, I32, I32, P, P, P, P, P, P],
+        "qmoe_fp4_gemv_fc1_swiglu": [P, I32, I32, W, P, P, ctypes.POINTER(SwigluC), P, P, SZ, I32, P],
+        "qmoe_fp4_gemv_fc2": [P, I32, I32, W, P, P, P, SZ, I32, P],
+        "qmoe_finalize": [P, P, P, I32, I32, I32, P, P],
+        "qmoe_dequant_fp4": [W, P, P],
+    }
+    for name, args in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    L.qmoe_status_str.argtypes = [ctypes.c_int]
+    L.qmoe_status_str.restype = ctypes.c_char_p
+    return L
+
+
+lib = _load()
+
+
+@dataclasses.dataclass
+class FP4Weights:
+    """Device tensors of one FC layer: w [E][K][N/2] uint8, scales [E][K/B][N] uint8, gscale [E] f32 or None."""
+    w: torch.Tensor
+    scales: torch.Tensor
+    gscale: torch.Tensor | None
+    fmt: int
+
+    def c(self) -> Fp4WeightsC:
+        E, K, half = self.w.shape
+        return Fp4WeightsC(self.w.data_ptr(), self.scales.data_ptr(),
+                           None if self.gscale is None else self.gscale.data_ptr(), E, K, 2 * half, self.fmt)
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _check(fn, st):
+    if st != QMOE_OK:
+        raise QmoeError(fn, st)
+
+
+def qmoe_route_topk(logits, k, topk_idx, topk_w, expert_offsets, perm_to_expanded, expanded_to_perm, stream=None):
+    T, E = logits.shape
+    _check("qmoe_route_topk", lib.qmoe_route_topk(
+        _ptr(logits), T, E, k, _ptr(topk_idx), _ptr(topk_w), _ptr(expert_offsets), _ptr(perm_to_expanded),
+        _ptr(expanded_to_perm), _stream(stream)))
+
+
+def fc_workspace_bytes(which: int, T: int, k: int, w: FP4Weights, path=QMOE_PATH_AUTO) -> int:
+    """Workspace size of qmoe_fp4_gemv_fc1_swiglu (which=1) or qmoe_fp4_gemv_fc2 (which=2)."""
+    n = ctypes.c_size_t(0)
+    wc = w.c()
+    dummy = 256  # aligned non-null placeholders: a size query launches nothing
+    if which == 1:
+        st = lib.qmoe_fp4_gemv_fc1_swiglu(dummy, T, k, ctypes.byref(wc), dummy, dummy, None, dummy, None,
+                                          ctypes.byref(n), path, None)
+    else:
+        st = lib.qmoe_fp4_gemv_fc2(dummy, T, k, ctypes.byref(wc), dummy, dummy, None, ctypes.byref(n), path, None)
+    _check("fc_workspace_bytes", st)
+    return n.value
+
+
+def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """Workspace of at least nbytes (scratch: its contents do not matter)."""
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def qmoe_fp4_gemv_fc1_swiglu(x, k, w1: FP4Weights, expert_offsets, perm_to_expanded, h, ws, act=None,
+                             path=QMOE_PATH_AUTO, stream=None):
+    T = x.shape[0]
+    wc = w1.c()
+    n = ctypes.c_size_t(ws.numel() * ws.element_size())
+    a = None if act is None else ctypes.byref(SwigluC(*act))
+    _check("qmoe_fp4_gemv_fc1_swiglu", lib.qmoe_fp4_gemv_fc1_swiglu(
+        _ptr(x), T, k, ctypes.byref(wc), _ptr(expert_offsets), _ptr(perm_to_expanded), a, _ptr(h), _ptr(ws),
+        ctypes.byref(n), path, _stream(stream)))
+
+
+def qmoe_fp4_gemv_fc2(h, T, k, w2: FP4Weights, expert_offsets, y_rows, ws, path=QMOE_PATH_AUTO, stream=None):
+    wc = w2.c()
+    n = ctypes.c_size_t(ws.numel() * ws.element_size())
+    _check("qmoe_fp4_gemv_fc2", lib.qmoe_fp4_gemv_fc2(
+        _ptr(h), T, k, ctypes.byref(wc), _ptr(expert_offsets), _ptr(y_rows), _ptr(ws), ctypes.byref(n), path,
+        _stream(stream)))
+
+
+def qmoe_finalize(y_rows, topk_w, expanded_to_perm, out, stream=None):
+    T, k = topk_w.shape
+    H = out.shape[1]
+    _check("qmoe_finalize", lib.qmoe_finalize(_ptr(y_rows), _ptr(topk_w), _ptr(expanded_to_perm), T, k, H,
+                                               _ptr(out), _stream(stream)))
+
+
+def qmoe_dequant_fp4(w: FP4Weights, out, stream=None):
+    wc = w.c()
+    _check("qmoe_dequant_fp4", lib.qmoe_dequant_fp4(ctypes.byref(wc), _ptr(out), _stream(stream)))

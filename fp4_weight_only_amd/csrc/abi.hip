@@ -1,0 +1,179 @@
+// C ABI of libqmoe: argument validation (host only, before any launch) and
+// dispatch to the gfx950 kernels.
+#include <math.h>
+
+#include "../../include/qmoe.h"
+#include "qmoe_internal.h"
+
+using namespace qmoe;
+
+namespace {
+
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+inline int block_of(int32_t fmt) { return fmt == QMOE_FMT_NVFP4 ? 16 : 32; }
+
+inline qmoe_status check_launch(hipError_t e) { return e == hipSuccess ? QMOE_OK : QMOE_ELAUNCH; }
+
+// Common checks of an FP4 weight descriptor.
+qmoe_status check_weights(const qmoe_fp4_weights *w) {
+  if (!w || !w->w || !w->scales) return QMOE_EINVAL;
+  if (w->fmt != QMOE_FMT_NVFP4 && w->fmt != QMOE_FMT_MXFP4) return QMOE_EINVAL;
+  if (w->E < 1 || w->K < 1 || w->N < 1) return QMOE_EINVAL;
+  if (w->fmt == QMOE_FMT_NVFP4 && !w->gscale) return QMOE_EINVAL;
+  if (!aligned16(w->w) || !aligned16(w->scales) || (w->gscale && !aligned16(w->gscale))) return QMOE_EALIGN;
+  if (w->K % block_of(w->fmt) != 0) return QMOE_EUNSUPPORTED;
+  return QMOE_OK;
+}
+
+struct FcShape {
+  int32_t rows;
+  int32_t max_rows_per_expert;  // a token selects an expert at most once
+};
+
+qmoe_status check_fc(const qmoe_fp4_weights *w, int32_t T, int32_t k, const void *act, const void *offsets,
+                     const void *out, qmoe_path path, FcShape *shape) {
+  if (!act || !offsets || !out) return QMOE_EINVAL;
+  if (T < 1 || k < 1) return QMOE_EINVAL;
+  qmoe_status st = check_weights(w);
+  if (st != QMOE_OK) return st;
+  if (k > w->E) return QMOE_EINVAL;
+  if (path != QMOE_PATH_AUTO && path != QMOE_PATH_GEMV && path != QMOE_PATH_GROUPED) return QMOE_EINVAL;
+  if (!aligned16(act) || !aligned16(offsets) || !aligned16(out)) return QMOE_EALIGN;
+  if (w->E > QMOE_MAX_EXPERTS || k > QMOE_MAX_TOPK) return QMOE_EUNSUPPORTED;
+  if (w->N % 32 != 0) return QMOE_EUNSUPPORTED;
+  const int64_t rows = (int64_t)T * k;
+  if (rows > (1 << 24)) return QMOE_EUNSUPPORTED;
+  shape->rows = (int32_t)rows;
+  shape->max_rows_per_expert = T;
+  return QMOE_OK;
+}
+
+// Resolves AUTO and checks the row window of each path.
+qmoe_status resolve_path(qmoe_path path, int32_t rows, qmoe_path *out) {
+  qmoe_path p = path;
+  if (p == QMOE_PATH_AUTO) p = rows <= QMOE_GEMV_MAX_ROWS ? QMOE_PATH_GEMV : QMOE_PATH_GROUPED;
+  if (p == QMOE_PATH_GEMV && rows > QMOE_GEMV_MAX_ROWS) return QMOE_EUNSUPPORTED;
+  if (p == QMOE_PATH_GROUPED) return QMOE_EUNSUPPORTED;  // grouped GEMM path not built in this library yet
+  *out = p;
+  return QMOE_OK;
+}
+
+qmoe_status run_gemv(GemvArgs &a, const qmoe_fp4_weights *w, int max_rows, void *ws, size_t *ws_bytes,
+                     hipStream_t stream) {
+  const size_t need = gemv_workspace_bytes(a.rows, w->E, w->K, w->N);
+  if (!ws_bytes) return QMOE_EINVAL;
+  if (!ws) {
+    *ws_bytes = need;
+    return QMOE_OK;
+  }
+  if (*ws_bytes < need) return QMOE_EWORKSPACE;
+  if (!aligned16(ws)) return QMOE_EALIGN;
+  a.w = w->w;
+  a.scales = w->scales;
+  a.gscale = w->gscale;
+  a.E = w->E;
+  a.K = w->K;
+  a.N = w->N;
+  gemv_plan(a, ws);
+  return check_launch(launch_fp4_gemv(a, w->fmt == QMOE_FMT_NVFP4 ? 0 : 1, max_rows, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qmoe_status_str(qmoe_status s) {
+  switch (s) {
+    case QMOE_OK: return "QMOE_OK";
+    case QMOE_EINVAL: return "QMOE_EINVAL: invalid argument";
+    case QMOE_EUNSUPPORTED: return "QMOE_EUNSUPPORTED: shape or path not supported";
+    case QMOE_EALIGN: return "QMOE_EALIGN: device pointer not 16-byte aligned";
+    case QMOE_EWORKSPACE: return "QMOE_EWORKSPACE: workspace too small";
+    case QMOE_ELAUNCH: return "QMOE_ELAUNCH: kernel launch failed";
+  }
+  return "QMOE_UNKNOWN";
+}
+
+qmoe_status qmoe_route_topk(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *topk_idx, float *topk_w,
+                            int32_t *expert_offsets, int32_t *perm_to_expanded, int32_t *expanded_to_perm,
+                            hipStream_t stream) {
+  if (!logits || !topk_idx || !topk_w || !expert_offsets || !perm_to_expanded || !expanded_to_perm)
+    return QMOE_EINVAL;
+  if (T < 1 || E < 1 || k < 1 || k > E) return QMOE_EINVAL;
+  if (!aligned16(logits) || !aligned16(topk_idx) || !aligned16(topk_w) || !aligned16(expert_offsets) ||
+      !aligned16(perm_to_expanded) || !aligned16(expanded_to_perm))
+    return QMOE_EALIGN;
+  if (E > QMOE_MAX_EXPERTS || k > QMOE_MAX_TOPK) return QMOE_EUNSUPPORTED;
+  if ((int64_t)T * k > (1 << 24)) return QMOE_EUNSUPPORTED;
+  return check_launch(
+      launch_route(logits, T, E, k, topk_idx, topk_w, expert_offsets, perm_to_expanded, expanded_to_perm, stream));
+}
+
+qmoe_status qmoe_fp4_gemv_fc1_swiglu(const uint16_t *x, int32_t T, int32_t k, const qmoe_fp4_weights *w1,
+                                     const int32_t *expert_offsets, const int32_t *perm_to_expanded,
+                                     const qmoe_swiglu *act, uint16_t *h, void *ws, size_t *ws_bytes,
+                                     qmoe_path path, hipStream_t stream) {
+  FcShape sh;
+  qmoe_status st = check_fc(w1, T, k, x, expert_offsets, h, path, &sh);
+  if (st != QMOE_OK) return st;
+  if (!perm_to_expanded) return QMOE_EINVAL;
+  if (!aligned16(perm_to_expanded)) return QMOE_EALIGN;
+  qmoe_path p;
+  st = resolve_path(path, sh.rows, &p);
+  if (st != QMOE_OK) return st;
+  GemvArgs a = {};
+  a.act = x;
+  a.p2e = perm_to_expanded;
+  a.offsets = expert_offsets;
+  a.topk = k;
+  a.rows = sh.rows;
+  a.fc1 = 1;
+  a.alpha = act ? act->alpha : 1.0f;
+  a.beta = act ? act->beta : 0.0f;
+  a.limit = act ? act->limit : INFINITY;
+  a.out_bf16 = h;
+  return run_gemv(a, w1, sh.max_rows_per_expert, ws, ws_bytes, stream);
+}
+
+qmoe_status qmoe_fp4_gemv_fc2(const uint16_t *h, int32_t T, int32_t k, const qmoe_fp4_weights *w2,
+                              const int32_t *expert_offsets, float *y_rows, void *ws, size_t *ws_bytes,
+                              qmoe_path path, hipStream_t stream) {
+  FcShape sh;
+  qmoe_status st = check_fc(w2, T, k, h, expert_offsets, y_rows, path, &sh);
+  if (st != QMOE_OK) return st;
+  qmoe_path p;
+  st = resolve_path(path, sh.rows, &p);
+  if (st != QMOE_OK) return st;
+  GemvArgs a = {};
+  a.act = h;
+  a.offsets = expert_offsets;
+  a.topk = k;
+  a.rows = sh.rows;
+  a.fc1 = 0;
+  a.out_f32 = y_rows;
+  return run_gemv(a, w2, sh.max_rows_per_expert, ws, ws_bytes, stream);
+}
+
+qmoe_status qmoe_finalize(const float *y_rows, const float *topk_w, const int32_t *expanded_to_perm, int32_t T,
+                          int32_t k, int32_t H, uint16_t *out, hipStream_t stream) {
+  if (!y_rows || !topk_w || !expanded_to_perm || !out) return QMOE_EINVAL;
+  if (T < 1 || k < 1 || H < 1) return QMOE_EINVAL;
+  if (!aligned16(y_rows) || !aligned16(topk_w) || !aligned16(expanded_to_perm) || !aligned16(out))
+    return QMOE_EALIGN;
+  if (k > QMOE_MAX_TOPK || H % 8 != 0) return QMOE_EUNSUPPORTED;
+  return check_launch(launch_finalize(y_rows, topk_w, expanded_to_perm, T, k, H, out, stream));
+}
+
+qmoe_status qmoe_dequant_fp4(const qmoe_fp4_weights *w, uint16_t *out, hipStream_t stream) {
+  qmoe_status st = check_weights(w);
+  if (st != QMOE_OK) return st;
+  if (!out) return QMOE_EINVAL;
+  if (!aligned16(out)) return QMOE_EALIGN;
+  if (w->K % 64 != 0 || w->N % 256 != 0) return QMOE_EUNSUPPORTED;
+  if (w->E > 65535 || w->K / 64 > 65535 || w->N / 256 > 65535) return QMOE_EUNSUPPORTED;
+  return check_launch(
+      launch_dequant(w->w, w->scales, w->gscale, w->E, w->K, w->N, w->fmt == QMOE_FMT_NVFP4 ? 0 : 1, out, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,44 @@
+// Internal host-side launch interface between the C ABI (abi.hip) and the
+// kernels.  Arguments are validated by the ABI before any launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qmoe {
+
+constexpr int kGemvTileN = 256;    // output columns per GEMV block (32 lanes x 8 columns)
+constexpr int kGemvLaneK = 32;     // k rows per lane
+constexpr int kGemvChunkK = 256;   // k rows per GEMV block (4 waves x 2 halves x 32)
+
+struct GemvArgs {
+  const uint16_t *act;     // FC1: x [T][K]; FC2: h [rows][K]
+  const int32_t *p2e;      // FC1 only: permuted row -> expanded row
+  const int32_t *offsets;  // [E+1]
+  const uint8_t *w;
+  const uint8_t *scales;
+  const float *gscale;     // may be null
+  int32_t E, K, N, topk, rows;
+  int32_t nslots, ntiles, nchunks;
+  int32_t fc1;             // 1: act rows gathered by token, SwiGLU epilogue, bf16 out
+  float alpha, beta, limit;
+  uint16_t *out_bf16;      // FC1: h [rows][N/2]
+  float *out_f32;          // FC2: y [rows][N]
+  float *partials;         // [nchunks][rows][N] split-K partials (nchunks > 1)
+};
+
+size_t gemv_workspace_bytes(int32_t rows, int32_t E, int32_t K, int32_t N);
+void gemv_plan(GemvArgs &a, void *ws);
+hipError_t launch_fp4_gemv(const GemvArgs &a, int fmt, int max_rows_per_expert, hipStream_t s);
+
+hipError_t launch_route(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *idx, float *w,
+                        int32_t *offsets, int32_t *p2e, int32_t *e2p, hipStream_t s);
+
+hipError_t launch_finalize(const float *y, const float *w, const int32_t *e2p, int32_t T, int32_t k,
+                           int32_t H, uint16_t *out, hipStream_t s);
+
+hipError_t launch_dequant(const uint8_t *w, const uint8_t *scales, const float *g, int32_t E, int32_t K,
+                          int32_t N, int fmt, uint16_t *out, hipStream_t s);
+
+}  // namespace qmoe

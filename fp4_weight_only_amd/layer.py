@@ -1,0 +1,52 @@
+"""One MoE expert layer on the GPU through the C ABI: route -> FC1+SwiGLU -> FC2 -> finalize.
+
+Buffers are allocated once per shape; run() enqueues the four calls on the
+current stream and allocates nothing.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (QMOE_PATH_AUTO, FP4Weights, alloc_workspace, fc_workspace_bytes, qmoe_finalize,
+               qmoe_fp4_gemv_fc1_swiglu, qmoe_fp4_gemv_fc2, qmoe_route_topk)
+
+
+class MoELayer:
+    def __init__(self, T: int, E: int, k: int, H: int, I: int, w1: FP4Weights, w2: FP4Weights,
+                 path: int = QMOE_PATH_AUTO, act=None, device="cuda"):
+        self.T, self.E, self.k, self.H, self.I = T, E, k, H, I
+        self.w1, self.w2, self.path, self.act = w1, w2, path, act
+        R = T * k
+        dev = torch.device(device)
+        self.topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+        self.p2e = torch.empty((R,), dtype=torch.int32, device=dev)
+        self.e2p = torch.empty((R,), dtype=torch.int32, device=dev)
+        self.h = torch.empty((R, I), dtype=torch.bfloat16, device=dev)
+        self.y = torch.empty((R, H), dtype=torch.float32, device=dev)
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        need = max(fc_workspace_bytes(1, T, k, w1, path), fc_workspace_bytes(2, T, k, w2, path))
+        self.ws = alloc_workspace(need, dev)
+
+    def set_weights(self, w1: FP4Weights, w2: FP4Weights):
+        self.w1, self.w2 = w1, w2
+
+    def route(self, logits):
+        qmoe_route_topk(logits, self.k, self.topk_idx, self.topk_w, self.offsets, self.p2e, self.e2p)
+
+    def fc1(self, x):
+        qmoe_fp4_gemv_fc1_swiglu(x, self.k, self.w1, self.offsets, self.p2e, self.h, self.ws, self.act, self.path)
+
+    def fc2(self):
+        qmoe_fp4_gemv_fc2(self.h, self.T, self.k, self.w2, self.offsets, self.y, self.ws, self.path)
+
+    def finalize(self):
+        qmoe_finalize(self.y, self.topk_w, self.e2p, self.out)
+
+    def run(self, logits, x):
+        self.route(logits)
+        self.fc1(x)
+        self.fc2()
+        self.finalize()
+        return self.out

@@ -1,0 +1,207 @@
+/*
+ * qmoe.h -- C ABI of the FP4 weight-only MoE expert path for AMD MI355X (gfx950).
+ *
+ * The path is the one of "MoE and QMoE -- CUDA Operator Documentation",
+ * section 1: router (top-k softmax) -> permute by expert -> GEMM1 ->
+ * SwiGLU -> GEMM2 -> un-permute -> weighted sum, with FP4 (E2M1) weights and
+ * bf16 activations (W4A16).  Five calls cover it:
+ *
+ *   qmoe_route_topk           softmax top-k routing + expert maps
+ *   qmoe_fp4_gemv_fc1_swiglu  FC1 over the routed rows, fused SwiGLU
+ *   qmoe_fp4_gemv_fc2         FC2 over the routed rows
+ *   qmoe_finalize             weighted un-permute
+ *   qmoe_dequant_fp4          standalone FP4 -> bf16 weight dequant
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers named in a call are device pointers unless stated otherwise;
+ *   qmoe_fp4_weights and qmoe_swiglu are host structs whose members point to
+ *   device memory.  Every device pointer must be 16-byte aligned
+ *   (QMOE_EALIGN otherwise).  The caller owns every buffer; the library
+ *   allocates nothing, keeps no state between calls and never synchronises.
+ * - Work is enqueued on `stream` (a hipStream_t; 0 is the null stream) and is
+ *   asynchronous.  All argument checks run on the host before any launch; a
+ *   failed check returns its status and enqueues nothing.  QMOE_ELAUNCH
+ *   reports a launch error; device faults surface at the caller's next
+ *   synchronisation.
+ * - bf16 values are passed as their 16-bit patterns (uint16_t).
+ *
+ * Data layouts
+ * ------------
+ * FP4 weights of one FC layer, E experts, reduction length K, N outputs:
+ *   w      [E][K][N/2] uint8: byte (e,k,j) holds column 2j in its low nibble
+ *          and column 2j+1 in its high nibble (the [K, N/2] "2 per byte
+ *          along N" packing of the operator documentation, section 6.5).
+ *          A nibble is an E2M1 code: bit 3 sign, bits 2..1 exponent (bias 1),
+ *          bit 0 mantissa.
+ *   scales [E][K/B][N] uint8: one block scale per B consecutive k of a
+ *          column (the [e][k/group_size][n] order the decode GEMV reads,
+ *          section 9b.2).  NVFP4: B = 16, E4M3FN bytes (section 9b).
+ *          MXFP4: B = 32, E8M0 bytes (section 6.5).
+ *   gscale [E] float32 per-expert global scale; required for NVFP4, optional
+ *          for MXFP4 (NULL means 1.0).
+ *   weight(e,k,n) = e2m1(code) * scale(e, k/B, n) * gscale(e).
+ * FC1: K = hidden H, N = 2*I, columns interleaved (2j = gate, 2j+1 = linear).
+ * FC2: K = I, N = H.
+ */
+#ifndef QMOE_H
+#define QMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *hipStream_t;
+
+typedef enum {
+  QMOE_OK = 0,
+  QMOE_EINVAL = 1,        /* null pointer, non-positive size, k > E, missing NVFP4 global scale, bad enum */
+  QMOE_EUNSUPPORTED = 2,  /* valid request outside what the kernels cover (see each call)                */
+  QMOE_EALIGN = 3,        /* a device pointer is not 16-byte aligned                                       */
+  QMOE_EWORKSPACE = 4,    /* the workspace passed is smaller than the size the call needs                 */
+  QMOE_ELAUNCH = 5        /* the kernel launch failed                                                      */
+} qmoe_status;
+
+typedef enum {
+  QMOE_FMT_NVFP4 = 0,     /* E4M3FN block-16 scales, float32 per-expert global scale required */
+  QMOE_FMT_MXFP4 = 1      /* E8M0 block-32 scales, global scale optional (NULL = 1.0)         */
+} qmoe_fmt;
+
+typedef enum {
+  QMOE_PATH_AUTO = 0,     /* GEMV for T*k <= 64 expanded rows, GROUPED above                   */
+  QMOE_PATH_GEMV = 1,     /* FP4 decode GEMV; rejects T*k > 64 with QMOE_EUNSUPPORTED          */
+  QMOE_PATH_GROUPED = 2   /* MFMA bf16 grouped GEMM over LDS-dequantised weight tiles          */
+} qmoe_path;
+
+typedef struct {
+  const uint8_t *w;       /* [E][K][N/2] device */
+  const uint8_t *scales;  /* [E][K/B][N] device */
+  const float *gscale;    /* [E] device, or NULL (MXFP4 only) */
+  int32_t E, K, N;
+  int32_t fmt;            /* qmoe_fmt */
+} qmoe_fp4_weights;
+
+typedef struct {
+  float alpha, beta, limit;  /* SwiGLU(G, L) = G*sigmoid(alpha*G)*(L+beta), G = min(gate, limit), L = clamp(lin, -limit, limit) */
+} qmoe_swiglu;
+
+#define QMOE_MAX_EXPERTS 256
+#define QMOE_MAX_TOPK 8
+#define QMOE_GEMV_MAX_ROWS 64
+
+/*
+ * qmoe_route_topk -- softmax top-k routing and the per-expert permutation.
+ *
+ * Passages: operator documentation section 1 ("router (top-k softmax) ->
+ * permute by expert"); PR 31156 "[CUDA] Cut the MoE routing prologue/epilogue
+ * cost for small-batch decode" (register bitonic top-k per row with a stable
+ * packed key; expert maps ranked by wave ballots).
+ *
+ * logits     [T][E] float32 router logits.
+ * topk_idx   [T][k] int32 out: selected experts, largest logit first, equal
+ *            logits ordered by lower expert index, -0 equal to +0.
+ * topk_w     [T][k] float32 out: softmax over the k selected logits (sums to 1).
+ * expert_offsets [E+1] int32 out: exclusive prefix sum of per-expert row counts;
+ *            expert_offsets[E] = T*k.
+ * perm_to_expanded [T*k] int32 out: permuted row p -> expanded row r = t*k + j.
+ *            Rows are grouped by ascending expert, in ascending r inside an expert.
+ * expanded_to_perm [T*k] int32 out: the inverse map.
+ * Limits: 1 <= k <= min(E, 8), 1 <= E <= 256, T >= 1, T*k <= 2^24
+ * (QMOE_EUNSUPPORTED beyond E or k limits).  NaN logits give unspecified
+ * selections (but valid indices).
+ */
+qmoe_status qmoe_route_topk(const float *logits, int32_t T, int32_t E, int32_t k,
+                            int32_t *topk_idx, float *topk_w, int32_t *expert_offsets,
+                            int32_t *perm_to_expanded, int32_t *expanded_to_perm,
+                            hipStream_t stream);
+
+/*
+ * qmoe_fp4_gemv_fc1_swiglu -- FC1 of every routed row with fused SwiGLU.
+ *
+ * Passages: PR 31159 "[CUDA] Speed up the NVFP4 QMoE decode GEMV and enable it
+ * for MTP verify" (fused FP4 decode GEMV, expanded rows up to 64); operator
+ * documentation sections 8 (SwiGLU, interleaved fusion) and 9b.2 (block-size
+ * generic GEMV, scales[e][k/B][n]); section 12.1 (split-K SwiGLU: partials
+ * first, SwiGLU on the reduced sum).
+ *
+ * x          [T][K] bf16 activations (K = H).
+ * w1         FC1 weights, N = 2*I.
+ * expert_offsets, perm_to_expanded  as written by qmoe_route_topk (same T, k).
+ * act        SwiGLU parameters, or NULL for the standard SiLU(gate)*linear.
+ * h          [T*k][I] bf16 out, in permuted row order:
+ *            h[p][j] = bf16_rne(SwiGLU(u[p][2j], u[p][2j+1])),
+ *            u[p][n] = sum_k x[t(p)][k] * weight(e(p), k, n), accumulated in float32.
+ * ws, ws_bytes  workspace.  With ws == NULL the call writes the size it
+ *            needs to *ws_bytes and returns QMOE_OK without launching.
+ *            Otherwise *ws_bytes is the size of ws (QMOE_EWORKSPACE if too
+ *            small).  The workspace is scratch (split-K partial sums); its
+ *            contents on entry do not matter.  Calls that share a workspace
+ *            must be ordered (same stream).
+ * path       AUTO, GEMV (T*k <= 64) or GROUPED.
+ * Limits: K % B == 0, N % 32 == 0, E <= 256, k <= 8 (QMOE_EUNSUPPORTED).
+ */
+qmoe_status qmoe_fp4_gemv_fc1_swiglu(const uint16_t *x, int32_t T, int32_t k,
+                                     const qmoe_fp4_weights *w1,
+                                     const int32_t *expert_offsets, const int32_t *perm_to_expanded,
+                                     const qmoe_swiglu *act, uint16_t *h,
+                                     void *ws, size_t *ws_bytes, qmoe_path path,
+                                     hipStream_t stream);
+
+/*
+ * qmoe_fp4_gemv_fc2 -- FC2 of every routed row.
+ *
+ * Passages: PR 31159 (the plain FP4 decode GEMV, "moe_gemv_kernel"); operator
+ * documentation section 9b.2.
+ *
+ * h          [T*k][K] bf16 in permuted row order (K = I), as written by
+ *            qmoe_fp4_gemv_fc1_swiglu.
+ * w2         FC2 weights, N = H.
+ * y_rows     [T*k][N] float32 out, permuted row order:
+ *            y[p][n] = sum_i h[p][i] * weight(e(p), i, n), accumulated in float32.
+ * T, k       token count and top-k of the routing (T*k rows; at most T rows
+ *            per expert).  Workspace and path as for FC1.
+ */
+qmoe_status qmoe_fp4_gemv_fc2(const uint16_t *h, int32_t T, int32_t k,
+                              const qmoe_fp4_weights *w2, const int32_t *expert_offsets,
+                              float *y_rows, void *ws, size_t *ws_bytes, qmoe_path path,
+                              hipStream_t stream);
+
+/*
+ * qmoe_finalize -- weighted un-permute.
+ *
+ * Passages: operator documentation section 1 ("un-permute -> weighted sum");
+ * PR 31156 (finalize stages the routing metadata once per block and splits
+ * columns over blocks).
+ *
+ * out[t][n] = bf16_rne( sum_{j<k} topk_w[t][j] * y_rows[expanded_to_perm[t*k+j]][n] ),
+ * summed in float32 in ascending j.  y_rows [T*k][H] float32, topk_w [T][k],
+ * out [T][H] bf16.  Limits: H % 8 == 0, k <= 8.
+ */
+qmoe_status qmoe_finalize(const float *y_rows, const float *topk_w, const int32_t *expanded_to_perm,
+                          int32_t T, int32_t k, int32_t H, uint16_t *out, hipStream_t stream);
+
+/*
+ * qmoe_dequant_fp4 -- FP4 weights to bf16, transposed to [E][N][K].
+ *
+ * Passages: PR 31349 "[CUDA] Coalesce QMoE MXFP4/NVFP4 weight dequantization"
+ * (tiled, coalesced dequant; one kernel for both scale codecs; no integer
+ * division); operator documentation sections 4.3 and 6.5.
+ *
+ * out[e][n][k] = bf16_rne( f32_rne( e2m1(code) * scale ) * gscale(e) ); the
+ * product e2m1*scale is exact, so the output is bit-exact.  MXFP4 without a
+ * global scale is exact in bf16.
+ * Limits: K % 64 == 0, N % 256 == 0 (QMOE_EUNSUPPORTED otherwise).
+ */
+qmoe_status qmoe_dequant_fp4(const qmoe_fp4_weights *w, uint16_t *out, hipStream_t stream);
+
+/* Static string naming a status code. */
+const char *qmoe_status_str(qmoe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMOE_H */

@@ -1,0 +1,128 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects bad arguments with exact status codes before
+any launch (every call here returns during host-side validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmoe.h")
+
+
+@pytest.fixture(scope="module")
+def q():
+    import fp4_weight_only_amd
+    return fp4_weight_only_amd
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmoe_\w+)\s*\(", src)))
+
+
+def test_header_declarations_are_exported(q):
+    names = declared_functions()
+    assert set(names) == set(q.EXPORTS), names
+    for n in names:
+        assert hasattr(q.lib, n), n
+
+
+def test_exported_symbols_in_dynamic_table(q):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
+    for n in declared_functions():
+        assert re.search(rf"\bT {n}$", out, flags=re.M), n
+
+
+def test_status_strings(q):
+    for s in range(6):
+        assert q.lib.qmoe_status_str(s).startswith(b"QMOE_")
+
+
+A = 4096          # an aligned placeholder address (never dereferenced: validation fails first)
+MIS = 4096 + 4    # misaligned placeholder
+
+
+def weights(q, E=8, K=256, N=256, fmt=0, w=A, s=A, g=A):
+    return q.Fp4WeightsC(w, s, g, E, K, N, fmt)
+
+
+def route(q, logits=A, T=1, E=8, k=2, idx=A, w=A, off=A, p2e=A, e2p=A):
+    return q.lib.qmoe_route_topk(logits, T, E, k, idx, w, off, p2e, e2p, None)
+
+
+def test_route_validation(q):
+    assert route(q, logits=None) == q.QMOE_EINVAL
+    assert route(q, T=0) == q.QMOE_EINVAL
+    assert route(q, k=0) == q.QMOE_EINVAL
+    assert route(q, k=9, E=8) == q.QMOE_EINVAL            # k > E
+    assert route(q, idx=MIS) == q.QMOE_EALIGN
+    assert route(q, E=257, k=2) == q.QMOE_EUNSUPPORTED
+    assert route(q, E=64, k=9) == q.QMOE_EUNSUPPORTED
+
+
+def fc1(q, wc, T=1, k=2, x=A, off=A, p2e=A, h=A, ws=None, nbytes=0, path=0):
+    n = ctypes.c_size_t(nbytes)
+    st = q.lib.qmoe_fp4_gemv_fc1_swiglu(x, T, k, ctypes.byref(wc), off, p2e, None, h, ws, ctypes.byref(n), path, None)
+    return st, n.value
+
+
+def fc2(q, wc, T=1, k=2, h=A, off=A, y=A, ws=None, nbytes=0, path=0):
+    n = ctypes.c_size_t(nbytes)
+    st = q.lib.qmoe_fp4_gemv_fc2(h, T, k, ctypes.byref(wc), off, y, ws, ctypes.byref(n), path, None)
+    return st, n.value
+
+
+def test_fc_validation(q):
+    assert fc1(q, weights(q, g=0))[0] == q.QMOE_EINVAL                  # NVFP4 needs a global scale
+    assert fc1(q, weights(q, fmt=1, g=0))[0] == q.QMOE_OK               # MXFP4 does not (size query)
+    assert fc1(q, weights(q, fmt=7))[0] == q.QMOE_EINVAL
+    assert fc1(q, weights(q), x=None)[0] == q.QMOE_EINVAL
+    assert fc1(q, weights(q, w=MIS))[0] == q.QMOE_EALIGN
+    assert fc1(q, weights(q), x=MIS)[0] == q.QMOE_EALIGN
+    assert fc1(q, weights(q, K=200))[0] == q.QMOE_EUNSUPPORTED          # K % 16
+    assert fc1(q, weights(q, fmt=1, K=272))[0] == q.QMOE_EUNSUPPORTED   # K % 32 for MXFP4
+    assert fc1(q, weights(q, N=240))[0] == q.QMOE_EUNSUPPORTED          # N % 32
+    assert fc1(q, weights(q, E=300), k=2)[0] == q.QMOE_EUNSUPPORTED
+    assert fc1(q, weights(q), k=9)[0] == q.QMOE_EINVAL                  # k > E
+    assert fc1(q, weights(q), path=5)[0] == q.QMOE_EINVAL
+    assert fc2(q, weights(q), y=None)[0] == q.QMOE_EINVAL
+
+
+def test_gemv_row_window(q):
+    st, _ = fc1(q, weights(q, E=64), T=8, k=8, path=q.QMOE_PATH_GEMV)       # 64 rows
+    assert st == q.QMOE_OK
+    st, _ = fc1(q, weights(q, E=64), T=13, k=5, path=q.QMOE_PATH_GEMV)      # 65 rows
+    assert st == q.QMOE_EUNSUPPORTED
+    st, _ = fc2(q, weights(q, E=64), T=9, k=8, path=q.QMOE_PATH_GEMV)
+    assert st == q.QMOE_EUNSUPPORTED
+
+
+def test_workspace_query_and_too_small(q):
+    st, need = fc1(q, weights(q, E=256, K=2048, N=1536), T=4, k=8)
+    assert st == q.QMOE_OK and need > 0
+    # 32 rows x 1536 columns x 8 k-chunks of float32 partials, plus counters
+    assert need >= 8 * 32 * 1536 * 4
+    st, _ = fc1(q, weights(q, E=256, K=2048, N=1536), T=4, k=8, ws=A, nbytes=need - 1)
+    assert st == q.QMOE_EWORKSPACE
+    st, need2 = fc2(q, weights(q, E=256, K=768, N=2048), T=4, k=8)
+    assert st == q.QMOE_OK and need2 > 0
+
+
+def test_finalize_and_dequant_validation(q):
+    L = q.lib
+    assert L.qmoe_finalize(None, A, A, 1, 2, 256, A, None) == q.QMOE_EINVAL
+    assert L.qmoe_finalize(A, A, A, 1, 9, 256, A, None) == q.QMOE_EUNSUPPORTED
+    assert L.qmoe_finalize(A, A, A, 1, 2, 250, A, None) == q.QMOE_EUNSUPPORTED
+    assert L.qmoe_finalize(A, MIS, A, 1, 2, 256, A, None) == q.QMOE_EALIGN
+    wc = weights(q, K=100)
+    assert L.qmoe_dequant_fp4(ctypes.byref(wc), A, None) == q.QMOE_EUNSUPPORTED
+    wc = weights(q, K=256, N=128)
+    assert L.qmoe_dequant_fp4(ctypes.byref(wc), A, None) == q.QMOE_EUNSUPPORTED
+    wc = weights(q, g=0)
+    assert L.qmoe_dequant_fp4(ctypes.byref(wc), A, None) == q.QMOE_EINVAL
+    wc = weights(q)
+    assert L.qmoe_dequant_fp4(ctypes.byref(wc), MIS, None) == q.QMOE_EALIGN

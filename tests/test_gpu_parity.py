@@ -1,0 +1,283 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Bit-exact: routing indices, expert maps, dequantized bf16.  Floating-point
+outputs: the oracle.tolerance rule.  Stage-wise checks feed the oracle the
+GPU's own previous-stage outputs; end-to-end checks run the oracle from the
+inputs alone.  Each case prints its name before it touches the GPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import bf16_dev, bf16_host, layer_dev, print_case, to_dev, weights_dev
+from oracle import codecs, dequant, moe, route, tolerance
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import fp4_weight_only_amd  # noqa: F401  (raises if the library is not built)
+
+
+# Shapes the oracle finishes in seconds that still span several tiles, several
+# k chunks and ragged tails (N not a multiple of 256, K not of 256).
+SMALL = [
+    synth.shrink(synth.TINY, seed=0),
+    synth.shrink(synth.DECODE, E=37, T=7, k=5, H=320, I=144, seed=1),         # 35 rows, ragged N/K
+    synth.shrink(synth.MTP8, E=64, T=8, k=8, H=512, I=272, seed=2),           # 64 rows, hot experts m=8
+    synth.shrink(synth.MX_DECODE, E=40, T=8, k=8, H=544, I=160, seed=3),      # MXFP4, ragged
+    synth.shrink(synth.DECODE, E=16, T=64, k=1, H=256, I=64, seed=4),         # m up to 64 per expert
+    synth.shrink(synth.MX_DECODE, E=4, T=16, k=4, H=1024, I=512, seed=5),     # every expert has 16 rows
+]
+FULL = [synth.TINY, synth.DECODE, synth.MTP4, synth.MTP8]
+
+
+def run_gpu_layer(L, act=None):
+    layer, logits, x = layer_dev(L, act=act)
+    print_case("layer", L.cfg.name)
+    layer.run(logits, x)
+    torch.cuda.synchronize()
+    return dict(idx=layer.topk_idx.cpu().numpy(), w=layer.topk_w.cpu().numpy().astype(np.float64),
+                offsets=layer.offsets.cpu().numpy(), p2e=layer.p2e.cpu().numpy(), e2p=layer.e2p.cpu().numpy(),
+                h=bf16_host(layer.h), y=layer.y.cpu().numpy().astype(np.float64),
+                out=codecs.bf16_to_f64(bf16_host(layer.out)))
+
+
+def assert_close(name, gpu, ref):
+    ok, rep = tolerance.check(gpu, ref)
+    print(name, rep, flush=True)
+    assert ok, (name, rep)
+
+
+def check_layer(L, act=None, cols1=None, cols2=None):
+    c = L.cfg
+    g = run_gpu_layer(L, act)
+    oact = None if act is None else dict(alpha=act[0], beta=act[1], limit=act[2])
+    # routing and maps: bit-exact
+    idx, wts = route.route_topk(L.logits, c.k)
+    off, p2e, e2p = route.expert_maps(idx, c.E)
+    assert np.array_equal(g["idx"], idx)
+    assert np.array_equal(g["offsets"], off)
+    assert np.array_equal(g["p2e"], p2e)
+    assert np.array_equal(g["e2p"], e2p)
+    assert_close("topk_w", g["w"], wts)
+    # FC1 stage (inputs identical to the oracle's)
+    h_ref, u_ref = moe.fc1_swiglu(L.x, c.k, L.w1, L.s1, L.g1, c.fmt, off, p2e, oact, cols=cols1)
+    hsel = slice(None) if cols1 is None else cols1
+    assert_close("h", codecs.bf16_to_f64(g["h"])[:, hsel], codecs.bf16_to_f64(h_ref)[:, hsel])
+    # FC2 stage, fed the GPU's h
+    y_ref = moe.fc2(g["h"], L.w2, L.s2, L.g2, c.fmt, off, cols=cols2)
+    ysel = slice(None) if cols2 is None else cols2
+    assert_close("y", g["y"][:, ysel], y_ref)
+    # finalize stage, fed the GPU's y and weights
+    out_ref = moe.finalize(g["y"], g["w"], g["e2p"], c.T, c.k)
+    assert_close("out(stage)", g["out"], out_ref)
+    # end to end
+    if cols1 is None and cols2 is None:
+        r = moe.layer(L, oact)
+        assert_close("out(e2e)", g["out"], r["out"])
+    return g
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_layer_small(cfg):
+    check_layer(synth.layer_inputs(cfg))
+
+
+@pytest.mark.parametrize("cfg", FULL, ids=lambda c: c.name)
+def test_layer_full(cfg):
+    check_layer(synth.layer_inputs(cfg))
+
+
+def test_layer_mxfp4_decode_full_sampled():
+    L = synth.layer_inputs(synth.MX_DECODE)
+    rng = np.random.default_rng(0)
+    cols1 = np.sort(rng.choice(L.cfg.I, 160, replace=False))
+    cols2 = np.sort(rng.choice(L.cfg.H, 320, replace=False))
+    check_layer(L, cols1=cols1, cols2=cols2)
+
+
+def test_gptoss_swiglu_variant():
+    cfg = synth.shrink(synth.DECODE, E=16, T=4, k=4, H=256, I=128, seed=7)
+    L = synth.layer_inputs(cfg)
+    check_layer(L, act=(1.702, 1.0, 7.0))
+
+
+def test_route_ties_and_signed_zero():
+    import fp4_weight_only_amd as q
+    lg = np.zeros((6, 256), np.float32)
+    lg[0, :] = 0.0
+    lg[1, ::2] = -0.0
+    lg[2, [5, 9, 200, 3]] = 2.5
+    lg[3, :] = np.float32(-1e30)
+    lg[3, 255] = np.float32(-np.inf)
+    lg[4, :] = np.arange(256, dtype=np.float32)[::-1] * 0 + 1.0
+    lg[5, 17] = np.inf
+    T, E, k = lg.shape[0], 256, 8
+    d = dict(idx=torch.empty((T, k), dtype=torch.int32, device="cuda"),
+             w=torch.empty((T, k), dtype=torch.float32, device="cuda"),
+             off=torch.empty((E + 1,), dtype=torch.int32, device="cuda"),
+             p2e=torch.empty((T * k,), dtype=torch.int32, device="cuda"),
+             e2p=torch.empty((T * k,), dtype=torch.int32, device="cuda"))
+    print_case("route ties")
+    q.qmoe_route_topk(to_dev(lg), k, d["idx"], d["w"], d["off"], d["p2e"], d["e2p"])
+    torch.cuda.synchronize()
+    idx, w = route.route_topk(lg, k)
+    assert np.array_equal(d["idx"].cpu().numpy(), idx)
+    gw = d["w"].cpu().numpy()
+    fin = np.isfinite(w)
+    np.testing.assert_allclose(gw[:5], w[:5], rtol=1e-6)
+    off, p2e, e2p = route.expert_maps(idx, E)
+    assert np.array_equal(d["off"].cpu().numpy(), off)
+    assert np.array_equal(d["p2e"].cpu().numpy(), p2e)
+    assert fin[:5].all()
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (3, 5, 5), (512, 256, 8), (100, 200, 3), (4096, 256, 1)])
+def test_route_shapes(T, E, k):
+    import fp4_weight_only_amd as q
+    rng = np.random.default_rng(T * 7 + E)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    lg[:, rng.integers(0, E, 3)] += 1.0  # some duplicates and skew
+    d = dict(idx=torch.empty((T, k), dtype=torch.int32, device="cuda"),
+             w=torch.empty((T, k), dtype=torch.float32, device="cuda"),
+             off=torch.empty((E + 1,), dtype=torch.int32, device="cuda"),
+             p2e=torch.empty((T * k,), dtype=torch.int32, device="cuda"),
+             e2p=torch.empty((T * k,), dtype=torch.int32, device="cuda"))
+    print_case("route", T, E, k)
+    q.qmoe_route_topk(to_dev(lg), k, d["idx"], d["w"], d["off"], d["p2e"], d["e2p"])
+    torch.cuda.synchronize()
+    idx, w = route.route_topk(lg, k)
+    assert np.array_equal(d["idx"].cpu().numpy(), idx)
+    assert_close("topk_w", d["w"].cpu().numpy(), w)
+    off, p2e, e2p = route.expert_maps(idx, E)
+    assert np.array_equal(d["off"].cpu().numpy(), off)
+    assert np.array_equal(d["p2e"].cpu().numpy(), p2e)
+    assert np.array_equal(d["e2p"].cpu().numpy(), e2p)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_every_code_in_every_nibble_through_the_gemv(fmt):
+    """Closed form: one nonzero code per column, so u = x_k * e2m1 * scale * g exactly."""
+    import fp4_weight_only_amd as q
+    from fp4_weight_only_amd.layer import MoELayer
+    B = 16 if fmt == "nvfp4" else 32
+    K, N = 256, 512
+    rng = np.random.default_rng(11)
+    w = np.zeros((1, K, N // 2), np.uint8)
+    rows = rng.integers(0, K, N)
+    codes = np.arange(N) % 16                        # every code in every nibble position
+    for n in range(N):
+        w[0, rows[n], n // 2] |= np.uint8(codes[n] << (4 * (n % 2)))
+    if fmt == "nvfp4":
+        s = np.full((1, K // B, N), 0x38, np.uint8)  # 1.0
+        g = np.array([0.75], np.float32)
+    else:
+        s = np.full((1, K // B, N), 127, np.uint8)
+        g = None
+    x = synth.to_bf16_bits((rng.standard_normal((1, K)) * 3).astype(np.float32))
+    wd = weights_dev(w, s, g, fmt)
+    w2 = weights_dev(np.zeros((1, N // 2, 16), np.uint8), np.full((1, N // 2 // B, 32), 0x38 if fmt == "nvfp4" else 127, np.uint8),
+                     g, fmt)
+    layer = MoELayer(1, 1, 1, 32, N // 2, wd, w2)
+    print_case("closed form", fmt)
+    layer.route(to_dev(np.zeros((1, 1), np.float32)))
+    layer.fc1(bf16_dev(x))
+    torch.cuda.synchronize()
+    h = codecs.bf16_to_f64(bf16_host(layer.h))[0]
+    x64 = codecs.bf16_to_f64(x)[0]
+    u = x64[rows] * codecs.e2m1_value(codes) * (0.75 if fmt == "nvfp4" else 1.0)
+    u32 = u.astype(np.float32).astype(np.float64)   # the exact product rounded once
+    href = codecs.bf16_from_f64(moe.swiglu(u32[0::2], u32[1::2]))
+    got = bf16_host(layer.h)[0]
+    # products are exact; only SwiGLU's exp differs from float64 in the last float32 bits.
+    # Values are compared (a gate of -0 summed onto a +0 accumulator is +0: same value).
+    ok, rep = tolerance.check(h, codecs.bf16_to_f64(href))
+    assert ok, rep
+    diff = codecs.bf16_to_f64(got) != codecs.bf16_to_f64(href)
+    assert np.count_nonzero(diff) <= 2, np.nonzero(diff)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_dequant_small_exhaustive_scales(fmt):
+    import fp4_weight_only_amd as q
+    B = 16 if fmt == "nvfp4" else 32
+    E, K, N = 2, 64 * 8, 256 * 2
+    rng = np.random.default_rng(12)
+    w = synth.packed_codes(synth.stream(1, 2), (E, K, N // 2))
+    s = (np.arange(E * (K // B) * N) % 256).astype(np.uint8).reshape(E, K // B, N)   # every scale byte
+    if fmt == "nvfp4":
+        s[s == 0x7F] = 0x38
+        s[s == 0xFF] = 0xB8
+        g = np.array([1.3, 0.6], np.float32)
+    else:
+        s[s == 255] = 127
+        g = None
+    out = torch.empty((E, N, K), dtype=torch.bfloat16, device="cuda")
+    print_case("dequant small", fmt)
+    q.qmoe_dequant_fp4(weights_dev(w, s, g, fmt), out)
+    torch.cuda.synchronize()
+    ref = dequant.dequant_bf16(w, s, g, fmt)
+    assert np.array_equal(bf16_host(out), ref)
+    _ = rng
+
+
+def test_dequant_full_config():
+    import fp4_weight_only_amd as q
+    c = synth.DEQUANT
+    w, s, g = synth.dequant_inputs(c)
+    out = torch.empty((c.E, c.N, c.K), dtype=torch.bfloat16, device="cuda")
+    print_case("dequant full", c.name)
+    q.qmoe_dequant_fp4(weights_dev(w, s, g, c.fmt), out)
+    torch.cuda.synchronize()
+    got = bf16_host(out)
+    for e in range(c.E):                       # expert by expert to bound host memory
+        ref = dequant.dequant_bf16(w[e:e + 1], s[e:e + 1], None, c.fmt)[0]
+        assert np.array_equal(got[e], ref), e
+
+
+def test_gemv_window_and_paths():
+    import fp4_weight_only_amd as q
+    cfg = synth.shrink(synth.DECODE, E=32, T=8, k=8, H=256, I=64, seed=9)
+    L = synth.layer_inputs(cfg)
+    check_layer(L)                                       # 64 rows: GEMV window edge
+    cfg65 = synth.shrink(synth.DECODE, E=32, T=13, k=5, H=256, I=64, seed=9)   # 65 rows
+    L65 = synth.layer_inputs(cfg65)
+    c = L65.cfg
+    w1 = weights_dev(L65.w1, L65.s1, L65.g1, c.fmt)
+    with pytest.raises(q.QmoeError) as ei:          # the size query already refuses 65 rows on GEMV
+        q.fc_workspace_bytes(1, c.T, c.k, w1, q.QMOE_PATH_GEMV)
+    assert ei.value.status == q.QMOE_EUNSUPPORTED
+    R = c.T * c.k
+    off = torch.zeros((c.E + 1,), dtype=torch.int32, device="cuda")
+    p2e = torch.zeros((R,), dtype=torch.int32, device="cuda")
+    h = torch.empty((R, c.I), dtype=torch.bfloat16, device="cuda")
+    ws = q.alloc_workspace(1 << 20)
+    with pytest.raises(q.QmoeError) as ei:          # refused on the host, nothing launched
+        q.qmoe_fp4_gemv_fc1_swiglu(bf16_dev(L65.x), c.k, w1, off, p2e, h, ws, path=q.QMOE_PATH_GEMV)
+    assert ei.value.status == q.QMOE_EUNSUPPORTED
+
+
+def test_determinism_and_poisoned_buffers():
+    cfg = synth.shrink(synth.MTP8, E=48, T=8, k=8, H=512, I=384, seed=13)
+    L = synth.layer_inputs(cfg)
+    layer, logits, x = layer_dev(L)
+    print_case("determinism", cfg.name)
+    layer.run(logits, x)
+    torch.cuda.synchronize()
+    first = [bf16_host(layer.h).copy(), layer.y.cpu().numpy().copy(), bf16_host(layer.out).copy()]
+    poison = [float("nan"), float("inf"), -float("inf"), 1e30]
+    for pv in poison:
+        layer.h.fill_(pv)
+        layer.y.fill_(pv)
+        layer.out.fill_(pv)
+        layer.ws.view(torch.float32).fill_(pv)      # the workspace is pure scratch
+        layer.run(logits, x)
+        torch.cuda.synchronize()
+        again = [bf16_host(layer.h), layer.y.cpu().numpy(), bf16_host(layer.out)]
+        for a, b in zip(first, again):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
