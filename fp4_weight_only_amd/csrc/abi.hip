@@ -2,7 +2,7 @@
 // dispatch to the gfx950 kernels.
 #include <math.h>
 
-#include "../../include/qmoe.h"
+#include "qmoe.h"
 #include "qmoe_internal.h"
 
 using namespace qmoe;
@@ -61,7 +61,7 @@ qmoe_status resolve_path(qmoe_path path, int32_t rows, qmoe_path *out) {
 
 qmoe_status run_gemv(GemvArgs &a, const qmoe_fp4_weights *w, int max_rows, void *ws, size_t *ws_bytes,
                      hipStream_t stream) {
-  const size_t need = gemv_workspace_bytes(a.rows, w->E, w->K, w->N);
+  const size_t need = gemv_workspace_bytes(a.rows, max_rows, w->E, w->K, w->N);
   if (!ws_bytes) return QMOE_EINVAL;
   if (!ws) {
     *ws_bytes = need;
@@ -75,7 +75,7 @@ qmoe_status run_gemv(GemvArgs &a, const qmoe_fp4_weights *w, int max_rows, void 
   a.E = w->E;
   a.K = w->K;
   a.N = w->N;
-  gemv_plan(a, ws);
+  gemv_plan(a, max_rows, ws);
   return check_launch(launch_fp4_gemv(a, w->fmt == QMOE_FMT_NVFP4 ? 0 : 1, max_rows, stream));
 }
 

@@ -8,12 +8,14 @@
 // FC2 writes float32 y.
 //
 // gfx950 design:
-// * A workgroup is 4 waves on one 256-column tile and a 256-row k chunk of
-//   one routed expert.  In a wave, lanes 0..31 each own 8 consecutive columns
-//   (one dword per k row, so 32 lanes read one 128-byte line of the row) and
-//   the two 32-lane halves own different 32-row k ranges.  All 32 dword loads
-//   of a lane are issued before any decode so the weight stream has many
-//   requests in flight.
+// * A workgroup covers one 256-column tile of one routed expert and a k
+//   chunk of W*64 rows (W = 4 waves; fewer when K is shorter).  In a wave, lanes 0..31 each own 8 consecutive
+//   columns (one dword per k row: 32 lanes read one 128-byte line of a row)
+//   and the two 32-lane halves own consecutive 32-row k ranges.
+// * Weights and scales are read with buffer loads from a per-expert buffer
+//   resource: the row offset is a scalar (no per-load vector address math)
+//   and rows past K or columns past N fall outside the resource and read
+//   as zero.  All 32 loads of a lane are issued before any decode.
 // * Decode: two k rows of one dword each become K-paired bf16x2 registers by
 //   bit assembly (no table); v_dot2c_f32_bf16 multiplies a K pair of
 //   activations by a K pair of weights.  Products are summed per scale block
@@ -24,23 +26,26 @@
 //   largest |a|, which keeps every product a normal float32; the group's
 //   partial is multiplied back by 2^(126-P).  Power-of-two scaling commutes
 //   with rounding, so this changes no result.
-// * The 8 k groups of a workgroup reduce through LDS in a fixed order.  When
-//   K spans several chunks (split-K) each workgroup writes g * partial to the
-//   workspace and a second, small kernel sums the chunks in order and runs
-//   the epilogue (the two-pass split-K SwiGLU of section 12.1).  Kernel
-//   boundaries order the passes: no fences, no atomics, deterministic sums.
+// * Split-K inside the workgroup: the two halves of a wave add through a
+//   lane swap, then the W waves through LDS, in a fixed order.  When K spans
+//   several chunks each workgroup writes g * partial to the workspace and a
+//   second, small kernel sums the chunks in order and runs the epilogue (the
+//   two-pass split-K SwiGLU of section 12.1); kernel boundaries order the
+//   passes: no fences, no atomics, deterministic sums.
 // * Work items (expert slot, column tile) are spread round-robin over the 8
 //   XCDs and all k chunks of an item land on the same XCD.
 // * The routed experts are found on the device from expert_offsets (wave
 //   ballots); grids are sized for the worst case and idle slots exit.  Rows
-//   of an expert are processed in passes of one or two rows.
+//   of an expert are processed in passes of one row (single-token batches)
+//   or of two rows.
 #include "device_common.h"
 #include "qmoe_internal.h"
 
 namespace qmoe {
 
-constexpr int kThreads = 256;
-constexpr int kKGroups = 8;  // 4 waves x 2 halves
+constexpr int kMaxChunkK = kGemvMaxWaves * kGemvWaveK;
+constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past any resource: loads return 0
+constexpr int kBufNontemporal = 2;            // cache policy: streaming (nt)
 
 // Finds the expert holding the s-th non-empty row range.  Every lane gets
 // the same answer; returns -1 if fewer than s+1 experts have rows.
@@ -74,7 +79,7 @@ __device__ __forceinline__ int find_slot_expert(const int32_t *__restrict__ off,
 }
 
 template <int FMT>
-__device__ __forceinline__ void decode_scales(uint2 sb, float (&sc)[8]) {
+__device__ __forceinline__ void decode_scales(u32x2_t sb, float (&sc)[8]) {
   if constexpr (FMT == 0) {
     sc[0] = e4m3_to_f32<0>(sb.x);
     sc[1] = e4m3_to_f32<1>(sb.x);
@@ -101,16 +106,16 @@ __device__ __forceinline__ float swiglu(float gate, float lin, float alpha, floa
 
 template <int MRMAX>
 struct Smem {
-  uint16_t xs[MRMAX][kGemvChunkK];
-  int pexp[MRMAX][kKGroups];
-  float red[kKGroups][MRMAX][kGemvTileN];
+  uint16_t xs[MRMAX][kMaxChunkK];                 // pre-scaled activations of the chunk
+  int pexp[MRMAX][kMaxChunkK / kGemvLaneK];       // pre-scale exponent per (row, 32-k group)
+  float red[kGemvMaxWaves][MRMAX][kGemvTileN];    // per-wave partial sums
 };
 
-// Decode + dot2 over the lane's 32 k rows for MR staged rows; leaves the
-// group partials (already multiplied back by 2^(126-P)) in LDS.
+// Decode + dot2 over the lane's 32 k rows for MR staged rows; the wave's
+// partial (halves added, multiplied back by 2^(126-P)) goes to LDS.
 template <int FMT, int MR, int MRMAX>
-__device__ __forceinline__ void lane_dot(Smem<MRMAX> &sm, const uint32_t (&A)[kGemvLaneK], const uint2 (&SB)[2], int g,
-                                         int nl) {
+__device__ __forceinline__ void lane_dot(Smem<MRMAX> &sm, const uint32_t (&A)[kGemvLaneK], const u32x2_t (&SB)[2],
+                                         int g, int wave, int lane) {
   constexpr int B = (FMT == 0) ? 16 : 32;
   constexpr int NBLK = kGemvLaneK / B;
   float acc[MR][8];
@@ -120,6 +125,20 @@ __device__ __forceinline__ void lane_dot(Smem<MRMAX> &sm, const uint32_t (&A)[kG
     for (int c = 0; c < 8; ++c) acc[r][c] = 0.f;
 #pragma unroll
   for (int b = 0; b < NBLK; ++b) {
+    // One row: the activation K pairs of this scale block are read once up
+    // front.  Two rows: read per K pair (a preload would cost ~100 VGPRs).
+    constexpr bool kPre = (MR == 1);
+    uint32_t xq[kPre ? B / 2 : 1];
+    if constexpr (kPre) {
+#pragma unroll
+      for (int q = 0; q < B / 8; ++q) {
+        const u32x4_t v = *(const u32x4_t *)&sm.xs[0][g * kGemvLaneK + b * B + q * 8];
+        xq[4 * q + 0] = v.x;
+        xq[4 * q + 1] = v.y;
+        xq[4 * q + 2] = v.z;
+        xq[4 * q + 3] = v.w;
+      }
+    }
     float bs[MR][8];
 #pragma unroll
     for (int r = 0; r < MR; ++r)
@@ -129,14 +148,21 @@ __device__ __forceinline__ void lane_dot(Smem<MRMAX> &sm, const uint32_t (&A)[kG
     for (int kp = 0; kp < B / 2; ++kp) {
       uint32_t w[8];
       e2m1_kpair_to_bf16x2(A[b * B + 2 * kp], A[b * B + 2 * kp + 1], w);
-      const int kloc = g * kGemvLaneK + b * B + 2 * kp;
 #pragma unroll
       for (int r = 0; r < MR; ++r) {
-        const uint32_t xp = *(const uint32_t *)&sm.xs[r][kloc];
+        const uint32_t xp =
+            kPre ? xq[kPre ? kp : 0] : *(const uint32_t *)&sm.xs[r][g * kGemvLaneK + b * B + 2 * kp];
 #pragma unroll
         for (int c = 0; c < 8; ++c) bs[r][c] = dot2_bf16(xp, w[c], bs[r][c]);
       }
-      // keep each K pair's decode next to its dot2s: bounds the live weights to 8 registers
+      // Keep each K pair's decode next to its dot2s (bounds the live decoded
+      // weights to 8 registers): the empty asm pins the partial sums here so
+      // no dot2 is sunk towards its later use, and the barrier stops the
+      // scheduler from hoisting the next decode.
+#pragma unroll
+      for (int r = 0; r < MR; ++r)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) asm volatile("" : "+v"(bs[r][c]));
       __builtin_amdgcn_sched_barrier(0);
     }
     float sc[8];
@@ -146,13 +172,19 @@ __device__ __forceinline__ void lane_dot(Smem<MRMAX> &sm, const uint32_t (&A)[kG
 #pragma unroll
       for (int c = 0; c < 8; ++c) acc[r][c] = fmaf(sc[c], bs[r][c], acc[r][c]);
   }
+  const int nl = lane & 31;
 #pragma unroll
   for (int r = 0; r < MR; ++r) {
     const int sh = 126 - sm.pexp[r][g];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[r][c] = ldexpf(acc[r][c], sh);
-    *(float4 *)&sm.red[g][r][nl * 8] = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
-    *(float4 *)&sm.red[g][r][nl * 8 + 4] = make_float4(acc[r][4], acc[r][5], acc[r][6], acc[r][7]);
+    for (int c = 0; c < 8; ++c) {
+      const float v = ldexpf(acc[r][c], sh);
+      acc[r][c] = v + __shfl_xor(v, 32);  // lower half + upper half, same order in every lane pair
+    }
+    if (lane < 32) {
+      *(float4 *)&sm.red[wave][r][nl * 8] = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
+      *(float4 *)&sm.red[wave][r][nl * 8 + 4] = make_float4(acc[r][4], acc[r][5], acc[r][6], acc[r][7]);
+    }
   }
 }
 
@@ -163,8 +195,12 @@ __device__ __forceinline__ void store_fc1(const GemvArgs &a, int p, int col, flo
     a.out_bf16[(size_t)p * (a.N >> 1) + (col >> 1)] = (uint16_t)bf16_rne(swiglu(u, partner, a.alpha, a.beta, a.limit));
 }
 
+// Both row modes use the same workgroup size.
+template <int MRMAX>
+constexpr int max_waves() { return kGemvMaxWaves; }
+
 template <int FMT, int MRMAX>
-__global__ __launch_bounds__(kThreads) void fp4_gemv_kernel(GemvArgs a) {
+__global__ __launch_bounds__(max_waves<MRMAX>() * 64) void fp4_gemv_kernel(GemvArgs a) {
   constexpr int B = (FMT == 0) ? 16 : 32;
   constexpr int NBLK = kGemvLaneK / B;
   __shared__ __attribute__((aligned(16))) Smem<MRMAX> sm;
@@ -172,6 +208,8 @@ __global__ __launch_bounds__(kThreads) void fp4_gemv_kernel(GemvArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = lane_id();
+  const int W = a.waves;
+  const int KC = W * kGemvWaveK;
 
   // Work item: XCD-aware decode of the linear workgroup id.
   const int L = blockIdx.x;
@@ -187,101 +225,97 @@ __global__ __launch_bounds__(kThreads) void fp4_gemv_kernel(GemvArgs a) {
   const int row0 = a.offsets[e];
   const int m = a.offsets[e + 1] - row0;
 
-  // ---- issue the weight and scale loads of this lane -----------------------
+  // ---- weight and scale loads of this lane ----------------------------------
   const int nl = lane & 31;
-  const int kh = lane >> 5;
-  const int g = wave * 2 + kh;  // k group 0..7
+  const int g = wave * 2 + (lane >> 5);  // 32-row k group inside the chunk
   const int col0 = tile * kGemvTileN + nl * 8;
-  const int klane = kc * kGemvChunkK + g * kGemvLaneK;
-  const bool col_ok = col0 < a.N;
-  const size_t rowbytes = (size_t)(a.N >> 1);
-  const uint8_t *wp = a.w + ((size_t)e * a.K + klane) * rowbytes + (col0 >> 1);
-  // Branch-free loads: rows past K (or columns past N) read row/column 0 of
-  // the expert and are masked to code 0 afterwards.
-  uint32_t A[kGemvLaneK];
-  const uint8_t *wbase = a.w + (size_t)e * a.K * rowbytes;
-#pragma unroll
-  for (int i = 0; i < kGemvLaneK; ++i) {
-    const bool ok = col_ok && (klane + i < a.K);
-    const uint8_t *src = ok ? (wp + (size_t)i * rowbytes) : wbase;
-    A[i] = __builtin_nontemporal_load((const uint32_t *)src);
-    A[i] = ok ? A[i] : 0u;
-  }
-  uint2 SB[2] = {make_uint2(0u, 0u), make_uint2(0u, 0u)};
+  const int kl = kc * KC + g * kGemvLaneK;  // first k row of this lane
+  const uint32_t rowbytes = (uint32_t)(a.N >> 1);
   const int KB = a.K / B;
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.w + (size_t)e * a.K * rowbytes), (short)0, (int)((uint32_t)a.K * rowbytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.scales + (size_t)e * KB * a.N), (short)0, (int)((uint32_t)KB * a.N), 0x00020000);
+  const bool col_ok = col0 < a.N;
+  const uint32_t woff = col_ok ? (uint32_t)kl * rowbytes + (uint32_t)(col0 >> 1) : kOutOfRange;
+  const uint32_t soff = col_ok ? (uint32_t)(kl / B) * (uint32_t)a.N + (uint32_t)col0 : kOutOfRange;
+  uint32_t A[kGemvLaneK];
 #pragma unroll
-  for (int b = 0; b < NBLK; ++b) {
-    const int kb = klane / B + b;
-    if (col_ok && klane + b * B < a.K) SB[b] = *(const uint2 *)(a.scales + ((size_t)e * KB + kb) * a.N + col0);
-  }
+  for (int i = 0; i < kGemvLaneK; ++i)
+    A[i] = __builtin_amdgcn_raw_buffer_load_b32(wr, woff, i * (int)rowbytes, kBufNontemporal);
+  u32x2_t SB[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+    SB[b] = (b < NBLK) ? __builtin_amdgcn_raw_buffer_load_b64(sr, soff, b * a.N, 0) : u32x2_t{0u, 0u};
   const float gs = a.gscale ? a.gscale[e] : 1.0f;
-  const int col = tile * kGemvTileN + tid;  // column of this thread in the reduction
 
-  // ---- passes of up to MRMAX rows ---------------------------------------------
+  // ---- passes of up to MRMAX rows -----------------------------------------------
 #pragma nounroll
   for (int rbase = 0; rbase < m; rbase += MRMAX) {
-    // Opaque to the optimiser: keeps the weight decode inside the pass (a
-    // decode hoisted out of this loop would hold 128 registers live).
+    // Opaque to the optimiser: keeps the decode inside the pass (hoisted out
+    // of this loop it would keep all 128 decoded registers live).
 #pragma unroll
     for (int i = 0; i < kGemvLaneK; ++i) asm volatile("" : "+v"(A[i]));
     const int rem = m - rbase;
     const int mr = rem < MRMAX ? rem : MRMAX;
-    // Stage mr activation rows of this k chunk, pre-scaled per (row, k group).
+    // Stage the chunk's activation rows, pre-scaled per (row, 32-k group):
+    // one thread per 8 values, 4 consecutive threads per group.
     {
-      const int r = tid >> 5;         // up to 8 rows x 32 threads, 8 values each
-      const int kk = (tid & 31) * 8;  // k offset inside the chunk
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      const int kabs = kc * kGemvChunkK + kk;
+      const int per_row = KC / 8;
+      const int r = tid / per_row;
+      const int kk = (tid - r * per_row) * 8;
+      const int kabs = kc * KC + kk;
+      u32x4_t v = {0u, 0u, 0u, 0u};
       if (r < mr && kabs < a.K) {
         const int p = row0 + rbase + r;
         const int src = a.fc1 ? (a.p2e[p] / a.topk) : p;
-        v = *(const uint4 *)(a.act + (size_t)src * a.K + kabs);
+        v = *(const u32x4_t *)(a.act + (size_t)src * a.K + kabs);
       }
       uint32_t mx = 0;
-      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        mx = max(mx, wv[q] & 0x7FFFu);
-        mx = max(mx, (wv[q] >> 16) & 0x7FFFu);
+        mx = max(mx, v[q] & 0x7FFFu);
+        mx = max(mx, (v[q] >> 16) & 0x7FFFu);
       }
-      // the 4 threads of a 32-wide k group share one exponent
       mx = max(mx, dpp_u32<kDppXor1>(mx));
       mx = max(mx, dpp_u32<kDppXor2>(mx));
       const int ef = (int)(mx >> 7);  // biased exponent of max |a| (0: zero/subnormal)
       const int P = (mx == 0u) ? 0 : 252 - (ef < 1 ? 1 : ef);
-      uint32_t o[4];
+      u32x4_t o;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float lo = ldexpf(__uint_as_float(wv[q] << 16), P);
-        const float hi = ldexpf(__uint_as_float(wv[q] & 0xFFFF0000u), P);
+        const float lo = ldexpf(__uint_as_float(v[q] << 16), P);
+        const float hi = ldexpf(__uint_as_float(v[q] & 0xFFFF0000u), P);
         o[q] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
       }
       if (r < MRMAX) {
-        *(uint4 *)&sm.xs[r][kk] = make_uint4(o[0], o[1], o[2], o[3]);
-        if ((tid & 3) == 0) sm.pexp[r][(tid & 31) >> 2] = P;
+        *(u32x4_t *)&sm.xs[r][kk] = o;
+        if ((tid & 3) == 0) sm.pexp[r][kk / kGemvLaneK] = P;
       }
     }
     __syncthreads();
 
     if (MRMAX == 1 || mr == 1)
-      lane_dot<FMT, 1, MRMAX>(sm, A, SB, g, nl);
+      lane_dot<FMT, 1, MRMAX>(sm, A, SB, g, wave, lane);
     else
-      lane_dot<FMT, MRMAX, MRMAX>(sm, A, SB, g, nl);
+      lane_dot<FMT, MRMAX, MRMAX>(sm, A, SB, g, wave, lane);
     __syncthreads();
 
-    // ---- reduce the 8 k groups (fixed order); thread = column ---------------
-    for (int r = 0; r < mr; ++r) {
-      float s = sm.red[0][r][tid];
-#pragma unroll
-      for (int q = 1; q < kKGroups; ++q) s += sm.red[q][r][tid];
-      const int p = row0 + rbase + r;
-      const float u = gs * s;
-      if (a.nchunks > 1) {
-        if (col < a.N) a.partials[((size_t)kc * a.rows + p) * a.N + col] = u;
-      } else if (a.fc1) {
-        store_fc1(a, p, col, u);
-      } else if (col < a.N) {
-        a.out_f32[(size_t)p * a.N + col] = u;
+    // ---- reduce the W waves (fixed order); one thread per column ------------
+    for (int cl = tid; cl < kGemvTileN; cl += W * 64) {
+      const int col = tile * kGemvTileN + cl;
+      for (int r = 0; r < mr; ++r) {
+        float s = sm.red[0][r][cl];
+        for (int q = 1; q < W; ++q) s += sm.red[q][r][cl];
+        const int p = row0 + rbase + r;
+        const float u = gs * s;
+        if (a.nchunks > 1) {
+          if (col < a.N) a.partials[((size_t)kc * a.rows + p) * a.N + col] = u;
+        } else if (a.fc1) {
+          store_fc1(a, p, col, u);
+        } else if (col < a.N) {
+          a.out_f32[(size_t)p * a.N + col] = u;
+        }
       }
     }
     __syncthreads();
@@ -290,9 +324,9 @@ __global__ __launch_bounds__(kThreads) void fp4_gemv_kernel(GemvArgs a) {
 
 // Split-K epilogue: sums the k-chunk partials of every (row, column) in chunk
 // order, then SwiGLU -> bf16 h (FC1) or float32 y (FC2).
-__global__ __launch_bounds__(kThreads) void splitk_epilogue_kernel(GemvArgs a) {
+__global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemvArgs a) {
   const int p = blockIdx.y;
-  const int col = blockIdx.x * kThreads + threadIdx.x;
+  const int col = blockIdx.x * 256 + threadIdx.x;
   float s = 0.f;
   if (col < a.N) {
     s = a.partials[(size_t)p * a.N + col];
@@ -304,40 +338,59 @@ __global__ __launch_bounds__(kThreads) void splitk_epilogue_kernel(GemvArgs a) {
     a.out_f32[(size_t)p * a.N + col] = s;
 }
 
-size_t gemv_workspace_bytes(int32_t rows, int32_t E, int32_t K, int32_t N) {
-  (void)E;
-  const int nchunks = (K + kGemvChunkK - 1) / kGemvChunkK;
+// Four waves (a 256-row k chunk) per workgroup: the kernel is bound by VALU
+// issue (bit-assembled decode), so many small workgroups balance the CUs
+// best; measured against 2, 8 and 16 waves on the decode and MTP layers.
+// Shorter K uses fewer waves.
+static void plan_chunks(int items, int K, int maxw, int &nchunks, int &waves) {
+  (void)items;
+  const int slabs = (K + kGemvWaveK - 1) / kGemvWaveK;
+  const int w = maxw < 4 ? maxw : 4;
+  waves = slabs < w ? slabs : w;
+  nchunks = (slabs + waves - 1) / waves;
+}
+
+static int plan_max_waves(int max_rows_per_expert) {
+  return max_rows_per_expert <= 1 ? max_waves<1>() : max_waves<2>();
+}
+
+size_t gemv_workspace_bytes(int32_t rows, int32_t max_rows_per_expert, int32_t E, int32_t K, int32_t N) {
+  const int nslots = rows < E ? rows : E;
+  const int ntiles = (N + kGemvTileN - 1) / kGemvTileN;
+  int nchunks, waves;
+  plan_chunks(nslots * ntiles, K, plan_max_waves(max_rows_per_expert), nchunks, waves);
   const size_t part = nchunks > 1 ? (size_t)nchunks * rows * N * sizeof(float) : 0;
   return part > 256 ? part : 256;
 }
 
-void gemv_plan(GemvArgs &a, void *ws) {
+void gemv_plan(GemvArgs &a, int max_rows_per_expert, void *ws) {
   a.nslots = a.rows < a.E ? a.rows : a.E;
   a.ntiles = (a.N + kGemvTileN - 1) / kGemvTileN;
-  a.nchunks = (a.K + kGemvChunkK - 1) / kGemvChunkK;
+  plan_chunks(a.nslots * a.ntiles, a.K, plan_max_waves(max_rows_per_expert), a.nchunks, a.waves);
   a.partials = (float *)ws;
 }
 
 hipError_t launch_fp4_gemv(const GemvArgs &a, int fmt, int max_rows_per_expert, hipStream_t s) {
   const int items = a.nslots * a.ntiles;
   const dim3 grid((unsigned)(((items + 7) / 8) * 8 * a.nchunks));
+  const dim3 block((unsigned)(a.waves * 64));
   // One row per pass when no expert can hold more than one row (one token),
-  // else two: the 2-row body needs 120 VGPRs, 4 rows would need ~170.
+  // else two: the 2-row body needs ~120 VGPRs, 4 rows would need ~170.
   if (fmt == 0) {
     if (max_rows_per_expert <= 1)
-      fp4_gemv_kernel<0, 1><<<grid, kThreads, 0, s>>>(a);
+      fp4_gemv_kernel<0, 1><<<grid, block, 0, s>>>(a);
     else
-      fp4_gemv_kernel<0, 2><<<grid, kThreads, 0, s>>>(a);
+      fp4_gemv_kernel<0, 2><<<grid, block, 0, s>>>(a);
   } else {
     if (max_rows_per_expert <= 1)
-      fp4_gemv_kernel<1, 1><<<grid, kThreads, 0, s>>>(a);
+      fp4_gemv_kernel<1, 1><<<grid, block, 0, s>>>(a);
     else
-      fp4_gemv_kernel<1, 2><<<grid, kThreads, 0, s>>>(a);
+      fp4_gemv_kernel<1, 2><<<grid, block, 0, s>>>(a);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.nchunks == 1) return err;
-  const dim3 g2((unsigned)((a.N + kThreads - 1) / kThreads), (unsigned)a.rows);
-  splitk_epilogue_kernel<<<g2, kThreads, 0, s>>>(a);
+  const dim3 g2((unsigned)((a.N + 255) / 256), (unsigned)a.rows);
+  splitk_epilogue_kernel<<<g2, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

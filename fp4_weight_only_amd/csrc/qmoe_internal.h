@@ -10,7 +10,8 @@ namespace qmoe {
 
 constexpr int kGemvTileN = 256;    // output columns per GEMV block (32 lanes x 8 columns)
 constexpr int kGemvLaneK = 32;     // k rows per lane
-constexpr int kGemvChunkK = 256;   // k rows per GEMV block (4 waves x 2 halves x 32)
+constexpr int kGemvWaveK = 64;     // k rows per wave (two 32-lane halves)
+constexpr int kGemvMaxWaves = 4;   // waves per GEMV block (k chunk of 256 rows)
 
 struct GemvArgs {
   const uint16_t *act;     // FC1: x [T][K]; FC2: h [rows][K]
@@ -21,6 +22,7 @@ struct GemvArgs {
   const float *gscale;     // may be null
   int32_t E, K, N, topk, rows;
   int32_t nslots, ntiles, nchunks;
+  int32_t waves;           // waves per block; the k chunk is waves * 64 rows
   int32_t fc1;             // 1: act rows gathered by token, SwiGLU epilogue, bf16 out
   float alpha, beta, limit;
   uint16_t *out_bf16;      // FC1: h [rows][N/2]
@@ -28,8 +30,8 @@ struct GemvArgs {
   float *partials;         // [nchunks][rows][N] split-K partials (nchunks > 1)
 };
 
-size_t gemv_workspace_bytes(int32_t rows, int32_t E, int32_t K, int32_t N);
-void gemv_plan(GemvArgs &a, void *ws);
+size_t gemv_workspace_bytes(int32_t rows, int32_t max_rows_per_expert, int32_t E, int32_t K, int32_t N);
+void gemv_plan(GemvArgs &a, int max_rows_per_expert, void *ws);
 hipError_t launch_fp4_gemv(const GemvArgs &a, int fmt, int max_rows_per_expert, hipStream_t s);
 
 hipError_t launch_route(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *idx, float *w,

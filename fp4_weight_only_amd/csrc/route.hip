@@ -13,7 +13,8 @@
 //
 // The expert maps rank the T*k expanded rows by expert with wave ballots
 // (8 ballots match the expert-id bits, popcount below the lane gives the
-// rank), the ballot-based ranking the same PR adopts.
+// rank), the ballot-based ranking the same PR adopts.  For up to 16 tokens
+// both steps run in one workgroup (one launch, selections passed in LDS).
 #include "device_common.h"
 #include "qmoe_internal.h"
 
@@ -82,15 +83,11 @@ __device__ __forceinline__ void merge_step(uint64_t (&L)[NP]) {
   }
 }
 
-// One wave per token; E <= 256 (4 keys per lane), k <= NP.
+// Top-k of one token by one wave; E <= 256 (4 keys per lane), k <= NP.
+// Lanes j < k return the j-th selected expert and its softmax weight.
 template <int NP>
-__global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict__ logits, int T, int E, int k,
-                                                         int32_t *__restrict__ idx, float *__restrict__ wts) {
-  const int wave = threadIdx.x >> 6;
-  const int lane = lane_id();
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= T) return;  // wave-uniform
-  const float *row = logits + (size_t)t * E;
+__device__ __forceinline__ void topk_token(const float *__restrict__ row, int E, int k, int lane, int &sel,
+                                           float &wsel) {
   uint64_t key[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -129,19 +126,33 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict
       mine_ex = ex[i];
     }
   }
+  sel = key_index(mine);
+  wsel = mine_ex / sum;
+}
+
+// One wave per token.
+template <int NP>
+__global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict__ logits, int T, int E, int k,
+                                                         int32_t *__restrict__ idx, float *__restrict__ wts) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = lane_id();
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;  // wave-uniform
+  int sel;
+  float wsel;
+  topk_token<NP>(logits + (size_t)t * E, E, k, lane, sel, wsel);
   if (lane < k) {
-    idx[(size_t)t * k + lane] = key_index(mine);
-    wts[(size_t)t * k + lane] = mine_ex / sum;
+    idx[(size_t)t * k + lane] = sel;
+    wts[(size_t)t * k + lane] = wsel;
   }
 }
 
-// Stable counting sort of the expanded rows by expert, one workgroup.
-// NW waves rank NW*64 rows per round with ballots; E <= 256.
+// Stable counting sort of the expanded rows by expert, by one workgroup of
+// NW waves: NW*64 rows are ranked per round with ballots; E <= 256.  idx
+// may point to global or LDS memory.
 template <int NW>
-__global__ __launch_bounds__(NW * 64) void expert_maps_kernel(const int32_t *__restrict__ idx, int R, int E,
-                                                              int32_t *__restrict__ offsets,
-                                                              int32_t *__restrict__ p2e,
-                                                              int32_t *__restrict__ e2p) {
+__device__ __forceinline__ void build_maps(const int32_t *idx, int R, int E, int32_t *__restrict__ offsets,
+                                           int32_t *__restrict__ p2e, int32_t *__restrict__ e2p) {
   __shared__ int cnt[256];
   __shared__ int base[256];
   __shared__ int wc[NW][256];
@@ -218,8 +229,63 @@ __global__ __launch_bounds__(NW * 64) void expert_maps_kernel(const int32_t *__r
   }
 }
 
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void expert_maps_kernel(const int32_t *__restrict__ idx, int R, int E,
+                                                              int32_t *__restrict__ offsets,
+                                                              int32_t *__restrict__ p2e,
+                                                              int32_t *__restrict__ e2p) {
+  build_maps<NW>(idx, R, E, offsets, p2e, e2p);
+}
+
+// Decode-sized batches (T <= NW): top-k and maps in one workgroup, the
+// selections handed over through LDS.
+template <int NP, int NW>
+__global__ __launch_bounds__(NW * 64) void route_fused_kernel(const float *__restrict__ logits, int T, int E, int k,
+                                                              int32_t *__restrict__ idx, float *__restrict__ wts,
+                                                              int32_t *__restrict__ offsets,
+                                                              int32_t *__restrict__ p2e,
+                                                              int32_t *__restrict__ e2p) {
+  __shared__ int32_t sidx[NW * 8];
+  const int wave = threadIdx.x >> 6;
+  const int lane = lane_id();
+  if (wave < T) {  // wave-uniform
+    int sel;
+    float wsel;
+    topk_token<NP>(logits + (size_t)wave * E, E, k, lane, sel, wsel);
+    if (lane < k) {
+      idx[(size_t)wave * k + lane] = sel;
+      wts[(size_t)wave * k + lane] = wsel;
+      sidx[wave * k + lane] = sel;
+    }
+  }
+  __syncthreads();
+  build_maps<NW>(sidx, T * k, E, offsets, p2e, e2p);
+}
+
+template <int NP>
+static void launch_fused(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *idx, float *w,
+                         int32_t *offsets, int32_t *p2e, int32_t *e2p, hipStream_t s) {
+  if (T <= 4)
+    route_fused_kernel<NP, 4><<<1, 256, 0, s>>>(logits, T, E, k, idx, w, offsets, p2e, e2p);
+  else if (T <= 8)
+    route_fused_kernel<NP, 8><<<1, 512, 0, s>>>(logits, T, E, k, idx, w, offsets, p2e, e2p);
+  else
+    route_fused_kernel<NP, 16><<<1, 1024, 0, s>>>(logits, T, E, k, idx, w, offsets, p2e, e2p);
+}
+
 hipError_t launch_route(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *idx, float *w,
                         int32_t *offsets, int32_t *p2e, int32_t *e2p, hipStream_t s) {
+  if (T <= 16) {  // one launch: top-k and maps in one workgroup
+    if (k <= 1)
+      launch_fused<1>(logits, T, E, k, idx, w, offsets, p2e, e2p, s);
+    else if (k <= 2)
+      launch_fused<2>(logits, T, E, k, idx, w, offsets, p2e, e2p, s);
+    else if (k <= 4)
+      launch_fused<4>(logits, T, E, k, idx, w, offsets, p2e, e2p, s);
+    else
+      launch_fused<8>(logits, T, E, k, idx, w, offsets, p2e, e2p, s);
+    return hipGetLastError();
+  }
   const dim3 grid((T + 3) / 4);
   if (k <= 1)
     route_topk_kernel<1><<<grid, 256, 0, s>>>(logits, T, E, k, idx, w);

@@ -104,8 +104,8 @@ def test_gemv_row_window(q):
 def test_workspace_query_and_too_small(q):
     st, need = fc1(q, weights(q, E=256, K=2048, N=1536), T=4, k=8)
     assert st == q.QMOE_OK and need > 0
-    # 32 rows x 1536 columns x 8 k-chunks of float32 partials, plus counters
-    assert need >= 8 * 32 * 1536 * 4
+    # K = 2048 spans at least two k chunks: float32 partials of 32 rows x 1536 columns each
+    assert need >= 2 * 32 * 1536 * 4
     st, _ = fc1(q, weights(q, E=256, K=2048, N=1536), T=4, k=8, ws=A, nbytes=need - 1)
     assert st == q.QMOE_EWORKSPACE
     st, need2 = fc2(q, weights(q, E=256, K=768, N=2048), T=4, k=8)
