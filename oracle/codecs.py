@@ -110,3 +110,11 @@ def unpack_codes(packed) -> np.ndarray:
     out[..., 0::2] = p & 0x0F
     out[..., 1::2] = p >> 4
     return out
+
+
+def unpack_column(packed, cols) -> np.ndarray:
+    """Codes of the given columns n of a [..., N/2] packed array (byte n // 2, nibble n % 2)."""
+    p = np.asarray(packed, dtype=np.uint8)
+    cols = np.asarray(cols)
+    byte = p[..., cols // 2]
+    return np.where(cols % 2 == 1, byte >> 4, byte & 0x0F).astype(np.uint8)

@@ -26,12 +26,14 @@ from . import codecs
 def dequant_expert_f64(w_e, s_e, g_e, fmt: str, cols=None) -> np.ndarray:
     """One expert: packed [K][N/2], scales [K/B][N] -> float64 [K][N] (or [K][len(cols)])."""
     B = 16 if fmt == "nvfp4" else 32
-    codes = codecs.unpack_codes(w_e)                      # [K][N]
-    K, N = codes.shape
-    scales = codecs.block_scale_value(s_e, fmt)           # [K/B][N]
-    if cols is not None:
-        codes = codes[:, cols]
-        scales = scales[:, cols]
+    if cols is None:
+        codes = codecs.unpack_codes(w_e)                  # [K][N]
+        scales = codecs.block_scale_value(s_e, fmt)       # [K/B][N]
+    else:                                                 # only the requested columns
+        cols = np.asarray(cols)
+        codes = codecs.unpack_column(w_e, cols)
+        scales = codecs.block_scale_value(np.asarray(s_e)[:, cols], fmt)
+    K = codes.shape[0]
     val = codecs.e2m1_value(codes) * np.repeat(scales, B, axis=0)[:K]
     gv = 1.0 if g_e is None else float(np.float32(g_e))
     return val * gv

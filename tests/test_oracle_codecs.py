@@ -135,6 +135,7 @@ def test_bf16_from_f64_agrees_with_torch_on_float32_inputs():
 def test_unpack_low_nibble_is_even_column():
     p = np.array([[0x21, 0xF0]], np.uint8)
     assert codecs.unpack_codes(p).tolist() == [[1, 2, 0, 15]]
+    assert codecs.unpack_column(p, np.array([3, 0, 1])).tolist() == [[15, 1, 2]]
 
 
 @pytest.mark.parametrize("b", [0x7F, 0xFF])
