@@ -49,19 +49,20 @@ qmoe_status check_fc(const qmoe_fp4_weights *w, int32_t T, int32_t k, const void
   return QMOE_OK;
 }
 
-// Resolves AUTO and checks the row window of each path.
-qmoe_status resolve_path(qmoe_path path, int32_t rows, qmoe_path *out) {
+// Resolves AUTO and checks the row window and tile shape of each path.
+qmoe_status resolve_path(qmoe_path path, int32_t rows, const qmoe_fp4_weights *w, qmoe_path *out) {
   qmoe_path p = path;
   if (p == QMOE_PATH_AUTO) p = rows <= QMOE_GEMV_MAX_ROWS ? QMOE_PATH_GEMV : QMOE_PATH_GROUPED;
   if (p == QMOE_PATH_GEMV && rows > QMOE_GEMV_MAX_ROWS) return QMOE_EUNSUPPORTED;
-  if (p == QMOE_PATH_GROUPED) return QMOE_EUNSUPPORTED;  // grouped GEMM path not built in this library yet
+  if (p == QMOE_PATH_GROUPED && (w->K % 64 != 0 || w->N % 128 != 0)) return QMOE_EUNSUPPORTED;
   *out = p;
   return QMOE_OK;
 }
 
-qmoe_status run_gemv(GemvArgs &a, const qmoe_fp4_weights *w, int max_rows, void *ws, size_t *ws_bytes,
-                     hipStream_t stream) {
-  const size_t need = gemv_workspace_bytes(a.rows, max_rows, w->E, w->K, w->N);
+qmoe_status run_fc(GemvArgs &a, const qmoe_fp4_weights *w, int max_rows, qmoe_path path, void *ws,
+                   size_t *ws_bytes, hipStream_t stream) {
+  const size_t need = path == QMOE_PATH_GROUPED ? grouped_workspace_bytes()
+                                                : gemv_workspace_bytes(a.rows, max_rows, w->E, w->K, w->N);
   if (!ws_bytes) return QMOE_EINVAL;
   if (!ws) {
     *ws_bytes = need;
@@ -75,8 +76,10 @@ qmoe_status run_gemv(GemvArgs &a, const qmoe_fp4_weights *w, int max_rows, void 
   a.E = w->E;
   a.K = w->K;
   a.N = w->N;
+  const int fmt = w->fmt == QMOE_FMT_NVFP4 ? 0 : 1;
+  if (path == QMOE_PATH_GROUPED) return check_launch(launch_grouped(a, fmt, stream));
   gemv_plan(a, max_rows, ws);
-  return check_launch(launch_fp4_gemv(a, w->fmt == QMOE_FMT_NVFP4 ? 0 : 1, max_rows, stream));
+  return check_launch(launch_fp4_gemv(a, fmt, max_rows, stream));
 }
 
 }  // namespace
@@ -120,7 +123,7 @@ qmoe_status qmoe_fp4_gemv_fc1_swiglu(const uint16_t *x, int32_t T, int32_t k, co
   if (!perm_to_expanded) return QMOE_EINVAL;
   if (!aligned16(perm_to_expanded)) return QMOE_EALIGN;
   qmoe_path p;
-  st = resolve_path(path, sh.rows, &p);
+  st = resolve_path(path, sh.rows, w1, &p);
   if (st != QMOE_OK) return st;
   GemvArgs a = {};
   a.act = x;
@@ -133,7 +136,7 @@ qmoe_status qmoe_fp4_gemv_fc1_swiglu(const uint16_t *x, int32_t T, int32_t k, co
   a.beta = act ? act->beta : 0.0f;
   a.limit = act ? act->limit : INFINITY;
   a.out_bf16 = h;
-  return run_gemv(a, w1, sh.max_rows_per_expert, ws, ws_bytes, stream);
+  return run_fc(a, w1, sh.max_rows_per_expert, p, ws, ws_bytes, stream);
 }
 
 qmoe_status qmoe_fp4_gemv_fc2(const uint16_t *h, int32_t T, int32_t k, const qmoe_fp4_weights *w2,
@@ -143,7 +146,7 @@ qmoe_status qmoe_fp4_gemv_fc2(const uint16_t *h, int32_t T, int32_t k, const qmo
   qmoe_status st = check_fc(w2, T, k, h, expert_offsets, y_rows, path, &sh);
   if (st != QMOE_OK) return st;
   qmoe_path p;
-  st = resolve_path(path, sh.rows, &p);
+  st = resolve_path(path, sh.rows, w2, &p);
   if (st != QMOE_OK) return st;
   GemvArgs a = {};
   a.act = h;
@@ -152,7 +155,7 @@ qmoe_status qmoe_fp4_gemv_fc2(const uint16_t *h, int32_t T, int32_t k, const qmo
   a.rows = sh.rows;
   a.fc1 = 0;
   a.out_f32 = y_rows;
-  return run_gemv(a, w2, sh.max_rows_per_expert, ws, ws_bytes, stream);
+  return run_fc(a, w2, sh.max_rows_per_expert, p, ws, ws_bytes, stream);
 }
 
 qmoe_status qmoe_finalize(const float *y_rows, const float *topk_w, const int32_t *expanded_to_perm, int32_t T,

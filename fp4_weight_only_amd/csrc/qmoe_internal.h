@@ -34,6 +34,9 @@ size_t gemv_workspace_bytes(int32_t rows, int32_t max_rows_per_expert, int32_t E
 void gemv_plan(GemvArgs &a, int max_rows_per_expert, void *ws);
 hipError_t launch_fp4_gemv(const GemvArgs &a, int fmt, int max_rows_per_expert, hipStream_t s);
 
+size_t grouped_workspace_bytes();
+hipError_t launch_grouped(GemvArgs &a, int fmt, hipStream_t s);
+
 hipError_t launch_route(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *idx, float *w,
                         int32_t *offsets, int32_t *p2e, int32_t *e2p, hipStream_t s);
 

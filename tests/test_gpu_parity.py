@@ -3,7 +3,9 @@
 Bit-exact: routing indices, expert maps, dequantized bf16.  Floating-point
 outputs: the oracle.tolerance rule.  Stage-wise checks feed the oracle the
 GPU's own previous-stage outputs; end-to-end checks run the oracle from the
-inputs alone.  Each case prints its name before it touches the GPU.
+inputs alone, taking h's bf16 rounding the GPU's way only where the tests/ties
+rule shows it is a float32 rounding tie.  Each case prints its name before it
+touches the GPU.
 """
 import numpy as np
 import pytest
@@ -11,6 +13,7 @@ import torch
 
 import synth
 from gpu_util import bf16_dev, bf16_host, layer_dev, print_case, to_dev, weights_dev
+from ties import h_roundings_differ_only_at_ties
 from oracle import codecs, dequant, moe, route, tolerance
 
 pytestmark = pytest.mark.gpu
@@ -36,8 +39,8 @@ SMALL = [
 FULL = [synth.TINY, synth.DECODE, synth.MTP4, synth.MTP8]
 
 
-def run_gpu_layer(L, act=None):
-    layer, logits, x = layer_dev(L, act=act)
+def run_gpu_layer(L, act=None, path=None):
+    layer, logits, x = layer_dev(L, act=act, path=path)
     print_case("layer", L.cfg.name)
     layer.run(logits, x)
     torch.cuda.synchronize()
@@ -53,9 +56,9 @@ def assert_close(name, gpu, ref):
     assert ok, (name, rep)
 
 
-def check_layer(L, act=None, cols1=None, cols2=None):
+def check_layer(L, act=None, cols1=None, cols2=None, path=None):
     c = L.cfg
-    g = run_gpu_layer(L, act)
+    g = run_gpu_layer(L, act, path)
     oact = None if act is None else dict(alpha=act[0], beta=act[1], limit=act[2])
     # routing and maps: bit-exact
     idx, wts = route.route_topk(L.logits, c.k)
@@ -76,10 +79,13 @@ def check_layer(L, act=None, cols1=None, cols2=None):
     # finalize stage, fed the GPU's y and weights
     out_ref = moe.finalize(g["y"], g["w"], g["e2p"], c.T, c.k)
     assert_close("out(stage)", g["out"], out_ref)
-    # end to end
+    # end to end: the oracle chain from the inputs, with h's rounding taken the
+    # GPU's way only where it is a tie (see h_roundings_differ_only_at_ties)
     if cols1 is None and cols2 is None:
-        r = moe.layer(L, oact)
-        assert_close("out(e2e)", g["out"], r["out"])
+        # (after the tie check the GPU's h is that chain's h, so y_ref is its y)
+        ties = h_roundings_differ_only_at_ties(L, g["h"], h_ref, u_ref, oact, off, p2e)
+        print("h rounding ties", ties, flush=True)
+        assert_close("out(e2e)", g["out"], moe.finalize(y_ref, wts, e2p, c.T, c.k))
     return g
 
 
@@ -260,6 +266,44 @@ def test_gemv_window_and_paths():
     with pytest.raises(q.QmoeError) as ei:          # refused on the host, nothing launched
         q.qmoe_fp4_gemv_fc1_swiglu(bf16_dev(L65.x), c.k, w1, off, p2e, h, ws, path=q.QMOE_PATH_GEMV)
     assert ei.value.status == q.QMOE_EUNSUPPORTED
+    check_layer(L65)                                     # 65 rows: AUTO takes the grouped GEMM
+
+
+# Grouped (prefill) path: several 64-row tiles per hot expert, 16-row sub-tiles,
+# both codecs, and the same small shape through both paths.
+GROUPED = [
+    synth.shrink(synth.MX_PREFILL, E=16, T=64, k=4, H=512, I=256, seed=21),   # 256 rows, Zipf: tiles of 64+
+    synth.shrink(synth.MX_PREFILL, E=64, T=128, k=8, H=256, I=128, seed=22),  # 1024 rows
+    synth.shrink(synth.DECODE, E=8, T=40, k=2, H=256, I=128, seed=23),        # NVFP4, 80 rows
+    synth.shrink(synth.MTP8, E=24, T=24, k=8, H=384, I=192, seed=24),         # NVFP4, hot experts m=24
+]
+
+
+@pytest.mark.parametrize("cfg", GROUPED, ids=lambda c: c.name)
+def test_grouped_small(cfg):
+    check_layer(synth.layer_inputs(cfg))
+
+
+@pytest.mark.parametrize("cfg", [synth.shrink(synth.MTP8, E=32, T=8, k=8, H=512, I=256, seed=25),
+                                 synth.shrink(synth.MX_DECODE, E=32, T=8, k=8, H=512, I=256, seed=26)],
+                         ids=lambda c: c.name)
+def test_same_shape_both_paths(cfg):
+    import fp4_weight_only_amd as q
+    L = synth.layer_inputs(cfg)
+    g1 = check_layer(L, path=q.QMOE_PATH_GEMV)
+    g2 = check_layer(L, path=q.QMOE_PATH_GROUPED)
+    assert np.array_equal(g1["idx"], g2["idx"])
+    ok, rep = tolerance.check(g2["out"], g1["out"])
+    print("gemv vs grouped", rep)
+
+
+def test_prefill_full_sampled():
+    """4096 routed rows, E=256, hidden 4096, intermediate 2048, MXFP4, Zipf routing."""
+    L = synth.layer_inputs(synth.MX_PREFILL)
+    rng = np.random.default_rng(1)
+    cols1 = np.sort(rng.choice(L.cfg.I, 96, replace=False))
+    cols2 = np.sort(rng.choice(L.cfg.H, 128, replace=False))
+    check_layer(L, cols1=cols1, cols2=cols2)
 
 
 def test_determinism_and_poisoned_buffers():
