@@ -1,27 +1,38 @@
-"""Benchmark of the FP4 weight-only MoE decode layer on one MI355X.
+"""Benchmark of the FP4 weight-only MoE expert path on one MI355X.
 
-Workload: the NVFP4 MTP-verify decode layer (4 tokens x top-8 = 32 expanded
-rows, E=256, hidden 2048, intermediate 768, three hot experts), seeded
-synthetic inputs.  A step is one pass of the whole hot path over one layer:
-qmoe_route_topk -> qmoe_fp4_gemv_fc1_swiglu -> qmoe_fp4_gemv_fc2 ->
-qmoe_finalize.  Steps rotate over LAYERS distinct copies of the layer weights
-so every timed weight byte comes from HBM, not from the 256 MB Infinity Cache.
-The steps are captured once in a HIP graph and replayed (the launch path of a
-serving loop); --eager times plain launches instead.
+Default workload: the NVFP4 MTP-verify decode layer (4 tokens x top-8 = 32
+expanded rows, E=256, hidden 2048, intermediate 768, three hot experts),
+seeded synthetic inputs.  A step is one pass of the whole hot path over one
+layer: qmoe_route_topk -> qmoe_fp4_gemv_fc1_swiglu -> qmoe_fp4_gemv_fc2 ->
+qmoe_finalize.  Steps rotate over distinct copies of the layer weights so
+every timed weight byte comes from HBM, not from the 256 MB Infinity Cache.
+The steps are captured once in a HIP graph and replayed (the launch path of
+a serving loop); --eager times plain launches instead.
 
 value = achieved GB/s on weight bytes (packed E2M1 + block scales + global
 scales of the experts the routing actually selected) per layer.
 
-roofline: the dominant kernel (FC1 GEMV + SwiGLU), HBM-bound; its average
-duration comes from HIP events around graph replays that hold only FC1
-launches over the rotated copies, recorded on the stream they run on.
+Other workloads (--workload): decode / mtp8 / mx_decode (same layer path),
+prefill (MXFP4 512 tokens, grouped-GEMM path; also reports TFLOP/s and the
+fraction of the bf16 MFMA peak), dequant (MXFP4 standalone dequant, GB/s on
+read + write bytes).  --calibrate-copy runs a plain device-to-device copy of
+known size, the reference kernel for scaling HBM traffic counters.
+
+roofline: the dominant kernel of the workload (FC1 for the layer workloads,
+the dequant kernel for dequant), HBM-bound; its average duration comes from
+HIP events around graph replays that hold only that call over the rotated
+copies, recorded on the stream they run on.  roofline.traffic is the HBM
+byte count per launch measured with FETCH_SIZE + WRITE_SIZE counters and
+scaled by the copy calibration, read from profiles/ and reported only while
+the kernel source it was taken on is unchanged (else null).
 
 cpu_baseline: the CPU oracle (test infrastructure, float64 numpy, one
-thread) timed on the same layer.
+thread) timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,7 +43,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "NVFP4 MoE decode GEMV µs/layer + achieved HBM GB/s (% of peak), 4–64 rows"
 HBM_PEAK_GBS = 8000.0
-LAYERS = 40
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+CSRC = os.path.join(ROOT, "fp4_weight_only_amd", "csrc")
+LAYER_WORKLOADS = ("mtp4", "mtp8", "decode", "mx_decode", "prefill")
 
 
 def parse():
@@ -41,29 +54,103 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=80)
     ap.add_argument("--eager", action="store_true")
-    ap.add_argument("--workload", default="mtp4", choices=["mtp4", "mtp8", "decode", "mx_decode"])
+    ap.add_argument("--workload", default="mtp4", choices=LAYER_WORKLOADS + ("dequant",))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="time a plain 1 GiB device copy (reference kernel for traffic counters) and exit")
     return ap.parse_args()
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
+def kernel_sources_digest(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
-    import numpy as np
-    import torch
 
-    import fp4_weight_only_amd as q
-    import synth
+def measured_traffic(name: str, sources) -> int | None:
+    """HBM bytes per launch from profiles/traffic_<name>.txt if its source digest is current."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_digest") != kernel_sources_digest(sources):
+        return None
+    return int(vals["traffic_bytes_per_launch"])
+
+
+class Timer:
+    """Graph capture + HIP-event timing on one stream."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def capture(self, fn, n):
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(self.stream):
+            for i in range(n):      # warm the allocator/launch path outside the capture
+                fn(i)
+        self.stream.synchronize()
+        with torch.cuda.graph(g, stream=self.stream):
+            for i in range(n):
+                fn(i)
+        return g
+
+    def run(self, fn, period, steps, warmup, eager=False):
+        """Average ms per fn call over `steps` calls (fn(i) rotates over `period` inputs)."""
+        torch = self.torch
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(self.stream):
+            if eager:
+                for i in range(warmup):
+                    fn(i)
+                torch.cuda.synchronize()
+                ev0.record(self.stream)
+                for i in range(steps):
+                    fn(i)
+                ev1.record(self.stream)
+                torch.cuda.synchronize()
+            else:
+                g = self.capture(fn, period)
+                rem = steps % period
+                g_rem = self.capture(fn, rem) if rem else None
+                for _ in range(max(1, warmup // period)):
+                    g.replay()
+                torch.cuda.synchronize()
+                ev0.record(self.stream)
+                for _ in range(steps // period):
+                    g.replay()
+                if g_rem is not None:
+                    g_rem.replay()
+                ev1.record(self.stream)
+                torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / steps
+
+
+def base_result(metric, value, unit, args, ms, config, dtype="bf16", higher=True):
+    return {"metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": higher, "scaling": "weak",
+            "vs_baseline": None, "dtype": dtype, "data": "synthetic", "config": config}
+
+
+def bench_layer(args, torch, q, synth, np):
     from fp4_weight_only_amd.layer import MoELayer
 
-    cfg = {"mtp4": synth.MTP4, "mtp8": synth.MTP8, "decode": synth.DECODE, "mx_decode": synth.MX_DECODE}[args.workload]
-    layers = LAYERS if cfg.fmt == synth.NVFP4 else 8
+    cfg = {"mtp4": synth.MTP4, "mtp8": synth.MTP8, "decode": synth.DECODE, "mx_decode": synth.MX_DECODE,
+           "prefill": synth.MX_PREFILL}[args.workload]
+    prefill = args.workload == "prefill"
+    # distinct weight copies: > 256 MB Infinity Cache worth of selected experts
+    layers = 40 if cfg.fmt == synth.NVFP4 else (2 if prefill else 8)
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     t0 = time.time()
     L = synth.layer_inputs(cfg)
     print(f"# generated {cfg.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
@@ -90,10 +177,12 @@ def main():
     fc2_w = cfg.I * (cfg.H // 2) + (cfg.I // B) * cfg.H + (4 if L.g2 is not None else 0)
     weight_bytes = D * (fc1_w + fc2_w)
     R = cfg.rows
-    fc1_bytes = D * fc1_w + R * cfg.H * 2 + R * cfg.I * 2 + (cfg.E + 1 + R) * 4   # weights, x rows, h, maps
+    # FC1 algorithmic bytes: selected experts' weights, x rows of the tokens, h, maps
+    fc1_bytes = D * fc1_w + cfg.T * cfg.H * 2 + R * cfg.I * 2 + (cfg.E + 1 + R) * 4
     print(f"# rows={R} distinct experts={D} weight bytes/layer={weight_bytes}", file=sys.stderr, flush=True)
 
     stream = torch.cuda.Stream()
+    tm = Timer(torch, stream)
 
     def step(i):
         w1, w2 = copies[i % layers]
@@ -101,103 +190,94 @@ def main():
         layer.run(logits, x)
 
     def fc1_only(i):
-        w1, _ = copies[i % layers]
-        layer.w1 = w1
+        layer.w1 = copies[i % layers][0]
         layer.fc1(x)
 
-    def capture(fn, n):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(stream):
-            for i in range(n):      # warm the allocator/launch path outside the capture
-                fn(i)
-        stream.synchronize()
-        with torch.cuda.graph(g, stream=stream):
-            for i in range(n):
-                fn(i)
-        return g
-
-    K, W = args.steps, args.warmup
-    if args.eager:
-        with torch.cuda.stream(stream):
-            for i in range(W):
-                step(i)
-            stream.synchronize()
-            t_start = torch.cuda.Event(enable_timing=True)
-            t_end = torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            t_start.record(stream)
-            for i in range(K):
-                step(i)
-            t_end.record(stream)
-            torch.cuda.synchronize()
-        total_ms = t_start.elapsed_time(t_end)
-    else:
-        graph = capture(step, layers)
-        rem = K % layers
-        graph_rem = capture(step, rem) if rem else None
-        with torch.cuda.stream(stream):
-            for _ in range(max(1, W // layers)):
-                graph.replay()
-            torch.cuda.synchronize()
-            t_start = torch.cuda.Event(enable_timing=True)
-            t_end = torch.cuda.Event(enable_timing=True)
-            t_start.record(stream)
-            for _ in range(K // layers):
-                graph.replay()
-            if graph_rem is not None:
-                graph_rem.replay()
-            t_end.record(stream)
-            torch.cuda.synchronize()
-        total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / K
-    value = weight_bytes / (ms_per_step * 1e-3) / 1e9
-
-    # dominant kernel: FC1 GEMV + SwiGLU, replayed alone over the rotated copies
-    g1 = capture(fc1_only, layers)
-    reps = 10
-    with torch.cuda.stream(stream):
-        g1.replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            g1.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-    fc1_us = e0.elapsed_time(e1) * 1e3 / (reps * layers)
-    fc1_gbs = fc1_bytes / (fc1_us * 1e-6) / 1e9
+    ms = tm.run(step, layers, args.steps, args.warmup, args.eager)
+    value = weight_bytes / (ms * 1e-3) / 1e9
+    fc1_ms = tm.run(fc1_only, layers, max(layers * 10, 40), layers, args.eager)
+    fc1_gbs = fc1_bytes / (fc1_ms * 1e-3) / 1e9
     layer.set_weights(*copies[0])
 
-    result = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": round(ms_per_step, 6),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": cfg.name, "rows": R, "distinct_experts": D, "layer_copies": layers,
-                   "launch": "eager" if args.eager else "hip_graph"},
-        "us_per_layer": round(ms_per_step * 1e3, 3),
-        "hbm_frac_weight_bytes": round(value / HBM_PEAK_GBS, 4),
-        "weight_bytes_per_layer": weight_bytes,
-        "roofline": {"bound": "hbm", "kernel": "fp4_gemv_kernel (FC1+SwiGLU)", "achieved": round(fc1_gbs, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(fc1_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "avg_us": round(fc1_us, 3), "bytes_per_launch": fc1_bytes},
-    }
-
+    if prefill:
+        sources = ("grouped.hip", "device_common.h", "qmoe_internal.h")
+        kname, tname = "grouped_gemm_kernel (FC1+SwiGLU)", "grouped_fc1_prefill"
+        metric = "MXFP4 MoE prefill layer µs/layer + achieved HBM GB/s on weight bytes"
+    else:
+        sources = ("gemv.hip", "device_common.h", "qmoe_internal.h")
+        kname, tname = "fp4_gemv_kernel + splitk_epilogue_kernel (FC1+SwiGLU)", f"gemv_fc1_{args.workload}"
+        metric = METRIC
+    config = {"workload": cfg.name, "rows": R, "distinct_experts": D, "layer_copies": layers,
+              "launch": "eager" if args.eager else "hip_graph"}
+    result = base_result(metric, value, "GB/s", args, ms, config)
+    result.update({"us_per_layer": round(ms * 1e3, 3), "hbm_frac_weight_bytes": round(value / HBM_PEAK_GBS, 4),
+                   "weight_bytes_per_layer": weight_bytes})
+    if prefill:
+        flops = 2.0 * R * (cfg.H * 2 * cfg.I + cfg.I * cfg.H)
+        tflops = flops / (ms * 1e-3) / 1e12
+        fc1_tflops = 2.0 * R * cfg.H * 2 * cfg.I / (fc1_ms * 1e-3) / 1e12
+        result.update({"layer_tflops": round(tflops, 2), "mfma_frac_layer": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                       "fc1_tflops": round(fc1_tflops, 2),
+                       "fc1_mfma_frac": round(fc1_tflops / MFMA_BF16_PEAK_TFLOPS, 4)})
+    traffic = measured_traffic(tname, sources)
+    result["roofline"] = {"bound": "hbm", "kernel": kname, "achieved": round(fc1_gbs, 2), "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": round(fc1_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                          "avg_us": round(fc1_ms * 1e3, 3), "bytes_per_launch": fc1_bytes}
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(L, weight_bytes, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
+        result["cpu_baseline"] = (cpu_baseline_prefill(L, D, fc1_w + fc2_w, args.cpu_seconds) if prefill
+                                  else cpu_baseline_layer(L, weight_bytes, args.cpu_seconds))
+    return result
 
 
-def cpu_baseline(L, weight_bytes, budget_s):
+def bench_dequant(args, torch, q, synth, np):
+    cfg = synth.DEQUANT
+    dev = torch.device("cuda:0")
+    w, s, g = synth.dequant_inputs(cfg)
+    fmt = q.QMOE_FMT_MXFP4 if cfg.fmt == synth.MXFP4 else q.QMOE_FMT_NVFP4
+    sets = 4   # input/output buffer sets: ~1 GB, beyond the Infinity Cache
+    bufs = []
+    for _ in range(sets):
+        wd = q.FP4Weights(torch.from_numpy(w).to(dev), torch.from_numpy(s).to(dev),
+                          None if g is None else torch.from_numpy(g).to(dev), fmt)
+        bufs.append((wd, torch.empty((cfg.E, cfg.N, cfg.K), dtype=torch.bfloat16, device=dev)))
+    rd = w.nbytes + s.nbytes + (0 if g is None else g.nbytes)
+    wr = cfg.E * cfg.N * cfg.K * 2
+    stream = torch.cuda.Stream()
+    tm = Timer(torch, stream)
+
+    def step(i):
+        wd, out = bufs[i % sets]
+        q.qmoe_dequant_fp4(wd, out)
+
+    ms = tm.run(step, sets, args.steps, args.warmup, args.eager)
+    gbs = (rd + wr) / (ms * 1e-3) / 1e9
+    config = {"workload": cfg.name, "read_bytes": rd, "write_bytes": wr, "buffer_sets": sets,
+              "launch": "eager" if args.eager else "hip_graph"}
+    result = base_result("MXFP4 standalone dequant GB/s (read + write bytes)", gbs, "GB/s", args, ms, config,
+                         dtype="u8")
+    traffic = measured_traffic("dequant", ("dequant.hip", "device_common.h", "qmoe_internal.h"))
+    result["roofline"] = {"bound": "hbm", "kernel": "dequant_kernel<MXFP4>", "achieved": round(gbs, 2),
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                          "traffic": traffic, "avg_us": round(ms * 1e3, 3), "bytes_per_launch": rd + wr}
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_dequant(w, s, g, cfg, args.cpu_seconds)
+    return result
+
+
+def calibrate_copy(args, torch):
+    """A plain device copy of 1 GiB (read 1 GiB + write 1 GiB per launch)."""
+    n = 1 << 30
+    dev = torch.device("cuda:0")
+    a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    stream = torch.cuda.Stream()
+    tm = Timer(torch, stream)
+    ms = tm.run(lambda i: b.copy_(a), 1, args.steps, args.warmup, eager=True)
+    return {"calibration": "device copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
+            "avg_us": round(ms * 1e3, 3), "gbs": round(2 * n / (ms * 1e-3) / 1e9, 2)}
+
+
+def cpu_baseline_layer(L, weight_bytes, budget_s):
     """The oracle as it stands, one thread, on the same layer (bounded sample)."""
     from threadpoolctl import threadpool_limits
 
@@ -215,6 +295,75 @@ def cpu_baseline(L, weight_bytes, budget_s):
             "sample": f"{n} full layers of {L.cfg.name} (route, FC1+SwiGLU, FC2, finalize), float64 numpy, "
                       f"{per_layer * 1e3:.1f} ms/layer",
             "host_cores_total": os.cpu_count()}
+
+
+def cpu_baseline_prefill(L, D, expert_bytes, budget_s):
+    """The oracle's FC1+SwiGLU and FC2 on the rows of the first experts (in expert order) until the
+    budget runs out; GB/s on the weight bytes of the experts processed."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import dequant, moe, route
+    c = L.cfg
+    with threadpool_limits(limits=1):
+        idx, _ = route.route_topk(L.logits, c.k)
+        off, p2e, _ = route.expert_maps(idx, c.E)
+        x64 = moe.codecs.bf16_to_f64(L.x)
+        n, rows, t0 = 0, 0, time.perf_counter()
+        for e in range(c.E):
+            lo, hi = int(off[e]), int(off[e + 1])
+            if lo == hi:
+                continue
+            u = x64[np.asarray(p2e[lo:hi]) // c.k] @ dequant.dequant_expert_f64(L.w1[e], L.s1[e], None, c.fmt)
+            hb = moe.codecs.bf16_from_f64(moe.swiglu(u[:, 0::2], u[:, 1::2]))
+            moe.codecs.bf16_to_f64(hb) @ dequant.dequant_expert_f64(L.w2[e], L.s2[e], None, c.fmt)
+            n, rows = n + 1, rows + hi - lo
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        el = time.perf_counter() - t0
+    return {"value": round(n * expert_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"FC1+SwiGLU and FC2 of {n} of {D} routed experts ({rows} of {c.rows} rows) of {c.name}, "
+                      f"float64 numpy, {el:.1f} s", "host_cores_total": os.cpu_count()}
+
+
+def cpu_baseline_dequant(w, s, g, cfg, budget_s):
+    from threadpoolctl import threadpool_limits
+
+    from oracle import dequant
+    with threadpool_limits(limits=1):
+        n, t0 = 0, time.perf_counter()
+        while n < cfg.E:
+            dequant.dequant_bf16(w[n:n + 1], s[n:n + 1], None if g is None else g[n:n + 1], cfg.fmt)
+            n += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        el = time.perf_counter() - t0
+    per = (w[0].nbytes + s[0].nbytes + cfg.N * cfg.K * 2)
+    return {"value": round(n * per / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} of {cfg.E} experts of {cfg.name}, float64 numpy, {el:.1f} s",
+            "host_cores_total": os.cpu_count()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        print(json.dumps(calibrate_copy(args, torch)), flush=True)
+        return
+    import fp4_weight_only_amd as q
+    import synth
+    if args.workload == "dequant":
+        result = bench_dequant(args, torch, q, synth, np)
+    else:
+        result = bench_layer(args, torch, q, synth, np)
+    print(json.dumps(result), flush=True)
 
 
 if __name__ == "__main__":
