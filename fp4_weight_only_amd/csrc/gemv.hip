@@ -16,16 +16,12 @@
 //   resource: the row offset is a scalar (no per-load vector address math)
 //   and rows past K or columns past N fall outside the resource and read
 //   as zero.  All 32 loads of a lane are issued before any decode.
-// * Decode: two k rows of one dword each become K-paired bf16x2 registers by
-//   bit assembly (no table); v_dot2c_f32_bf16 multiplies a K pair of
+// * Decode: two k rows of one dword each become K-paired bf16x2 registers:
+//   gfx950's FP4 conversion turns a byte (two codes) into two exact bf16 and
+//   a byte permute pairs row k with row k+1 (four VALU instructions per 8
+//   codes, no table, no branch); v_dot2c_f32_bf16 multiplies a K pair of
 //   activations by a K pair of weights.  Products are summed per scale block
 //   and the block scale is applied once per (row, column, block).
-// * The bf16 weights carry a factor 2^-126 (the code bits sit at the bottom
-//   of the exponent field).  The staged activations are pre-scaled by a
-//   power of two P chosen per row and 32-wide k group from the group's
-//   largest |a|, which keeps every product a normal float32; the group's
-//   partial is multiplied back by 2^(126-P).  Power-of-two scaling commutes
-//   with rounding, so this changes no result.
 // * Split-K inside the workgroup: the two halves of a wave add through a
 //   lane swap, then the W waves through LDS, in a fixed order.  When K spans
 //   several chunks each workgroup writes g * partial to the workspace and a
@@ -36,8 +32,8 @@
 //   XCDs and all k chunks of an item land on the same XCD.
 // * The routed experts are found on the device from expert_offsets (wave
 //   ballots); grids are sized for the worst case and idle slots exit.  Rows
-//   of an expert are processed in passes of one row (single-token batches)
-//   or of two rows.
+//   of an expert are processed in passes of one row (single-token batches),
+//   two rows (up to 3 tokens) or four rows.
 #include "device_common.h"
 #include "qmoe_internal.h"
 
@@ -106,13 +102,12 @@ __device__ __forceinline__ float swiglu(float gate, float lin, float alpha, floa
 
 template <int MRMAX>
 struct Smem {
-  uint16_t xs[MRMAX][kMaxChunkK];                 // pre-scaled activations of the chunk
-  int pexp[MRMAX][kMaxChunkK / kGemvLaneK];       // pre-scale exponent per (row, 32-k group)
+  uint16_t xs[MRMAX][kMaxChunkK];                 // activations of the chunk
   float red[kGemvMaxWaves][MRMAX][kGemvTileN];    // per-wave partial sums
 };
 
 // Decode + dot2 over the lane's 32 k rows for MR staged rows; the wave's
-// partial (halves added, multiplied back by 2^(126-P)) goes to LDS.
+// partial (the two halves added) goes to LDS.
 template <int FMT, int MR, int MRMAX>
 __device__ __forceinline__ void lane_dot(Smem<MRMAX> &sm, const uint32_t (&A)[kGemvLaneK], const u32x2_t (&SB)[2],
                                          int g, int wave, int lane) {
@@ -147,7 +142,7 @@ __device__ __forceinline__ void lane_dot(Smem<MRMAX> &sm, const uint32_t (&A)[kG
 #pragma unroll
     for (int kp = 0; kp < B / 2; ++kp) {
       uint32_t w[8];
-      e2m1_kpair_to_bf16x2(A[b * B + 2 * kp], A[b * B + 2 * kp + 1], w);
+      e2m1_kpair_cvt(A[b * B + 2 * kp], A[b * B + 2 * kp + 1], w);
 #pragma unroll
       for (int r = 0; r < MR; ++r) {
         const uint32_t xp =
@@ -175,12 +170,9 @@ __device__ __forceinline__ void lane_dot(Smem<MRMAX> &sm, const uint32_t (&A)[kG
   const int nl = lane & 31;
 #pragma unroll
   for (int r = 0; r < MR; ++r) {
-    const int sh = 126 - sm.pexp[r][g];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const float v = ldexpf(acc[r][c], sh);
-      acc[r][c] = v + __shfl_xor(v, 32);  // lower half + upper half, same order in every lane pair
-    }
+    for (int c = 0; c < 8; ++c)
+      acc[r][c] = acc[r][c] + __shfl_xor(acc[r][c], 32);  // lower half + upper half, same order in every lane pair
     if (lane < 32) {
       *(float4 *)&sm.red[wave][r][nl * 8] = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
       *(float4 *)&sm.red[wave][r][nl * 8 + 4] = make_float4(acc[r][4], acc[r][5], acc[r][6], acc[r][7]);
@@ -195,7 +187,7 @@ __device__ __forceinline__ void store_fc1(const GemvArgs &a, int p, int col, flo
     a.out_bf16[(size_t)p * (a.N >> 1) + (col >> 1)] = (uint16_t)bf16_rne(swiglu(u, partner, a.alpha, a.beta, a.limit));
 }
 
-// Both row modes use the same workgroup size.
+// Every row mode uses the same workgroup size.
 template <int MRMAX>
 constexpr int max_waves() { return kGemvMaxWaves; }
 
@@ -258,12 +250,12 @@ __global__ __launch_bounds__(max_waves<MRMAX>() * 64) void fp4_gemv_kernel(GemvA
     for (int i = 0; i < kGemvLaneK; ++i) asm volatile("" : "+v"(A[i]));
     const int rem = m - rbase;
     const int mr = rem < MRMAX ? rem : MRMAX;
-    // Stage the chunk's activation rows, pre-scaled per (row, 32-k group):
-    // one thread per 8 values, 4 consecutive threads per group.
-    {
+    // Stage the chunk's activation rows (rows past mr as zeros): one thread
+    // per 8 values.
+    for (int i = tid; i < MRMAX * (KC / 8); i += W * 64) {
       const int per_row = KC / 8;
-      const int r = tid / per_row;
-      const int kk = (tid - r * per_row) * 8;
+      const int r = i / per_row;
+      const int kk = (i - r * per_row) * 8;
       const int kabs = kc * KC + kk;
       u32x4_t v = {0u, 0u, 0u, 0u};
       if (r < mr && kabs < a.K) {
@@ -271,34 +263,16 @@ __global__ __launch_bounds__(max_waves<MRMAX>() * 64) void fp4_gemv_kernel(GemvA
         const int src = a.fc1 ? (a.p2e[p] / a.topk) : p;
         v = *(const u32x4_t *)(a.act + (size_t)src * a.K + kabs);
       }
-      uint32_t mx = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        mx = max(mx, v[q] & 0x7FFFu);
-        mx = max(mx, (v[q] >> 16) & 0x7FFFu);
-      }
-      mx = max(mx, dpp_u32<kDppXor1>(mx));
-      mx = max(mx, dpp_u32<kDppXor2>(mx));
-      const int ef = (int)(mx >> 7);  // biased exponent of max |a| (0: zero/subnormal)
-      const int P = (mx == 0u) ? 0 : 252 - (ef < 1 ? 1 : ef);
-      u32x4_t o;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float lo = ldexpf(__uint_as_float(v[q] << 16), P);
-        const float hi = ldexpf(__uint_as_float(v[q] & 0xFFFF0000u), P);
-        o[q] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
-      }
-      if (r < MRMAX) {
-        *(u32x4_t *)&sm.xs[r][kk] = o;
-        if ((tid & 3) == 0) sm.pexp[r][kk / kGemvLaneK] = P;
-      }
+      *(u32x4_t *)&sm.xs[r][kk] = v;
     }
     __syncthreads();
 
     if (MRMAX == 1 || mr == 1)
       lane_dot<FMT, 1, MRMAX>(sm, A, SB, g, wave, lane);
+    else if (MRMAX == 2 || mr == 2)
+      lane_dot<FMT, 2, MRMAX>(sm, A, SB, g, wave, lane);
     else
-      lane_dot<FMT, MRMAX, MRMAX>(sm, A, SB, g, wave, lane);
+      lane_dot<FMT, 4, MRMAX>(sm, A, SB, g, wave, lane);  // 3 or 4 rows
     __syncthreads();
 
     // ---- reduce the W waves (fixed order); one thread per column ------------
@@ -351,7 +325,8 @@ static void plan_chunks(int items, int K, int maxw, int &nchunks, int &waves) {
 }
 
 static int plan_max_waves(int max_rows_per_expert) {
-  return max_rows_per_expert <= 1 ? max_waves<1>() : max_waves<2>();
+  (void)max_rows_per_expert;
+  return kGemvMaxWaves;
 }
 
 size_t gemv_workspace_bytes(int32_t rows, int32_t max_rows_per_expert, int32_t E, int32_t K, int32_t N) {
@@ -374,18 +349,23 @@ hipError_t launch_fp4_gemv(const GemvArgs &a, int fmt, int max_rows_per_expert, 
   const int items = a.nslots * a.ntiles;
   const dim3 grid((unsigned)(((items + 7) / 8) * 8 * a.nchunks));
   const dim3 block((unsigned)(a.waves * 64));
-  // One row per pass when no expert can hold more than one row (one token),
-  // else two: the 2-row body needs ~120 VGPRs, 4 rows would need ~170.
+  // Rows per pass: one when no expert can hold more than one row (one
+  // token), two for up to three tokens, else four.
+  const int mr = max_rows_per_expert <= 1 ? 1 : (max_rows_per_expert <= 3 ? 2 : 4);
   if (fmt == 0) {
-    if (max_rows_per_expert <= 1)
+    if (mr == 1)
       fp4_gemv_kernel<0, 1><<<grid, block, 0, s>>>(a);
-    else
+    else if (mr == 2)
       fp4_gemv_kernel<0, 2><<<grid, block, 0, s>>>(a);
-  } else {
-    if (max_rows_per_expert <= 1)
-      fp4_gemv_kernel<1, 1><<<grid, block, 0, s>>>(a);
     else
+      fp4_gemv_kernel<0, 4><<<grid, block, 0, s>>>(a);
+  } else {
+    if (mr == 1)
+      fp4_gemv_kernel<1, 1><<<grid, block, 0, s>>>(a);
+    else if (mr == 2)
       fp4_gemv_kernel<1, 2><<<grid, block, 0, s>>>(a);
+    else
+      fp4_gemv_kernel<1, 4><<<grid, block, 0, s>>>(a);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.nchunks == 1) return err;
