@@ -44,44 +44,29 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t w) {
   return __builtin_amdgcn_cvt_f32_fp8((int)w, SEL);
 }
 
-// Two E2M1 words A (row k) and B (row k+1), each holding 8 columns (low
-// nibble first), become 8 bf16x2 registers: column c as {lo: A.c, hi: B.c},
-// the K-pair a dot2 consumes.  Each bf16 is assembled directly from the code
-// bits: sign to bit 15, exponent+mantissa bits to bits 8..6, so the value is
-// e2m1 * 2^-126 (code 1 is the bf16 subnormal 2^-127).  The caller folds the
-// 2^126 into a power-of-two pre-scale of the activations.
-__device__ __forceinline__ void e2m1_kpair_to_bf16x2(uint32_t a, uint32_t b, uint32_t (&w)[8]) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    // bytes [a.j, 0, b.j, 0]: each 16-bit half holds one byte (two codes).
-    const uint32_t sel = (uint32_t)j | (0x0Cu << 8) | ((uint32_t)(4 + j) << 16) | (0x0Cu << 24);
-    const uint32_t q = __builtin_amdgcn_perm(b, a, sel);
-    const uint32_t ev_code = q << 6;                  // even code -> bits 8..6 / 24..22
-    const uint32_t ev_sign = (q << 12) & 0x80008000u;  // even sign -> bits 15 / 31
-    const uint32_t od_code = q << 2;                  // odd code  -> bits 8..6 / 24..22
-    const uint32_t od_sign = (q << 8) & 0x80008000u;   // odd sign  -> bits 15 / 31
-    w[2 * j] = (ev_code & 0x01C001C0u) | ev_sign;
-    w[2 * j + 1] = (od_code & 0x01C001C0u) | od_sign;
-  }
-}
-
-// The same K pairs from gfx950's FP4 conversion: one instruction turns byte j
-// of a word (codes of columns 2j and 2j+1) into two bf16 (scale 1: the exact
-// code values), and a byte permute pairs row k with row k+1 of each column.
-// Four VALU instructions per 8 codes, against about nine for bit assembly.
+// Two E2M1 words A (row k) and B (row k+1), 8 columns each (low nibble
+// first), become 8 bf16x2 K pairs, column c as {lo: A.c, hi: B.c}, the pair
+// a dot2 consumes.  A nibble zip puts the codes of one column's two rows into
+// one byte (even columns from the low nibbles, odd columns from the high
+// nibbles: two shifts and two bit-field inserts), and gfx950's FP4
+// conversion turns each byte into its two exact bf16 values (scale 1).
+// Twelve VALU instructions per 16 codes, no table, no branch.
 template <int J>
-__device__ __forceinline__ void e2m1_kpair_cvt_byte(uint32_t a, uint32_t b, uint32_t &even, uint32_t &odd) {
-  const uint32_t pa = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(a, 1.0f, J));
-  const uint32_t pb = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(b, 1.0f, J));
-  even = __builtin_amdgcn_perm(pb, pa, 0x05040100u);  // {pa.lo, pb.lo}
-  odd = __builtin_amdgcn_perm(pb, pa, 0x07060302u);   // {pa.hi, pb.hi}
+__device__ __forceinline__ uint32_t fp4_byte_to_bf16x2(uint32_t v) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, J));
 }
 
 __device__ __forceinline__ void e2m1_kpair_cvt(uint32_t a, uint32_t b, uint32_t (&w)[8]) {
-  e2m1_kpair_cvt_byte<0>(a, b, w[0], w[1]);
-  e2m1_kpair_cvt_byte<1>(a, b, w[2], w[3]);
-  e2m1_kpair_cvt_byte<2>(a, b, w[4], w[5]);
-  e2m1_kpair_cvt_byte<3>(a, b, w[6], w[7]);
+  const uint32_t ev = (a & 0x0F0F0F0Fu) | ((b << 4) & 0xF0F0F0F0u);
+  const uint32_t od = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+  w[0] = fp4_byte_to_bf16x2<0>(ev);
+  w[1] = fp4_byte_to_bf16x2<0>(od);
+  w[2] = fp4_byte_to_bf16x2<1>(ev);
+  w[3] = fp4_byte_to_bf16x2<1>(od);
+  w[4] = fp4_byte_to_bf16x2<2>(ev);
+  w[5] = fp4_byte_to_bf16x2<2>(od);
+  w[6] = fp4_byte_to_bf16x2<3>(ev);
+  w[7] = fp4_byte_to_bf16x2<3>(od);
 }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {

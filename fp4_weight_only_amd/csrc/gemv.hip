@@ -16,10 +16,9 @@
 //   resource: the row offset is a scalar (no per-load vector address math)
 //   and rows past K or columns past N fall outside the resource and read
 //   as zero.  All 32 loads of a lane are issued before any decode.
-// * Decode: two k rows of one dword each become K-paired bf16x2 registers:
-//   gfx950's FP4 conversion turns a byte (two codes) into two exact bf16 and
-//   a byte permute pairs row k with row k+1 (four VALU instructions per 8
-//   codes, no table, no branch); v_dot2c_f32_bf16 multiplies a K pair of
+// * Decode: a nibble zip and gfx950's FP4 -> bf16 conversion turn two k rows
+//   of a lane's 8 columns into 8 K-paired bf16x2 registers (twelve VALU
+//   instructions per 16 codes, no table, no branch); v_dot2c_f32_bf16 multiplies a K pair of
 //   activations by a K pair of weights.  Products are summed per scale block
 //   and the block scale is applied once per (row, column, block).
 // * Split-K inside the workgroup: the two halves of a wave add through a
@@ -43,9 +42,10 @@ constexpr int kMaxChunkK = kGemvMaxWaves * kGemvWaveK;
 constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past any resource: loads return 0
 constexpr int kBufNontemporal = 2;            // cache policy: streaming (nt)
 
-// Finds the expert holding the s-th non-empty row range.  Every lane gets
-// the same answer; returns -1 if fewer than s+1 experts have rows.
-__device__ __forceinline__ int find_slot_expert(const int32_t *__restrict__ off, int E, int s) {
+// Finds the expert holding the s-th non-empty row range, with its first row
+// and row count.  Every lane gets the same answer; returns -1 if fewer than
+// s+1 experts have rows.
+__device__ __forceinline__ int find_slot_expert(const int32_t *__restrict__ off, int E, int s, int &row0, int &m) {
   const int lane = lane_id();
   const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int o[5];
@@ -61,16 +61,22 @@ __device__ __forceinline__ int find_slot_expert(const int32_t *__restrict__ off,
     ne[i] = (4 * lane + i < E) && (o[i + 1] > o[i]);
     before += __popcll(__ballot(ne[i]) & lt);
   }
-  int found = -1;
+  int found = -1, r0 = 0, cnt = 0;
   int run = before;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if (ne[i] && run == s) found = 4 * lane + i;
+    if (ne[i] && run == s) {
+      found = 4 * lane + i;
+      r0 = o[i];
+      cnt = o[i + 1] - o[i];
+    }
     run += ne[i] ? 1 : 0;
   }
   const unsigned long long fb = __ballot(found >= 0);
   if (fb == 0ull) return -1;
   const int src = __ffsll((long long)fb) - 1;
+  row0 = __builtin_amdgcn_readlane(r0, src);
+  m = __builtin_amdgcn_readlane(cnt, src);
   return __builtin_amdgcn_readlane(found, src);
 }
 
@@ -139,14 +145,28 @@ __device__ __forceinline__ void lane_dot(Smem<MRMAX> &sm, const uint32_t (&A)[kG
     for (int r = 0; r < MR; ++r)
 #pragma unroll
       for (int c = 0; c < 8; ++c) bs[r][c] = 0.f;
+    // More rows: the activation K pairs are read one K pair ahead, so the
+    // LDS latency hides behind the current pair's decode and dot2s.
+    uint32_t xn[MR];
+    if constexpr (!kPre) {
+#pragma unroll
+      for (int r = 0; r < MR; ++r) xn[r] = *(const uint32_t *)&sm.xs[r][g * kGemvLaneK + b * B];
+    }
 #pragma unroll
     for (int kp = 0; kp < B / 2; ++kp) {
+      uint32_t xc[MR];
+      if constexpr (!kPre) {
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+          xc[r] = xn[r];
+          if (kp + 1 < B / 2) xn[r] = *(const uint32_t *)&sm.xs[r][g * kGemvLaneK + b * B + 2 * (kp + 1)];
+        }
+      }
       uint32_t w[8];
       e2m1_kpair_cvt(A[b * B + 2 * kp], A[b * B + 2 * kp + 1], w);
 #pragma unroll
       for (int r = 0; r < MR; ++r) {
-        const uint32_t xp =
-            kPre ? xq[kPre ? kp : 0] : *(const uint32_t *)&sm.xs[r][g * kGemvLaneK + b * B + 2 * kp];
+        const uint32_t xp = kPre ? xq[kPre ? kp : 0] : xc[r];
 #pragma unroll
         for (int c = 0; c < 8; ++c) bs[r][c] = dot2_bf16(xp, w[c], bs[r][c]);
       }
@@ -212,10 +232,12 @@ __global__ __launch_bounds__(max_waves<MRMAX>() * 64) void fp4_gemv_kernel(GemvA
   const int slot = item / a.ntiles;
   const int tile = item - slot * a.ntiles;
 
-  const int e = find_slot_expert(a.offsets, a.E, slot);
+  // FC1 gathers its x rows through perm_to_expanded (at most 64 rows on this
+  // path): fetch it together with the offsets, one lane per row.
+  const int p2e_l = (a.fc1 && lane < a.rows) ? a.p2e[lane] : 0;
+  int row0 = 0, m = 0;
+  const int e = find_slot_expert(a.offsets, a.E, slot, row0, m);
   if (e < 0) return;  // uniform over the workgroup
-  const int row0 = a.offsets[e];
-  const int m = a.offsets[e + 1] - row0;
 
   // ---- weight and scale loads of this lane ----------------------------------
   const int nl = lane & 31;
@@ -252,18 +274,22 @@ __global__ __launch_bounds__(max_waves<MRMAX>() * 64) void fp4_gemv_kernel(GemvA
     const int mr = rem < MRMAX ? rem : MRMAX;
     // Stage the chunk's activation rows (rows past mr as zeros): one thread
     // per 8 values.
-    for (int i = tid; i < MRMAX * (KC / 8); i += W * 64) {
+    // The loop is wave-uniform so the row lookup runs with every lane active.
+    for (int i0 = wave * 64; i0 < MRMAX * (KC / 8); i0 += W * 64) {
+      const int i = i0 + lane;
+      const bool on = i < MRMAX * (KC / 8);
       const int per_row = KC / 8;
-      const int r = i / per_row;
+      const int r = on ? i / per_row : 0;
       const int kk = (i - r * per_row) * 8;
       const int kabs = kc * KC + kk;
+      const int p = row0 + rbase + r;
+      const int tok = __shfl(p2e_l, p & 63, 64) / a.topk;
       u32x4_t v = {0u, 0u, 0u, 0u};
-      if (r < mr && kabs < a.K) {
-        const int p = row0 + rbase + r;
-        const int src = a.fc1 ? (a.p2e[p] / a.topk) : p;
+      if (on && r < mr && kabs < a.K) {
+        const int src = a.fc1 ? tok : p;
         v = *(const u32x4_t *)(a.act + (size_t)src * a.K + kabs);
       }
-      *(u32x4_t *)&sm.xs[r][kk] = v;
+      if (on) *(u32x4_t *)&sm.xs[r][kk] = v;
     }
     __syncthreads();
 
