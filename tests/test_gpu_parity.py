@@ -208,9 +208,13 @@ def test_every_code_in_every_nibble_through_the_gemv(fmt):
     assert np.count_nonzero(diff) <= 2, np.nonzero(diff)
 
 
-@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "mxfp4_g"])
 def test_dequant_small_exhaustive_scales(fmt):
+    """Every scale byte (NaN bytes aside) with random codes; MXFP4 with and
+    without a global scale (the two take different conversion paths)."""
     import fp4_weight_only_amd as q
+    with_g = fmt == "mxfp4_g"
+    fmt = "mxfp4" if with_g else fmt
     B = 16 if fmt == "nvfp4" else 32
     E, K, N = 2, 64 * 8, 256 * 2
     rng = np.random.default_rng(12)
@@ -222,14 +226,35 @@ def test_dequant_small_exhaustive_scales(fmt):
         g = np.array([1.3, 0.6], np.float32)
     else:
         s[s == 255] = 127
-        g = None
+        g = np.array([1.3, 0.6], np.float32) if with_g else None
     out = torch.empty((E, N, K), dtype=torch.bfloat16, device="cuda")
-    print_case("dequant small", fmt)
+    print_case("dequant small", fmt, "g" if g is not None else "")
     q.qmoe_dequant_fp4(weights_dev(w, s, g, fmt), out)
     torch.cuda.synchronize()
     ref = dequant.dequant_bf16(w, s, g, fmt)
     assert np.array_equal(bf16_host(out), ref)
     _ = rng
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+@pytest.mark.parametrize("K,N", [(320, 512), (320, 256), (512, 256)])
+def test_dequant_tile_shapes(fmt, K, N):
+    """Shapes the largest dequant tile does not divide (K % 128, N % 512)."""
+    import fp4_weight_only_amd as q
+    B = 16 if fmt == "nvfp4" else 32
+    E = 3
+    w = synth.packed_codes(synth.stream(2, 2), (E, K, N // 2))
+    if fmt == "nvfp4":
+        s = synth.e4m3_scales(synth.stream(2, 3), (E, K // B, N))
+        g = synth.global_scales(synth.stream(2, 4), E)
+    else:
+        s = synth.e8m0_scales(synth.stream(2, 3), (E, K // B, N))
+        g = None
+    out = torch.empty((E, N, K), dtype=torch.bfloat16, device="cuda")
+    print_case("dequant shape", fmt, K, N)
+    q.qmoe_dequant_fp4(weights_dev(w, s, g, fmt), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_host(out), dequant.dequant_bf16(w, s, g, fmt))
 
 
 def test_dequant_full_config():
