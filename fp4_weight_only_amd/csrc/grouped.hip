@@ -1,5 +1,5 @@
 // Prefill path: grouped GEMM over routed rows with bf16 MFMA, FP4 weights
-// dequantised into LDS tiles, gfx950.
+// kept packed in LDS and decoded straight into MFMA operands, gfx950.
 //
 // What it computes (operator documentation section 4.3, the dequant-to-A16
 // path for shapes outside the decode GEMV; section 9b.1/9b.5, prefill-sized
@@ -10,28 +10,32 @@
 //
 // gfx950 design:
 // * Work item = (expert, 64-row m tile, 128-column n tile); a workgroup of 4
-//   waves (2 x 2) computes 64 x 128 with v_mfma_f32_16x16x32_bf16, each wave
-//   32 rows x 64 columns (2 x 4 MFMA tiles, 32 float32 accumulators).
-// * The k loop steps 64 rows.  Per step the activation tile (64 rows x 64 k,
-//   rows gathered through the permutation for FC1) and the packed weight
-//   tile (64 k x 128 columns, 4 KB) are loaded to registers one step ahead,
-//   then written to a double-buffered LDS tile; the weight tile is
-//   dequantised on the way into LDS, stored transposed ([n][k]) so each lane
-//   reads its MFMA operand (8 consecutive k of one column) as one 16-byte
-//   read.  One barrier per step.
-// * Dequant: the product code * block scale is exact in bf16 (2 significant
-//   bits times a power of two, or times E4M3's 4 bits), so the MFMA operand
-//   is the exact weight without the global scale; g is applied to the float32
-//   accumulator in the epilogue.  MXFP4 tiles use the gfx950 scaled FP4->bf16
-//   conversion (the scale's exponent is the E8M0 block scale), one per column
-//   per K pair, plus one byte permute to pair k and k+1.  NVFP4 tiles are
-//   dequantised through float32 (code value times the E4M3 scale).
-// * 16-row MFMA sub-tiles with no routed rows are skipped, so a small expert
-//   costs one 16-row MFMA tile, not 64.
+//   waves steps through K in 128-k slices.  Wave w owns columns 32w..32w+31
+//   (two 16-column MFMA tiles) for every live 16-row sub-tile of the m tile,
+//   with v_mfma_f32_16x16x32_bf16.  Most experts of a prefill batch hold a
+//   handful of rows, so the cost is streaming and decoding weights; no weight
+//   element is decoded or read from LDS by more than one wave.
+// * Weights stay packed in LDS.  Each thread loads an 8 k x 8 column block
+//   of codes (8 dwords), and a nibble zip plus byte permutes turn it into
+//   one dword per column holding that column's 8 consecutive k codes: the
+//   MFMA B operand of one lane.  LDS holds the slice column-major (0.5 byte
+//   per weight, written once, read once); columns are rotated within groups
+//   of 8 so both the writes and the operand reads spread over all banks.
+// * Decode on read: four gfx950 FP4 -> bf16 conversions per operand.  For
+//   MXFP4 the E8M0 block scale is the conversion's exponent (exact); for
+//   NVFP4 the codes convert to float32, the E4M3 scale multiplies exactly
+//   and the hardware pack to bf16 is exact (2 x 4 significant bits).  The
+//   global scale multiplies the float32 accumulator in the epilogue.
+// * Activations: 64 rows x 128 k bf16 per slice (rows gathered through the
+//   permutation for FC1), 16-byte chunks XOR-swizzled by row so the operand
+//   reads are conflict free.
+// * Pipeline: global loads two slices ahead in registers, LDS double
+//   buffered, one barrier per slice.  16-row sub-tiles with no routed rows
+//   are skipped.
 // * Work items: the (expert, m tile) list is found on the device from
 //   expert_offsets; the grid covers the worst case (rows/64 + experts tiles)
 //   and idle items exit.  The m tiles of one expert for one n tile land on
-//   the same XCD, so repeated weight tiles of hot experts meet in one L2.
+//   the same XCD, so repeated weight slices of hot experts meet in one L2.
 #include "device_common.h"
 #include "qmoe_internal.h"
 
@@ -39,15 +43,21 @@ namespace qmoe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kBM = 64, kBN = 128, kBK = 64;
-constexpr int kLdA = kBK + 8;  // bf16 per LDS row of the activation tile (padding against bank conflicts)
-constexpr int kLdB = kBK + 8;  // bf16 per LDS row of the transposed weight tile (16-byte aligned rows)
+constexpr int kBM = 64, kBN = 128, kBK = 128;
+constexpr int kAChunks = kBK / 8;  // 16-byte chunks per activation row of a slice
+constexpr int kBStride = 18;       // dwords per LDS weight column (16 used; 3 workgroups fit a CU)
+constexpr uint32_t kGOutOfRange = 0x80000000u;
 
 struct GroupedSmem {
-  uint16_t a[2][kBM][kLdA];
-  uint16_t b[2][kBN][kLdB];
+  u32x4_t a[2][kBM][kAChunks];      // activations, chunk c of row r at c ^ (r & 15)
+  uint32_t bt[2][kBN][kBStride];    // packed codes, column-major, 8 k per dword
+  uint8_t sc[2][kBK / 16][kBN];     // block scales of the slice (B = 32 uses 4 rows)
 };
+
+// LDS slot of tile column n: rotated by n / 8 inside its group of 8.
+__device__ __forceinline__ int bt_col(int n) { return (n & ~7) | ((n + (n >> 3)) & 7); }
 
 // Finds the s-th (expert, m tile) item: experts in ascending order, each with
 // ceil(rows/64) tiles.  Returns the expert (-1 past the last item) and the
@@ -95,47 +105,36 @@ __device__ __forceinline__ float grouped_swiglu(float gate, float lin, float alp
   return G / (1.0f + expf(-alpha * G)) * (L + beta);
 }
 
-// Dequantises 16 columns x one K pair (rows k, k+1 as two 8-byte words) into
-// 16 bf16x2 registers: column c as {lo: w(k, c), hi: w(k+1, c)}.
+// One slice's global loads for one thread.
+struct SliceRegs {
+  u32x4_t A[4];    // activation row ra, k = 32 * aq .. +31
+  uint32_t B[8];   // packed rows 8 * rg + i, columns 8 * cg .. +7
+  uint32_t S;      // four block-scale bytes
+};
+
+// MFMA B operand of one lane: column n's 8 consecutive k codes (one dword),
+// decoded to bf16 with the column's block scale.
 template <int FMT>
-__device__ __forceinline__ void dequant_kpair16(u32x2_t r0, u32x2_t r1, u32x4_t sb, uint32_t (&out)[16]) {
-#pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    const uint32_t sbyte = (sb[c >> 2] >> (8 * (c & 3))) & 0xFFu;
-    const int wd = c >> 3;          // dword holding column c
-    const int byte = (c >> 1) & 3;  // byte inside it
-    if constexpr (FMT == 1) {
-      const float sf = e8m0_to_f32(sbyte);
-      // two codes -> two bf16 per conversion; keep the half of column c
-      uint32_t p0, p1;
-      switch (byte) {
-        case 0:
-          p0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(r0[wd], sf, 0));
-          p1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(r1[wd], sf, 0));
-          break;
-        case 1:
-          p0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(r0[wd], sf, 1));
-          p1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(r1[wd], sf, 1));
-          break;
-        case 2:
-          p0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(r0[wd], sf, 2));
-          p1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(r1[wd], sf, 2));
-          break;
-        default:
-          p0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(r0[wd], sf, 3));
-          p1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(r1[wd], sf, 3));
-          break;
-      }
-      // bytes of {p1, p0}: take half (c & 1) of each
-      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-      out[c] = __builtin_amdgcn_perm(p1, p0, sel);
-    } else {
-      const float sf = __builtin_amdgcn_cvt_f32_fp8((int)sbyte, 0);
-      const float v0 = e2m1_to_f32(r0[wd] >> (4 * (c & 7))) * sf;  // exact
-      const float v1 = e2m1_to_f32(r1[wd] >> (4 * (c & 7))) * sf;
-      out[c] = (__float_as_uint(v0) >> 16) | (__float_as_uint(v1) & 0xFFFF0000u);
-    }
+__device__ __forceinline__ bf16x8_t decode_operand(uint32_t d, uint32_t sbyte) {
+  u32x4_t o;
+  if constexpr (FMT == 1) {
+    const float sc = __uint_as_float(sbyte << 23);  // E8M0 as the conversion exponent
+    o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 0));
+    o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 1));
+    o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 2));
+    o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 3));
+  } else {
+    const float sf = __builtin_amdgcn_cvt_f32_fp8((int)sbyte, 0);
+    const f32x2_t f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0) * sf;
+    const f32x2_t f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1) * sf;
+    const f32x2_t f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2) * sf;
+    const f32x2_t f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3) * sf;
+    o.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(f0, bf16x2_t));
+    o.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(f1, bf16x2_t));
+    o.z = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2, bf16x2_t));
+    o.w = __builtin_bit_cast(uint32_t, __builtin_convertvector(f3, bf16x2_t));
   }
+  return __builtin_bit_cast(bf16x8_t, o);
 }
 
 template <int FMT>
@@ -159,101 +158,141 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemvArgs a) {
   const int row0 = a.offsets[e] + mt * kBM;
   const int mrows = min(kBM, a.offsets[e + 1] - row0);
   const int n0 = ntile * kBN;
+  const int steps = (a.K + kBK - 1) / kBK;
+  const bool ragged = (a.K % kBK) != 0;  // the last slice holds 64 valid k rows
 
   // ---- loader roles ----------------------------------------------------------
-  // activation tile: thread -> (row, 16 k)
-  const int ar = tid >> 2;
-  const int ak = (tid & 3) * 16;
+  // activations: thread -> (row ra, 32 k)
+  const int ra = tid >> 2;
+  const int aq = tid & 3;
   const uint16_t *arow = nullptr;
-  if (ar < mrows) {
-    const int p = row0 + ar;
+  if (ra < mrows) {
+    const int p = row0 + ra;
     const int src = a.fc1 ? (a.p2e[p] / a.topk) : p;
     arow = a.act + (size_t)src * a.K;
   }
-  // weight tile: thread -> (K pair kp, 16 columns cg*16)
-  const int cg = tid >> 5;  // 0..7
-  const int kp = tid & 31;  // 0..31
+  // weights: thread -> (8 k rows rg, 8 columns cg); 16 lanes read 64 bytes of a row
+  const int cg = tid & 15;
+  const int rg = tid >> 4;
   const uint32_t rowbytes = (uint32_t)(a.N >> 1);
   const int KB = a.K / B;
   const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(a.w + (size_t)e * a.K * rowbytes), (short)0, (int)((uint32_t)a.K * rowbytes), 0x00020000);
   const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(a.scales + (size_t)e * KB * a.N), (short)0, (int)((uint32_t)KB * a.N), 0x00020000);
-  const int bcol = n0 + cg * 16;
-  const uint32_t woff = (uint32_t)(2 * kp) * rowbytes + (uint32_t)(bcol >> 1);
+  const uint32_t woff = (uint32_t)(rg * 8) * rowbytes + (uint32_t)((n0 + cg * 8) >> 1);
+  // scales: thread -> (block row sb, 4 columns sq)
+  const int sq = tid & 31;
+  const int sb = tid >> 5;
+  constexpr int kSBlocks = kBK / B;
 
-  u32x4_t ra0, ra1;
-  u32x2_t rb0, rb1;
-  u32x4_t rs;
-  auto load_step = [&](int k0) {
-    if (arow) {
-      ra0 = *(const u32x4_t *)(arow + k0 + ak);
-      ra1 = *(const u32x4_t *)(arow + k0 + ak + 8);
-    } else {
-      ra0 = u32x4_t{0u, 0u, 0u, 0u};
-      ra1 = ra0;
-    }
-    const uint32_t o = woff + (uint32_t)k0 * rowbytes;
-    rb0 = __builtin_amdgcn_raw_buffer_load_b64(wrsrc, o, 0, 2);
-    rb1 = __builtin_amdgcn_raw_buffer_load_b64(wrsrc, o + rowbytes, 0, 2);
-    rs = __builtin_amdgcn_raw_buffer_load_b128(srsrc, (uint32_t)((k0 + 2 * kp) / B) * (uint32_t)a.N + (uint32_t)bcol, 0, 0);
-  };
-  auto store_step = [&](int buf) {
-    *(u32x4_t *)&sm.a[buf][ar][ak] = ra0;
-    *(u32x4_t *)&sm.a[buf][ar][ak + 8] = ra1;
-    uint32_t d[16];
-    dequant_kpair16<FMT>(rb0, rb1, rs, d);
-#pragma unroll
-    for (int c = 0; c < 16; ++c) *(uint32_t *)&sm.b[buf][cg * 16 + c][2 * kp] = d[c];
-  };
-
-  // ---- MFMA roles: wave (wr, wc) computes rows wr*32.., columns wc*64.. ------
-  const int wr = wave >> 1;
-  const int wc = wave & 1;
-  const int li = lane & 15;
-  const int lk = (lane >> 4) * 8;
-  const bool sub_live[2] = {wr * 32 < mrows, wr * 32 + 16 < mrows};
-  f32x4_t acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int steps = a.K / kBK;
-  load_step(0);
-  for (int s = 0; s < steps; ++s) {
-    const int buf = s & 1;
-    store_step(buf);
-    __syncthreads();
-    if (s + 1 < steps) load_step((s + 1) * kBK);
-#pragma unroll
-    for (int kk = 0; kk < kBK; kk += 32) {
-      bf16x8_t bv[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bv[j] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)&sm.b[buf][wc * 64 + j * 16 + li][kk + lk]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        if (!sub_live[i]) continue;  // wave-uniform
-        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)&sm.a[buf][wr * 32 + i * 16 + li][kk + lk]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[j], acc[i][j], 0, 0, 0);
-      }
-    }
-  }
-
-  // ---- epilogue: lane holds rows 4*(lane/16)+q, column lane%16 of each tile --
-  const float gs = a.gscale ? a.gscale[e] : 1.0f;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    if (!sub_live[i]) continue;
+  auto load_slice = [&](int s, SliceRegs &r) {
+    const int k0 = s * kBK;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int col = n0 + wc * 64 + j * 16 + li;
+      const int kk = k0 + aq * 32 + j * 8;
+      r.A[j] = (arow && kk < a.K) ? *(const u32x4_t *)(arow + kk) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    const uint32_t o = woff + (uint32_t)k0 * rowbytes;
+    if (!ragged || s + 1 < steps) {
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int r = wr * 32 + i * 16 + (lane >> 4) * 4 + qd;
-        const float u = gs * acc[i][j][qd];
+      for (int i = 0; i < 8; ++i) r.B[i] = __builtin_amdgcn_raw_buffer_load_b32(wrsrc, o, i * (int)rowbytes, 2);
+    } else {
+      // rows past K read as zero through an out-of-range vector offset
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        r.B[i] = __builtin_amdgcn_raw_buffer_load_b32(
+            wrsrc, k0 + rg * 8 + i < a.K ? o + (uint32_t)i * rowbytes : kGOutOfRange, 0, 2);
+    }
+    const int kb = k0 / B + sb;
+    r.S = (sb < kSBlocks && kb < KB)
+              ? __builtin_amdgcn_raw_buffer_load_b32(srsrc, (uint32_t)kb * (uint32_t)a.N + (uint32_t)(n0 + sq * 4), 0, 0)
+              : 0u;
+  };
+
+  auto store_slice = [&](int buf, const SliceRegs &r) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sm.a[buf][ra][(aq * 4 + j) ^ (ra & 15)] = r.A[j];
+    // nibble zip of row pairs, then one dword per column (rows 0..7 of the block)
+    uint32_t ev[4], od[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      ev[p] = (r.B[2 * p] & 0x0F0F0F0Fu) | ((r.B[2 * p + 1] << 4) & 0xF0F0F0F0u);
+      od[p] = ((r.B[2 * p] >> 4) & 0x0F0F0F0Fu) | (r.B[2 * p + 1] & 0xF0F0F0F0u);
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t j = (uint32_t)(c >> 1);
+      const uint32_t *z = (c & 1) ? od : ev;
+      const uint32_t lo = __builtin_amdgcn_perm(z[1], z[0], j | ((4u + j) << 8) | 0x0C0C0000u);
+      const uint32_t hi = __builtin_amdgcn_perm(z[3], z[2], 0x00000C0Cu | (j << 16) | ((4u + j) << 24));
+      sm.bt[buf][bt_col(cg * 8 + c)][rg] = lo | hi;
+    }
+    if (sb < kSBlocks) *(uint32_t *)&sm.sc[buf][sb][sq * 4] = r.S;
+  };
+
+  // ---- MFMA roles: wave w owns columns 32w..32w+31 ----------------------------
+  const int li = lane & 15;
+  const int lk = lane >> 4;
+  const int live = (mrows + 15) >> 4;  // 16-row sub-tiles holding routed rows
+  f32x4_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute_slice = [&](int buf, int s) {
+    const int nk = (ragged && s + 1 == steps) ? 2 : 4;  // 32-k sub-steps below K
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks >= nk) break;
+      bf16x8_t bv[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int col = wave * 32 + t * 16 + li;
+        const uint32_t d = sm.bt[buf][bt_col(col)][ks * 4 + lk];
+        const int blk = (ks * 32 + lk * 8) / B;
+        bv[t] = decode_operand<FMT>(d, sm.sc[buf][blk][col]);
+      }
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms) {
+        if (ms >= live) break;  // uniform
+        const int r = ms * 16 + li;
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, sm.a[buf][r][(ks * 4 + lk) ^ (r & 15)]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) acc[ms][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[t], acc[ms][t], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- pipeline: loads two slices ahead, LDS double buffered ------------------
+  SliceRegs r0, r1;
+  load_slice(0, r0);
+  if (steps > 1) load_slice(1, r1);
+  for (int s = 0; s < steps; s += 2) {
+    store_slice(0, r0);
+    if (s + 2 < steps) load_slice(s + 2, r0);
+    __syncthreads();
+    compute_slice(0, s);
+    if (s + 1 >= steps) break;
+    store_slice(1, r1);
+    if (s + 3 < steps) load_slice(s + 3, r1);
+    __syncthreads();
+    compute_slice(1, s + 1);
+  }
+
+  // ---- epilogue: lane holds rows 4*(lane/16)+i, column lane%16 of each tile --
+  const float gs = a.gscale ? a.gscale[e] : 1.0f;
+#pragma unroll
+  for (int ms = 0; ms < 4; ++ms) {
+    if (ms >= live) break;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int col = n0 + wave * 32 + t * 16 + li;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = ms * 16 + lk * 4 + i;
+        const float u = gs * acc[ms][t][i];
         if (a.fc1) {
           const float partner = __uint_as_float(dpp_u32<kDppXor1>(__float_as_uint(u)));
           if (r < mrows && (lane & 1) == 0)
