@@ -13,29 +13,34 @@
 //   waves steps through K in 128-k slices.  Wave w owns columns 32w..32w+31
 //   (two 16-column MFMA tiles) for every live 16-row sub-tile of the m tile,
 //   with v_mfma_f32_16x16x32_bf16.  Most experts of a prefill batch hold a
-//   handful of rows, so the cost is streaming and decoding weights; no weight
-//   element is decoded or read from LDS by more than one wave.
-// * Weights stay packed in LDS.  Each thread loads an 8 k x 8 column block
-//   of codes (8 dwords), and a nibble zip plus byte permutes turn it into
-//   one dword per column holding that column's 8 consecutive k codes: the
-//   MFMA B operand of one lane.  LDS holds the slice column-major (0.5 byte
-//   per weight, written once, read once); columns are rotated within groups
-//   of 8 so both the writes and the operand reads spread over all banks.
-// * Decode on read: four gfx950 FP4 -> bf16 conversions per operand.  For
-//   MXFP4 the E8M0 block scale is the conversion's exponent (exact); for
-//   NVFP4 the codes convert to float32, the E4M3 scale multiplies exactly
-//   and the hardware pack to bf16 is exact (2 x 4 significant bits).  The
-//   global scale multiplies the float32 accumulator in the epilogue.
+//   handful of rows, so the cost is streaming and decoding weights.
+// * Weights stay packed in LDS, copied as loaded: 128 k rows x 64 bytes per
+//   slice (four lanes load a row's 64 bytes; 8-byte units XOR-swizzled by
+//   row in LDS).  gfx950's 4-bit transpose read
+//   (ds_read_b64_tr_b4) hands each lane of a 16-lane group one column's 16
+//   consecutive k codes from the rows its group points at, which is two
+//   K-paired MFMA B operands (k 16g..16g+7 and 16g+8..16g+15 of a 64-k
+//   group, g = lane / 16).  The k order inside an MFMA is free as long as
+//   both operands share it, so the activation operand reads the matching
+//   16-byte chunks.  No VALU work transposes the weights.
+// * Decode on read: four gfx950 FP4 -> bf16 conversions per operand.  A
+//   lane's 16 k lie in one block, so the block scale is per lane: for MXFP4
+//   the E8M0 scale is the conversion's exponent (exact); for NVFP4 the codes
+//   convert to float32, the E4M3 scale multiplies exactly and the hardware
+//   pack to bf16 is exact (2 x 4 significant bits).  The global scale
+//   multiplies the float32 accumulator in the epilogue.
 // * Activations: 64 rows x 128 k bf16 per slice (rows gathered through the
 //   permutation for FC1), 16-byte chunks XOR-swizzled by row so the operand
 //   reads are conflict free.
 // * Pipeline: global loads two slices ahead in registers, LDS double
 //   buffered, one barrier per slice.  16-row sub-tiles with no routed rows
-//   are skipped.
+//   are skipped.  No weight element is decoded or read from LDS by more
+//   than one wave.
 // * Work items: the (expert, m tile) list is found on the device from
 //   expert_offsets; the grid covers the worst case (rows/64 + experts tiles)
-//   and idle items exit.  The m tiles of one expert for one n tile land on
-//   the same XCD, so repeated weight slices of hot experts meet in one L2.
+//   and idle items exit.  The n tiles of one (expert, m tile) run back to
+//   back on one XCD: its activation rows stay in that L2 for all n tiles, and
+//   the two 64-byte halves of each weight line are read close together.
 #include "device_common.h"
 #include "qmoe_internal.h"
 
@@ -46,18 +51,19 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kBM = 64, kBN = 128, kBK = 128;
-constexpr int kAChunks = kBK / 8;  // 16-byte chunks per activation row of a slice
-constexpr int kBStride = 18;       // dwords per LDS weight column (16 used; 3 workgroups fit a CU)
+constexpr int kAChunks = kBK / 8;    // 16-byte chunks per activation row of a slice
+constexpr int kBRow = kBN / 2;       // packed bytes per weight row of a slice
 constexpr uint32_t kGOutOfRange = 0x80000000u;
 
 struct GroupedSmem {
   u32x4_t a[2][kBM][kAChunks];      // activations, chunk c of row r at c ^ (r & 15)
-  uint32_t bt[2][kBN][kBStride];    // packed codes, column-major, 8 k per dword
+  uint8_t b[2][kBK][kBRow];         // packed codes, 8-byte unit u of row r at u ^ bswz(r)
   uint8_t sc[2][kBK / 16][kBN];     // block scales of the slice (B = 32 uses 4 rows)
 };
 
-// LDS slot of tile column n: rotated by n / 8 inside its group of 8.
-__device__ __forceinline__ int bt_col(int n) { return (n & ~7) | ((n + (n >> 3)) & 7); }
+// Unit swizzle of weight row r: the 16 rows a 16-lane group reads in one
+// transpose land on 16 distinct bank pairs.
+__device__ __forceinline__ int bswz(int r) { return (r >> 1) & 7; }
 
 // Finds the s-th (expert, m tile) item: experts in ascending order, each with
 // ceil(rows/64) tiles.  Returns the expert (-1 past the last item) and the
@@ -108,12 +114,12 @@ __device__ __forceinline__ float grouped_swiglu(float gate, float lin, float alp
 // One slice's global loads for one thread.
 struct SliceRegs {
   u32x4_t A[4];    // activation row ra, k = 32 * aq .. +31
-  uint32_t B[8];   // packed rows 8 * rg + i, columns 8 * cg .. +7
+  u32x4_t B[2];    // packed weight rows rb and rb + 64, bytes 16 * bq .. +15
   uint32_t S;      // four block-scale bytes
 };
 
-// MFMA B operand of one lane: column n's 8 consecutive k codes (one dword),
-// decoded to bf16 with the column's block scale.
+// MFMA B operand of one lane: 8 consecutive k codes of its column (one
+// dword, low nibble first), decoded to bf16 with the block scale.
 template <int FMT>
 __device__ __forceinline__ bf16x8_t decode_operand(uint32_t d, uint32_t sbyte) {
   u32x4_t o;
@@ -145,13 +151,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemvArgs a) {
   const int wave = tid >> 6;
   const int lane = lane_id();
 
-  // XCD-aware decode: consecutive logical items share an XCD.
+  // XCD-aware decode: consecutive logical items share an XCD, and the n
+  // tiles of one (expert, m tile) are consecutive items.
   const int G = gridDim.x;
   const int per = G >> 3;
   const int q = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  const int ntile = q / a.nslots;
-  const int slot = q - ntile * a.nslots;
-  if (ntile >= a.ntiles) return;
+  const int slot = q / a.ntiles;
+  const int ntile = q - slot * a.ntiles;
+  if (slot >= a.nslots) return;
   int mt = 0;
   const int e = find_mtile(a.offsets, a.E, slot, mt);
   if (e < 0) return;  // uniform over the workgroup
@@ -171,16 +178,17 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemvArgs a) {
     const int src = a.fc1 ? (a.p2e[p] / a.topk) : p;
     arow = a.act + (size_t)src * a.K;
   }
-  // weights: thread -> (8 k rows rg, 8 columns cg); 16 lanes read 64 bytes of a row
-  const int cg = tid & 15;
-  const int rg = tid >> 4;
+  // weights: thread -> (k rows rb, rb + 64; 16 bytes bq); four lanes read a
+  // row's 64 contiguous bytes
+  const int rb = tid >> 2;
+  const int bq = tid & 3;
   const uint32_t rowbytes = (uint32_t)(a.N >> 1);
   const int KB = a.K / B;
   const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(a.w + (size_t)e * a.K * rowbytes), (short)0, (int)((uint32_t)a.K * rowbytes), 0x00020000);
   const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(a.scales + (size_t)e * KB * a.N), (short)0, (int)((uint32_t)KB * a.N), 0x00020000);
-  const uint32_t woff = (uint32_t)(rg * 8) * rowbytes + (uint32_t)((n0 + cg * 8) >> 1);
+  const uint32_t woff = (uint32_t)rb * rowbytes + (uint32_t)(n0 >> 1) + (uint32_t)(bq * 16);
   // scales: thread -> (block row sb, 4 columns sq)
   const int sq = tid & 31;
   const int sb = tid >> 5;
@@ -194,15 +202,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemvArgs a) {
       r.A[j] = (arow && kk < a.K) ? *(const u32x4_t *)(arow + kk) : u32x4_t{0u, 0u, 0u, 0u};
     }
     const uint32_t o = woff + (uint32_t)k0 * rowbytes;
-    if (!ragged || s + 1 < steps) {
+    // rows past K (the last slice when K % 128 == 64) read as zero
 #pragma unroll
-      for (int i = 0; i < 8; ++i) r.B[i] = __builtin_amdgcn_raw_buffer_load_b32(wrsrc, o, i * (int)rowbytes, 2);
-    } else {
-      // rows past K read as zero through an out-of-range vector offset
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        r.B[i] = __builtin_amdgcn_raw_buffer_load_b32(
-            wrsrc, k0 + rg * 8 + i < a.K ? o + (uint32_t)i * rowbytes : kGOutOfRange, 0, 2);
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t oj = o + (uint32_t)(64 * j) * rowbytes;
+      r.B[j] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, k0 + rb + 64 * j < a.K ? oj : kGOutOfRange, 0, 2);
     }
     const int kb = k0 / B + sb;
     r.S = (sb < kSBlocks && kb < KB)
@@ -213,20 +217,15 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemvArgs a) {
   auto store_slice = [&](int buf, const SliceRegs &r) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) sm.a[buf][ra][(aq * 4 + j) ^ (ra & 15)] = r.A[j];
-    // nibble zip of row pairs, then one dword per column (rows 0..7 of the block)
-    uint32_t ev[4], od[4];
+    // 16-byte chunk bq holds units 2bq, 2bq+1; swizzled, it moves to chunk
+    // bq ^ (x >> 1) with its halves swapped when x is odd
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      ev[p] = (r.B[2 * p] & 0x0F0F0F0Fu) | ((r.B[2 * p + 1] << 4) & 0xF0F0F0F0u);
-      od[p] = ((r.B[2 * p] >> 4) & 0x0F0F0F0Fu) | (r.B[2 * p + 1] & 0xF0F0F0F0u);
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint32_t j = (uint32_t)(c >> 1);
-      const uint32_t *z = (c & 1) ? od : ev;
-      const uint32_t lo = __builtin_amdgcn_perm(z[1], z[0], j | ((4u + j) << 8) | 0x0C0C0000u);
-      const uint32_t hi = __builtin_amdgcn_perm(z[3], z[2], 0x00000C0Cu | (j << 16) | ((4u + j) << 24));
-      sm.bt[buf][bt_col(cg * 8 + c)][rg] = lo | hi;
+    for (int j = 0; j < 2; ++j) {
+      const int row = rb + 64 * j;
+      const int x = bswz(row);
+      u32x4_t v = r.B[j];
+      if (x & 1) v = u32x4_t{v.z, v.w, v.x, v.y};
+      *(u32x4_t *)&sm.b[buf][row][16 * (bq ^ (x >> 1))] = v;
     }
     if (sb < kSBlocks) *(uint32_t *)&sm.sc[buf][sb][sq * 4] = r.S;
   };
@@ -242,25 +241,38 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemvArgs a) {
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   auto compute_slice = [&](int buf, int s) {
-    const int nk = (ragged && s + 1 == steps) ? 2 : 4;  // 32-k sub-steps below K
+    const int nkg = (ragged && s + 1 == steps) ? 1 : 2;  // 64-k groups below K
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (ks >= nk) break;
-      bf16x8_t bv[2];
+    for (int kg = 0; kg < 2; ++kg) {
+      if (kg >= nkg) break;
+      // lane (lk, li) points at weight row kg*64 + 16*lk + li of its N tile;
+      // the transpose returns column li's codes of rows kg*64 + 16*lk + 0..15
+      const int row = kg * 64 + lk * 16 + li;
+      bf16x8_t bv[2][2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const int col = wave * 32 + t * 16 + li;
-        const uint32_t d = sm.bt[buf][bt_col(col)][ks * 4 + lk];
-        const int blk = (ks * 32 + lk * 8) / B;
-        bv[t] = decode_operand<FMT>(d, sm.sc[buf][blk][col]);
+        const int T = wave * 2 + t;
+        typedef int v2i_t __attribute__((ext_vector_type(2)));
+        const v2i_t v = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+            (__attribute__((address_space(3))) v2i_t *)(&sm.b[buf][row][8 * (T ^ bswz(row))]));
+        const int col = T * 16 + li;
+        const int blk = (kg * 64 + lk * 16) / B;
+        const uint32_t sbyte = sm.sc[buf][blk][col];
+        bv[t][0] = decode_operand<FMT>((uint32_t)v.x, sbyte);
+        bv[t][1] = decode_operand<FMT>((uint32_t)v.y, sbyte);
       }
 #pragma unroll
       for (int ms = 0; ms < 4; ++ms) {
         if (ms >= live) break;  // uniform
         const int r = ms * 16 + li;
-        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, sm.a[buf][r][(ks * 4 + lk) ^ (r & 15)]);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) acc[ms][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[t], acc[ms][t], 0, 0, 0);
+        for (int h = 0; h < 2; ++h) {
+          const int chunk = kg * 8 + lk * 2 + h;  // k = kg*64 + 16*lk + 8*h .. +7
+          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, sm.a[buf][r][chunk ^ (r & 15)]);
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            acc[ms][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[t][h], acc[ms][t], 0, 0, 0);
+        }
       }
     }
   };
