@@ -23,6 +23,8 @@ qmoe_status check_weights(const qmoe_fp4_weights *w) {
   if (w->fmt == QMOE_FMT_NVFP4 && !w->gscale) return QMOE_EINVAL;
   if (!aligned16(w->w) || !aligned16(w->scales) || (w->gscale && !aligned16(w->gscale))) return QMOE_EALIGN;
   if (w->K % block_of(w->fmt) != 0) return QMOE_EUNSUPPORTED;
+  // kernels address one expert's packed weights with 32-bit buffer offsets
+  if ((int64_t)w->K * w->N / 2 >= ((int64_t)1 << 31)) return QMOE_EUNSUPPORTED;
   return QMOE_OK;
 }
 
@@ -55,6 +57,8 @@ qmoe_status resolve_path(qmoe_path path, int32_t rows, const qmoe_fp4_weights *w
   if (p == QMOE_PATH_AUTO) p = rows <= QMOE_GEMV_MAX_ROWS ? QMOE_PATH_GEMV : QMOE_PATH_GROUPED;
   if (p == QMOE_PATH_GEMV && rows > QMOE_GEMV_MAX_ROWS) return QMOE_EUNSUPPORTED;
   if (p == QMOE_PATH_GROUPED && (w->K % 64 != 0 || w->N % 128 != 0)) return QMOE_EUNSUPPORTED;
+  // buffer resources address the activations of a call in 32 bits
+  if (p == QMOE_PATH_GROUPED && (int64_t)rows * w->K * 2 >= ((int64_t)1 << 31)) return QMOE_EUNSUPPORTED;
   *out = p;
   return QMOE_OK;
 }

@@ -9,14 +9,14 @@
 // float32 y.  Same outputs as the decode GEMV.
 //
 // gfx950 design:
-// * Work item = (expert, 64-row m tile, 128-column n tile); a workgroup of 4
+// * Work item = (expert, 64-row m tile, 256-column n tile); a workgroup of 8
 //   waves steps through K in 128-k slices.  Wave w owns columns 32w..32w+31
 //   (two 16-column MFMA tiles) for every live 16-row sub-tile of the m tile,
 //   with v_mfma_f32_16x16x32_bf16.  Most experts of a prefill batch hold a
 //   handful of rows, so the cost is streaming and decoding weights.
-// * Weights stay packed in LDS, copied as loaded: 128 k rows x 64 bytes per
-//   slice (four lanes load a row's 64 bytes; 8-byte units XOR-swizzled by
-//   row in LDS).  gfx950's 4-bit transpose read
+// * Weights stay packed in LDS, copied as loaded: 128 k rows x 128 bytes per
+//   slice (eight lanes load a row's 128-byte line; 8-byte units XOR-swizzled
+//   by row in LDS).  gfx950's 4-bit transpose read
 //   (ds_read_b64_tr_b4) hands each lane of a 16-lane group one column's 16
 //   consecutive k codes from the rows its group points at, which is two
 //   K-paired MFMA B operands (k 16g..16g+7 and 16g+8..16g+15 of a 64-k
@@ -32,15 +32,15 @@
 // * Activations: 64 rows x 128 k bf16 per slice (rows gathered through the
 //   permutation for FC1), 16-byte chunks XOR-swizzled by row so the operand
 //   reads are conflict free.
-// * Pipeline: global loads two slices ahead in registers, LDS double
-//   buffered, one barrier per slice.  16-row sub-tiles with no routed rows
+// * Pipeline: global loads two slices ahead in registers (up to 34 KB per
+//   workgroup per slice), LDS double buffered, one barrier per slice; two
+//   workgroups (16 waves, 128 VGPRs each) per CU.  16-row sub-tiles with no routed rows
 //   are skipped.  No weight element is decoded or read from LDS by more
 //   than one wave.
 // * Work items: the (expert, m tile) list is found on the device from
 //   expert_offsets; the grid covers the worst case (rows/64 + experts tiles)
 //   and idle items exit.  The n tiles of one (expert, m tile) run back to
-//   back on one XCD: its activation rows stay in that L2 for all n tiles, and
-//   the two 64-byte halves of each weight line are read close together.
+//   back on one XCD: its activation rows stay in that L2 for all n tiles.
 #include "device_common.h"
 #include "qmoe_internal.h"
 
@@ -50,20 +50,17 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kBM = 64, kBN = 128, kBK = 128;
+constexpr int kBM = 64, kBN = 256, kBK = 128;
+constexpr int kWaves = 8;            // wave w owns columns 32w..32w+31
 constexpr int kAChunks = kBK / 8;    // 16-byte chunks per activation row of a slice
-constexpr int kBRow = kBN / 2;       // packed bytes per weight row of a slice
+constexpr int kBRow = kBN / 2;       // packed bytes per weight row of a slice (one 128-byte line)
 constexpr uint32_t kGOutOfRange = 0x80000000u;
 
 struct GroupedSmem {
   u32x4_t a[2][kBM][kAChunks];      // activations, chunk c of row r at c ^ (r & 15)
-  uint8_t b[2][kBK][kBRow];         // packed codes, 8-byte unit u of row r at u ^ bswz(r)
+  uint8_t b[2][kBK][kBRow];         // packed codes, 8-byte unit u of row r at u ^ (r & 15)
   uint8_t sc[2][kBK / 16][kBN];     // block scales of the slice (B = 32 uses 4 rows)
 };
-
-// Unit swizzle of weight row r: the 16 rows a 16-lane group reads in one
-// transpose land on 16 distinct bank pairs.
-__device__ __forceinline__ int bswz(int r) { return (r >> 1) & 7; }
 
 // Finds the s-th (expert, m tile) item: experts in ascending order, each with
 // ceil(rows/64) tiles.  Returns the expert (-1 past the last item) and the
@@ -105,6 +102,16 @@ __device__ __forceinline__ int find_mtile(const int32_t *__restrict__ off, int E
   return __builtin_amdgcn_readlane(found, src);
 }
 
+// A wave-uniform pointer, moved to scalar registers (a buffer resource built
+// from it stays scalar; otherwise the compiler wraps every buffer load in a
+// waterfall loop).
+__device__ __forceinline__ void *uniform_ptr(const void *p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (void *)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ float grouped_swiglu(float gate, float lin, float alpha, float beta, float limit) {
   const float G = fminf(gate, limit);
   const float L = fminf(fmaxf(lin, -limit), limit);
@@ -113,7 +120,7 @@ __device__ __forceinline__ float grouped_swiglu(float gate, float lin, float alp
 
 // One slice's global loads for one thread.
 struct SliceRegs {
-  u32x4_t A[4];    // activation row ra, k = 32 * aq .. +31
+  u32x4_t A[2];    // activation row ra, k = 16 * aq .. +15
   u32x4_t B[2];    // packed weight rows rb and rb + 64, bytes 16 * bq .. +15
   uint32_t S;      // four block-scale bytes
 };
@@ -144,7 +151,7 @@ __device__ __forceinline__ bf16x8_t decode_operand(uint32_t d, uint32_t sbyte) {
 }
 
 template <int FMT>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemvArgs a) {
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void grouped_gemm_kernel(GemvArgs a) {
   constexpr int B = (FMT == 0) ? 16 : 32;
   __shared__ __attribute__((aligned(16))) GroupedSmem sm;
   const int tid = threadIdx.x;
@@ -160,8 +167,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemvArgs a) {
   const int ntile = q - slot * a.ntiles;
   if (slot >= a.nslots) return;
   int mt = 0;
-  const int e = find_mtile(a.offsets, a.E, slot, mt);
-  if (e < 0) return;  // uniform over the workgroup
+  const int ef = find_mtile(a.offsets, a.E, slot, mt);
+  if (ef < 0) return;  // uniform over the workgroup
+  // the expert is wave-uniform; saying so keeps the buffer resources in
+  // scalar registers (no per-load waterfall loops)
+  const int e = __builtin_amdgcn_readfirstlane(ef);
+  mt = __builtin_amdgcn_readfirstlane(mt);
   const int row0 = a.offsets[e] + mt * kBM;
   const int mrows = min(kBM, a.offsets[e + 1] - row0);
   const int n0 = ntile * kBN;
@@ -169,63 +180,71 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemvArgs a) {
   const bool ragged = (a.K % kBK) != 0;  // the last slice holds 64 valid k rows
 
   // ---- loader roles ----------------------------------------------------------
-  // activations: thread -> (row ra, 32 k)
-  const int ra = tid >> 2;
-  const int aq = tid & 3;
-  const uint16_t *arow = nullptr;
+  // Every load is a buffer load whose vector offset is fixed per thread for
+  // the whole kernel; the slice position rides in the scalar offset.  Rows
+  // outside the data get an out-of-range vector offset (reads return 0).  A
+  // ragged last slice (K % 128 == 64) is only read for its first 64 k.
+  // activations: thread -> (row ra, 16 k)
+  const int ra = tid >> 3;
+  const int aq = tid & 7;
+  const int act_rows = a.fc1 ? a.rows / a.topk : a.rows;
+  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+      uniform_ptr(a.act), (short)0, (int)((uint32_t)act_rows * (uint32_t)a.K * 2u), 0x00020000);
+  uint32_t avoff = kGOutOfRange;
   if (ra < mrows) {
     const int p = row0 + ra;
     const int src = a.fc1 ? (a.p2e[p] / a.topk) : p;
-    arow = a.act + (size_t)src * a.K;
+    avoff = (uint32_t)src * (uint32_t)a.K * 2u + (uint32_t)(aq * 32);
   }
-  // weights: thread -> (k rows rb, rb + 64; 16 bytes bq); four lanes read a
-  // row's 64 contiguous bytes
-  const int rb = tid >> 2;
-  const int bq = tid & 3;
+  // weights: thread -> (k rows rb, rb + 64; 16 bytes bq); eight lanes read a
+  // row's 128-byte line
+  const int rb = tid >> 3;
+  const int bq = tid & 7;
   const uint32_t rowbytes = (uint32_t)(a.N >> 1);
   const int KB = a.K / B;
   const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(a.w + (size_t)e * a.K * rowbytes), (short)0, (int)((uint32_t)a.K * rowbytes), 0x00020000);
+      uniform_ptr(a.w + (size_t)e * a.K * rowbytes), (short)0, (int)((uint32_t)a.K * rowbytes), 0x00020000);
   const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(a.scales + (size_t)e * KB * a.N), (short)0, (int)((uint32_t)KB * a.N), 0x00020000);
-  const uint32_t woff = (uint32_t)rb * rowbytes + (uint32_t)(n0 >> 1) + (uint32_t)(bq * 16);
+      uniform_ptr(a.scales + (size_t)e * KB * a.N), (short)0, (int)((uint32_t)KB * a.N), 0x00020000);
+  // a last tile of 128 columns (N % 256 == 128) reads nothing past N
+  const bool bcols = n0 + 32 * bq + 32 <= a.N;
+  const uint32_t bvoff0 = bcols ? (uint32_t)rb * rowbytes + (uint32_t)(n0 >> 1) + (uint32_t)(bq * 16) : kGOutOfRange;
+  const uint32_t bvoff1 = bcols ? bvoff0 + 64u * rowbytes : kGOutOfRange;
   // scales: thread -> (block row sb, 4 columns sq)
-  const int sq = tid & 31;
-  const int sb = tid >> 5;
+  const int sq = tid & 63;
+  const int sb = tid >> 6;
   constexpr int kSBlocks = kBK / B;
+  const uint32_t svoff = n0 + sq * 4 + 4 <= a.N ? (uint32_t)sb * (uint32_t)a.N + (uint32_t)(n0 + sq * 4) : kGOutOfRange;
 
   auto load_slice = [&](int s, SliceRegs &r) {
     const int k0 = s * kBK;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int kk = k0 + aq * 32 + j * 8;
-      r.A[j] = (arow && kk < a.K) ? *(const u32x4_t *)(arow + kk) : u32x4_t{0u, 0u, 0u, 0u};
-    }
-    const uint32_t o = woff + (uint32_t)k0 * rowbytes;
-    // rows past K (the last slice when K % 128 == 64) read as zero
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t oj = o + (uint32_t)(64 * j) * rowbytes;
-      r.B[j] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, k0 + rb + 64 * j < a.K ? oj : kGOutOfRange, 0, 2);
-    }
-    const int kb = k0 / B + sb;
-    r.S = (sb < kSBlocks && kb < KB)
-              ? __builtin_amdgcn_raw_buffer_load_b32(srsrc, (uint32_t)kb * (uint32_t)a.N + (uint32_t)(n0 + sq * 4), 0, 0)
-              : 0u;
+    const bool tail = ragged && s + 1 == steps;  // uniform
+    r.A[0] = __builtin_amdgcn_raw_buffer_load_b128(arsrc, avoff, k0 * 2, 0);
+    r.A[1] = __builtin_amdgcn_raw_buffer_load_b128(arsrc, avoff + 16u, k0 * 2, 0);
+    const int so = (int)((uint32_t)k0 * rowbytes);
+    r.B[0] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, bvoff0, so, 2);
+    r.B[1] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, tail ? kGOutOfRange : bvoff1, so, 2);
+    r.S = 0u;
+    if (sb < kSBlocks)
+      r.S = __builtin_amdgcn_raw_buffer_load_b32(srsrc, (tail && sb >= kSBlocks / 2) ? kGOutOfRange : svoff,
+                                                 (int)((uint32_t)(k0 / B) * (uint32_t)a.N), 0);
   };
+
+  // LDS positions of this thread's stores (unit u of weight row r sits at
+  // u ^ (r & 15): the two 8-byte halves of a loaded chunk land separately)
+  int bpos[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) bpos[j][h] = 8 * ((2 * bq + h) ^ ((rb + 64 * j) & 15));
 
   auto store_slice = [&](int buf, const SliceRegs &r) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sm.a[buf][ra][(aq * 4 + j) ^ (ra & 15)] = r.A[j];
-    // 16-byte chunk bq holds units 2bq, 2bq+1; swizzled, it moves to chunk
-    // bq ^ (x >> 1) with its halves swapped when x is odd
+    for (int h = 0; h < 2; ++h) sm.a[buf][ra][(2 * aq + h) ^ (ra & 15)] = r.A[h];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int row = rb + 64 * j;
-      const int x = bswz(row);
-      u32x4_t v = r.B[j];
-      if (x & 1) v = u32x4_t{v.z, v.w, v.x, v.y};
-      *(u32x4_t *)&sm.b[buf][row][16 * (bq ^ (x >> 1))] = v;
+      *(u32x2_t *)&sm.b[buf][rb + 64 * j][bpos[j][0]] = u32x2_t{r.B[j].x, r.B[j].y};
+      *(u32x2_t *)&sm.b[buf][rb + 64 * j][bpos[j][1]] = u32x2_t{r.B[j].z, r.B[j].w};
     }
     if (sb < kSBlocks) *(uint32_t *)&sm.sc[buf][sb][sq * 4] = r.S;
   };
@@ -234,6 +253,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemvArgs a) {
   const int li = lane & 15;
   const int lk = lane >> 4;
   const int live = (mrows + 15) >> 4;  // 16-row sub-tiles holding routed rows
+  const bool wave_cols = n0 + wave * 32 < a.N;  // uniform: this wave's columns exist
   f32x4_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -241,6 +261,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemvArgs a) {
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   auto compute_slice = [&](int buf, int s) {
+    if (!wave_cols) return;
     const int nkg = (ragged && s + 1 == steps) ? 1 : 2;  // 64-k groups below K
 #pragma unroll
     for (int kg = 0; kg < 2; ++kg) {
@@ -248,36 +269,32 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemvArgs a) {
       // lane (lk, li) points at weight row kg*64 + 16*lk + li of its N tile;
       // the transpose returns column li's codes of rows kg*64 + 16*lk + 0..15
       const int row = kg * 64 + lk * 16 + li;
-      bf16x8_t bv[2][2];
+      const int blk = (kg * 64 + lk * 16) / B;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int T = wave * 2 + t;
         typedef int v2i_t __attribute__((ext_vector_type(2)));
         const v2i_t v = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
-            (__attribute__((address_space(3))) v2i_t *)(&sm.b[buf][row][8 * (T ^ bswz(row))]));
-        const int col = T * 16 + li;
-        const int blk = (kg * 64 + lk * 16) / B;
-        const uint32_t sbyte = sm.sc[buf][blk][col];
-        bv[t][0] = decode_operand<FMT>((uint32_t)v.x, sbyte);
-        bv[t][1] = decode_operand<FMT>((uint32_t)v.y, sbyte);
-      }
-#pragma unroll
-      for (int ms = 0; ms < 4; ++ms) {
-        if (ms >= live) break;  // uniform
-        const int r = ms * 16 + li;
+            (__attribute__((address_space(3))) v2i_t *)(&sm.b[buf][row][8 * (T ^ (row & 15))]));
+        const uint32_t sbyte = sm.sc[buf][blk][T * 16 + li];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
+          // decoded just before its MFMAs: one operand live at a time
+          const bf16x8_t bv = decode_operand<FMT>(h ? (uint32_t)v.y : (uint32_t)v.x, sbyte);
           const int chunk = kg * 8 + lk * 2 + h;  // k = kg*64 + 16*lk + 8*h .. +7
-          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, sm.a[buf][r][chunk ^ (r & 15)]);
 #pragma unroll
-          for (int t = 0; t < 2; ++t)
-            acc[ms][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[t][h], acc[ms][t], 0, 0, 0);
+          for (int ms = 0; ms < 4; ++ms) {
+            if (ms >= live) break;  // uniform
+            const int r = ms * 16 + li;
+            const bf16x8_t av = __builtin_bit_cast(bf16x8_t, sm.a[buf][r][chunk ^ (r & 15)]);
+            acc[ms][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[ms][t], 0, 0, 0);
+          }
         }
       }
     }
   };
 
-  // ---- pipeline: loads two slices ahead, LDS double buffered ------------------
+  // ---- pipeline: loads two slices ahead in registers, LDS double buffered ----
   SliceRegs r0, r1;
   load_slice(0, r0);
   if (steps > 1) load_slice(1, r1);
@@ -294,6 +311,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemvArgs a) {
   }
 
   // ---- epilogue: lane holds rows 4*(lane/16)+i, column lane%16 of each tile --
+  if (!wave_cols) return;
   const float gs = a.gscale ? a.gscale[e] : 1.0f;
 #pragma unroll
   for (int ms = 0; ms < 4; ++ms) {
@@ -323,13 +341,13 @@ size_t grouped_workspace_bytes() { return 256; }
 hipError_t launch_grouped(GemvArgs &a, int fmt, hipStream_t s) {
   const int erows = a.rows < a.E ? a.rows : a.E;
   a.nslots = (a.rows + kBM - 1) / kBM + erows;  // worst-case (expert, m tile) count
-  a.ntiles = a.N / kBN;
+  a.ntiles = (a.N + kBN - 1) / kBN;  // N % 128 == 0: the last tile may hold 128 columns
   const int items = a.nslots * a.ntiles;
   const dim3 grid((unsigned)(((items + 7) / 8) * 8));
   if (fmt == 0)
-    grouped_gemm_kernel<0><<<grid, 256, 0, s>>>(a);
+    grouped_gemm_kernel<0><<<grid, kWaves * 64, 0, s>>>(a);
   else
-    grouped_gemm_kernel<1><<<grid, 256, 0, s>>>(a);
+    grouped_gemm_kernel<1><<<grid, kWaves * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
