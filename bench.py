@@ -3,8 +3,9 @@
 Default workload: the NVFP4 MTP-verify decode layer (4 tokens x top-8 = 32
 expanded rows, E=256, hidden 2048, intermediate 768, three hot experts),
 seeded synthetic inputs.  A step is one pass of the whole hot path over one
-layer: qmoe_route_topk -> qmoe_fp4_gemv_fc1_swiglu -> qmoe_fp4_gemv_fc2 ->
-qmoe_finalize.  Steps rotate over distinct copies of the layer weights so
+layer: qmoe_route_topk -> qmoe_fp4_gemv_fc1_swiglu -> qmoe_fp4_gemv_fc2_finalize
+(FC2 and the weighted un-permute in one call, bit-identical to
+qmoe_fp4_gemv_fc2 followed by qmoe_finalize).  Steps rotate over distinct copies of the layer weights so
 every timed weight byte comes from HBM, not from the 256 MB Infinity Cache.
 The steps are captured once in a HIP graph and replayed (the launch path of
 a serving loop); --eager times plain launches instead.
@@ -187,7 +188,7 @@ def bench_layer(args, torch, q, synth, np):
     def step(i):
         w1, w2 = copies[i % layers]
         layer.set_weights(w1, w2)
-        layer.run(logits, x)
+        layer.run(logits, x, fused=True)
 
     def fc1_only(i):
         layer.w1 = copies[i % layers][0]

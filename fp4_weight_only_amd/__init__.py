@@ -25,7 +25,8 @@ QMOE_FMT_NVFP4, QMOE_FMT_MXFP4 = 0, 1
 QMOE_PATH_AUTO, QMOE_PATH_GEMV, QMOE_PATH_GROUPED = 0, 1, 2
 GEMV_MAX_ROWS = 64
 
-EXPORTS = ("qmoe_route_topk", "qmoe_fp4_gemv_fc1_swiglu", "qmoe_fp4_gemv_fc2", "qmoe_finalize",
+EXPORTS = ("qmoe_route_topk", "qmoe_fp4_gemv_fc1_swiglu", "qmoe_fp4_gemv_fc2", "qmoe_fp4_gemv_fc2_finalize",
+           "qmoe_finalize",
            "qmoe_dequant_fp4", "qmoe_status_str")
 
 
@@ -54,6 +55,7 @@ def _load():
         "qmoe_route_topk": [P, I32, I32, I32, P, P, P, P, P, P],
         "qmoe_fp4_gemv_fc1_swiglu": [P, I32, I32, W, P, P, ctypes.POINTER(SwigluC), P, P, SZ, I32, P],
         "qmoe_fp4_gemv_fc2": [P, I32, I32, W, P, P, P, SZ, I32, P],
+        "qmoe_fp4_gemv_fc2_finalize": [P, I32, I32, W, P, P, P, P, P, SZ, I32, P],
         "qmoe_finalize": [P, P, P, I32, I32, I32, P, P],
         "qmoe_dequant_fp4": [W, P, P],
     }
@@ -106,15 +108,19 @@ def qmoe_route_topk(logits, k, topk_idx, topk_w, expert_offsets, perm_to_expande
 
 
 def fc_workspace_bytes(which: int, T: int, k: int, w: FP4Weights, path=QMOE_PATH_AUTO) -> int:
-    """Workspace size of qmoe_fp4_gemv_fc1_swiglu (which=1) or qmoe_fp4_gemv_fc2 (which=2)."""
+    """Workspace size of qmoe_fp4_gemv_fc1_swiglu (which=1), qmoe_fp4_gemv_fc2 (which=2) or
+    qmoe_fp4_gemv_fc2_finalize (which=3)."""
     n = ctypes.c_size_t(0)
     wc = w.c()
     dummy = 256  # aligned non-null placeholders: a size query launches nothing
     if which == 1:
         st = lib.qmoe_fp4_gemv_fc1_swiglu(dummy, T, k, ctypes.byref(wc), dummy, dummy, None, dummy, None,
                                           ctypes.byref(n), path, None)
-    else:
+    elif which == 2:
         st = lib.qmoe_fp4_gemv_fc2(dummy, T, k, ctypes.byref(wc), dummy, dummy, None, ctypes.byref(n), path, None)
+    else:
+        st = lib.qmoe_fp4_gemv_fc2_finalize(dummy, T, k, ctypes.byref(wc), dummy, dummy, dummy, dummy, None,
+                                            ctypes.byref(n), path, None)
     _check("fc_workspace_bytes", st)
     return n.value
 
@@ -141,6 +147,16 @@ def qmoe_fp4_gemv_fc2(h, T, k, w2: FP4Weights, expert_offsets, y_rows, ws, path=
     _check("qmoe_fp4_gemv_fc2", lib.qmoe_fp4_gemv_fc2(
         _ptr(h), T, k, ctypes.byref(wc), _ptr(expert_offsets), _ptr(y_rows), _ptr(ws), ctypes.byref(n), path,
         _stream(stream)))
+
+
+def qmoe_fp4_gemv_fc2_finalize(h, k, w2: FP4Weights, expert_offsets, topk_w, expanded_to_perm, out, ws,
+                               path=QMOE_PATH_AUTO, stream=None):
+    T = out.shape[0]
+    wc = w2.c()
+    n = ctypes.c_size_t(ws.numel() * ws.element_size())
+    _check("qmoe_fp4_gemv_fc2_finalize", lib.qmoe_fp4_gemv_fc2_finalize(
+        _ptr(h), T, k, ctypes.byref(wc), _ptr(expert_offsets), _ptr(topk_w), _ptr(expanded_to_perm), _ptr(out),
+        _ptr(ws), ctypes.byref(n), path, _stream(stream)))
 
 
 def qmoe_finalize(y_rows, topk_w, expanded_to_perm, out, stream=None):

@@ -162,6 +162,60 @@ qmoe_status qmoe_fp4_gemv_fc2(const uint16_t *h, int32_t T, int32_t k, const qmo
   return run_fc(a, w2, sh.max_rows_per_expert, p, ws, ws_bytes, stream);
 }
 
+qmoe_status qmoe_fp4_gemv_fc2_finalize(const uint16_t *h, int32_t T, int32_t k, const qmoe_fp4_weights *w2,
+                                       const int32_t *expert_offsets, const float *topk_w,
+                                       const int32_t *expanded_to_perm, uint16_t *out, void *ws, size_t *ws_bytes,
+                                       qmoe_path path, hipStream_t stream) {
+  FcShape sh;
+  qmoe_status st = check_fc(w2, T, k, h, expert_offsets, out, path, &sh);
+  if (st != QMOE_OK) return st;
+  if (!topk_w || !expanded_to_perm) return QMOE_EINVAL;
+  if (!aligned16(topk_w) || !aligned16(expanded_to_perm)) return QMOE_EALIGN;
+  if (w2->N % 8 != 0) return QMOE_EUNSUPPORTED;
+  qmoe_path p;
+  st = resolve_path(path, sh.rows, w2, &p);
+  if (st != QMOE_OK) return st;
+  GemvArgs a = {};
+  a.act = h;
+  a.offsets = expert_offsets;
+  a.topk = k;
+  a.rows = sh.rows;
+  a.fc1 = 0;
+  a.force_partials = 1;
+  a.w = w2->w;
+  a.scales = w2->scales;
+  a.gscale = w2->gscale;
+  a.E = w2->E;
+  a.K = w2->K;
+  a.N = w2->N;
+  // workspace: the GEMV's split-K partials, or the grouped path's float32 rows
+  const size_t plane = (size_t)sh.rows * w2->N;
+  size_t need = p == QMOE_PATH_GROUPED
+                    ? plane * sizeof(float)
+                    : gemv_workspace_bytes(sh.rows, sh.max_rows_per_expert, w2->E, w2->K, w2->N, true);
+  if (need < 256) need = 256;
+  if (!ws_bytes) return QMOE_EINVAL;
+  if (!ws) {
+    *ws_bytes = need;
+    return QMOE_OK;
+  }
+  if (*ws_bytes < need) return QMOE_EWORKSPACE;
+  if (!aligned16(ws)) return QMOE_EALIGN;
+  const int fmt = w2->fmt == QMOE_FMT_NVFP4 ? 0 : 1;
+  int nsplit = 1;
+  if (p == QMOE_PATH_GROUPED) {
+    a.out_f32 = (float *)ws;
+    st = check_launch(launch_grouped(a, fmt, stream));
+  } else {
+    gemv_plan(a, sh.max_rows_per_expert, ws);
+    nsplit = a.nchunks;
+    st = check_launch(launch_fp4_gemv(a, fmt, sh.max_rows_per_expert, stream));
+  }
+  if (st != QMOE_OK) return st;
+  return check_launch(
+      launch_finalize((const float *)ws, nsplit, plane, topk_w, expanded_to_perm, T, k, w2->N, out, stream));
+}
+
 qmoe_status qmoe_finalize(const float *y_rows, const float *topk_w, const int32_t *expanded_to_perm, int32_t T,
                           int32_t k, int32_t H, uint16_t *out, hipStream_t stream) {
   if (!y_rows || !topk_w || !expanded_to_perm || !out) return QMOE_EINVAL;
@@ -169,7 +223,7 @@ qmoe_status qmoe_finalize(const float *y_rows, const float *topk_w, const int32_
   if (!aligned16(y_rows) || !aligned16(topk_w) || !aligned16(expanded_to_perm) || !aligned16(out))
     return QMOE_EALIGN;
   if (k > QMOE_MAX_TOPK || H % 8 != 0) return QMOE_EUNSUPPORTED;
-  return check_launch(launch_finalize(y_rows, topk_w, expanded_to_perm, T, k, H, out, stream));
+  return check_launch(launch_finalize(y_rows, 1, 0, topk_w, expanded_to_perm, T, k, H, out, stream));
 }
 
 qmoe_status qmoe_dequant_fp4(const qmoe_fp4_weights *w, uint16_t *out, hipStream_t stream) {

@@ -309,7 +309,7 @@ __global__ __launch_bounds__(max_waves<MRMAX>() * 64) void fp4_gemv_kernel(GemvA
         for (int q = 1; q < W; ++q) s += sm.red[q][r][cl];
         const int p = row0 + rbase + r;
         const float u = gs * s;
-        if (a.nchunks > 1) {
+        if (a.nchunks > 1 || a.force_partials) {
           if (col < a.N) a.partials[((size_t)kc * a.rows + p) * a.N + col] = u;
         } else if (a.fc1) {
           store_fc1(a, p, col, u);
@@ -355,12 +355,13 @@ static int plan_max_waves(int max_rows_per_expert) {
   return kGemvMaxWaves;
 }
 
-size_t gemv_workspace_bytes(int32_t rows, int32_t max_rows_per_expert, int32_t E, int32_t K, int32_t N) {
+size_t gemv_workspace_bytes(int32_t rows, int32_t max_rows_per_expert, int32_t E, int32_t K, int32_t N,
+                            bool force_partials) {
   const int nslots = rows < E ? rows : E;
   const int ntiles = (N + kGemvTileN - 1) / kGemvTileN;
   int nchunks, waves;
   plan_chunks(nslots * ntiles, K, plan_max_waves(max_rows_per_expert), nchunks, waves);
-  const size_t part = nchunks > 1 ? (size_t)nchunks * rows * N * sizeof(float) : 0;
+  const size_t part = (nchunks > 1 || force_partials) ? (size_t)nchunks * rows * N * sizeof(float) : 0;
   return part > 256 ? part : 256;
 }
 
@@ -394,7 +395,7 @@ hipError_t launch_fp4_gemv(const GemvArgs &a, int fmt, int max_rows_per_expert, 
       fp4_gemv_kernel<1, 4><<<grid, block, 0, s>>>(a);
   }
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || a.nchunks == 1) return err;
+  if (err != hipSuccess || a.nchunks == 1 || a.force_partials) return err;
   const dim3 g2((unsigned)((a.N + 255) / 256), (unsigned)a.rows);
   splitk_epilogue_kernel<<<g2, 256, 0, s>>>(a);
   return hipGetLastError();

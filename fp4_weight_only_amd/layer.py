@@ -1,4 +1,5 @@
-"""One MoE expert layer on the GPU through the C ABI: route -> FC1+SwiGLU -> FC2 -> finalize.
+"""One MoE expert layer on the GPU through the C ABI: route -> FC1+SwiGLU -> FC2 -> finalize
+(or FC2 and finalize fused).
 
 Buffers are allocated once per shape; run() enqueues the four calls on the
 current stream and allocates nothing.
@@ -8,7 +9,7 @@ from __future__ import annotations
 import torch
 
 from . import (QMOE_PATH_AUTO, FP4Weights, alloc_workspace, fc_workspace_bytes, qmoe_finalize,
-               qmoe_fp4_gemv_fc1_swiglu, qmoe_fp4_gemv_fc2, qmoe_route_topk)
+               qmoe_fp4_gemv_fc1_swiglu, qmoe_fp4_gemv_fc2, qmoe_fp4_gemv_fc2_finalize, qmoe_route_topk)
 
 
 class MoELayer:
@@ -26,7 +27,8 @@ class MoELayer:
         self.h = torch.empty((R, I), dtype=torch.bfloat16, device=dev)
         self.y = torch.empty((R, H), dtype=torch.float32, device=dev)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-        need = max(fc_workspace_bytes(1, T, k, w1, path), fc_workspace_bytes(2, T, k, w2, path))
+        need = max(fc_workspace_bytes(1, T, k, w1, path), fc_workspace_bytes(2, T, k, w2, path),
+                   fc_workspace_bytes(3, T, k, w2, path))
         self.ws = alloc_workspace(need, dev)
 
     def set_weights(self, w1: FP4Weights, w2: FP4Weights):
@@ -44,9 +46,18 @@ class MoELayer:
     def finalize(self):
         qmoe_finalize(self.y, self.topk_w, self.e2p, self.out)
 
-    def run(self, logits, x):
+    def fc2_finalize(self):
+        qmoe_fp4_gemv_fc2_finalize(self.h, self.k, self.w2, self.offsets, self.topk_w, self.e2p, self.out, self.ws,
+                                   self.path)
+
+    def run(self, logits, x, fused: bool = False):
+        """route -> FC1+SwiGLU -> FC2 -> finalize; fused=True runs FC2 and the
+        finalize as one call (y is then not written)."""
         self.route(logits)
         self.fc1(x)
-        self.fc2()
-        self.finalize()
+        if fused:
+            self.fc2_finalize()
+        else:
+            self.fc2()
+            self.finalize()
         return self.out

@@ -12,6 +12,10 @@
  *   qmoe_finalize             weighted un-permute
  *   qmoe_dequant_fp4          standalone FP4 -> bf16 weight dequant
  *
+ * and one fused call for the decode layer's tail:
+ *
+ *   qmoe_fp4_gemv_fc2_finalize  FC2 + weighted un-permute without y_rows
+ *
  * Conventions shared by every call
  * --------------------------------
  * - Pointers named in a call are device pointers unless stated otherwise;
@@ -168,6 +172,31 @@ qmoe_status qmoe_fp4_gemv_fc2(const uint16_t *h, int32_t T, int32_t k,
                               const qmoe_fp4_weights *w2, const int32_t *expert_offsets,
                               float *y_rows, void *ws, size_t *ws_bytes, qmoe_path path,
                               hipStream_t stream);
+
+/*
+ * qmoe_fp4_gemv_fc2_finalize -- FC2 and the weighted un-permute in one call.
+ *
+ * Passages: operator documentation section 9.8 (epilogue fusion: the
+ * finalize folded into the second GEMM's epilogue) and section 12.1;
+ * PR 31156 (finalize reads each token's routing metadata once).
+ *
+ * out[t][n] = bf16_rne( sum_{j<k} topk_w[t][j] * y[expanded_to_perm[t*k+j]][n] )
+ * with y = FC2(h) as qmoe_fp4_gemv_fc2 computes it, without writing y_rows:
+ * the GEMV path keeps FC2's split-K partial sums in the workspace and the
+ * finalize kernel adds them per routed row in the same order the split-K
+ * epilogue would, so out equals qmoe_fp4_gemv_fc2 followed by qmoe_finalize
+ * bit for bit.  The grouped path writes y's float32 rows to the workspace.
+ *
+ * h, T, k, w2, expert_offsets: as qmoe_fp4_gemv_fc2.  topk_w, expanded_to_perm:
+ * as qmoe_finalize.  out [T][H] bf16 (H = w2->N).
+ * ws, ws_bytes, path: as qmoe_fp4_gemv_fc2 (the size differs: query it).
+ * Limits: those of qmoe_fp4_gemv_fc2 and qmoe_finalize.
+ */
+qmoe_status qmoe_fp4_gemv_fc2_finalize(const uint16_t *h, int32_t T, int32_t k,
+                                       const qmoe_fp4_weights *w2, const int32_t *expert_offsets,
+                                       const float *topk_w, const int32_t *expanded_to_perm,
+                                       uint16_t *out, void *ws, size_t *ws_bytes, qmoe_path path,
+                                       hipStream_t stream);
 
 /*
  * qmoe_finalize -- weighted un-permute.

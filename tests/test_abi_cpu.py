@@ -112,6 +112,26 @@ def test_workspace_query_and_too_small(q):
     assert st == q.QMOE_OK and need2 > 0
 
 
+def test_fc2_finalize_validation_and_workspace(q):
+    L = q.lib
+    wc = weights(q, E=256, K=768, N=2048)
+    n = ctypes.c_size_t(0)
+    call = lambda h=A, w=wc, off=A, tw=A, e2p=A, out=A, ws=None, T=4, k=8, path=0: L.qmoe_fp4_gemv_fc2_finalize(
+        h, T, k, ctypes.byref(w), off, tw, e2p, out, ws, ctypes.byref(n), path, None)
+    assert call() == q.QMOE_OK and n.value > 0
+    # FC2 partials are kept even when they span several k chunks: at least one float32 plane of 32 x 2048
+    assert n.value >= 32 * 2048 * 4
+    need = n.value
+    n.value = need - 1
+    assert call(ws=A) == q.QMOE_EWORKSPACE
+    assert call(tw=None) == q.QMOE_EINVAL
+    assert call(e2p=None) == q.QMOE_EINVAL
+    assert call(tw=MIS) == q.QMOE_EALIGN
+    assert call(T=9, path=q.QMOE_PATH_GEMV) == q.QMOE_EUNSUPPORTED      # 72 rows on the GEMV
+    n.value = 0
+    assert call(T=9) == q.QMOE_OK and n.value >= 72 * 2048 * 4          # grouped: float32 rows in the workspace
+
+
 def test_finalize_and_dequant_validation(q):
     L = q.lib
     assert L.qmoe_finalize(None, A, A, 1, 2, 256, A, None) == q.QMOE_EINVAL

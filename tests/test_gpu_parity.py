@@ -208,6 +208,34 @@ def test_every_code_in_every_nibble_through_the_gemv(fmt):
     assert np.count_nonzero(diff) <= 2, np.nonzero(diff)
 
 
+FUSED = [
+    synth.TINY,
+    synth.shrink(synth.DECODE, E=37, T=7, k=5, H=320, I=144, seed=1),      # ragged K/N, several k chunks
+    synth.MTP4,
+    synth.MTP8,
+    synth.shrink(synth.MX_DECODE, E=40, T=8, k=8, H=544, I=160, seed=3),
+    synth.shrink(synth.MX_PREFILL, E=16, T=64, k=4, H=512, I=256, seed=21),  # grouped path
+]
+
+
+@pytest.mark.parametrize("cfg", FUSED, ids=lambda c: c.name)
+def test_fc2_finalize_fused_equals_separate_calls(cfg):
+    """qmoe_fp4_gemv_fc2_finalize adds FC2's partial sums per routed row in the
+    order the split-K epilogue does, then weights them as qmoe_finalize does:
+    the output must equal the separate calls bit for bit (the separate path is
+    checked against the oracle by the layer tests)."""
+    L = synth.layer_inputs(cfg)
+    layer, logits, x = layer_dev(L)
+    print_case("fused fc2+finalize", cfg.name)
+    layer.run(logits, x)
+    torch.cuda.synchronize()
+    ref = bf16_host(layer.out).copy()
+    layer.out.view(torch.int16).fill_(0x7FC1)   # poison
+    layer.run(logits, x, fused=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_host(layer.out), ref)
+
+
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "mxfp4_g"])
 def test_dequant_small_exhaustive_scales(fmt):
     """Every scale byte (NaN bytes aside) with random codes; MXFP4 with and
