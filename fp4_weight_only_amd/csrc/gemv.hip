@@ -323,19 +323,44 @@ __global__ __launch_bounds__(max_waves<MRMAX>() * 64) void fp4_gemv_kernel(GemvA
 }
 
 // Split-K epilogue: sums the k-chunk partials of every (row, column) in chunk
-// order, then SwiGLU -> bf16 h (FC1) or float32 y (FC2).
-__global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemvArgs a) {
+// order, then SwiGLU -> bf16 h (FC1) or float32 y (FC2).  One thread owns 4
+// columns (two gate/up pairs for FC1), one wave 256 columns of one row.
+// Chunks are read kEpiGroup at a time with every load unconditional (indices
+// past the last chunk re-read it and contribute -0, which leaves any float
+// sum unchanged), so a row's partials are in flight together rather than one
+// memory round trip per chunk.
+constexpr int kEpiGroup = 8;
+
+__global__ __launch_bounds__(64) void splitk_epilogue_kernel(GemvArgs a) {
   const int p = blockIdx.y;
-  const int col = blockIdx.x * 256 + threadIdx.x;
-  float s = 0.f;
-  if (col < a.N) {
-    s = a.partials[(size_t)p * a.N + col];
-    for (int q = 1; q < a.nchunks; ++q) s += a.partials[((size_t)q * a.rows + p) * a.N + col];
+  const int col = (blockIdx.x * 64 + threadIdx.x) * 4;
+  if (col >= a.N) return;
+  const size_t plane = (size_t)a.rows * a.N;
+  const float *src = a.partials + (size_t)p * a.N + col;
+  float4 s = make_float4(-0.f, -0.f, -0.f, -0.f);
+  for (int c = 0; c < a.nchunks; c += kEpiGroup) {
+    float4 v[kEpiGroup];
+#pragma unroll
+    for (int g = 0; g < kEpiGroup; ++g) {
+      const int q = c + g < a.nchunks ? c + g : a.nchunks - 1;
+      v[g] = *(const float4 *)(src + (size_t)q * plane);
+    }
+#pragma unroll
+    for (int g = 0; g < kEpiGroup; ++g) {
+      const bool live = c + g < a.nchunks;
+      s.x += live ? v[g].x : -0.f;
+      s.y += live ? v[g].y : -0.f;
+      s.z += live ? v[g].z : -0.f;
+      s.w += live ? v[g].w : -0.f;
+    }
   }
-  if (a.fc1)
-    store_fc1(a, p, col, s);
-  else if (col < a.N)
-    a.out_f32[(size_t)p * a.N + col] = s;
+  if (a.fc1) {
+    const uint32_t h0 = bf16_rne(swiglu(s.x, s.y, a.alpha, a.beta, a.limit));
+    const uint32_t h1 = bf16_rne(swiglu(s.z, s.w, a.alpha, a.beta, a.limit));
+    *(uint32_t *)(a.out_bf16 + (size_t)p * (a.N >> 1) + (col >> 1)) = h0 | (h1 << 16);
+  } else {
+    *(float4 *)(a.out_f32 + (size_t)p * a.N + col) = s;
+  }
 }
 
 // Four waves (a 256-row k chunk) per workgroup: the kernel is bound by VALU
@@ -397,7 +422,7 @@ hipError_t launch_fp4_gemv(const GemvArgs &a, int fmt, int max_rows_per_expert, 
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.nchunks == 1 || a.force_partials) return err;
   const dim3 g2((unsigned)((a.N + 255) / 256), (unsigned)a.rows);
-  splitk_epilogue_kernel<<<g2, 256, 0, s>>>(a);
+  splitk_epilogue_kernel<<<g2, 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
