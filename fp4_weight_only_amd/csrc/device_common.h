@@ -84,12 +84,4 @@ constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowMirror = 0x140;
 
-// ds_swizzle bit-mask mode: lane ^ 16 inside each 32-lane half.
-__device__ __forceinline__ uint32_t swz_xor16(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
-}
-__device__ __forceinline__ uint32_t bperm_xor32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_ds_bpermute((lane_id() ^ 32) << 2, (int)v);
-}
-
 }  // namespace qmoe

@@ -1,137 +1,126 @@
 // Softmax top-k routing and expert maps for gfx950.
 //
-// Top-k follows the register-only design of "[CUDA] Cut the MoE routing
+// Top-k keeps the register-only shape of "[CUDA] Cut the MoE routing
 // prologue/epilogue cost for small-batch decode" (PR 31156): one token per
-// wave, every key in registers, each lane sorts its own keys and the wave
-// runs a butterfly of bitonic top-N merges, C[i] = max(A[i], B[N-1-i]),
-// which is symmetric so both partners keep the same list; no LDS and no
-// barrier.  On wave64 the partner moves are DPP (quad_perm, row half-mirror,
-// row mirror), ds_swizzle (lane ^ 16) and ds_bpermute (lane ^ 32).  The key
-// is 64-bit: an order-preserving image of the exact float32 logit (with -0
-// folded onto +0) above the complemented expert index, so equal logits
-// select the lower expert and the selection is exact.
+// wave, every logit in registers (4 per lane for E <= 256), no LDS and no
+// barrier.  The selection itself is k rounds of a wave-wide argmax rather
+// than a merge network: each round takes the maximum of an order-preserving
+// 32-bit image of the exact float32 logits (-0 folded onto +0) with four DPP
+// max steps inside each 16-lane row and four lane reads, then four ballots
+// find the lowest expert index holding that maximum, which leaves the round.
+// The selection is exact and equal logits select the lower expert; the
+// winners come out largest first.
 //
 // The expert maps rank the T*k expanded rows by expert with wave ballots
 // (8 ballots match the expert-id bits, popcount below the lane gives the
 // rank), the ballot-based ranking the same PR adopts.  For up to 16 tokens
-// both steps run in one workgroup (one launch, selections passed in LDS).
+// both steps run in one workgroup (one launch, selections passed in LDS);
+// up to 64 expanded rows the maps take a single wave and no barrier.
 #include "device_common.h"
 #include "qmoe_internal.h"
 
 namespace qmoe {
 
-__device__ __forceinline__ uint64_t make_key(float v, int e) {
+__device__ __forceinline__ uint32_t ord_key(float v) {
   uint32_t u = __float_as_uint(v);
   u = (u == 0x80000000u) ? 0u : u;
-  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-__device__ __forceinline__ float key_value(uint64_t key) {
-  const uint32_t ord = (uint32_t)(key >> 32);
+__device__ __forceinline__ float ord_value(uint32_t ord) {
   return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
 }
-__device__ __forceinline__ int key_index(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
 
-__device__ __forceinline__ void cswap_desc(uint64_t &a, uint64_t &b) {
-  const uint64_t hi = a > b ? a : b;
-  const uint64_t lo = a > b ? b : a;
-  a = hi;
-  b = lo;
+// Maximum / minimum over the wave; the result is uniform.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
+  auto op = [](uint32_t a, uint32_t b) { return MAX ? max(a, b) : min(a, b); };
+  v = op(v, dpp_u32<kDppXor1>(v));
+  v = op(v, dpp_u32<kDppXor2>(v));
+  v = op(v, dpp_u32<kDppRowHalfMirror>(v));
+  v = op(v, dpp_u32<kDppRowMirror>(v));  // every lane holds its 16-lane row's result
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return op(op(a, b), op(c, d));
 }
 
-template <int STEP>
-__device__ __forceinline__ uint64_t partner(uint64_t v) {
-  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  if constexpr (STEP == 0) {
-    lo = dpp_u32<kDppXor1>(lo);
-    hi = dpp_u32<kDppXor1>(hi);
-  } else if constexpr (STEP == 1) {
-    lo = dpp_u32<kDppXor2>(lo);
-    hi = dpp_u32<kDppXor2>(hi);
-  } else if constexpr (STEP == 2) {
-    lo = dpp_u32<kDppRowHalfMirror>(lo);
-    hi = dpp_u32<kDppRowHalfMirror>(hi);
-  } else if constexpr (STEP == 3) {
-    lo = dpp_u32<kDppRowMirror>(lo);
-    hi = dpp_u32<kDppRowMirror>(hi);
-  } else if constexpr (STEP == 4) {
-    lo = swz_xor16(lo);
-    hi = swz_xor16(hi);
-  } else {
-    lo = bperm_xor32(lo);
-    hi = bperm_xor32(hi);
-  }
-  return ((uint64_t)hi << 32) | lo;
-}
+constexpr uint32_t kNoExpert = 0xFFFFu;  // padding / consumed slot: loses every tie
 
-// Merge this lane's descending top-NP list with its partner group's list.
-template <int NP, int STEP>
-__device__ __forceinline__ void merge_step(uint64_t (&L)[NP]) {
-  uint64_t B[NP];
-#pragma unroll
-  for (int i = 0; i < NP; ++i) B[i] = partner<STEP>(L[i]);
-#pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const uint64_t o = B[NP - 1 - i];
-    L[i] = L[i] > o ? L[i] : o;  // bitonic: top NP of the union
-  }
-#pragma unroll
-  for (int d = NP / 2; d >= 1; d /= 2) {
-#pragma unroll
-    for (int i = 0; i < NP; ++i)
-      if ((i & d) == 0) cswap_desc(L[i], L[i + d]);
-  }
-}
-
-// Top-k of one token by one wave; E <= 256 (4 keys per lane), k <= NP.
-// Lanes j < k return the j-th selected expert and its softmax weight.
-template <int NP>
+// Top-k of one token by one wave; E <= 256 (expert lane + 64 i in key i of
+// a lane), 1 <= k <= 8, k <= E.  Lanes j < k return the j-th selected expert
+// and its softmax weight.
+//
+// Each lane first sorts its four keys (value descending, lower expert first
+// on equal values), so a round only compares the lanes' heads: the wave
+// maximum of the heads, the one lane holding it (a wave minimum of the
+// expert index breaks the rare tie between lanes), and that lane drops its
+// head.
 __device__ __forceinline__ void topk_token(const float *__restrict__ row, int E, int k, int lane, int &sel,
                                            float &wsel) {
-  uint64_t key[4];
+  uint32_t kv[4], ex[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
-    key[i] = (e < E) ? make_key(row[e], e) : 0ull;
+    kv[i] = (e < E) ? ord_key(row[e]) : 0u;
+    ex[i] = (e < E) ? (uint32_t)e : kNoExpert;
   }
-  cswap_desc(key[0], key[1]);
-  cswap_desc(key[2], key[3]);
-  cswap_desc(key[0], key[2]);
-  cswap_desc(key[1], key[3]);
-  cswap_desc(key[1], key[2]);
-  uint64_t L[NP];
+  auto order = [&](int a, int b) {  // slot a before slot b
+    const bool sw = kv[b] > kv[a] || (kv[b] == kv[a] && ex[b] < ex[a]);
+    const uint32_t ka = kv[a], xa = ex[a];
+    kv[a] = sw ? kv[b] : ka;
+    ex[a] = sw ? ex[b] : xa;
+    kv[b] = sw ? ka : kv[b];
+    ex[b] = sw ? xa : ex[b];
+  };
+  order(0, 1);
+  order(2, 3);
+  order(0, 2);
+  order(1, 3);
+  order(1, 2);
+  uint32_t top0 = 0u, mine_key = 0u;
+  int mine = 0;
 #pragma unroll
-  for (int i = 0; i < NP; ++i) L[i] = (i < 4) ? key[i] : 0ull;
-  merge_step<NP, 0>(L);
-  merge_step<NP, 1>(L);
-  merge_step<NP, 2>(L);
-  merge_step<NP, 3>(L);
-  merge_step<NP, 4>(L);
-  merge_step<NP, 5>(L);
-  // Every lane now holds the token's top-NP, largest first.
-  const float lmax = key_value(L[0]);
-  float ex[NP];
-  float sum = 0.f;
-#pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    ex[i] = (i < k) ? expf(key_value(L[i]) - lmax) : 0.f;
-    sum += ex[i];
-  }
-  uint64_t mine = 0;
-  float mine_ex = 0.f;
-#pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    if (lane == i) {
-      mine = L[i];
-      mine_ex = ex[i];
+  for (int r = 0; r < 8; ++r) {
+    if (r < k) {  // uniform
+      const uint32_t M = wave_reduce_u32<true>(kv[0]);
+      const uint64_t hit = __ballot(kv[0] == M);
+      int wl = __builtin_ctzll(hit);
+      if (__popcll(hit) != 1) {  // equal heads in several lanes: lowest expert index
+        const uint32_t cand = (kv[0] == M) ? ex[0] : 0xFFFFFFFFu;
+        const uint32_t emin = wave_reduce_u32<false>(cand);
+        wl = __builtin_ctzll(__ballot(cand == emin));
+      }
+      const int e = __builtin_amdgcn_readlane((int)ex[0], wl);
+      if (r == 0) top0 = M;
+      if (lane == r) {
+        mine = e;
+        mine_key = M;
+      }
+      if (lane == wl) {
+        kv[0] = kv[1];
+        ex[0] = ex[1];
+        kv[1] = kv[2];
+        ex[1] = ex[2];
+        kv[2] = kv[3];
+        ex[2] = ex[3];
+        kv[3] = 0u;
+        ex[3] = kNoExpert;
+      }
     }
   }
-  sel = key_index(mine);
+  // softmax over the selected logits, largest first: lane j < k owns exp of
+  // the j-th; the sum is taken in selection order
+  const float lmax = ord_value(top0);
+  const float mine_ex = (lane < k) ? expf(ord_value(mine_key) - lmax) : 0.f;
+  float sum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine_ex), r));
+  sel = mine;
   wsel = mine_ex / sum;
 }
 
 // One wave per token.
-template <int NP>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict__ logits, int T, int E, int k,
                                                          int32_t *__restrict__ idx, float *__restrict__ wts) {
   const int wave = threadIdx.x >> 6;
@@ -140,7 +129,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict
   if (t >= T) return;  // wave-uniform
   int sel;
   float wsel;
-  topk_token<NP>(logits + (size_t)t * E, E, k, lane, sel, wsel);
+  topk_token(logits + (size_t)t * E, E, k, lane, sel, wsel);
   if (lane < k) {
     idx[(size_t)t * k + lane] = sel;
     wts[(size_t)t * k + lane] = wsel;
@@ -229,6 +218,65 @@ __device__ __forceinline__ void build_maps(const int32_t *idx, int R, int E, int
   }
 }
 
+// The same maps for R <= 64 rows by one wave, with no barrier: row r sits in
+// lane r.  Matching the expert-id bits from the most significant down, a row
+// also counts the rows whose id first differs by a 0 where its own has a 1,
+// i.e. the rows of smaller experts, so its position is that count plus its
+// rank among equal ids.  The offsets come from per-expert counts in LDS
+// (written by the first row of each expert; one wave's LDS accesses complete
+// in program order) and a wave prefix sum.
+__device__ __forceinline__ void build_maps_wave(const int32_t *idx, int R, int E, int32_t *__restrict__ offsets,
+                                                int32_t *__restrict__ p2e, int32_t *__restrict__ e2p,
+                                                int32_t (&cnt)[256]) {
+  const int lane = lane_id();
+  const bool valid = lane < R;
+  const int e = valid ? idx[lane] : 0;
+  *(int4 *)&cnt[4 * lane] = make_int4(0, 0, 0, 0);
+  uint64_t match = __ballot(valid);
+  int less = 0;
+#pragma unroll
+  for (int b = 7; b >= 0; --b) {
+    const uint64_t m = __ballot(valid && ((e >> b) & 1));
+    if ((e >> b) & 1) {
+      less += __popcll(match & ~m);
+      match &= m;
+    } else {
+      match &= ~m;
+    }
+  }
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int rank = __popcll(match & lt);
+  __builtin_amdgcn_wave_barrier();
+  if (valid && rank == 0) cnt[e] = __popcll(match);
+  __builtin_amdgcn_wave_barrier();
+  if (valid) {
+    const int p = less + rank;
+    p2e[p] = lane;
+    e2p[lane] = p;
+  }
+  // exclusive scan of the counts: lane owns experts 4*lane .. 4*lane+3
+  const int4 c4 = *(const int4 *)&cnt[4 * lane];
+  const int c[4] = {c4.x, c4.y, c4.z, c4.w};
+  const int s = c[0] + c[1] + c[2] + c[3];
+  int incl = s;  // inclusive prefix inside each 16-lane row, then across rows
+  incl += (int)__builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, true);  // row_shr:1
+  incl += (int)__builtin_amdgcn_update_dpp(0, incl, 0x112, 0xF, 0xF, true);  // row_shr:2
+  incl += (int)__builtin_amdgcn_update_dpp(0, incl, 0x114, 0xF, 0xF, true);  // row_shr:4
+  incl += (int)__builtin_amdgcn_update_dpp(0, incl, 0x118, 0xF, 0xF, true);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(incl, 15);
+  const int r1 = __builtin_amdgcn_readlane(incl, 31);
+  const int r2 = __builtin_amdgcn_readlane(incl, 47);
+  const int row = lane >> 4;
+  incl += (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+  int run = incl - s;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (4 * lane + i < E) offsets[4 * lane + i] = run;
+    run += c[i];
+  }
+  if (lane == 0) offsets[E] = R;
+}
+
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void expert_maps_kernel(const int32_t *__restrict__ idx, int R, int E,
                                                               int32_t *__restrict__ offsets,
@@ -239,19 +287,20 @@ __global__ __launch_bounds__(NW * 64) void expert_maps_kernel(const int32_t *__r
 
 // Decode-sized batches (T <= NW): top-k and maps in one workgroup, the
 // selections handed over through LDS.
-template <int NP, int NW>
+template <int NW>
 __global__ __launch_bounds__(NW * 64) void route_fused_kernel(const float *__restrict__ logits, int T, int E, int k,
                                                               int32_t *__restrict__ idx, float *__restrict__ wts,
                                                               int32_t *__restrict__ offsets,
                                                               int32_t *__restrict__ p2e,
                                                               int32_t *__restrict__ e2p) {
   __shared__ int32_t sidx[NW * 8];
+  __shared__ __attribute__((aligned(16))) int32_t cnt[256];
   const int wave = threadIdx.x >> 6;
   const int lane = lane_id();
   if (wave < T) {  // wave-uniform
     int sel;
     float wsel;
-    topk_token<NP>(logits + (size_t)wave * E, E, k, lane, sel, wsel);
+    topk_token(logits + (size_t)wave * E, E, k, lane, sel, wsel);
     if (lane < k) {
       idx[(size_t)wave * k + lane] = sel;
       wts[(size_t)wave * k + lane] = wsel;
@@ -259,42 +308,26 @@ __global__ __launch_bounds__(NW * 64) void route_fused_kernel(const float *__res
     }
   }
   __syncthreads();
-  build_maps<NW>(sidx, T * k, E, offsets, p2e, e2p);
-}
-
-template <int NP>
-static void launch_fused(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *idx, float *w,
-                         int32_t *offsets, int32_t *p2e, int32_t *e2p, hipStream_t s) {
-  if (T <= 4)
-    route_fused_kernel<NP, 4><<<1, 256, 0, s>>>(logits, T, E, k, idx, w, offsets, p2e, e2p);
-  else if (T <= 8)
-    route_fused_kernel<NP, 8><<<1, 512, 0, s>>>(logits, T, E, k, idx, w, offsets, p2e, e2p);
-  else
-    route_fused_kernel<NP, 16><<<1, 1024, 0, s>>>(logits, T, E, k, idx, w, offsets, p2e, e2p);
+  if (T * k <= 64) {  // uniform
+    if (wave == 0) build_maps_wave(sidx, T * k, E, offsets, p2e, e2p, cnt);
+  } else {
+    build_maps<NW>(sidx, T * k, E, offsets, p2e, e2p);
+  }
 }
 
 hipError_t launch_route(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *idx, float *w,
                         int32_t *offsets, int32_t *p2e, int32_t *e2p, hipStream_t s) {
   if (T <= 16) {  // one launch: top-k and maps in one workgroup
-    if (k <= 1)
-      launch_fused<1>(logits, T, E, k, idx, w, offsets, p2e, e2p, s);
-    else if (k <= 2)
-      launch_fused<2>(logits, T, E, k, idx, w, offsets, p2e, e2p, s);
-    else if (k <= 4)
-      launch_fused<4>(logits, T, E, k, idx, w, offsets, p2e, e2p, s);
+    if (T <= 4)
+      route_fused_kernel<4><<<1, 256, 0, s>>>(logits, T, E, k, idx, w, offsets, p2e, e2p);
+    else if (T <= 8)
+      route_fused_kernel<8><<<1, 512, 0, s>>>(logits, T, E, k, idx, w, offsets, p2e, e2p);
     else
-      launch_fused<8>(logits, T, E, k, idx, w, offsets, p2e, e2p, s);
+      route_fused_kernel<16><<<1, 1024, 0, s>>>(logits, T, E, k, idx, w, offsets, p2e, e2p);
     return hipGetLastError();
   }
   const dim3 grid((T + 3) / 4);
-  if (k <= 1)
-    route_topk_kernel<1><<<grid, 256, 0, s>>>(logits, T, E, k, idx, w);
-  else if (k <= 2)
-    route_topk_kernel<2><<<grid, 256, 0, s>>>(logits, T, E, k, idx, w);
-  else if (k <= 4)
-    route_topk_kernel<4><<<grid, 256, 0, s>>>(logits, T, E, k, idx, w);
-  else
-    route_topk_kernel<8><<<grid, 256, 0, s>>>(logits, T, E, k, idx, w);
+  route_topk_kernel<<<grid, 256, 0, s>>>(logits, T, E, k, idx, w);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int R = T * k;

@@ -166,6 +166,32 @@ def test_route_shapes(T, E, k):
     assert np.array_equal(d["e2p"].cpu().numpy(), e2p)
 
 
+@pytest.mark.parametrize("T,E,k", [(1, 256, 8), (4, 256, 8), (8, 256, 8), (9, 256, 8), (16, 200, 8),
+                                   (40, 256, 8), (16, 256, 2)])
+def test_route_discrete_logits(T, E, k):
+    """Logits from four values: nearly every selection round meets equal
+    maxima in several lanes (lower expert index wins), and the expert maps
+    see few distinct experts with many rows each."""
+    import fp4_weight_only_amd as q
+    rng = np.random.default_rng(T * 131 + E + k)
+    lg = rng.integers(0, 4, (T, E)).astype(np.float32) - 1.5
+    d = dict(idx=torch.empty((T, k), dtype=torch.int32, device="cuda"),
+             w=torch.empty((T, k), dtype=torch.float32, device="cuda"),
+             off=torch.empty((E + 1,), dtype=torch.int32, device="cuda"),
+             p2e=torch.empty((T * k,), dtype=torch.int32, device="cuda"),
+             e2p=torch.empty((T * k,), dtype=torch.int32, device="cuda"))
+    print_case("route discrete", T, E, k)
+    q.qmoe_route_topk(to_dev(lg), k, d["idx"], d["w"], d["off"], d["p2e"], d["e2p"])
+    torch.cuda.synchronize()
+    idx, w = route.route_topk(lg, k)
+    assert np.array_equal(d["idx"].cpu().numpy(), idx)
+    assert_close("topk_w", d["w"].cpu().numpy(), w)
+    off, p2e, e2p = route.expert_maps(idx, E)
+    assert np.array_equal(d["off"].cpu().numpy(), off)
+    assert np.array_equal(d["p2e"].cpu().numpy(), p2e)
+    assert np.array_equal(d["e2p"].cpu().numpy(), e2p)
+
+
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
 def test_every_code_in_every_nibble_through_the_gemv(fmt):
     """Closed form: one nonzero code per column, so u = x_k * e2m1 * scale * g exactly."""
