@@ -239,6 +239,31 @@ __global__ __launch_bounds__(max_waves<MRMAX>() * 64) void fp4_gemv_kernel(GemvA
   const int e = find_slot_expert(a.offsets, a.E, slot, row0, m);
   if (e < 0) return;  // uniform over the workgroup
 
+  // ---- activation rows of the first pass, then the weights ---------------------
+  // The activation load goes out before the 32 weight loads: memory returns in
+  // issue order, so staging then waits for x alone, and the dot products can
+  // start on the first weight rows while the rest are still arriving.
+  // MRMAX * KC / 8 <= W * 64, so one 16-byte load per thread covers a pass.
+  static_assert(MRMAX <= 8, "one staging load per thread per pass");
+  const int per_row = KC / 8;
+  const int mr0 = m < MRMAX ? m : MRMAX;
+  u32x4_t xv0 = {0u, 0u, 0u, 0u};
+  int xr0 = 0, xk0 = 0;
+  const bool xon0 = tid < MRMAX * per_row;
+  {
+    const int r = xon0 ? tid / per_row : 0;
+    const int kk = (tid - r * per_row) * 8;
+    const int kabs = kc * KC + kk;
+    const int p = row0 + r;
+    const int tok = __shfl(p2e_l, p & 63, 64) / a.topk;
+    if (xon0 && r < mr0 && kabs < a.K) {
+      const int src = a.fc1 ? tok : p;
+      xv0 = *(const u32x4_t *)(a.act + (size_t)src * a.K + kabs);
+    }
+    xr0 = r;
+    xk0 = kk;
+  }
+
   // ---- weight and scale loads of this lane ----------------------------------
   const int nl = lane & 31;
   const int g = wave * 2 + (lane >> 5);  // 32-row k group inside the chunk
@@ -253,32 +278,30 @@ __global__ __launch_bounds__(max_waves<MRMAX>() * 64) void fp4_gemv_kernel(GemvA
   const bool col_ok = col0 < a.N;
   const uint32_t woff = col_ok ? (uint32_t)kl * rowbytes + (uint32_t)(col0 >> 1) : kOutOfRange;
   const uint32_t soff = col_ok ? (uint32_t)(kl / B) * (uint32_t)a.N + (uint32_t)col0 : kOutOfRange;
-  uint32_t A[kGemvLaneK];
-#pragma unroll
-  for (int i = 0; i < kGemvLaneK; ++i)
-    A[i] = __builtin_amdgcn_raw_buffer_load_b32(wr, woff, i * (int)rowbytes, kBufNontemporal);
+  // scales first: their decode does not wait for the weight rows
   u32x2_t SB[2];
 #pragma unroll
   for (int b = 0; b < 2; ++b)
     SB[b] = (b < NBLK) ? __builtin_amdgcn_raw_buffer_load_b64(sr, soff, b * a.N, 0) : u32x2_t{0u, 0u};
+  uint32_t A[kGemvLaneK];
+#pragma unroll
+  for (int i = 0; i < kGemvLaneK; ++i)
+    A[i] = __builtin_amdgcn_raw_buffer_load_b32(wr, woff, i * (int)rowbytes, kBufNontemporal);
   const float gs = a.gscale ? a.gscale[e] : 1.0f;
 
   // ---- passes of up to MRMAX rows -----------------------------------------------
-#pragma nounroll
-  for (int rbase = 0; rbase < m; rbase += MRMAX) {
-    // Opaque to the optimiser: keeps the decode inside the pass (hoisted out
-    // of this loop it would keep all 128 decoded registers live).
-#pragma unroll
-    for (int i = 0; i < kGemvLaneK; ++i) asm volatile("" : "+v"(A[i]));
+  // The first pass is peeled out of the loop: in straight-line code each dot
+  // product waits only for its own weight rows.
+  auto pass = [&](const int rbase) {
     const int rem = m - rbase;
     const int mr = rem < MRMAX ? rem : MRMAX;
     // Stage the chunk's activation rows (rows past mr as zeros): one thread
-    // per 8 values.
-    // The loop is wave-uniform so the row lookup runs with every lane active.
-    for (int i0 = wave * 64; i0 < MRMAX * (KC / 8); i0 += W * 64) {
-      const int i = i0 + lane;
-      const bool on = i < MRMAX * (KC / 8);
-      const int per_row = KC / 8;
+    // per 8 values; the first pass's load was issued with the weights.
+    if (rbase == 0) {
+      if (xon0) *(u32x4_t *)&sm.xs[xr0][xk0] = xv0;
+    } else {
+      const int i = tid;
+      const bool on = i < MRMAX * per_row;
       const int r = on ? i / per_row : 0;
       const int kk = (i - r * per_row) * 8;
       const int kabs = kc * KC + kk;
@@ -291,7 +314,7 @@ __global__ __launch_bounds__(max_waves<MRMAX>() * 64) void fp4_gemv_kernel(GemvA
       }
       if (on) *(u32x4_t *)&sm.xs[r][kk] = v;
     }
-    __syncthreads();
+    lds_barrier();
 
     if (MRMAX == 1 || mr == 1)
       lane_dot<FMT, 1, MRMAX>(sm, A, SB, g, wave, lane);
@@ -299,7 +322,14 @@ __global__ __launch_bounds__(max_waves<MRMAX>() * 64) void fp4_gemv_kernel(GemvA
       lane_dot<FMT, 2, MRMAX>(sm, A, SB, g, wave, lane);
     else
       lane_dot<FMT, 4, MRMAX>(sm, A, SB, g, wave, lane);  // 3 or 4 rows
-    __syncthreads();
+    // Opaque to the optimiser: a later pass sees the weights as new values,
+    // so their decode stays inside each pass (hoisted out of the loop it would
+    // keep all 128 decoded registers live).
+#pragma unroll
+    for (int i = 0; i < kGemvLaneK; ++i) asm volatile("" : "+v"(A[i]));
+#pragma unroll
+    for (int b = 0; b < 2; ++b) asm volatile("" : "+v"(SB[b]));
+    lds_barrier();
 
     // ---- reduce the W waves (fixed order); one thread per column ------------
     for (int cl = tid; cl < kGemvTileN; cl += W * 64) {
@@ -318,7 +348,12 @@ __global__ __launch_bounds__(max_waves<MRMAX>() * 64) void fp4_gemv_kernel(GemvA
         }
       }
     }
-    __syncthreads();
+  };
+  pass(0);
+#pragma nounroll
+  for (int rbase = MRMAX; rbase < m; rbase += MRMAX) {
+    lds_barrier();  // the previous pass's reduction has read sm.red
+    pass(rbase);
   }
 }
 
