@@ -12,7 +12,9 @@ dequantized weight is exact in float64).
 Readings (the pages leave these open):
   * FC1 output column 2j is the gate and 2j+1 the linear value (interleaved
     SwiGLU, operator documentation section 8; the adjacent gate/linear pair
-    of PR 32122).
+    of PR 32122).  With the concatenated layout (swiglu_fusion=2, section 8)
+    column j is the gate and column I+j the linear value; swiglu_fusion=0 is
+    read as interleaved, as the section says the QMoE operator treats it.
   * SwiGLU(G, L) = G * sigmoid(alpha*G) * (L + beta) with G = min(gate,
     limit) and L = clamp(linear, -limit, limit) (section 8); the defaults
     alpha=1, beta=0, limit=+inf are the standard SiLU(gate)*linear.
@@ -33,7 +35,7 @@ import numpy as np
 
 from . import codecs
 from .dequant import dequant_expert_f64
-from .route import expert_maps, route_topk
+from .route import expert_maps, route_topk, route_topk_router_weights
 
 
 def swiglu(gate, lin, alpha: float = 1.0, beta: float = 0.0, limit: float = np.inf) -> np.ndarray:
@@ -50,17 +52,25 @@ def _rows_of(offsets, e):
 def fc1_swiglu(x_bits, k: int, w1, s1, g1, fmt: str, offsets, p2e, act=None, cols=None):
     """x bf16 bits [T][H]; w1 [E][H][I]; s1 [E][H/B][2I] -> (h bf16 bits [R][I], u float64 [R][2I]).
 
-    cols: optional array of h columns j to compute (others left 0); FC1
-    columns 2j and 2j+1 are evaluated for each.
+    act: {"alpha", "beta", "limit", "fusion"} (fusion 2 = concatenated
+    gate | linear halves, otherwise interleaved).
+    cols: optional array of h columns j to compute (others left 0); the FC1
+    columns of each pair (2j and 2j+1, or j and I+j) are evaluated for each.
     """
     act = act or {}
+    concat = act.get("fusion", 1) == 2
     x64 = codecs.bf16_to_f64(x_bits)
     E = w1.shape[0]
     N = w1.shape[2] * 2
     I = N // 2
     R = int(offsets[E])
     u = np.zeros((R, N), dtype=np.float64)
-    fcols = None if cols is None else np.stack([2 * np.asarray(cols), 2 * np.asarray(cols) + 1], 1).reshape(-1)
+    if cols is None:
+        fcols = None
+    elif concat:
+        fcols = np.concatenate([np.asarray(cols), I + np.asarray(cols)])
+    else:
+        fcols = np.stack([2 * np.asarray(cols), 2 * np.asarray(cols) + 1], 1).reshape(-1)
     for e in range(E):
         lo, hi = _rows_of(offsets, e)
         if lo == hi:
@@ -72,7 +82,8 @@ def fc1_swiglu(x_bits, k: int, w1, s1, g1, fmt: str, offsets, p2e, act=None, col
             u[lo:hi] = ue
         else:
             u[lo:hi, fcols] = ue
-    h = swiglu(u[:, 0::2], u[:, 1::2], act.get("alpha", 1.0), act.get("beta", 0.0), act.get("limit", np.inf))
+    gate, lin = (u[:, :I], u[:, I:]) if concat else (u[:, 0::2], u[:, 1::2])
+    h = swiglu(gate, lin, act.get("alpha", 1.0), act.get("beta", 0.0), act.get("limit", np.inf))
     hb = codecs.bf16_from_f64(h)
     if cols is not None:
         mask = np.zeros(I, bool)
@@ -108,10 +119,14 @@ def finalize(y, topk_w, e2p, T: int, k: int) -> np.ndarray:
     return out
 
 
-def layer(inp, act=None) -> dict:
-    """The whole expert path on synth.LayerInputs; returns every intermediate."""
+def layer(inp, act=None, router_weights=None) -> dict:
+    """The whole expert path on synth.LayerInputs; returns every intermediate.
+    router_weights [T][E]: DeepSeek-style mixing weights (route.route_topk_router_weights)."""
     c = inp.cfg
-    idx, wts = route_topk(inp.logits, c.k)
+    if router_weights is None:
+        idx, wts = route_topk(inp.logits, c.k)
+    else:
+        idx, wts = route_topk_router_weights(inp.logits, router_weights, c.k)
     offsets, p2e, e2p = expert_maps(idx, c.E)
     h, u = fc1_swiglu(inp.x, c.k, inp.w1, inp.s1, inp.g1, c.fmt, offsets, p2e, act)
     y = fc2(h, inp.w2, inp.s2, inp.g2, c.fmt, offsets)

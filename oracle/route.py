@@ -9,7 +9,11 @@ unchanged across kernels).  Readings:
     to the lower expert index, -0 equal to +0;
   * the k weights are a softmax over the selected logits (equivalently the
     softmax over all E experts renormalised over the k chosen), so they sum
-    to 1.
+    to 1;
+  * with router_weights (operator documentation section 2, input 14,
+    DeepSeek-style routing) the logits only choose the experts and the k
+    mixing weights are router_weights[t, e] at the chosen experts, taken as
+    they are (no softmax, no renormalisation).
 
 Expert maps (PR 31156, the expert-map prologue; operator documentation
 section 1, "permute by expert"): expanded row r = t*k + j; rows are grouped
@@ -61,3 +65,15 @@ def expert_maps(idx, E: int):
         e2p[r] = p
     return (np.array(offsets, dtype=np.int32), np.array(p2e, dtype=np.int32),
             np.array(e2p, dtype=np.int32))
+
+
+def route_topk_router_weights(logits, router_weights, k: int):
+    """Selection on the logits as route_topk; mixing weights gathered from
+    router_weights [T][E] at the selected experts (section 2, input 14)."""
+    idx, _ = route_topk(logits, k)
+    rw = np.asarray(router_weights, dtype=np.float32)
+    wts = np.zeros(idx.shape, dtype=np.float64)
+    for t in range(idx.shape[0]):
+        for j in range(idx.shape[1]):
+            wts[t, j] = float(rw[t, idx[t, j]])
+    return idx, wts

@@ -9,14 +9,14 @@ Layouts (one MoE layer):
   x       bfloat16 bits (uint16) [T][H]
   w1      uint8 [E][H][I]       FC1 packed E2M1, K=H, N=2I; byte (e,k,j): low nibble = column 2j
   s1      uint8 [E][H/B][2I]    FC1 block scales (E4M3 bytes for NVFP4, E8M0 bytes for MXFP4)
-  g1      float32 [E] or None   FC1 per-expert global scale (NVFP4 only)
+  g1      float32 [E] or None   FC1 per-expert global scale (NVFP4; MXFP4 when mx_global)
   w2      uint8 [E][I][H/2]     FC2 packed E2M1, K=I, N=H
   s2      uint8 [E][I/B][H]
   g2      float32 [E] or None
 
 Random streams: one numpy PCG64 generator per (seed, tensor id), so every
 tensor is reproducible on its own.  Tensor ids: 0 logits, 1 x, 2 w1, 3 s1,
-4 g1, 5 w2, 6 s2, 7 g2, 8 hot/popularity permutation.
+4 g1, 5 w2, 6 s2, 7 g2, 8 hot/popularity permutation, 9 router weights.
 """
 from __future__ import annotations
 
@@ -88,6 +88,7 @@ class LayerConfig:
     routing: str = "normal"       # "normal" | "hot3" | "zipf"
     seed: int = 0
     positive_scales: bool = False
+    mx_global: bool = False       # MXFP4 with a per-expert global scale too
 
     @property
     def B(self) -> int:
@@ -157,8 +158,15 @@ def fc_weights(cfg: LayerConfig, which: int):
         gs = global_scales(stream(cfg.seed, base + 2), cfg.E)
     else:
         s = e8m0_scales(stream(cfg.seed, base + 1), (cfg.E, K // cfg.B, N))
-        gs = None
+        gs = global_scales(stream(cfg.seed, base + 2), cfg.E) if cfg.mx_global else None
     return w, s, gs
+
+
+def router_weights(cfg: LayerConfig) -> np.ndarray:
+    """float32 [T][E] mixing weights for DeepSeek-style routing: sigmoid
+    scores of their own normal draws, in (0, 1)."""
+    z = stream(cfg.seed, 9).standard_normal(size=(cfg.T, cfg.E))
+    return (1.0 / (1.0 + np.exp(-z))).astype(np.float32)
 
 
 @dataclasses.dataclass
@@ -201,5 +209,6 @@ def shrink(cfg: LayerConfig, E: int | None = None, H: int | None = None, I: int 
     c = dataclasses.replace(
         cfg, E=E or cfg.E, H=H or cfg.H, I=I or cfg.I, T=T or cfg.T, k=k or cfg.k,
         seed=cfg.seed if seed is None else seed)
-    return dataclasses.replace(c, name=f"{cfg.fmt}_T{c.T}_E{c.E}_top{c.k}_H{c.H}_I{c.I}_{c.routing}_s{c.seed}")
+    g = "_g" if c.mx_global else ""
+    return dataclasses.replace(c, name=f"{cfg.fmt}{g}_T{c.T}_E{c.E}_top{c.k}_H{c.H}_I{c.I}_{c.routing}_s{c.seed}")
 

@@ -6,6 +6,8 @@ over the definition's indices on tiny shapes, closed forms (a single nonzero
 code per column, powers of two), and the textbook dense SwiGLU FFN
 (torch.nn.functional.silu) that an E=1, k=1 layer reduces to.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import scipy.special
@@ -169,13 +171,19 @@ def test_swiglu_special_cases():
 # ------------------------------------------------------------ FC1 / FC2 ----
 
 def _tiny_layer(fmt, seed=0, E=3, H=64, I=32, T=3, k=2):
+    """fmt "mxfp4_g": MXFP4 with per-expert global scales."""
     base = synth.TINY if fmt == "nvfp4" else synth.MX_DECODE
-    return synth.layer_inputs(synth.shrink(base, E=E, H=H, I=I, T=T, k=k, seed=seed))
+    cfg = synth.shrink(base, E=E, H=H, I=I, T=T, k=k, seed=seed)
+    if fmt == "mxfp4_g":
+        cfg = dataclasses.replace(cfg, mx_global=True)
+    return synth.layer_inputs(cfg)
 
 
-@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
-def test_fc1_fc2_equal_bruteforce_loops(fmt):
-    L = _tiny_layer(fmt)
+@pytest.mark.parametrize("fmt_case", ["nvfp4", "mxfp4", "mxfp4_g"])
+def test_fc1_fc2_equal_bruteforce_loops(fmt_case):
+    L = _tiny_layer(fmt_case)
+    fmt = "nvfp4" if fmt_case == "nvfp4" else "mxfp4"
+    assert (L.g1 is None) == (fmt_case == "mxfp4")
     c = L.cfg
     idx, _ = route.route_topk(L.logits, c.k)
     off, p2e, _ = route.expert_maps(idx, c.E)
@@ -244,6 +252,77 @@ def test_layer_E1_k1_is_dense_swiglu_ffn():
     # the float32 hop before bf16 can differ from one rounding by an ulp of h
     assert ok, rep
     np.testing.assert_allclose(r["u"], u.numpy(), rtol=1e-13)
+
+
+def _concat_to_interleaved(w, s):
+    """Column permutation written out nibble by nibble: interleaved column 2j
+    takes concatenated column j (gate), 2j+1 takes column I+j (linear)."""
+    E, K, half = w.shape
+    I = half
+    codes = np.zeros((E, K, 2 * half), np.uint8)
+    for n in range(2 * half):
+        codes[:, :, n] = (w[:, :, n // 2] >> (4 * (n % 2))) & 15
+    perm = np.empty(2 * I, np.int64)
+    perm[0::2] = np.arange(I)
+    perm[1::2] = I + np.arange(I)
+    ci = codes[:, :, perm]
+    wi = (ci[:, :, 0::2] | (ci[:, :, 1::2] << 4)).astype(np.uint8)
+    return wi, s[:, :, perm]
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_concat_swiglu_equals_interleaved_on_permuted_columns(fmt):
+    L = _tiny_layer(fmt, seed=11, E=4, T=4, k=2, H=64, I=32)
+    c = L.cfg
+    idx, _ = route.route_topk(L.logits, c.k)
+    off, p2e, _ = route.expert_maps(idx, c.E)
+    act = dict(alpha=1.702, beta=1.0, limit=7.0)
+    hc, uc = moe.fc1_swiglu(L.x, c.k, L.w1, L.s1, L.g1, fmt, off, p2e, dict(act, fusion=2))
+    wi, si = _concat_to_interleaved(L.w1, L.s1)
+    hi, ui = moe.fc1_swiglu(L.x, c.k, wi, si, L.g1, fmt, off, p2e, dict(act, fusion=1))
+    np.testing.assert_array_equal(hc, hi)
+    np.testing.assert_array_equal(uc[:, :c.I], ui[:, 0::2])
+    np.testing.assert_array_equal(uc[:, c.I:], ui[:, 1::2])
+    # fusion 0 is read as interleaved
+    h0, _ = moe.fc1_swiglu(L.x, c.k, wi, si, L.g1, fmt, off, p2e, dict(act, fusion=0))
+    np.testing.assert_array_equal(h0, hi)
+    # sampled columns give the same values as the full computation
+    cols = np.array([0, 5, 31])
+    hs, _ = moe.fc1_swiglu(L.x, c.k, L.w1, L.s1, L.g1, fmt, off, p2e, dict(act, fusion=2), cols=cols)
+    np.testing.assert_array_equal(hs[:, cols], hc[:, cols])
+
+
+def test_concat_layer_E1_k1_is_dense_swiglu_ffn():
+    L = _tiny_layer("nvfp4", seed=12, E=1, T=4, k=1, H=64, I=48)
+    r = moe.layer(L, act=dict(fusion=2))
+    W1 = torch.tensor(table_dequant(L.w1[0], L.s1[0], L.g1[0], "nvfp4"))
+    x = torch.tensor(codecs.bf16_to_f64(L.x))
+    u = x @ W1
+    h = torch.nn.functional.silu(u[:, :48]) * u[:, 48:]
+    hb = torch.tensor(codecs.bf16_to_f64(r["h"]))
+    torch.testing.assert_close(hb, h, rtol=2 ** -8, atol=1e-30)
+
+
+def test_router_weights_are_gathered_at_the_selection():
+    rng = np.random.default_rng(13)
+    T, E, k = 5, 40, 6
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    rw = (np.arange(T)[:, None] * 1000 + np.arange(E)[None, :] + 0.5).astype(np.float32)
+    idx, w = route.route_topk_router_weights(lg, rw, k)
+    ref_idx, _ = route.route_topk(lg, k)
+    np.testing.assert_array_equal(idx, ref_idx)
+    for t in range(T):
+        order = np.lexsort((np.arange(E), -lg[t].astype(np.float64)))[:k]
+        np.testing.assert_array_equal(idx[t], order)
+        np.testing.assert_array_equal(w[t], t * 1000 + order + 0.5)   # row t, the chosen columns
+    L = _tiny_layer("nvfp4", seed=14, E=6, T=3, k=2)
+    rws = synth.router_weights(L.cfg)
+    a = moe.layer(L, router_weights=rws)
+    b = moe.layer(L)
+    np.testing.assert_array_equal(a["idx"], b["idx"])
+    np.testing.assert_array_equal(a["y"], b["y"])
+    np.testing.assert_allclose(a["out"], moe.finalize(b["y"], rws[np.arange(3)[:, None], b["idx"]], b["e2p"], 3, 2),
+                               rtol=1e-15)
 
 
 def test_finalize_k1_and_identical_rows():
