@@ -25,7 +25,7 @@ QMOE_FMT_NVFP4, QMOE_FMT_MXFP4 = 0, 1
 QMOE_PATH_AUTO, QMOE_PATH_GEMV, QMOE_PATH_GROUPED = 0, 1, 2
 GEMV_MAX_ROWS = 64
 
-EXPORTS = ("qmoe_route_topk", "qmoe_fp4_gemv_fc1_swiglu", "qmoe_fp4_gemv_fc2", "qmoe_fp4_gemv_fc2_finalize",
+EXPORTS = ("qmoe_route_topk", "qmoe_route_topk_router_weights", "qmoe_fp4_gemv_fc1_swiglu", "qmoe_fp4_gemv_fc2", "qmoe_fp4_gemv_fc2_finalize",
            "qmoe_finalize",
            "qmoe_dequant_fp4", "qmoe_status_str")
 
@@ -41,8 +41,21 @@ class Fp4WeightsC(ctypes.Structure):
                 ("E", ctypes.c_int32), ("K", ctypes.c_int32), ("N", ctypes.c_int32), ("fmt", ctypes.c_int32)]
 
 
+QMOE_SWIGLU_INTERLEAVED = 1
+QMOE_SWIGLU_CONCAT = 2
+
+
 class SwigluC(ctypes.Structure):
-    _fields_ = [("alpha", ctypes.c_float), ("beta", ctypes.c_float), ("limit", ctypes.c_float)]
+    _fields_ = [("alpha", ctypes.c_float), ("beta", ctypes.c_float), ("limit", ctypes.c_float),
+                ("fusion", ctypes.c_int32)]
+
+
+def _swiglu(act):
+    """act: None, (alpha, beta, limit) or (alpha, beta, limit, fusion) -> ctypes pointer or None."""
+    if act is None:
+        return None
+    a = tuple(act)
+    return ctypes.byref(SwigluC(*a) if len(a) == 4 else SwigluC(*a, QMOE_SWIGLU_INTERLEAVED))
 
 
 def _load():
@@ -53,6 +66,7 @@ def _load():
     W = ctypes.POINTER(Fp4WeightsC)
     sig = {
         "qmoe_route_topk": [P, I32, I32, I32, P, P, P, P, P, P],
+        "qmoe_route_topk_router_weights": [P, P, I32, I32, I32, P, P, P, P, P, P],
         "qmoe_fp4_gemv_fc1_swiglu": [P, I32, I32, W, P, P, ctypes.POINTER(SwigluC), P, P, SZ, I32, P],
         "qmoe_fp4_gemv_fc2": [P, I32, I32, W, P, P, P, SZ, I32, P],
         "qmoe_fp4_gemv_fc2_finalize": [P, I32, I32, W, P, P, P, P, P, SZ, I32, P],
@@ -107,14 +121,22 @@ def qmoe_route_topk(logits, k, topk_idx, topk_w, expert_offsets, perm_to_expande
         _ptr(expanded_to_perm), _stream(stream)))
 
 
-def fc_workspace_bytes(which: int, T: int, k: int, w: FP4Weights, path=QMOE_PATH_AUTO) -> int:
-    """Workspace size of qmoe_fp4_gemv_fc1_swiglu (which=1), qmoe_fp4_gemv_fc2 (which=2) or
-    qmoe_fp4_gemv_fc2_finalize (which=3)."""
+def qmoe_route_topk_router_weights(logits, router_weights, k, topk_idx, topk_w, expert_offsets, perm_to_expanded,
+                                   expanded_to_perm, stream=None):
+    T, E = logits.shape
+    _check("qmoe_route_topk_router_weights", lib.qmoe_route_topk_router_weights(
+        _ptr(logits), _ptr(router_weights), T, E, k, _ptr(topk_idx), _ptr(topk_w), _ptr(expert_offsets),
+        _ptr(perm_to_expanded), _ptr(expanded_to_perm), _stream(stream)))
+
+
+def fc_workspace_bytes(which: int, T: int, k: int, w: FP4Weights, path=QMOE_PATH_AUTO, act=None) -> int:
+    """Workspace size of qmoe_fp4_gemv_fc1_swiglu (which=1, with its act), qmoe_fp4_gemv_fc2
+    (which=2) or qmoe_fp4_gemv_fc2_finalize (which=3)."""
     n = ctypes.c_size_t(0)
     wc = w.c()
     dummy = 256  # aligned non-null placeholders: a size query launches nothing
     if which == 1:
-        st = lib.qmoe_fp4_gemv_fc1_swiglu(dummy, T, k, ctypes.byref(wc), dummy, dummy, None, dummy, None,
+        st = lib.qmoe_fp4_gemv_fc1_swiglu(dummy, T, k, ctypes.byref(wc), dummy, dummy, _swiglu(act), dummy, None,
                                           ctypes.byref(n), path, None)
     elif which == 2:
         st = lib.qmoe_fp4_gemv_fc2(dummy, T, k, ctypes.byref(wc), dummy, dummy, None, ctypes.byref(n), path, None)
@@ -135,7 +157,7 @@ def qmoe_fp4_gemv_fc1_swiglu(x, k, w1: FP4Weights, expert_offsets, perm_to_expan
     T = x.shape[0]
     wc = w1.c()
     n = ctypes.c_size_t(ws.numel() * ws.element_size())
-    a = None if act is None else ctypes.byref(SwigluC(*act))
+    a = _swiglu(act)
     _check("qmoe_fp4_gemv_fc1_swiglu", lib.qmoe_fp4_gemv_fc1_swiglu(
         _ptr(x), T, k, ctypes.byref(wc), _ptr(expert_offsets), _ptr(perm_to_expanded), a, _ptr(h), _ptr(ws),
         ctypes.byref(n), path, _stream(stream)))

@@ -65,8 +65,9 @@ qmoe_status resolve_path(qmoe_path path, int32_t rows, const qmoe_fp4_weights *w
 
 qmoe_status run_fc(GemvArgs &a, const qmoe_fp4_weights *w, int max_rows, qmoe_path path, void *ws,
                    size_t *ws_bytes, hipStream_t stream) {
-  const size_t need = path == QMOE_PATH_GROUPED ? grouped_workspace_bytes()
-                                                : gemv_workspace_bytes(a.rows, max_rows, w->E, w->K, w->N);
+  const bool concat = a.concat != 0;
+  const size_t need = path == QMOE_PATH_GROUPED ? grouped_workspace_bytes(a.rows, w->N, concat)
+                                                : gemv_workspace_bytes(a.rows, max_rows, w->E, w->K, w->N, concat);
   if (!ws_bytes) return QMOE_EINVAL;
   if (!ws) {
     *ws_bytes = need;
@@ -81,7 +82,16 @@ qmoe_status run_fc(GemvArgs &a, const qmoe_fp4_weights *w, int max_rows, qmoe_pa
   a.K = w->K;
   a.N = w->N;
   const int fmt = w->fmt == QMOE_FMT_NVFP4 ? 0 : 1;
-  if (path == QMOE_PATH_GROUPED) return check_launch(launch_grouped(a, fmt, stream));
+  if (path == QMOE_PATH_GROUPED) {
+    if (!concat) return check_launch(launch_grouped(a, fmt, stream));
+    // concatenated SwiGLU: g * u as float32 rows, then the pairing epilogue
+    a.out_f32 = (float *)ws;
+    qmoe_status st = check_launch(launch_grouped(a, fmt, stream));
+    if (st != QMOE_OK) return st;
+    a.partials = (float *)ws;
+    a.nchunks = 1;
+    return check_launch(launch_splitk_epilogue(a, stream));
+  }
   gemv_plan(a, max_rows, ws);
   return check_launch(launch_fp4_gemv(a, fmt, max_rows, stream));
 }
@@ -114,7 +124,24 @@ qmoe_status qmoe_route_topk(const float *logits, int32_t T, int32_t E, int32_t k
   if (E > QMOE_MAX_EXPERTS || k > QMOE_MAX_TOPK) return QMOE_EUNSUPPORTED;
   if ((int64_t)T * k > (1 << 24)) return QMOE_EUNSUPPORTED;
   return check_launch(
-      launch_route(logits, T, E, k, topk_idx, topk_w, expert_offsets, perm_to_expanded, expanded_to_perm, stream));
+      launch_route(logits, nullptr, T, E, k, topk_idx, topk_w, expert_offsets, perm_to_expanded, expanded_to_perm,
+                   stream));
+}
+
+qmoe_status qmoe_route_topk_router_weights(const float *logits, const float *router_weights, int32_t T, int32_t E,
+                                           int32_t k, int32_t *topk_idx, float *topk_w, int32_t *expert_offsets,
+                                           int32_t *perm_to_expanded, int32_t *expanded_to_perm, hipStream_t stream) {
+  if (!logits || !router_weights || !topk_idx || !topk_w || !expert_offsets || !perm_to_expanded ||
+      !expanded_to_perm)
+    return QMOE_EINVAL;
+  if (T < 1 || E < 1 || k < 1 || k > E) return QMOE_EINVAL;
+  if (!aligned16(logits) || !aligned16(router_weights) || !aligned16(topk_idx) || !aligned16(topk_w) ||
+      !aligned16(expert_offsets) || !aligned16(perm_to_expanded) || !aligned16(expanded_to_perm))
+    return QMOE_EALIGN;
+  if (E > QMOE_MAX_EXPERTS || k > QMOE_MAX_TOPK) return QMOE_EUNSUPPORTED;
+  if ((int64_t)T * k > (1 << 24)) return QMOE_EUNSUPPORTED;
+  return check_launch(launch_route(logits, router_weights, T, E, k, topk_idx, topk_w, expert_offsets,
+                                   perm_to_expanded, expanded_to_perm, stream));
 }
 
 qmoe_status qmoe_fp4_gemv_fc1_swiglu(const uint16_t *x, int32_t T, int32_t k, const qmoe_fp4_weights *w1,
@@ -139,6 +166,9 @@ qmoe_status qmoe_fp4_gemv_fc1_swiglu(const uint16_t *x, int32_t T, int32_t k, co
   a.alpha = act ? act->alpha : 1.0f;
   a.beta = act ? act->beta : 0.0f;
   a.limit = act ? act->limit : INFINITY;
+  const int32_t fusion = act ? act->fusion : QMOE_SWIGLU_INTERLEAVED;
+  if (fusion != 0 && fusion != QMOE_SWIGLU_INTERLEAVED && fusion != QMOE_SWIGLU_CONCAT) return QMOE_EINVAL;
+  a.concat = fusion == QMOE_SWIGLU_CONCAT;
   a.out_bf16 = h;
   return run_fc(a, w1, sh.max_rows_per_expert, p, ws, ws_bytes, stream);
 }

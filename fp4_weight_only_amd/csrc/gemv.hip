@@ -339,7 +339,7 @@ __global__ __launch_bounds__(max_waves<MRMAX>() * 64) void fp4_gemv_kernel(GemvA
         for (int q = 1; q < W; ++q) s += sm.red[q][r][cl];
         const int p = row0 + rbase + r;
         const float u = gs * s;
-        if (a.nchunks > 1 || a.force_partials) {
+        if (a.nchunks > 1 || a.force_partials || a.concat) {
           if (col < a.N) a.partials[((size_t)kc * a.rows + p) * a.N + col] = u;
         } else if (a.fc1) {
           store_fc1(a, p, col, u);
@@ -359,36 +359,55 @@ __global__ __launch_bounds__(max_waves<MRMAX>() * 64) void fp4_gemv_kernel(GemvA
 
 // Split-K epilogue: sums the k-chunk partials of every (row, column) in chunk
 // order, then SwiGLU -> bf16 h (FC1) or float32 y (FC2).  One thread owns 4
-// columns (two gate/up pairs for FC1), one wave 256 columns of one row.
-// Chunks are read kEpiGroup at a time with every load unconditional (indices
-// past the last chunk re-read it and contribute -0, which leaves any float
-// sum unchanged), so a row's partials are in flight together rather than one
-// memory round trip per chunk.
+// output columns (FC1 interleaved: two gate/linear pairs; FC1 concatenated:
+// four h columns, their gates at j and linear values at N/2 + j), one wave
+// 256 of one row; rows in grid x.  Chunks are read kEpiGroup at a time with
+// every load unconditional (indices past the last chunk re-read it and
+// contribute -0, which leaves any float sum unchanged), so a row's partials
+// are in flight together rather than one memory round trip per chunk.
 constexpr int kEpiGroup = 8;
 
-__global__ __launch_bounds__(64) void splitk_epilogue_kernel(GemvArgs a) {
-  const int p = blockIdx.y;
-  const int col = (blockIdx.x * 64 + threadIdx.x) * 4;
-  if (col >= a.N) return;
-  const size_t plane = (size_t)a.rows * a.N;
-  const float *src = a.partials + (size_t)p * a.N + col;
+__device__ __forceinline__ float4 sum_chunks(const float *src, size_t plane, int nchunks) {
   float4 s = make_float4(-0.f, -0.f, -0.f, -0.f);
-  for (int c = 0; c < a.nchunks; c += kEpiGroup) {
+  for (int c = 0; c < nchunks; c += kEpiGroup) {
     float4 v[kEpiGroup];
 #pragma unroll
     for (int g = 0; g < kEpiGroup; ++g) {
-      const int q = c + g < a.nchunks ? c + g : a.nchunks - 1;
+      const int q = c + g < nchunks ? c + g : nchunks - 1;
       v[g] = *(const float4 *)(src + (size_t)q * plane);
     }
 #pragma unroll
     for (int g = 0; g < kEpiGroup; ++g) {
-      const bool live = c + g < a.nchunks;
+      const bool live = c + g < nchunks;
       s.x += live ? v[g].x : -0.f;
       s.y += live ? v[g].y : -0.f;
       s.z += live ? v[g].z : -0.f;
       s.w += live ? v[g].w : -0.f;
     }
   }
+  return s;
+}
+
+__global__ __launch_bounds__(64) void splitk_epilogue_kernel(GemvArgs a) {
+  const int p = blockIdx.x;
+  const int col = (blockIdx.y * 64 + threadIdx.x) * 4;
+  const size_t plane = (size_t)a.rows * a.N;
+  const float *row = a.partials + (size_t)p * a.N;
+  if (a.concat) {
+    const int I = a.N >> 1;
+    if (col >= I) return;
+    const float4 gt = sum_chunks(row + col, plane, a.nchunks);
+    const float4 ln = sum_chunks(row + I + col, plane, a.nchunks);
+    uint2 o;
+    o.x = bf16_rne(swiglu(gt.x, ln.x, a.alpha, a.beta, a.limit)) |
+          (bf16_rne(swiglu(gt.y, ln.y, a.alpha, a.beta, a.limit)) << 16);
+    o.y = bf16_rne(swiglu(gt.z, ln.z, a.alpha, a.beta, a.limit)) |
+          (bf16_rne(swiglu(gt.w, ln.w, a.alpha, a.beta, a.limit)) << 16);
+    *(uint2 *)(a.out_bf16 + (size_t)p * I + col) = o;
+    return;
+  }
+  if (col >= a.N) return;
+  const float4 s = sum_chunks(row + col, plane, a.nchunks);
   if (a.fc1) {
     const uint32_t h0 = bf16_rne(swiglu(s.x, s.y, a.alpha, a.beta, a.limit));
     const uint32_t h1 = bf16_rne(swiglu(s.z, s.w, a.alpha, a.beta, a.limit));
@@ -396,6 +415,13 @@ __global__ __launch_bounds__(64) void splitk_epilogue_kernel(GemvArgs a) {
   } else {
     *(float4 *)(a.out_f32 + (size_t)p * a.N + col) = s;
   }
+}
+
+hipError_t launch_splitk_epilogue(const GemvArgs &a, hipStream_t s) {
+  const int cols = a.concat ? (a.N >> 1) : a.N;
+  const dim3 g2((unsigned)a.rows, (unsigned)((cols / 4 + 63) / 64));
+  splitk_epilogue_kernel<<<g2, 64, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 // Four waves (a 256-row k chunk) per workgroup: the kernel is bound by VALU
@@ -455,10 +481,8 @@ hipError_t launch_fp4_gemv(const GemvArgs &a, int fmt, int max_rows_per_expert, 
       fp4_gemv_kernel<1, 4><<<grid, block, 0, s>>>(a);
   }
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || a.nchunks == 1 || a.force_partials) return err;
-  const dim3 g2((unsigned)((a.N + 255) / 256), (unsigned)a.rows);
-  splitk_epilogue_kernel<<<g2, 64, 0, s>>>(a);
-  return hipGetLastError();
+  if (err != hipSuccess || a.force_partials || (a.nchunks == 1 && !a.concat)) return err;
+  return launch_splitk_epilogue(a, s);
 }
 
 }  // namespace qmoe

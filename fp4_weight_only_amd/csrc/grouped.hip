@@ -323,7 +323,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
       for (int i = 0; i < 4; ++i) {
         const int r = ms * 16 + lk * 4 + i;
         const float u = gs * acc[ms][t][i];
-        if (a.fc1) {
+        if (a.fc1 && !a.concat) {
           const float partner = __uint_as_float(dpp_u32<kDppXor1>(__float_as_uint(u)));
           if (r < mrows && (lane & 1) == 0)
             a.out_bf16[(size_t)(row0 + r) * (a.N >> 1) + (col >> 1)] =
@@ -336,7 +336,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   }
 }
 
-size_t grouped_workspace_bytes() { return 256; }
+// The concatenated SwiGLU layout pairs columns from different tiles: FC1
+// then writes g * u as float32 rows to the workspace and the split-K
+// epilogue (one chunk) forms h.
+size_t grouped_workspace_bytes(int32_t rows, int32_t N, bool concat) {
+  const size_t u = concat ? (size_t)rows * N * sizeof(float) : 0;
+  return u > 256 ? u : 256;
+}
 
 hipError_t launch_grouped(GemvArgs &a, int fmt, hipStream_t s) {
   const int erows = a.rows < a.E ? a.rows : a.E;

@@ -25,6 +25,7 @@ struct GemvArgs {
   int32_t waves;           // waves per block; the k chunk is waves * 64 rows
   int32_t fc1;             // 1: act rows gathered by token, SwiGLU epilogue, bf16 out
   int32_t force_partials;  // GEMV: write g * partial sums even for one k chunk, run no epilogue
+  int32_t concat;          // FC1: gate = column j, linear = column N/2 + j (else 2j, 2j+1)
   float alpha, beta, limit;
   uint16_t *out_bf16;      // FC1: h [rows][N/2]
   float *out_f32;          // FC2: y [rows][N]
@@ -36,10 +37,14 @@ size_t gemv_workspace_bytes(int32_t rows, int32_t max_rows_per_expert, int32_t E
 void gemv_plan(GemvArgs &a, int max_rows_per_expert, void *ws);
 hipError_t launch_fp4_gemv(const GemvArgs &a, int fmt, int max_rows_per_expert, hipStream_t s);
 
-size_t grouped_workspace_bytes();
+// Sums a.nchunks planes of a.partials per (row, column) and writes SwiGLU ->
+// bf16 h (a.fc1) or float32 y.
+hipError_t launch_splitk_epilogue(const GemvArgs &a, hipStream_t s);
+
+size_t grouped_workspace_bytes(int32_t rows, int32_t N, bool concat);
 hipError_t launch_grouped(GemvArgs &a, int fmt, hipStream_t s);
 
-hipError_t launch_route(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *idx, float *w,
+hipError_t launch_route(const float *logits, const float *rw, int32_t T, int32_t E, int32_t k, int32_t *idx, float *w,
                         int32_t *offsets, int32_t *p2e, int32_t *e2p, hipStream_t s);
 
 hipError_t launch_finalize(const float *y, int nsplit, size_t plane, const float *w, const int32_t *e2p, int32_t T,

@@ -49,15 +49,17 @@ constexpr uint32_t kNoExpert = 0xFFFFu;  // padding / consumed slot: loses every
 
 // Top-k of one token by one wave; E <= 256 (expert lane + 64 i in key i of
 // a lane), 1 <= k <= 8, k <= E.  Lanes j < k return the j-th selected expert
-// and its softmax weight.
+// and its weight: the softmax over the selected logits, or, given the
+// token's router_weights row rw (DeepSeek-style routing, operator
+// documentation section 2, input 14), rw at the selected expert as it is.
 //
 // Each lane first sorts its four keys (value descending, lower expert first
 // on equal values), so a round only compares the lanes' heads: the wave
 // maximum of the heads, the one lane holding it (a wave minimum of the
 // expert index breaks the rare tie between lanes), and that lane drops its
 // head.
-__device__ __forceinline__ void topk_token(const float *__restrict__ row, int E, int k, int lane, int &sel,
-                                           float &wsel) {
+__device__ __forceinline__ void topk_token(const float *__restrict__ row, const float *__restrict__ rw, int E, int k,
+                                           int lane, int &sel, float &wsel) {
   uint32_t kv[4], ex[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -109,6 +111,11 @@ __device__ __forceinline__ void topk_token(const float *__restrict__ row, int E,
       }
     }
   }
+  sel = mine;
+  if (rw) {  // uniform
+    wsel = (lane < k) ? rw[mine] : 0.f;
+    return;
+  }
   // softmax over the selected logits, largest first: lane j < k owns exp of
   // the j-th; the sum is taken in selection order
   const float lmax = ord_value(top0);
@@ -116,12 +123,12 @@ __device__ __forceinline__ void topk_token(const float *__restrict__ row, int E,
   float sum = 0.f;
 #pragma unroll
   for (int r = 0; r < 8; ++r) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine_ex), r));
-  sel = mine;
   wsel = mine_ex / sum;
 }
 
 // One wave per token.
-__global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict__ logits, int T, int E, int k,
+__global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict__ logits,
+                                                         const float *__restrict__ rw, int T, int E, int k,
                                                          int32_t *__restrict__ idx, float *__restrict__ wts) {
   const int wave = threadIdx.x >> 6;
   const int lane = lane_id();
@@ -129,7 +136,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict
   if (t >= T) return;  // wave-uniform
   int sel;
   float wsel;
-  topk_token(logits + (size_t)t * E, E, k, lane, sel, wsel);
+  topk_token(logits + (size_t)t * E, rw ? rw + (size_t)t * E : nullptr, E, k, lane, sel, wsel);
   if (lane < k) {
     idx[(size_t)t * k + lane] = sel;
     wts[(size_t)t * k + lane] = wsel;
@@ -288,7 +295,8 @@ __global__ __launch_bounds__(NW * 64) void expert_maps_kernel(const int32_t *__r
 // Decode-sized batches (T <= NW): top-k and maps in one workgroup, the
 // selections handed over through LDS.
 template <int NW>
-__global__ __launch_bounds__(NW * 64) void route_fused_kernel(const float *__restrict__ logits, int T, int E, int k,
+__global__ __launch_bounds__(NW * 64) void route_fused_kernel(const float *__restrict__ logits,
+                                                              const float *__restrict__ rw, int T, int E, int k,
                                                               int32_t *__restrict__ idx, float *__restrict__ wts,
                                                               int32_t *__restrict__ offsets,
                                                               int32_t *__restrict__ p2e,
@@ -300,7 +308,7 @@ __global__ __launch_bounds__(NW * 64) void route_fused_kernel(const float *__res
   if (wave < T) {  // wave-uniform
     int sel;
     float wsel;
-    topk_token(logits + (size_t)wave * E, E, k, lane, sel, wsel);
+    topk_token(logits + (size_t)wave * E, rw ? rw + (size_t)wave * E : nullptr, E, k, lane, sel, wsel);
     if (lane < k) {
       idx[(size_t)wave * k + lane] = sel;
       wts[(size_t)wave * k + lane] = wsel;
@@ -315,19 +323,19 @@ __global__ __launch_bounds__(NW * 64) void route_fused_kernel(const float *__res
   }
 }
 
-hipError_t launch_route(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *idx, float *w,
+hipError_t launch_route(const float *logits, const float *rw, int32_t T, int32_t E, int32_t k, int32_t *idx, float *w,
                         int32_t *offsets, int32_t *p2e, int32_t *e2p, hipStream_t s) {
   if (T <= 16) {  // one launch: top-k and maps in one workgroup
     if (T <= 4)
-      route_fused_kernel<4><<<1, 256, 0, s>>>(logits, T, E, k, idx, w, offsets, p2e, e2p);
+      route_fused_kernel<4><<<1, 256, 0, s>>>(logits, rw, T, E, k, idx, w, offsets, p2e, e2p);
     else if (T <= 8)
-      route_fused_kernel<8><<<1, 512, 0, s>>>(logits, T, E, k, idx, w, offsets, p2e, e2p);
+      route_fused_kernel<8><<<1, 512, 0, s>>>(logits, rw, T, E, k, idx, w, offsets, p2e, e2p);
     else
-      route_fused_kernel<16><<<1, 1024, 0, s>>>(logits, T, E, k, idx, w, offsets, p2e, e2p);
+      route_fused_kernel<16><<<1, 1024, 0, s>>>(logits, rw, T, E, k, idx, w, offsets, p2e, e2p);
     return hipGetLastError();
   }
   const dim3 grid((T + 3) / 4);
-  route_topk_kernel<<<grid, 256, 0, s>>>(logits, T, E, k, idx, w);
+  route_topk_kernel<<<grid, 256, 0, s>>>(logits, rw, T, E, k, idx, w);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int R = T * k;

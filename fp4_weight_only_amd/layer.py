@@ -9,7 +9,8 @@ from __future__ import annotations
 import torch
 
 from . import (QMOE_PATH_AUTO, FP4Weights, alloc_workspace, fc_workspace_bytes, qmoe_finalize,
-               qmoe_fp4_gemv_fc1_swiglu, qmoe_fp4_gemv_fc2, qmoe_fp4_gemv_fc2_finalize, qmoe_route_topk)
+               qmoe_fp4_gemv_fc1_swiglu, qmoe_fp4_gemv_fc2, qmoe_fp4_gemv_fc2_finalize, qmoe_route_topk,
+               qmoe_route_topk_router_weights)
 
 
 class MoELayer:
@@ -27,15 +28,19 @@ class MoELayer:
         self.h = torch.empty((R, I), dtype=torch.bfloat16, device=dev)
         self.y = torch.empty((R, H), dtype=torch.float32, device=dev)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-        need = max(fc_workspace_bytes(1, T, k, w1, path), fc_workspace_bytes(2, T, k, w2, path),
+        need = max(fc_workspace_bytes(1, T, k, w1, path, act), fc_workspace_bytes(2, T, k, w2, path),
                    fc_workspace_bytes(3, T, k, w2, path))
         self.ws = alloc_workspace(need, dev)
 
     def set_weights(self, w1: FP4Weights, w2: FP4Weights):
         self.w1, self.w2 = w1, w2
 
-    def route(self, logits):
-        qmoe_route_topk(logits, self.k, self.topk_idx, self.topk_w, self.offsets, self.p2e, self.e2p)
+    def route(self, logits, router_weights=None):
+        if router_weights is None:
+            qmoe_route_topk(logits, self.k, self.topk_idx, self.topk_w, self.offsets, self.p2e, self.e2p)
+        else:
+            qmoe_route_topk_router_weights(logits, router_weights, self.k, self.topk_idx, self.topk_w, self.offsets,
+                                           self.p2e, self.e2p)
 
     def fc1(self, x):
         qmoe_fp4_gemv_fc1_swiglu(x, self.k, self.w1, self.offsets, self.p2e, self.h, self.ws, self.act, self.path)
@@ -50,10 +55,11 @@ class MoELayer:
         qmoe_fp4_gemv_fc2_finalize(self.h, self.k, self.w2, self.offsets, self.topk_w, self.e2p, self.out, self.ws,
                                    self.path)
 
-    def run(self, logits, x, fused: bool = False):
+    def run(self, logits, x, fused: bool = False, router_weights=None):
         """route -> FC1+SwiGLU -> FC2 -> finalize; fused=True runs FC2 and the
-        finalize as one call (y is then not written)."""
-        self.route(logits)
+        finalize as one call (y is then not written); router_weights [T][E]
+        selects DeepSeek-style mixing weights."""
+        self.route(logits, router_weights)
         self.fc1(x)
         if fused:
             self.fc2_finalize()

@@ -7,6 +7,8 @@
  * bf16 activations (W4A16).  Five calls cover it:
  *
  *   qmoe_route_topk           softmax top-k routing + expert maps
+ *                             (qmoe_route_topk_router_weights: DeepSeek-style
+ *                             mixing weights from a second tensor)
  *   qmoe_fp4_gemv_fc1_swiglu  FC1 over the routed rows, fused SwiGLU
  *   qmoe_fp4_gemv_fc2         FC2 over the routed rows
  *   qmoe_finalize             weighted un-permute
@@ -45,7 +47,8 @@
  *   gscale [E] float32 per-expert global scale; required for NVFP4, optional
  *          for MXFP4 (NULL means 1.0).
  *   weight(e,k,n) = e2m1(code) * scale(e, k/B, n) * gscale(e).
- * FC1: K = hidden H, N = 2*I, columns interleaved (2j = gate, 2j+1 = linear).
+ * FC1: K = hidden H, N = 2*I, columns interleaved (2j = gate, 2j+1 = linear),
+ *      or concatenated (j = gate, I + j = linear) with qmoe_swiglu.fusion = 2.
  * FC2: K = I, N = H.
  */
 #ifndef QMOE_H
@@ -88,8 +91,15 @@ typedef struct {
   int32_t fmt;            /* qmoe_fmt */
 } qmoe_fp4_weights;
 
+/* FC1 column layout of the SwiGLU pair (the swiglu_fusion attribute,
+ * operator documentation section 8).  0 is read as interleaved, as the
+ * section says the QMoE operator treats swiglu_fusion = 0. */
+#define QMOE_SWIGLU_INTERLEAVED 1  /* gate = column 2j, linear = column 2j+1 */
+#define QMOE_SWIGLU_CONCAT 2       /* gate = column j, linear = column I + j */
+
 typedef struct {
   float alpha, beta, limit;  /* SwiGLU(G, L) = G*sigmoid(alpha*G)*(L+beta), G = min(gate, limit), L = clamp(lin, -limit, limit) */
+  int32_t fusion;            /* 0 or QMOE_SWIGLU_INTERLEAVED, or QMOE_SWIGLU_CONCAT; other values: QMOE_EINVAL */
 } qmoe_swiglu;
 
 #define QMOE_MAX_EXPERTS 256
@@ -123,6 +133,24 @@ qmoe_status qmoe_route_topk(const float *logits, int32_t T, int32_t E, int32_t k
                             hipStream_t stream);
 
 /*
+ * qmoe_route_topk_router_weights -- top-k routing with separate mixing weights.
+ *
+ * Passage: operator documentation section 2, input 14 (router_weights,
+ * DeepSeek-style routing: router_probs only selects the experts, the mixing
+ * weights are router_weights gathered at the selected indices).
+ *
+ * As qmoe_route_topk, with router_weights [T][E] float32 in; the selection
+ * is made on logits alone, and topk_w[t][j] = router_weights[t][topk_idx[t][j]]
+ * exactly (no softmax, no renormalisation).  router_weights NULL: QMOE_EINVAL
+ * (call qmoe_route_topk for softmax weights).  Same limits.
+ */
+qmoe_status qmoe_route_topk_router_weights(const float *logits, const float *router_weights,
+                                           int32_t T, int32_t E, int32_t k,
+                                           int32_t *topk_idx, float *topk_w, int32_t *expert_offsets,
+                                           int32_t *perm_to_expanded, int32_t *expanded_to_perm,
+                                           hipStream_t stream);
+
+/*
  * qmoe_fp4_gemv_fc1_swiglu -- FC1 of every routed row with fused SwiGLU.
  *
  * Passages: PR 31159 "[CUDA] Speed up the NVFP4 QMoE decode GEMV and enable it
@@ -134,15 +162,18 @@ qmoe_status qmoe_route_topk(const float *logits, int32_t T, int32_t E, int32_t k
  * x          [T][K] bf16 activations (K = H).
  * w1         FC1 weights, N = 2*I.
  * expert_offsets, perm_to_expanded  as written by qmoe_route_topk (same T, k).
- * act        SwiGLU parameters, or NULL for the standard SiLU(gate)*linear.
+ * act        SwiGLU parameters and column layout, or NULL for the standard
+ *            SiLU(gate)*linear on interleaved columns.
  * h          [T*k][I] bf16 out, in permuted row order:
- *            h[p][j] = bf16_rne(SwiGLU(u[p][2j], u[p][2j+1])),
+ *            h[p][j] = bf16_rne(SwiGLU(u[p][2j], u[p][2j+1])) (interleaved) or
+ *            bf16_rne(SwiGLU(u[p][j], u[p][I+j])) (concatenated),
  *            u[p][n] = sum_k x[t(p)][k] * weight(e(p), k, n), accumulated in float32.
  * ws, ws_bytes  workspace.  With ws == NULL the call writes the size it
  *            needs to *ws_bytes and returns QMOE_OK without launching.
  *            Otherwise *ws_bytes is the size of ws (QMOE_EWORKSPACE if too
- *            small).  The workspace is scratch (split-K partial sums); its
- *            contents on entry do not matter.  Calls that share a workspace
+ *            small).  The workspace is scratch (split-K partial sums, or
+ *            the concatenated layout's float32 u rows); its contents on
+ *            entry do not matter.  Calls that share a workspace
  *            must be ordered (same stream).
  * path       AUTO, GEMV (T*k <= 64) or GROUPED.
  * Limits: K % B == 0, N % 32 == 0, E <= 256, k <= 8 (QMOE_EUNSUPPORTED).

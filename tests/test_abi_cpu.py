@@ -132,6 +132,41 @@ def test_fc2_finalize_validation_and_workspace(q):
     assert call(T=9) == q.QMOE_OK and n.value >= 72 * 2048 * 4          # grouped: float32 rows in the workspace
 
 
+def test_route_router_weights_validation(q):
+    L = q.lib
+    call = lambda lg=A, rw=A, T=1, E=8, k=2, idx=A: L.qmoe_route_topk_router_weights(
+        lg, rw, T, E, k, idx, A, A, A, A, None)
+    assert call(rw=None) == q.QMOE_EINVAL
+    assert call(lg=None) == q.QMOE_EINVAL
+    assert call(k=9) == q.QMOE_EINVAL
+    assert call(rw=MIS) == q.QMOE_EALIGN
+    assert call(E=257) == q.QMOE_EUNSUPPORTED
+
+
+def fc1_act(q, wc, act, T=1, k=2, path=0):
+    n = ctypes.c_size_t(0)
+    st = q.lib.qmoe_fp4_gemv_fc1_swiglu(A, T, k, ctypes.byref(wc), A, A, ctypes.byref(act), A, None,
+                                        ctypes.byref(n), path, None)
+    return st, n.value
+
+
+def test_swiglu_fusion_modes_and_workspace(q):
+    wc = weights(q, E=16, K=256, N=512)          # K = 256: one k chunk on the GEMV
+    std = lambda f: q.SwigluC(1.0, 0.0, float("inf"), f)
+    st0, n0 = fc1_act(q, wc, std(0))
+    st1, n1 = fc1_act(q, wc, std(q.QMOE_SWIGLU_INTERLEAVED))
+    st2, n2 = fc1_act(q, wc, std(q.QMOE_SWIGLU_CONCAT))
+    assert st0 == st1 == st2 == q.QMOE_OK
+    assert n0 == n1                                  # fusion 0 is the interleaved layout
+    assert n2 >= 2 * 512 * 4                         # concatenated: float32 partials of 2 rows x 512
+    assert fc1_act(q, wc, std(3))[0] == q.QMOE_EINVAL
+    assert fc1_act(q, wc, std(-1))[0] == q.QMOE_EINVAL
+    st, ng = fc1_act(q, wc, std(q.QMOE_SWIGLU_CONCAT), T=32, k=4, path=q.QMOE_PATH_GROUPED)
+    assert st == q.QMOE_OK and ng >= 128 * 512 * 4   # grouped: float32 u rows
+    st, ng1 = fc1_act(q, wc, std(q.QMOE_SWIGLU_INTERLEAVED), T=32, k=4, path=q.QMOE_PATH_GROUPED)
+    assert st == q.QMOE_OK and ng1 < ng
+
+
 def test_finalize_and_dequant_validation(q):
     L = q.lib
     assert L.qmoe_finalize(None, A, A, 1, 2, 256, A, None) == q.QMOE_EINVAL

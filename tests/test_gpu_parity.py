@@ -39,10 +39,10 @@ SMALL = [
 FULL = [synth.TINY, synth.DECODE, synth.MTP4, synth.MTP8]
 
 
-def run_gpu_layer(L, act=None, path=None):
+def run_gpu_layer(L, act=None, path=None, rw=None):
     layer, logits, x = layer_dev(L, act=act, path=path)
-    print_case("layer", L.cfg.name)
-    layer.run(logits, x)
+    print_case("layer", L.cfg.name, "act", act, "router_weights", rw is not None)
+    layer.run(logits, x, router_weights=None if rw is None else to_dev(rw))
     torch.cuda.synchronize()
     return dict(idx=layer.topk_idx.cpu().numpy(), w=layer.topk_w.cpu().numpy().astype(np.float64),
                 offsets=layer.offsets.cpu().numpy(), p2e=layer.p2e.cpu().numpy(), e2p=layer.e2p.cpu().numpy(),
@@ -56,12 +56,18 @@ def assert_close(name, gpu, ref):
     assert ok, (name, rep)
 
 
-def check_layer(L, act=None, cols1=None, cols2=None, path=None):
+def check_layer(L, act=None, cols1=None, cols2=None, path=None, rw=None):
+    """act: (alpha, beta, limit[, fusion]); rw: router_weights [T][E] or None."""
     c = L.cfg
-    g = run_gpu_layer(L, act, path)
-    oact = None if act is None else dict(alpha=act[0], beta=act[1], limit=act[2])
+    g = run_gpu_layer(L, act, path, rw)
+    oact = None if act is None else dict(alpha=act[0], beta=act[1], limit=act[2],
+                                         fusion=act[3] if len(act) > 3 else 1)
     # routing and maps: bit-exact
-    idx, wts = route.route_topk(L.logits, c.k)
+    if rw is None:
+        idx, wts = route.route_topk(L.logits, c.k)
+    else:
+        idx, wts = route.route_topk_router_weights(L.logits, rw, c.k)
+        assert np.array_equal(g["w"], wts)     # a gather: exact
     off, p2e, e2p = route.expert_maps(idx, c.E)
     assert np.array_equal(g["idx"], idx)
     assert np.array_equal(g["offsets"], off)
@@ -105,6 +111,66 @@ def test_layer_mxfp4_decode_full_sampled():
     cols1 = np.sort(rng.choice(L.cfg.I, 160, replace=False))
     cols2 = np.sort(rng.choice(L.cfg.H, 320, replace=False))
     check_layer(L, cols1=cols1, cols2=cols2)
+
+
+# Variants: concatenated SwiGLU columns (swiglu_fusion=2), MXFP4 with
+# per-expert global scales, DeepSeek-style router weights; each on the GEMV
+# path and on the grouped path.
+VARIANT_GEMV = synth.shrink(synth.DECODE, E=37, T=7, k=5, H=320, I=144, seed=31)       # 35 rows, ragged
+VARIANT_GROUPED = synth.shrink(synth.MX_PREFILL, E=24, T=48, k=4, H=512, I=256, seed=32)
+STD, GPTOSS = (1.0, 0.0, float("inf")), (1.702, 1.0, 7.0)
+
+
+@pytest.mark.parametrize("cfg", [VARIANT_GEMV, synth.shrink(synth.MTP8, E=64, T=8, k=8, H=512, I=272, seed=33),
+                                 VARIANT_GROUPED], ids=lambda c: c.name)
+@pytest.mark.parametrize("act", [STD, GPTOSS], ids=["std", "gptoss"])
+def test_concat_swiglu_layer(cfg, act):
+    check_layer(synth.layer_inputs(cfg), act=act + (2,))
+
+
+def test_concat_swiglu_single_chunk_gemv():
+    # K = 256: one k chunk, so the concatenated layout alone forces the
+    # partial-sum path
+    cfg = synth.shrink(synth.TINY, E=8, T=3, k=2, H=256, I=96, seed=34)
+    check_layer(synth.layer_inputs(cfg), act=STD + (2,))
+
+
+@pytest.mark.parametrize("cfg", [synth.shrink(synth.MX_DECODE, E=40, T=8, k=8, H=544, I=160, seed=35),
+                                 VARIANT_GROUPED], ids=lambda c: c.name)
+def test_mxfp4_global_scale_layer(cfg):
+    import dataclasses
+    L = synth.layer_inputs(dataclasses.replace(cfg, mx_global=True, name=cfg.name + "_g"))
+    assert L.g1 is not None and L.g2 is not None
+    check_layer(L)
+
+
+@pytest.mark.parametrize("cfg", [VARIANT_GEMV, synth.MTP4, VARIANT_GROUPED], ids=lambda c: c.name)
+def test_router_weights_layer(cfg):
+    L = synth.layer_inputs(cfg)
+    check_layer(L, rw=synth.router_weights(cfg))
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 256, 8), (8, 256, 8), (40, 200, 6), (512, 256, 8)])
+def test_route_router_weights(T, E, k):
+    import fp4_weight_only_amd as q
+    rng = np.random.default_rng(T + E + k)
+    lg = rng.integers(0, 6, (T, E)).astype(np.float32)          # ties too
+    rw = rng.random((T, E)).astype(np.float32)
+    d = dict(idx=torch.empty((T, k), dtype=torch.int32, device="cuda"),
+             w=torch.empty((T, k), dtype=torch.float32, device="cuda"),
+             off=torch.empty((E + 1,), dtype=torch.int32, device="cuda"),
+             p2e=torch.empty((T * k,), dtype=torch.int32, device="cuda"),
+             e2p=torch.empty((T * k,), dtype=torch.int32, device="cuda"))
+    print_case("route router_weights", T, E, k)
+    q.qmoe_route_topk_router_weights(to_dev(lg), to_dev(rw), k, d["idx"], d["w"], d["off"], d["p2e"], d["e2p"])
+    torch.cuda.synchronize()
+    idx, w = route.route_topk_router_weights(lg, rw, k)
+    assert np.array_equal(d["idx"].cpu().numpy(), idx)
+    assert np.array_equal(d["w"].cpu().numpy().astype(np.float64), w)
+    off, p2e, e2p = route.expert_maps(idx, E)
+    assert np.array_equal(d["off"].cpu().numpy(), off)
+    assert np.array_equal(d["p2e"].cpu().numpy(), p2e)
+    assert np.array_equal(d["e2p"].cpu().numpy(), e2p)
 
 
 def test_gptoss_swiglu_variant():

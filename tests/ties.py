@@ -49,7 +49,10 @@ def h_error_bound(L, u_ref, oact, off, p2e):
     A = fc1_abs_sum(L, off, p2e)
     n = c.H + 16
     gam = 2 * n * U32 / (1 - 2 * n * U32)
-    gate, lin = u_ref[:, 0::2], u_ref[:, 1::2]
+    I = u_ref.shape[1] // 2
+    concat = act.get("fusion", 1) == 2   # gate = column j, linear = column I + j
+    gsel, lsel = (slice(0, I), slice(I, None)) if concat else (slice(0, None, 2), slice(1, None, 2))
+    gate, lin = u_ref[:, gsel], u_ref[:, lsel]
     G = np.minimum(gate, lim)
     Lc = np.clip(lin, -lim, lim)
     with np.errstate(over="ignore"):
@@ -57,7 +60,7 @@ def h_error_bound(L, u_ref, oact, off, p2e):
     d_gate = np.where(gate < lim, (sg + al * G * sg * (1 - sg)) * (Lc + be), 0.0)
     d_lin = np.where(np.abs(lin) < lim, G * sg, 0.0)
     hf = moe.swiglu(gate, lin, al, be, lim)
-    dh = 2 * (np.abs(d_gate) * gam * A[:, 0::2] + np.abs(d_lin) * gam * A[:, 1::2]) + 16 * U32 * np.abs(hf)
+    dh = 2 * (np.abs(d_gate) * gam * A[:, gsel] + np.abs(d_lin) * gam * A[:, lsel]) + 16 * U32 * np.abs(hf)
     floor = (np.abs(G * (Lc + be)) + 1.0) * 2.0 ** -126
     return hf, dh, floor
 
