@@ -1,4 +1,4 @@
-"""FP4 weight dequantization (float64).  Test infrastructure only.
+"""FP4 and FP8 weight dequantization (float64).  Test infrastructure only.
 
 Definition (operator documentation section 6.5 and section 13, "Reference
 computation"): a weight is its E2M1 value times its block scale times the
@@ -10,6 +10,12 @@ with B = 16 and E4M3FN scales for NVFP4 (section 9b), B = 32 and E8M0 scales
 for MXFP4; MXFP4 without a global scale uses g = 1 (reading: the MXFP4
 workloads give no global scale).  The packed layout is [E][K][N/2] and the
 scale layout [E][K/B][N].
+
+FP8 W8A16 (operator documentation sections 6.4 and 10): raw E4M3FN bytes
+laid out [E][N][K] (each output column's K weights contiguous), no block
+scales, one float32 global scale per expert applied to the product:
+
+    W[e, k, n] = e4m3(byte[e, n, k]) * g[e]
 
 The bf16 output of the standalone dequant ("[CUDA] Coalesce QMoE MXFP4/NVFP4
 weight dequantization") is laid out [E][N][K].  Reading of its rounding: the
@@ -52,3 +58,34 @@ def dequant_bf16(w, s, g, fmt: str) -> np.ndarray:
         f32 = codecs.f32_round(exact)
         out.append(codecs.bf16_from_f32_bits(f32).T)
     return np.ascontiguousarray(np.stack(out))
+
+
+def dequant_fp8_expert_f64(w_e, g_e, cols=None) -> np.ndarray:
+    """One FP8 expert: bytes [N][K] -> float64 [K][N] (or [K][len(cols)])."""
+    w_e = np.asarray(w_e)
+    if cols is not None:
+        w_e = w_e[np.asarray(cols)]
+    return codecs.e4m3fn_value(w_e).T * float(np.float32(g_e))
+
+
+def dequant_fp8_bf16(w, g) -> np.ndarray:
+    """All FP8 experts -> bfloat16 bits [E][N][K]: the product e4m3 * g (at
+    most 28 significant bits, exact in float64) rounds once to float32 and
+    once to bfloat16, as the FP4 dequant's rounding reading."""
+    out = []
+    for e in range(w.shape[0]):
+        exact = codecs.e4m3fn_value(w[e]) * float(np.float32(g[e]))
+        out.append(codecs.bf16_from_f32_bits(codecs.f32_round(exact)))
+    return np.ascontiguousarray(np.stack(out))
+
+
+def expert_weights_f64(w_e, s_e, g_e, fmt: str, cols=None) -> np.ndarray:
+    """float64 [K][N] weights of one expert in any of the three codecs."""
+    if fmt == "fp8":
+        return dequant_fp8_expert_f64(w_e, g_e, cols)
+    return dequant_expert_f64(w_e, s_e, g_e, fmt, cols)
+
+
+def fc_n(w, fmt: str) -> int:
+    """Output count N of an FC layer's weight tensor."""
+    return w.shape[1] if fmt == "fp8" else 2 * w.shape[2]

@@ -34,7 +34,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import codecs
-from .dequant import dequant_expert_f64
+from .dequant import expert_weights_f64, fc_n
 from .route import expert_maps, route_topk, route_topk_router_weights
 
 
@@ -50,7 +50,8 @@ def _rows_of(offsets, e):
 
 
 def fc1_swiglu(x_bits, k: int, w1, s1, g1, fmt: str, offsets, p2e, act=None, cols=None):
-    """x bf16 bits [T][H]; w1 [E][H][I]; s1 [E][H/B][2I] -> (h bf16 bits [R][I], u float64 [R][2I]).
+    """x bf16 bits [T][H]; w1 [E][H][I] packed FP4 with s1 [E][H/B][2I], or FP8 w1 [E][2I][H]
+    with s1 None -> (h bf16 bits [R][I], u float64 [R][2I]).
 
     act: {"alpha", "beta", "limit", "fusion"} (fusion 2 = concatenated
     gate | linear halves, otherwise interleaved).
@@ -61,7 +62,7 @@ def fc1_swiglu(x_bits, k: int, w1, s1, g1, fmt: str, offsets, p2e, act=None, col
     concat = act.get("fusion", 1) == 2
     x64 = codecs.bf16_to_f64(x_bits)
     E = w1.shape[0]
-    N = w1.shape[2] * 2
+    N = fc_n(w1, fmt)
     I = N // 2
     R = int(offsets[E])
     u = np.zeros((R, N), dtype=np.float64)
@@ -75,7 +76,7 @@ def fc1_swiglu(x_bits, k: int, w1, s1, g1, fmt: str, offsets, p2e, act=None, col
         lo, hi = _rows_of(offsets, e)
         if lo == hi:
             continue
-        wd = dequant_expert_f64(w1[e], s1[e], None if g1 is None else g1[e], fmt, fcols)
+        wd = expert_weights_f64(w1[e], None if s1 is None else s1[e], None if g1 is None else g1[e], fmt, fcols)
         toks = [int(p2e[p]) // k for p in range(lo, hi)]
         ue = x64[toks] @ wd
         if fcols is None:
@@ -93,17 +94,18 @@ def fc1_swiglu(x_bits, k: int, w1, s1, g1, fmt: str, offsets, p2e, act=None, col
 
 
 def fc2(h_bits, w2, s2, g2, fmt: str, offsets, cols=None) -> np.ndarray:
-    """h bf16 bits [R][I]; w2 [E][I][H/2] -> y float64 [R][H] (or [R][len(cols)])."""
+    """h bf16 bits [R][I]; w2 [E][I][H/2] packed FP4 (or FP8 [E][H][I]) -> y float64 [R][H]
+    (or [R][len(cols)])."""
     h64 = codecs.bf16_to_f64(h_bits)
     E = w2.shape[0]
-    N = w2.shape[2] * 2 if cols is None else len(cols)
+    N = fc_n(w2, fmt) if cols is None else len(cols)
     R = int(offsets[E])
     y = np.zeros((R, N), dtype=np.float64)
     for e in range(E):
         lo, hi = _rows_of(offsets, e)
         if lo == hi:
             continue
-        wd = dequant_expert_f64(w2[e], s2[e], None if g2 is None else g2[e], fmt, cols)
+        wd = expert_weights_f64(w2[e], None if s2 is None else s2[e], None if g2 is None else g2[e], fmt, cols)
         y[lo:hi] = h64[lo:hi] @ wd
     return y
 

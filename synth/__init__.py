@@ -13,6 +13,9 @@ Layouts (one MoE layer):
   w2      uint8 [E][I][H/2]     FC2 packed E2M1, K=I, N=H
   s2      uint8 [E][I/B][H]
   g2      float32 [E] or None
+FP8 (W8A16) layers instead hold w1 uint8 [E][2I][H] and w2 uint8 [E][H][I]
+(E4M3FN bytes, each output column's K weights contiguous), s1 = s2 = None,
+and global scales g1, g2.
 
 Random streams: one numpy PCG64 generator per (seed, tensor id), so every
 tensor is reproducible on its own.  Tensor ids: 0 logits, 1 x, 2 w1, 3 s1,
@@ -27,7 +30,8 @@ import torch
 
 NVFP4 = "nvfp4"
 MXFP4 = "mxfp4"
-BLOCK = {NVFP4: 16, MXFP4: 32}
+FP8 = "fp8"          # W8A16: E4M3FN weight bytes [E][N][K], per-expert global scale, no block scales
+BLOCK = {NVFP4: 16, MXFP4: 32, FP8: 1}
 
 # E4M3 scale bytes whose magnitude lies in [2^-4, 2^2]: exponent field 3..8
 # with any mantissa field, plus exponent field 9 with mantissa field 0, both
@@ -70,6 +74,16 @@ def e4m3_scales(g: np.random.Generator, shape, positive_only: bool = False) -> n
 
 def e8m0_scales(g: np.random.Generator, shape) -> np.ndarray:
     return g.integers(_E8M0_LO, _E8M0_HI + 1, size=shape, dtype=np.uint8)
+
+
+# E4M3FN weight bytes with magnitude in [2^-3, 2^3): exponent field 4..9, any
+# mantissa, both signs (never the NaN bytes).  Chosen by bit fields only.
+_FP8_WEIGHT_BYTES = np.array([(s << 7) | (e << 3) | m for s in (0, 1) for e in range(4, 10) for m in range(8)],
+                             dtype=np.uint8)
+
+
+def fp8_weight_bytes(g: np.random.Generator, shape) -> np.ndarray:
+    return _FP8_WEIGHT_BYTES[g.integers(0, len(_FP8_WEIGHT_BYTES), size=shape)]
 
 
 def global_scales(g: np.random.Generator, n: int) -> np.ndarray:
@@ -123,7 +137,10 @@ MTP8 = LayerConfig("mtp_nvfp4_T8_E256_top8_H2048_I768_hot3", NVFP4, T=8, E=256, 
 MX_DECODE = LayerConfig("decode_mxfp4_T8_E256_top8_H4096_I2048", MXFP4, T=8, E=256, k=8, H=4096, I=2048)
 MX_PREFILL = LayerConfig("prefill_mxfp4_T512_E256_top8_H4096_I2048_zipf", MXFP4, T=512, E=256, k=8, H=4096, I=2048, routing="zipf")
 
-LAYER_CONFIGS = {c.name: c for c in (TINY, DECODE, MTP4, MTP8, MX_DECODE, MX_PREFILL)}
+# W8A16 decode at the NVFP4 MTP-verify shape (the pages' FP8 path, sections 6.4 and 10).
+FP8_MTP4 = LayerConfig("mtp_fp8_T4_E256_top8_H2048_I768_hot3", FP8, T=4, E=256, k=8, H=2048, I=768, routing="hot3")
+
+LAYER_CONFIGS = {c.name: c for c in (TINY, DECODE, MTP4, MTP8, MX_DECODE, MX_PREFILL, FP8_MTP4)}
 
 HOT_BOOST = 6.0
 
@@ -152,6 +169,9 @@ def fc_weights(cfg: LayerConfig, which: int):
     """which=1: FC1 (K=H, N=2I); which=2: FC2 (K=I, N=H). Returns (w, s, g)."""
     K, N = (cfg.H, 2 * cfg.I) if which == 1 else (cfg.I, cfg.H)
     base = 2 if which == 1 else 5
+    if cfg.fmt == FP8:
+        w = fp8_weight_bytes(stream(cfg.seed, base), (cfg.E, N, K))
+        return w, None, global_scales(stream(cfg.seed, base + 2), cfg.E)
     w = packed_codes(stream(cfg.seed, base), (cfg.E, K, N // 2))
     if cfg.fmt == NVFP4:
         s = e4m3_scales(stream(cfg.seed, base + 1), (cfg.E, K // cfg.B, N), cfg.positive_scales)

@@ -179,10 +179,20 @@ def _tiny_layer(fmt, seed=0, E=3, H=64, I=32, T=3, k=2):
     return synth.layer_inputs(cfg)
 
 
-@pytest.mark.parametrize("fmt_case", ["nvfp4", "mxfp4", "mxfp4_g"])
+def torch_fp8_weights(w_e, g_e):
+    """Independent FP8 decode: torch's float8_e4m3fn cast of the [N][K] bytes, times g, as [K][N]."""
+    v = torch.from_numpy(np.ascontiguousarray(w_e, np.uint8)).view(torch.float8_e4m3fn).to(torch.float64)
+    return v.numpy().T * float(g_e)
+
+
+@pytest.mark.parametrize("fmt_case", ["nvfp4", "mxfp4", "mxfp4_g", "fp8"])
 def test_fc1_fc2_equal_bruteforce_loops(fmt_case):
-    L = _tiny_layer(fmt_case)
-    fmt = "nvfp4" if fmt_case == "nvfp4" else "mxfp4"
+    if fmt_case == "fp8":
+        L = synth.layer_inputs(synth.shrink(synth.FP8_MTP4, E=3, H=64, I=32, T=3, k=2, seed=0))
+        fmt = "fp8"
+    else:
+        L = _tiny_layer(fmt_case)
+        fmt = "nvfp4" if fmt_case == "nvfp4" else "mxfp4"
     assert (L.g1 is None) == (fmt_case == "mxfp4")
     c = L.cfg
     idx, _ = route.route_topk(L.logits, c.k)
@@ -192,8 +202,11 @@ def test_fc1_fc2_equal_bruteforce_loops(fmt_case):
     x64 = codecs.bf16_to_f64(L.x)
     h64 = codecs.bf16_to_f64(h)
     for e in range(c.E):
-        W1 = table_dequant(L.w1[e], L.s1[e], None if L.g1 is None else L.g1[e], fmt)
-        W2 = table_dequant(L.w2[e], L.s2[e], None if L.g2 is None else L.g2[e], fmt)
+        if fmt == "fp8":
+            W1, W2 = torch_fp8_weights(L.w1[e], L.g1[e]), torch_fp8_weights(L.w2[e], L.g2[e])
+        else:
+            W1 = table_dequant(L.w1[e], L.s1[e], None if L.g1 is None else L.g1[e], fmt)
+            W2 = table_dequant(L.w2[e], L.s2[e], None if L.g2 is None else L.g2[e], fmt)
         for p in range(off[e], off[e + 1]):
             t = p2e[p] // c.k
             for n in range(2 * c.I):
@@ -323,6 +336,46 @@ def test_router_weights_are_gathered_at_the_selection():
     np.testing.assert_array_equal(a["y"], b["y"])
     np.testing.assert_allclose(a["out"], moe.finalize(b["y"], rws[np.arange(3)[:, None], b["idx"]], b["e2p"], 3, 2),
                                rtol=1e-15)
+
+
+def test_fp8_dequant_every_byte_matches_torch():
+    # every byte value at every (n, k) position pattern; [E][N][K] layout
+    E, N, K = 2, 16, 32
+    w = (np.arange(E * N * K) * 37 % 256).astype(np.uint8).reshape(E, N, K)
+    assert set(np.unique(w)) == set(range(256))
+    g = np.array([1.0, 0.8125], np.float32)
+    for e in range(E):
+        got = dequant.dequant_fp8_expert_f64(w[e], g[e])
+        ref = torch_fp8_weights(w[e], g[e])
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2 * (N * K // 256)   # 0x7F, 0xFF
+        np.testing.assert_array_equal(got[~nan], ref[~nan])
+        cols = np.array([3, 0, 15])
+        np.testing.assert_array_equal(dequant.dequant_fp8_expert_f64(w[e], g[e], cols)[:, :2],
+                                      got[:, cols[:2]])
+    # bf16 output: torch's float32 product, then its bfloat16 cast
+    gb = np.array([1.3, 0.6], np.float32)
+    wb = np.where((w & 0x7F) == 0x7F, 0, w).astype(np.uint8)          # finite bytes only
+    got = dequant.dequant_fp8_bf16(wb, gb)
+    for e in range(E):
+        t = torch.from_numpy(wb[e]).view(torch.float8_e4m3fn).to(torch.float32) * float(gb[e])
+        ref = t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        np.testing.assert_array_equal(got[e], ref)
+
+
+def test_fp8_layer_E1_k1_is_dense_swiglu_ffn():
+    L = synth.layer_inputs(synth.shrink(synth.FP8_MTP4, E=1, T=5, k=1, H=64, I=48, seed=15))
+    r = moe.layer(L)
+    W1 = torch.tensor(torch_fp8_weights(L.w1[0], L.g1[0]))
+    W2 = torch.tensor(torch_fp8_weights(L.w2[0], L.g2[0]))
+    x = torch.tensor(codecs.bf16_to_f64(L.x))
+    u = x @ W1
+    h = torch.nn.functional.silu(u[:, 0::2]) * u[:, 1::2]
+    np.testing.assert_allclose(r["u"], u.numpy(), rtol=1e-13)
+    hb = torch.tensor(codecs.bf16_to_f64(r["h"]))
+    torch.testing.assert_close(hb, h, rtol=2 ** -8, atol=1e-30)
+    ref = (hb @ W2).numpy()
+    np.testing.assert_allclose(r["y"], ref, rtol=1e-12)
 
 
 def test_finalize_k1_and_identical_rows():
