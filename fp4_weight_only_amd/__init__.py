@@ -27,13 +27,19 @@ GEMV_MAX_ROWS = 64
 
 EXPORTS = ("qmoe_route_topk", "qmoe_route_topk_router_weights", "qmoe_fp4_gemv_fc1_swiglu", "qmoe_fp4_gemv_fc2", "qmoe_fp4_gemv_fc2_finalize",
            "qmoe_finalize",
-           "qmoe_dequant_fp4", "qmoe_status_str")
+           "qmoe_dequant_fp4", "qmoe_fp8_gemv_fc1_swiglu", "qmoe_fp8_gemv_fc2", "qmoe_dequant_fp8",
+           "qmoe_status_str")
 
 
 class QmoeError(RuntimeError):
     def __init__(self, fn: str, status: int):
         self.status = status
         super().__init__(f"{fn}: {lib.qmoe_status_str(status).decode()}")
+
+
+class Fp8WeightsC(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("gscale", ctypes.c_void_p),
+                ("E", ctypes.c_int32), ("K", ctypes.c_int32), ("N", ctypes.c_int32)]
 
 
 class Fp4WeightsC(ctypes.Structure):
@@ -64,6 +70,7 @@ def _load():
     L = ctypes.CDLL(LIB_PATH)
     P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)
     W = ctypes.POINTER(Fp4WeightsC)
+    W8 = ctypes.POINTER(Fp8WeightsC)
     sig = {
         "qmoe_route_topk": [P, I32, I32, I32, P, P, P, P, P, P],
         "qmoe_route_topk_router_weights": [P, P, I32, I32, I32, P, P, P, P, P, P],
@@ -72,6 +79,9 @@ def _load():
         "qmoe_fp4_gemv_fc2_finalize": [P, I32, I32, W, P, P, P, P, P, SZ, I32, P],
         "qmoe_finalize": [P, P, P, I32, I32, I32, P, P],
         "qmoe_dequant_fp4": [W, P, P],
+        "qmoe_fp8_gemv_fc1_swiglu": [P, I32, I32, W8, P, P, ctypes.POINTER(SwigluC), P, P, SZ, P],
+        "qmoe_fp8_gemv_fc2": [P, I32, I32, W8, P, P, P, SZ, P],
+        "qmoe_dequant_fp8": [W8, P, P],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -97,6 +107,17 @@ class FP4Weights:
         E, K, half = self.w.shape
         return Fp4WeightsC(self.w.data_ptr(), self.scales.data_ptr(),
                            None if self.gscale is None else self.gscale.data_ptr(), E, K, 2 * half, self.fmt)
+
+
+@dataclasses.dataclass
+class FP8Weights:
+    """Device tensors of one FP8 (W8A16) FC layer: w [E][N][K] uint8 E4M3 bytes, gscale [E] f32."""
+    w: torch.Tensor
+    gscale: torch.Tensor
+
+    def c(self) -> Fp8WeightsC:
+        E, N, K = self.w.shape
+        return Fp8WeightsC(self.w.data_ptr(), self.gscale.data_ptr(), E, K, N)
 
 
 def _stream(stream):
@@ -191,3 +212,40 @@ def qmoe_finalize(y_rows, topk_w, expanded_to_perm, out, stream=None):
 def qmoe_dequant_fp4(w: FP4Weights, out, stream=None):
     wc = w.c()
     _check("qmoe_dequant_fp4", lib.qmoe_dequant_fp4(ctypes.byref(wc), _ptr(out), _stream(stream)))
+
+
+def fp8_workspace_bytes(which: int, T: int, k: int, w: FP8Weights, act=None) -> int:
+    """Workspace size of qmoe_fp8_gemv_fc1_swiglu (which=1, with its act) or qmoe_fp8_gemv_fc2 (which=2)."""
+    n = ctypes.c_size_t(0)
+    wc = w.c()
+    dummy = 256
+    if which == 1:
+        st = lib.qmoe_fp8_gemv_fc1_swiglu(dummy, T, k, ctypes.byref(wc), dummy, dummy, _swiglu(act), dummy, None,
+                                          ctypes.byref(n), None)
+    else:
+        st = lib.qmoe_fp8_gemv_fc2(dummy, T, k, ctypes.byref(wc), dummy, dummy, None, ctypes.byref(n), None)
+    _check("fp8_workspace_bytes", st)
+    return n.value
+
+
+def qmoe_fp8_gemv_fc1_swiglu(x, k, w1: FP8Weights, expert_offsets, perm_to_expanded, h, ws, act=None,
+                             stream=None):
+    T = x.shape[0]
+    wc = w1.c()
+    n = ctypes.c_size_t(ws.numel() * ws.element_size())
+    _check("qmoe_fp8_gemv_fc1_swiglu", lib.qmoe_fp8_gemv_fc1_swiglu(
+        _ptr(x), T, k, ctypes.byref(wc), _ptr(expert_offsets), _ptr(perm_to_expanded), _swiglu(act), _ptr(h),
+        _ptr(ws), ctypes.byref(n), _stream(stream)))
+
+
+def qmoe_fp8_gemv_fc2(h, T, k, w2: FP8Weights, expert_offsets, y_rows, ws, stream=None):
+    wc = w2.c()
+    n = ctypes.c_size_t(ws.numel() * ws.element_size())
+    _check("qmoe_fp8_gemv_fc2", lib.qmoe_fp8_gemv_fc2(
+        _ptr(h), T, k, ctypes.byref(wc), _ptr(expert_offsets), _ptr(y_rows), _ptr(ws), ctypes.byref(n),
+        _stream(stream)))
+
+
+def qmoe_dequant_fp8(w: FP8Weights, out, stream=None):
+    wc = w.c()
+    _check("qmoe_dequant_fp8", lib.qmoe_dequant_fp8(ctypes.byref(wc), _ptr(out), _stream(stream)))

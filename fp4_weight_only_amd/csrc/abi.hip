@@ -96,6 +96,41 @@ qmoe_status run_fc(GemvArgs &a, const qmoe_fp4_weights *w, int max_rows, qmoe_pa
   return check_launch(launch_fp4_gemv(a, fmt, max_rows, stream));
 }
 
+qmoe_status check_fp8_fc(const qmoe_fp8_weights *w, int32_t T, int32_t k, const void *act, const void *offsets,
+                         const void *out, FcShape *shape) {
+  if (!w || !w->w || !w->gscale || !act || !offsets || !out) return QMOE_EINVAL;
+  if (T < 1 || k < 1 || w->E < 1 || w->K < 1 || w->N < 1 || k > w->E) return QMOE_EINVAL;
+  if (!aligned16(w->w) || !aligned16(w->gscale) || !aligned16(act) || !aligned16(offsets) || !aligned16(out))
+    return QMOE_EALIGN;
+  if (w->E > QMOE_MAX_EXPERTS || k > QMOE_MAX_TOPK) return QMOE_EUNSUPPORTED;
+  if (w->K % 16 != 0 || w->N % 32 != 0) return QMOE_EUNSUPPORTED;
+  // one expert's bytes are addressed with 32-bit buffer offsets
+  if ((int64_t)w->K * w->N >= ((int64_t)1 << 31)) return QMOE_EUNSUPPORTED;
+  const int64_t rows = (int64_t)T * k;
+  if (rows > QMOE_GEMV_MAX_ROWS) return QMOE_EUNSUPPORTED;
+  shape->rows = (int32_t)rows;
+  shape->max_rows_per_expert = T;
+  return QMOE_OK;
+}
+
+qmoe_status run_fp8(GemvArgs &a, const qmoe_fp8_weights *w, int max_rows, void *ws, size_t *ws_bytes,
+                    hipStream_t stream) {
+  const size_t need = fp8_workspace_bytes(a.rows, w->N, a.concat != 0);
+  if (!ws_bytes) return QMOE_EINVAL;
+  if (!ws) {
+    *ws_bytes = need;
+    return QMOE_OK;
+  }
+  if (*ws_bytes < need) return QMOE_EWORKSPACE;
+  if (!aligned16(ws)) return QMOE_EALIGN;
+  a.w = w->w;
+  a.gscale = w->gscale;
+  a.E = w->E;
+  a.K = w->K;
+  a.N = w->N;
+  return check_launch(launch_fp8_gemv(a, max_rows, ws, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -265,6 +300,56 @@ qmoe_status qmoe_dequant_fp4(const qmoe_fp4_weights *w, uint16_t *out, hipStream
   if (w->E > 65535 || w->K / 64 > 65535 || w->N / 256 > 65535) return QMOE_EUNSUPPORTED;
   return check_launch(
       launch_dequant(w->w, w->scales, w->gscale, w->E, w->K, w->N, w->fmt == QMOE_FMT_NVFP4 ? 0 : 1, out, stream));
+}
+
+qmoe_status qmoe_fp8_gemv_fc1_swiglu(const uint16_t *x, int32_t T, int32_t k, const qmoe_fp8_weights *w1,
+                                     const int32_t *expert_offsets, const int32_t *perm_to_expanded,
+                                     const qmoe_swiglu *act, uint16_t *h, void *ws, size_t *ws_bytes,
+                                     hipStream_t stream) {
+  FcShape sh;
+  qmoe_status st = check_fp8_fc(w1, T, k, x, expert_offsets, h, &sh);
+  if (st != QMOE_OK) return st;
+  if (!perm_to_expanded) return QMOE_EINVAL;
+  if (!aligned16(perm_to_expanded)) return QMOE_EALIGN;
+  GemvArgs a = {};
+  a.act = x;
+  a.p2e = perm_to_expanded;
+  a.offsets = expert_offsets;
+  a.topk = k;
+  a.rows = sh.rows;
+  a.fc1 = 1;
+  a.alpha = act ? act->alpha : 1.0f;
+  a.beta = act ? act->beta : 0.0f;
+  a.limit = act ? act->limit : INFINITY;
+  const int32_t fusion = act ? act->fusion : QMOE_SWIGLU_INTERLEAVED;
+  if (fusion != 0 && fusion != QMOE_SWIGLU_INTERLEAVED && fusion != QMOE_SWIGLU_CONCAT) return QMOE_EINVAL;
+  a.concat = fusion == QMOE_SWIGLU_CONCAT;
+  a.out_bf16 = h;
+  return run_fp8(a, w1, sh.max_rows_per_expert, ws, ws_bytes, stream);
+}
+
+qmoe_status qmoe_fp8_gemv_fc2(const uint16_t *h, int32_t T, int32_t k, const qmoe_fp8_weights *w2,
+                              const int32_t *expert_offsets, float *y_rows, void *ws, size_t *ws_bytes,
+                              hipStream_t stream) {
+  FcShape sh;
+  qmoe_status st = check_fp8_fc(w2, T, k, h, expert_offsets, y_rows, &sh);
+  if (st != QMOE_OK) return st;
+  GemvArgs a = {};
+  a.act = h;
+  a.offsets = expert_offsets;
+  a.topk = k;
+  a.rows = sh.rows;
+  a.fc1 = 0;
+  a.out_f32 = y_rows;
+  return run_fp8(a, w2, sh.max_rows_per_expert, ws, ws_bytes, stream);
+}
+
+qmoe_status qmoe_dequant_fp8(const qmoe_fp8_weights *w, uint16_t *out, hipStream_t stream) {
+  if (!w || !w->w || !w->gscale || !out) return QMOE_EINVAL;
+  if (w->E < 1 || w->K < 1 || w->N < 1) return QMOE_EINVAL;
+  if (!aligned16(w->w) || !aligned16(w->gscale) || !aligned16(out)) return QMOE_EALIGN;
+  if (((int64_t)w->K * w->N) % 16 != 0 || w->E > 65535) return QMOE_EUNSUPPORTED;
+  return check_launch(launch_fp8_dequant(w->w, w->gscale, w->E, w->K, w->N, out, stream));
 }
 
 }  // extern "C"

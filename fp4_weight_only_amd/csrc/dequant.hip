@@ -27,7 +27,6 @@
 
 namespace qmoe {
 
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // One output column c (8 consecutive k) of a thread: z holds the nibble-
 // zipped row pairs (0,1), (2,3), (4,5), (6,7); byte c/2 of the even (c even)

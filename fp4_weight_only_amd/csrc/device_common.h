@@ -10,6 +10,13 @@ namespace qmoe {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair (first in the low half), each rounded to
+// nearest even by the hardware conversion.
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
 
 constexpr int kWave = 64;
 
@@ -83,6 +90,52 @@ constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowMirror = 0x140;
+
+// Finds the expert holding the s-th non-empty row range, with its first row
+// and row count.  Every lane gets the same answer; returns -1 if fewer than
+// s+1 experts have rows.
+__device__ __forceinline__ int find_slot_expert(const int32_t *__restrict__ off, int E, int s, int &row0, int &m) {
+  const int lane = lane_id();
+  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int o[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int e = 4 * lane + i;
+    o[i] = (e <= E) ? off[e] : 0;
+  }
+  int before = 0;
+  bool ne[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ne[i] = (4 * lane + i < E) && (o[i + 1] > o[i]);
+    before += __popcll(__ballot(ne[i]) & lt);
+  }
+  int found = -1, r0 = 0, cnt = 0;
+  int run = before;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (ne[i] && run == s) {
+      found = 4 * lane + i;
+      r0 = o[i];
+      cnt = o[i + 1] - o[i];
+    }
+    run += ne[i] ? 1 : 0;
+  }
+  const unsigned long long fb = __ballot(found >= 0);
+  if (fb == 0ull) return -1;
+  const int src = __ffsll((long long)fb) - 1;
+  row0 = __builtin_amdgcn_readlane(r0, src);
+  m = __builtin_amdgcn_readlane(cnt, src);
+  return __builtin_amdgcn_readlane(found, src);
+}
+
+// SwiGLU(G, L) = G * sigmoid(alpha G) * (L + beta), G = min(gate, limit),
+// L = clamp(lin, -limit, limit) (operator documentation section 8).
+__device__ __forceinline__ float swiglu(float gate, float lin, float alpha, float beta, float limit) {
+  const float G = fminf(gate, limit);
+  const float L = fminf(fmaxf(lin, -limit), limit);
+  return G / (1.0f + expf(-alpha * G)) * (L + beta);
+}
 
 // Workgroup barrier that orders LDS accesses only: __syncthreads() also
 // waits for the wave's outstanding global loads (its fence covers every

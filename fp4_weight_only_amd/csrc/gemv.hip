@@ -42,44 +42,6 @@ constexpr int kMaxChunkK = kGemvMaxWaves * kGemvWaveK;
 constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past any resource: loads return 0
 constexpr int kBufNontemporal = 2;            // cache policy: streaming (nt)
 
-// Finds the expert holding the s-th non-empty row range, with its first row
-// and row count.  Every lane gets the same answer; returns -1 if fewer than
-// s+1 experts have rows.
-__device__ __forceinline__ int find_slot_expert(const int32_t *__restrict__ off, int E, int s, int &row0, int &m) {
-  const int lane = lane_id();
-  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int o[5];
-#pragma unroll
-  for (int i = 0; i < 5; ++i) {
-    const int e = 4 * lane + i;
-    o[i] = (e <= E) ? off[e] : 0;
-  }
-  int before = 0;
-  bool ne[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ne[i] = (4 * lane + i < E) && (o[i + 1] > o[i]);
-    before += __popcll(__ballot(ne[i]) & lt);
-  }
-  int found = -1, r0 = 0, cnt = 0;
-  int run = before;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (ne[i] && run == s) {
-      found = 4 * lane + i;
-      r0 = o[i];
-      cnt = o[i + 1] - o[i];
-    }
-    run += ne[i] ? 1 : 0;
-  }
-  const unsigned long long fb = __ballot(found >= 0);
-  if (fb == 0ull) return -1;
-  const int src = __ffsll((long long)fb) - 1;
-  row0 = __builtin_amdgcn_readlane(r0, src);
-  m = __builtin_amdgcn_readlane(cnt, src);
-  return __builtin_amdgcn_readlane(found, src);
-}
-
 template <int FMT>
 __device__ __forceinline__ void decode_scales(u32x2_t sb, float (&sc)[8]) {
   if constexpr (FMT == 0) {
@@ -100,11 +62,6 @@ __device__ __forceinline__ void decode_scales(u32x2_t sb, float (&sc)[8]) {
   }
 }
 
-__device__ __forceinline__ float swiglu(float gate, float lin, float alpha, float beta, float limit) {
-  const float G = fminf(gate, limit);
-  const float L = fminf(fmaxf(lin, -limit), limit);
-  return G / (1.0f + expf(-alpha * G)) * (L + beta);
-}
 
 template <int MRMAX>
 struct Smem {

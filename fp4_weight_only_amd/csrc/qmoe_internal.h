@@ -44,6 +44,13 @@ hipError_t launch_splitk_epilogue(const GemvArgs &a, hipStream_t s);
 size_t grouped_workspace_bytes(int32_t rows, int32_t N, bool concat);
 hipError_t launch_grouped(GemvArgs &a, int fmt, hipStream_t s);
 
+// FP8 E4M3 weight-only GEMV ([E][N][K] bytes, a.gscale required; a.concat
+// uses ws for float32 u rows) and dequant.
+size_t fp8_workspace_bytes(int32_t rows, int32_t N, bool concat);
+hipError_t launch_fp8_gemv(GemvArgs &a, int max_rows_per_expert, void *ws, hipStream_t s);
+hipError_t launch_fp8_dequant(const uint8_t *w, const float *g, int32_t E, int32_t K, int32_t N, uint16_t *out,
+                              hipStream_t s);
+
 hipError_t launch_route(const float *logits, const float *rw, int32_t T, int32_t E, int32_t k, int32_t *idx, float *w,
                         int32_t *offsets, int32_t *p2e, int32_t *e2p, hipStream_t s);
 

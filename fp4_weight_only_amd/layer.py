@@ -2,15 +2,16 @@
 (or FC2 and finalize fused).
 
 Buffers are allocated once per shape; run() enqueues the four calls on the
-current stream and allocates nothing.
+current stream and allocates nothing.  The FC weights are FP4Weights
+(NVFP4/MXFP4) or FP8Weights (W8A16, decode path only).
 """
 from __future__ import annotations
 
 import torch
 
-from . import (QMOE_PATH_AUTO, FP4Weights, alloc_workspace, fc_workspace_bytes, qmoe_finalize,
-               qmoe_fp4_gemv_fc1_swiglu, qmoe_fp4_gemv_fc2, qmoe_fp4_gemv_fc2_finalize, qmoe_route_topk,
-               qmoe_route_topk_router_weights)
+from . import (QMOE_PATH_AUTO, FP4Weights, FP8Weights, alloc_workspace, fc_workspace_bytes, fp8_workspace_bytes,
+               qmoe_finalize, qmoe_fp4_gemv_fc1_swiglu, qmoe_fp4_gemv_fc2, qmoe_fp4_gemv_fc2_finalize,
+               qmoe_fp8_gemv_fc1_swiglu, qmoe_fp8_gemv_fc2, qmoe_route_topk, qmoe_route_topk_router_weights)
 
 
 class MoELayer:
@@ -28,8 +29,12 @@ class MoELayer:
         self.h = torch.empty((R, I), dtype=torch.bfloat16, device=dev)
         self.y = torch.empty((R, H), dtype=torch.float32, device=dev)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-        need = max(fc_workspace_bytes(1, T, k, w1, path, act), fc_workspace_bytes(2, T, k, w2, path),
-                   fc_workspace_bytes(3, T, k, w2, path))
+        self.fp8 = isinstance(w1, FP8Weights)
+        if self.fp8:
+            need = max(fp8_workspace_bytes(1, T, k, w1, act), fp8_workspace_bytes(2, T, k, w2))
+        else:
+            need = max(fc_workspace_bytes(1, T, k, w1, path, act), fc_workspace_bytes(2, T, k, w2, path),
+                       fc_workspace_bytes(3, T, k, w2, path))
         self.ws = alloc_workspace(need, dev)
 
     def set_weights(self, w1: FP4Weights, w2: FP4Weights):
@@ -43,10 +48,17 @@ class MoELayer:
                                            self.p2e, self.e2p)
 
     def fc1(self, x):
-        qmoe_fp4_gemv_fc1_swiglu(x, self.k, self.w1, self.offsets, self.p2e, self.h, self.ws, self.act, self.path)
+        if self.fp8:
+            qmoe_fp8_gemv_fc1_swiglu(x, self.k, self.w1, self.offsets, self.p2e, self.h, self.ws, self.act)
+        else:
+            qmoe_fp4_gemv_fc1_swiglu(x, self.k, self.w1, self.offsets, self.p2e, self.h, self.ws, self.act,
+                                     self.path)
 
     def fc2(self):
-        qmoe_fp4_gemv_fc2(self.h, self.T, self.k, self.w2, self.offsets, self.y, self.ws, self.path)
+        if self.fp8:
+            qmoe_fp8_gemv_fc2(self.h, self.T, self.k, self.w2, self.offsets, self.y, self.ws)
+        else:
+            qmoe_fp4_gemv_fc2(self.h, self.T, self.k, self.w2, self.offsets, self.y, self.ws, self.path)
 
     def finalize(self):
         qmoe_finalize(self.y, self.topk_w, self.e2p, self.out)
@@ -61,7 +73,7 @@ class MoELayer:
         selects DeepSeek-style mixing weights."""
         self.route(logits, router_weights)
         self.fc1(x)
-        if fused:
+        if fused and not self.fp8:  # FP8 has no fused FC2 + finalize call
             self.fc2_finalize()
         else:
             self.fc2()

@@ -14,6 +14,10 @@
  *   qmoe_finalize             weighted un-permute
  *   qmoe_dequant_fp4          standalone FP4 -> bf16 weight dequant
  *
+ * FP8 E4M3 weight-only (W8A16) layers have their own calls:
+ *
+ *   qmoe_fp8_gemv_fc1_swiglu, qmoe_fp8_gemv_fc2, qmoe_dequant_fp8
+ *
  * and one fused call for the decode layer's tail:
  *
  *   qmoe_fp4_gemv_fc2_finalize  FC2 + weighted un-permute without y_rows
@@ -101,6 +105,18 @@ typedef struct {
   float alpha, beta, limit;  /* SwiGLU(G, L) = G*sigmoid(alpha*G)*(L+beta), G = min(gate, limit), L = clamp(lin, -limit, limit) */
   int32_t fusion;            /* 0 or QMOE_SWIGLU_INTERLEAVED, or QMOE_SWIGLU_CONCAT; other values: QMOE_EINVAL */
 } qmoe_swiglu;
+
+/* FP8 E4M3 weights of one FC layer (W8A16, operator documentation sections
+ * 6.4 and 10): raw E4M3FN bytes, no block scales, no packing.
+ *   w      [E][N][K] uint8 device: byte (e,n,k) is weight (k, n) of expert e
+ *          (each output column's K weights contiguous).
+ *   gscale [E] float32 device, required: weight(e,k,n) = e4m3(byte) * gscale(e),
+ *          the per-expert scale the pages apply to the product in the epilogue. */
+typedef struct {
+  const uint8_t *w;
+  const float *gscale;
+  int32_t E, K, N;
+} qmoe_fp8_weights;
 
 #define QMOE_MAX_EXPERTS 256
 #define QMOE_MAX_TOPK 8
@@ -256,6 +272,42 @@ qmoe_status qmoe_finalize(const float *y_rows, const float *topk_w, const int32_
  * Limits: K % 64 == 0, N % 256 == 0 (QMOE_EUNSUPPORTED otherwise).
  */
 qmoe_status qmoe_dequant_fp4(const qmoe_fp4_weights *w, uint16_t *out, hipStream_t stream);
+
+/*
+ * qmoe_fp8_gemv_fc1_swiglu / qmoe_fp8_gemv_fc2 -- the FC calls for FP8 weights.
+ *
+ * Passages: operator documentation section 6.4 (FP8 e4m3: [E, N, K] bytes,
+ * pack size 1, per-expert global scale only) and section 10 (W8A16: bf16
+ * activations, GEMM output times the expert's global scale in the epilogue;
+ * the activation between the GEMMs as for FP4).
+ *
+ * Arguments, outputs and row order as qmoe_fp4_gemv_fc1_swiglu and
+ * qmoe_fp4_gemv_fc2, with w1 (K = H, N = 2*I) or w2 (K = I, N = H) in the FP8
+ * layout.  u[p][n] = gscale(e) * sum_k x[k] * e4m3(w[e][n][k]), accumulated in
+ * float32.  Decode path only: T*k <= 64 rows (no path argument).  The
+ * workspace is needed only for the concatenated SwiGLU layout (float32 u
+ * rows); the size query convention is the FP4 calls'.
+ * Limits: K % 16 == 0, N % 32 == 0, K*N < 2^31, E <= 256, k <= 8
+ * (QMOE_EUNSUPPORTED); NULL w or gscale: QMOE_EINVAL.
+ */
+qmoe_status qmoe_fp8_gemv_fc1_swiglu(const uint16_t *x, int32_t T, int32_t k,
+                                     const qmoe_fp8_weights *w1,
+                                     const int32_t *expert_offsets, const int32_t *perm_to_expanded,
+                                     const qmoe_swiglu *act, uint16_t *h,
+                                     void *ws, size_t *ws_bytes, hipStream_t stream);
+qmoe_status qmoe_fp8_gemv_fc2(const uint16_t *h, int32_t T, int32_t k,
+                              const qmoe_fp8_weights *w2, const int32_t *expert_offsets,
+                              float *y_rows, void *ws, size_t *ws_bytes, hipStream_t stream);
+
+/*
+ * qmoe_dequant_fp8 -- FP8 weights to bf16 (operator documentation section
+ * 4.3, the dequant-to-A16 fallback's FP8 helper; section 10.3).
+ *
+ * out [E][N][K] bf16 (same layout as w): bf16_rne(float32(e4m3 * gscale(e)))
+ * -- the product rounds to float32, then to bf16.  NaN bytes give NaN.
+ * Limits: K*N % 16 == 0, E <= 65535 (QMOE_EUNSUPPORTED).
+ */
+qmoe_status qmoe_dequant_fp8(const qmoe_fp8_weights *w, uint16_t *out, hipStream_t stream);
 
 /* Static string naming a status code. */
 const char *qmoe_status_str(qmoe_status s);

@@ -27,6 +27,8 @@ def fmt_code(fmt: str) -> int:
 
 def weights_dev(w, s, g, fmt):
     import fp4_weight_only_amd as q
+    if fmt == "fp8":
+        return q.FP8Weights(to_dev(w), to_dev(g))
     return q.FP4Weights(to_dev(w), to_dev(s), None if g is None else to_dev(g), fmt_code(fmt))
 
 

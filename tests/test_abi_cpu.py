@@ -167,6 +167,35 @@ def test_swiglu_fusion_modes_and_workspace(q):
     assert st == q.QMOE_OK and ng1 < ng
 
 
+def test_fp8_validation_and_workspace(q):
+    L = q.lib
+    W8 = lambda E=16, K=256, N=512, w=A, g=A: q.Fp8WeightsC(w, g, E, K, N)
+    n = ctypes.c_size_t(0)
+    fc1 = lambda wc, T=2, k=2, act=None, x=A, p2e=A: L.qmoe_fp8_gemv_fc1_swiglu(
+        x, T, k, ctypes.byref(wc), A, p2e, None if act is None else ctypes.byref(act), A, None, ctypes.byref(n), None)
+    fc2 = lambda wc, T=2, k=2, y=A: L.qmoe_fp8_gemv_fc2(A, T, k, ctypes.byref(wc), A, y, None, ctypes.byref(n), None)
+    assert fc1(W8()) == q.QMOE_OK and n.value == 256             # interleaved: no workspace beyond the minimum
+    assert fc1(W8(), act=q.SwigluC(1.0, 0.0, float("inf"), q.QMOE_SWIGLU_CONCAT)) == q.QMOE_OK
+    assert n.value >= 4 * 512 * 4                                # concatenated: float32 u rows
+    assert fc1(W8(), act=q.SwigluC(1.0, 0.0, float("inf"), 5)) == q.QMOE_EINVAL
+    assert fc1(W8(g=0)) == q.QMOE_EINVAL                         # the global scale is required
+    assert fc1(W8(w=0)) == q.QMOE_EINVAL
+    assert fc1(W8(), p2e=None) == q.QMOE_EINVAL
+    assert fc1(W8(w=MIS)) == q.QMOE_EALIGN
+    assert fc1(W8(K=200)) == q.QMOE_EUNSUPPORTED                 # K % 16
+    assert fc1(W8(N=528)) == q.QMOE_EUNSUPPORTED                 # N % 32
+    assert fc1(W8(E=64), T=13, k=5) == q.QMOE_EUNSUPPORTED       # 65 rows: decode path only
+    assert fc1(W8(E=300)) == q.QMOE_EUNSUPPORTED
+    assert fc1(W8(), k=17) == q.QMOE_EINVAL                      # k > E
+    assert fc1(W8(K=65536, N=32768)) == q.QMOE_EUNSUPPORTED      # one expert beyond 32-bit offsets
+    assert fc2(W8(), y=None) == q.QMOE_EINVAL
+    assert fc2(W8()) == q.QMOE_OK
+    dq = lambda wc, out=A: L.qmoe_dequant_fp8(ctypes.byref(wc), out, None)
+    assert dq(W8(g=0)) == q.QMOE_EINVAL
+    assert dq(W8(), out=MIS) == q.QMOE_EALIGN
+    assert dq(W8(K=17, N=33)) == q.QMOE_EUNSUPPORTED
+
+
 def test_finalize_and_dequant_validation(q):
     L = q.lib
     assert L.qmoe_finalize(None, A, A, 1, 2, 256, A, None) == q.QMOE_EINVAL

@@ -173,6 +173,60 @@ def test_route_router_weights(T, E, k):
     assert np.array_equal(d["e2p"].cpu().numpy(), e2p)
 
 
+# FP8 E4M3 weight-only (W8A16): [E][N][K] bytes, per-expert global scale.
+FP8_SMALL = [
+    synth.shrink(synth.FP8_MTP4, E=37, T=7, k=5, H=320, I=144, seed=41),     # 35 rows, ragged N
+    synth.shrink(synth.FP8_MTP4, E=8, T=2, k=2, H=2304, I=96, seed=42),      # K = 2304: two k passes
+    synth.shrink(synth.FP8_MTP4, E=16, T=64, k=1, H=256, I=64, seed=43),     # up to 64 rows per expert
+    synth.with_rows(synth.FP8_MTP4, 1, "fp8_T1"),
+    synth.FP8_MTP4,
+    synth.with_rows(synth.FP8_MTP4, 8, "fp8_T8"),
+]
+
+
+@pytest.mark.parametrize("cfg", FP8_SMALL, ids=lambda c: c.name)
+def test_fp8_layer(cfg):
+    check_layer(synth.layer_inputs(cfg))
+
+
+@pytest.mark.parametrize("act", [STD, GPTOSS], ids=["std", "gptoss"])
+def test_fp8_concat_and_gptoss(act):
+    cfg = synth.shrink(synth.FP8_MTP4, E=37, T=7, k=5, H=320, I=144, seed=44)
+    check_layer(synth.layer_inputs(cfg), act=act + (2,))
+    check_layer(synth.layer_inputs(cfg), act=act)
+
+
+def test_fp8_every_finite_byte_through_the_gemv():
+    # every finite E4M3 byte at every lane position of a 16-byte load
+    cfg = synth.shrink(synth.FP8_MTP4, E=2, T=2, k=1, H=512, I=128, seed=45)
+    L = synth.layer_inputs(cfg)
+    finite = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], np.uint8)
+    for w in (L.w1, L.w2):
+        E, N, K = w.shape
+        w[:] = finite[(np.arange(E * N * K).reshape(E, N, K) * 7 + np.arange(N)[None, :, None] * 3) % len(finite)]
+        assert set(np.unique(w)) == set(finite)
+    L.x[:] = synth.to_bf16_bits(np.full(L.x.shape, 0.01, np.float32))   # keep SwiGLU finite with 448-sized weights
+    check_layer(L)
+
+
+def test_fp8_dequant_every_byte():
+    import fp4_weight_only_amd as q
+    E, N, K = 3, 96, 160
+    rng = np.random.default_rng(46)
+    w = rng.integers(0, 256, (E, N, K), dtype=np.uint8)
+    w[0].reshape(-1)[:256] = np.arange(256)
+    g = np.array([1.0, 0.37, 1.9], np.float32)
+    out = torch.empty((E, N, K), dtype=torch.int16, device="cuda")
+    print_case("fp8 dequant", E, N, K)
+    q.qmoe_dequant_fp8(q.FP8Weights(to_dev(w), to_dev(g)), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    ref = dequant.dequant_fp8_bf16(w, g)
+    nan = (w & 0x7F) == 0x7F
+    assert np.all((got[nan] & 0x7F80) == 0x7F80) and np.all((got[nan] & 0x7F) != 0)   # NaN
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
 def test_gptoss_swiglu_variant():
     cfg = synth.shrink(synth.DECODE, E=16, T=4, k=4, H=256, I=128, seed=7)
     L = synth.layer_inputs(cfg)

@@ -22,7 +22,7 @@ def fc1_abs_sum(L, off, p2e):
     for e in range(c.E):
         lo, hi = int(off[e]), int(off[e + 1])
         if lo < hi:
-            wd = np.abs(dequant.dequant_expert_f64(L.w1[e], L.s1[e], None if L.g1 is None else L.g1[e], c.fmt))
+            wd = np.abs(dequant.expert_weights_f64(L.w1[e], None if L.s1 is None else L.s1[e], None if L.g1 is None else L.g1[e], c.fmt))
             A[lo:hi] = x[np.asarray(p2e[lo:hi]) // c.k] @ wd
     return A
 
