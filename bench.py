@@ -16,7 +16,9 @@ scales of the experts the routing actually selected) per layer.
 Other workloads (--workload): decode / mtp8 / mx_decode (same layer path),
 prefill (MXFP4 512 tokens, grouped-GEMM path; also reports TFLOP/s and the
 fraction of the bf16 MFMA peak), dequant (MXFP4 standalone dequant, GB/s on
-read + write bytes).  --calibrate-copy runs a plain device-to-device copy of
+read + write bytes), fp8 (the MTP-verify layer with FP8 E4M3 W8A16 weights:
+qmoe_fp8_gemv_fc1_swiglu -> qmoe_fp8_gemv_fc2 -> qmoe_finalize), fp8_dequant
+(FP8 standalone dequant at the dequant workload's shape).  --calibrate-copy runs a plain device-to-device copy of
 known size, the reference kernel for scaling HBM traffic counters.
 
 roofline: the dominant kernel of the workload (FC1 for the layer workloads,
@@ -46,7 +48,7 @@ METRIC = "NVFP4 MoE decode GEMV µs/layer + achieved HBM GB/s (% of peak), 4–6
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 CSRC = os.path.join(ROOT, "fp4_weight_only_amd", "csrc")
-LAYER_WORKLOADS = ("mtp4", "mtp8", "decode", "mx_decode", "prefill")
+LAYER_WORKLOADS = ("mtp4", "mtp8", "decode", "mx_decode", "prefill", "fp8")
 
 
 def parse():
@@ -55,7 +57,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=80)
     ap.add_argument("--eager", action="store_true")
-    ap.add_argument("--workload", default="mtp4", choices=LAYER_WORKLOADS + ("dequant",))
+    ap.add_argument("--workload", default="mtp4", choices=LAYER_WORKLOADS + ("dequant", "fp8_dequant"))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -147,10 +149,11 @@ def bench_layer(args, torch, q, synth, np):
     from fp4_weight_only_amd.layer import MoELayer
 
     cfg = {"mtp4": synth.MTP4, "mtp8": synth.MTP8, "decode": synth.DECODE, "mx_decode": synth.MX_DECODE,
-           "prefill": synth.MX_PREFILL}[args.workload]
+           "prefill": synth.MX_PREFILL, "fp8": synth.FP8_MTP4}[args.workload]
     prefill = args.workload == "prefill"
+    fp8 = cfg.fmt == synth.FP8
     # distinct weight copies: > 256 MB Infinity Cache worth of selected experts
-    layers = 40 if cfg.fmt == synth.NVFP4 else (2 if prefill else 8)
+    layers = 40 if cfg.fmt == synth.NVFP4 else (2 if prefill else (16 if fp8 else 8))
     dev = torch.device("cuda:0")
     t0 = time.time()
     L = synth.layer_inputs(cfg)
@@ -160,12 +163,15 @@ def bench_layer(args, torch, q, synth, np):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     fmt = q.QMOE_FMT_NVFP4 if cfg.fmt == synth.NVFP4 else q.QMOE_FMT_MXFP4
-    base = [to_dev(L.w1), to_dev(L.s1), None if L.g1 is None else to_dev(L.g1),
-            to_dev(L.w2), to_dev(L.s2), None if L.g2 is None else to_dev(L.g2)]
+    base = [to_dev(L.w1), None if L.s1 is None else to_dev(L.s1), None if L.g1 is None else to_dev(L.g1),
+            to_dev(L.w2), None if L.s2 is None else to_dev(L.s2), None if L.g2 is None else to_dev(L.g2)]
     copies = []
     for i in range(layers):
         t = [None if b is None else (b if i == 0 else b.clone()) for b in base]
-        copies.append((q.FP4Weights(t[0], t[1], t[2], fmt), q.FP4Weights(t[3], t[4], t[5], fmt)))
+        if fp8:
+            copies.append((q.FP8Weights(t[0], t[2]), q.FP8Weights(t[3], t[5])))
+        else:
+            copies.append((q.FP4Weights(t[0], t[1], t[2], fmt), q.FP4Weights(t[3], t[4], t[5], fmt)))
     logits = to_dev(L.logits)
     x = to_dev(L.x.view(np.int16)).view(torch.bfloat16)
     layer = MoELayer(cfg.T, cfg.E, cfg.k, cfg.H, cfg.I, copies[0][0], copies[0][1], device=dev)
@@ -174,8 +180,12 @@ def bench_layer(args, torch, q, synth, np):
     offsets = layer.offsets.cpu().numpy()
     D = int(np.count_nonzero(np.diff(offsets)))
     B = cfg.B
-    fc1_w = cfg.H * cfg.I + (cfg.H // B) * 2 * cfg.I + (4 if L.g1 is not None else 0)
-    fc2_w = cfg.I * (cfg.H // 2) + (cfg.I // B) * cfg.H + (4 if L.g2 is not None else 0)
+    if fp8:   # one byte per weight, no block scales
+        fc1_w = cfg.H * 2 * cfg.I + 4
+        fc2_w = cfg.I * cfg.H + 4
+    else:
+        fc1_w = cfg.H * cfg.I + (cfg.H // B) * 2 * cfg.I + (4 if L.g1 is not None else 0)
+        fc2_w = cfg.I * (cfg.H // 2) + (cfg.I // B) * cfg.H + (4 if L.g2 is not None else 0)
     weight_bytes = D * (fc1_w + fc2_w)
     R = cfg.rows
     # FC1 algorithmic bytes: selected experts' weights, x rows of the tokens, h, maps
@@ -204,6 +214,10 @@ def bench_layer(args, torch, q, synth, np):
         sources = ("grouped.hip", "device_common.h", "qmoe_internal.h")
         kname, tname = "grouped_gemm_kernel (FC1+SwiGLU)", "grouped_fc1_prefill"
         metric = "MXFP4 MoE prefill layer µs/layer + achieved HBM GB/s on weight bytes"
+    elif fp8:
+        sources = ("fp8.hip", "device_common.h", "qmoe_internal.h")
+        kname, tname = "fp8_gemv_kernel (FC1+SwiGLU)", "fp8_gemv_fc1_mtp4"
+        metric = "FP8 W8A16 MoE decode µs/layer + achieved HBM GB/s on weight bytes"
     else:
         sources = ("gemv.hip", "device_common.h", "qmoe_internal.h")
         kname, tname = "fp4_gemv_kernel + splitk_epilogue_kernel (FC1+SwiGLU)", f"gemv_fc1_{args.workload}"
@@ -262,6 +276,46 @@ def bench_dequant(args, torch, q, synth, np):
                           "traffic": traffic, "avg_us": round(ms * 1e3, 3), "bytes_per_launch": rd + wr}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_dequant(w, s, g, cfg, args.cpu_seconds)
+    return result
+
+
+def bench_fp8_dequant(args, torch, q, synth, np):
+    c = synth.DEQUANT
+    cfg = synth.LayerConfig("fp8_dequant_E32_K2048_N1536", synth.FP8, T=1, E=c.E, k=1, H=c.K, I=c.N // 2)
+    dev = torch.device("cuda:0")
+    w, _, g = synth.fc_weights(cfg, 1)          # [E][N][K] bytes, K = 2048, N = 1536
+    sets = 4
+    bufs = [(q.FP8Weights(torch.from_numpy(w).to(dev), torch.from_numpy(g).to(dev)),
+             torch.empty(w.shape, dtype=torch.bfloat16, device=dev)) for _ in range(sets)]
+    rd, wr = w.nbytes + g.nbytes, w.size * 2
+    tm = Timer(torch, torch.cuda.Stream())
+
+    def step(i):
+        wd, out = bufs[i % sets]
+        q.qmoe_dequant_fp8(wd, out)
+
+    ms = tm.run(step, sets, args.steps, args.warmup, args.eager)
+    gbs = (rd + wr) / (ms * 1e-3) / 1e9
+    config = {"workload": cfg.name, "read_bytes": rd, "write_bytes": wr, "buffer_sets": sets,
+              "launch": "eager" if args.eager else "hip_graph"}
+    result = base_result("FP8 standalone dequant GB/s (read + write bytes)", gbs, "GB/s", args, ms, config,
+                         dtype="u8")
+    result["roofline"] = {"bound": "hbm", "kernel": "fp8_dequant_kernel", "achieved": round(gbs, 2),
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                          "traffic": None, "avg_us": round(ms * 1e3, 3), "bytes_per_launch": rd + wr}
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+
+        from oracle import dequant
+        with threadpool_limits(limits=1):
+            n, t0 = 0, time.perf_counter()
+            while time.perf_counter() - t0 < args.cpu_seconds and n < c.E:
+                dequant.dequant_fp8_bf16(w[n:n + 1], g[n:n + 1])
+                n += 1
+            el = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(n * (w[0].nbytes * 3) / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+                                  "kind": "oracle", "sample": f"{n} of {c.E} experts, float64 numpy, {el:.1f} s",
+                                  "host_cores_total": os.cpu_count()}
     return result
 
 
@@ -362,6 +416,8 @@ def main():
     import synth
     if args.workload == "dequant":
         result = bench_dequant(args, torch, q, synth, np)
+    elif args.workload == "fp8_dequant":
+        result = bench_fp8_dequant(args, torch, q, synth, np)
     else:
         result = bench_layer(args, torch, q, synth, np)
     print(json.dumps(result), flush=True)
