@@ -6,9 +6,11 @@
 // 10: the product is scaled by the expert's global scale in the epilogue).
 //
 // GEMV: a column's K bytes are contiguous, so 16 lanes (one DPP row) share a
-// column and each lane loads 16 consecutive k with one 16-byte load; a wave
-// covers 4 columns, a workgroup 16, and the whole K in passes of 2048 (8
-// loads per lane per pass), so there is no split-K and no second launch.
+// column and each lane loads 16 consecutive k with one 16-byte load.  A lane
+// row covers CPR columns (1 for K >= 1536, 2 for K >= 768, else 4, so a lane
+// keeps up to 8 loads in flight even for short K), a wave 4 * CPR columns, a
+// workgroup of 8 waves 32 * CPR, over the whole K in passes (8 loads per lane
+// per pass): there is no split-K and no second launch.
 // The hardware FP8 -> bf16 conversion is exact; the k pairs meet the
 // activation pairs in dot2 instructions.  The 16 per-lane partial sums of a
 // column are added with a symmetric DPP butterfly inside the row, which
@@ -18,11 +20,10 @@
 
 namespace qmoe {
 
-constexpr int kF8Waves = 4;
-constexpr int kF8ColsPerWave = 4;
-constexpr int kF8TileN = kF8Waves * kF8ColsPerWave;  // 16 columns per workgroup
+constexpr int kF8Waves = 8;
 constexpr int kF8Loads = 8;                          // 16-byte loads per lane per pass
-constexpr int kF8PassK = 16 * 16 * kF8Loads;         // 2048 k per pass
+constexpr int kF8PassK = 16 * 16 * kF8Loads;         // 2048 k per pass (CPR = 1)
+constexpr int kF8TileN1 = kF8Waves * 4;              // 32 columns per workgroup and column per lane row
 constexpr uint32_t kF8OutOfRange = 0x80000000u;
 
 __device__ __forceinline__ float row16_sum(float v) {
@@ -41,9 +42,11 @@ __device__ __forceinline__ uint32_t fp8x2_hi(uint32_t v) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, true));
 }
 
-template <int MRMAX>
+template <int MRMAX, int CPR>
 __global__ __launch_bounds__(kF8Waves * 64) void fp8_gemv_kernel(GemvArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t xs[MRMAX][kF8PassK];
+  constexpr int PASSK = kF8PassK / CPR;       // k per pass: CPR columns x PASSK / 256 loads per lane
+  constexpr int NLD = PASSK / 256;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[MRMAX][PASSK];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = lane_id();
@@ -62,9 +65,10 @@ __global__ __launch_bounds__(kF8Waves * 64) void fp8_gemv_kernel(GemvArgs a) {
   const int e = find_slot_expert(a.offsets, a.E, slot, row0, m);
   if (e < 0) return;  // uniform over the workgroup
 
-  const int col = tile * kF8TileN + wave * kF8ColsPerWave + (lane >> 4);
+  // lane row rr of the wave takes columns base + 4 j + rr (j < CPR): an
+  // interleaved gate / linear pair sits in lane rows 2i, 2i+1 for every j
+  const int col0 = (tile * kF8Waves + wave) * 4 * CPR + (lane >> 4);
   const int q = lane & 15;
-  const bool col_ok = col < a.N;
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(a.w + (size_t)e * a.N * a.K), (short)0, (int)((uint32_t)a.N * (uint32_t)a.K), 0x00020000);
   const float gs = a.gscale[e];
@@ -73,12 +77,14 @@ __global__ __launch_bounds__(kF8Waves * 64) void fp8_gemv_kernel(GemvArgs a) {
   for (int rbase = 0; rbase < m; rbase += MRMAX) {
     const int rem = m - rbase;
     const int mr = rem < MRMAX ? rem : MRMAX;
-    float acc[MRMAX];
+    float acc[CPR][MRMAX];
 #pragma unroll
-    for (int r = 0; r < MRMAX; ++r) acc[r] = 0.f;
+    for (int j = 0; j < CPR; ++j)
+#pragma unroll
+      for (int r = 0; r < MRMAX; ++r) acc[j][r] = 0.f;
 
 #pragma nounroll
-    for (int k0 = 0; k0 < a.K; k0 += kF8PassK) {
+    for (int k0 = 0; k0 < a.K; k0 += PASSK) {
       // activation rows of the pass first (memory returns in issue order),
       // then this lane's weight bytes
       const int kx = k0 + tid * 8;
@@ -88,47 +94,56 @@ __global__ __launch_bounds__(kF8Waves * 64) void fp8_gemv_kernel(GemvArgs a) {
         const int p = row0 + rbase + r;
         const int tok = __shfl(p2e_l, p & 63, 64) / a.topk;
         xv[r] = u32x4_t{0u, 0u, 0u, 0u};
-        if (r < mr && tid * 8 < kF8PassK && kx < a.K) {
+        if (r < mr && tid * 8 < PASSK && kx < a.K) {
           const int src = a.fc1 ? tok : p;
           xv[r] = *(const u32x4_t *)(a.act + (size_t)src * a.K + kx);
         }
       }
-      u32x4_t W[kF8Loads];
+      u32x4_t W[CPR][NLD];
 #pragma unroll
-      for (int i = 0; i < kF8Loads; ++i) {
-        const int kk = k0 + i * 256 + q * 16;
-        const uint32_t voff = (col_ok && kk < a.K) ? (uint32_t)col * (uint32_t)a.K + (uint32_t)kk : kF8OutOfRange;
-        W[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wr, voff, 0, 2));
-      }
-      if (tid * 8 < kF8PassK) {
+      for (int j = 0; j < CPR; ++j)
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+          const int col = col0 + 4 * j;
+          const int kk = k0 + i * 256 + q * 16;
+          const uint32_t voff =
+              (col < a.N && kk < a.K) ? (uint32_t)col * (uint32_t)a.K + (uint32_t)kk : kF8OutOfRange;
+          W[j][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wr, voff, 0, 2));
+        }
+      if (tid * 8 < PASSK) {
 #pragma unroll
         for (int r = 0; r < MRMAX; ++r) *(u32x4_t *)&xs[r][tid * 8] = xv[r];
       }
       lds_barrier();
 #pragma unroll
-      for (int i = 0; i < kF8Loads; ++i) {
-        uint32_t w2[8];
-        w2[0] = fp8x2_lo(W[i].x);
-        w2[1] = fp8x2_hi(W[i].x);
-        w2[2] = fp8x2_lo(W[i].y);
-        w2[3] = fp8x2_hi(W[i].y);
-        w2[4] = fp8x2_lo(W[i].z);
-        w2[5] = fp8x2_hi(W[i].z);
-        w2[6] = fp8x2_lo(W[i].w);
-        w2[7] = fp8x2_hi(W[i].w);
+      for (int i = 0; i < NLD; ++i) {
 #pragma unroll
-        for (int r = 0; r < MRMAX; ++r) {
-          if (MRMAX > 1 && r >= mr) break;  // uniform
-          const u32x4_t x0 = *(const u32x4_t *)&xs[r][i * 256 + q * 16];
-          const u32x4_t x1 = *(const u32x4_t *)&xs[r][i * 256 + q * 16 + 8];
-          acc[r] = dot2_bf16(x0.x, w2[0], acc[r]);
-          acc[r] = dot2_bf16(x0.y, w2[1], acc[r]);
-          acc[r] = dot2_bf16(x0.z, w2[2], acc[r]);
-          acc[r] = dot2_bf16(x0.w, w2[3], acc[r]);
-          acc[r] = dot2_bf16(x1.x, w2[4], acc[r]);
-          acc[r] = dot2_bf16(x1.y, w2[5], acc[r]);
-          acc[r] = dot2_bf16(x1.z, w2[6], acc[r]);
-          acc[r] = dot2_bf16(x1.w, w2[7], acc[r]);
+        for (int j = 0; j < CPR; ++j) {
+          uint32_t w2[8];
+          w2[0] = fp8x2_lo(W[j][i].x);
+          w2[1] = fp8x2_hi(W[j][i].x);
+          w2[2] = fp8x2_lo(W[j][i].y);
+          w2[3] = fp8x2_hi(W[j][i].y);
+          w2[4] = fp8x2_lo(W[j][i].z);
+          w2[5] = fp8x2_hi(W[j][i].z);
+          w2[6] = fp8x2_lo(W[j][i].w);
+          w2[7] = fp8x2_hi(W[j][i].w);
+#pragma unroll
+          for (int r = 0; r < MRMAX; ++r) {
+            if (MRMAX > 1 && r >= mr) break;  // uniform
+            const u32x4_t x0 = *(const u32x4_t *)&xs[r][i * 256 + q * 16];
+            const u32x4_t x1 = *(const u32x4_t *)&xs[r][i * 256 + q * 16 + 8];
+            float v = acc[j][r];
+            v = dot2_bf16(x0.x, w2[0], v);
+            v = dot2_bf16(x0.y, w2[1], v);
+            v = dot2_bf16(x0.z, w2[2], v);
+            v = dot2_bf16(x0.w, w2[3], v);
+            v = dot2_bf16(x1.x, w2[4], v);
+            v = dot2_bf16(x1.y, w2[5], v);
+            v = dot2_bf16(x1.z, w2[6], v);
+            v = dot2_bf16(x1.w, w2[7], v);
+            acc[j][r] = v;
+          }
         }
       }
       lds_barrier();  // the next pass overwrites xs
@@ -136,19 +151,24 @@ __global__ __launch_bounds__(kF8Waves * 64) void fp8_gemv_kernel(GemvArgs a) {
 
     // column sums, global scale, outputs
 #pragma unroll
-    for (int r = 0; r < MRMAX; ++r) {
-      if (MRMAX > 1 && r >= mr) break;  // uniform
-      const float u = gs * row16_sum(acc[r]);
-      const int p = row0 + rbase + r;
-      if (a.fc1 && !a.concat) {
-        // the wave's 4 columns are consecutive: gate (even) rows of lanes
-        // 0-15 / 32-47 meet their linear values in lanes 16-31 / 48-63
-        const float partner = __shfl_xor(u, 16, 64);
-        if (q == 0 && ((lane >> 4) & 1) == 0 && col_ok)
-          a.out_bf16[(size_t)p * (a.N >> 1) + (col >> 1)] =
-              (uint16_t)bf16_rne(swiglu(u, partner, a.alpha, a.beta, a.limit));
-      } else if (q == 0 && col_ok) {
-        a.out_f32[(size_t)p * a.N + col] = u;  // FC2 y, or FC1 u for the concatenated layout
+    for (int j = 0; j < CPR; ++j) {
+      const int col = col0 + 4 * j;
+      const bool col_ok = col < a.N;
+#pragma unroll
+      for (int r = 0; r < MRMAX; ++r) {
+        if (MRMAX > 1 && r >= mr) break;  // uniform
+        const float u = gs * row16_sum(acc[j][r]);
+        const int p = row0 + rbase + r;
+        if (a.fc1 && !a.concat) {
+          // gate (even) columns in lane rows 0 / 2 meet their linear values
+          // in lane rows 1 / 3
+          const float partner = __shfl_xor(u, 16, 64);
+          if (q == 0 && ((lane >> 4) & 1) == 0 && col_ok)
+            a.out_bf16[(size_t)p * (a.N >> 1) + (col >> 1)] =
+                (uint16_t)bf16_rne(swiglu(u, partner, a.alpha, a.beta, a.limit));
+        } else if (q == 0 && col_ok) {
+          a.out_f32[(size_t)p * a.N + col] = u;  // FC2 y, or FC1 u for the concatenated layout
+        }
       }
     }
   }
@@ -160,19 +180,29 @@ size_t fp8_workspace_bytes(int32_t rows, int32_t N, bool concat) {
 }
 
 hipError_t launch_fp8_gemv(GemvArgs &a, int max_rows_per_expert, void *ws, hipStream_t s) {
+  const int cpr = a.K >= 1536 ? 1 : (a.K >= 768 ? 2 : 4);
   a.nslots = a.rows < a.E ? a.rows : a.E;
-  a.ntiles = (a.N + kF8TileN - 1) / kF8TileN;
+  a.ntiles = (a.N + kF8TileN1 * cpr - 1) / (kF8TileN1 * cpr);
   const int items = a.nslots * a.ntiles;
   const dim3 grid((unsigned)(((items + 7) / 8) * 8));
   const dim3 block(kF8Waves * 64);
   if (a.concat) a.out_f32 = (float *)ws;
   const int mr = max_rows_per_expert <= 1 ? 1 : (max_rows_per_expert <= 4 ? 4 : 8);
-  if (mr == 1)
-    fp8_gemv_kernel<1><<<grid, block, 0, s>>>(a);
-  else if (mr == 4)
-    fp8_gemv_kernel<4><<<grid, block, 0, s>>>(a);
-  else
-    fp8_gemv_kernel<8><<<grid, block, 0, s>>>(a);
+#define QMOE_F8_LAUNCH(MR)                                                   \
+  if (cpr == 1)                                                              \
+    fp8_gemv_kernel<MR, 1><<<grid, block, 0, s>>>(a);                        \
+  else if (cpr == 2)                                                         \
+    fp8_gemv_kernel<MR, 2><<<grid, block, 0, s>>>(a);                        \
+  else                                                                       \
+    fp8_gemv_kernel<MR, 4><<<grid, block, 0, s>>>(a);
+  if (mr == 1) {
+    QMOE_F8_LAUNCH(1)
+  } else if (mr == 4) {
+    QMOE_F8_LAUNCH(4)
+  } else {
+    QMOE_F8_LAUNCH(8)
+  }
+#undef QMOE_F8_LAUNCH
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !a.concat) return err;
   a.partials = (float *)ws;
