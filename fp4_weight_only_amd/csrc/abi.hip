@@ -107,7 +107,7 @@ qmoe_status check_fp8_fc(const qmoe_fp8_weights *w, int32_t T, int32_t k, const 
   // one expert's bytes are addressed with 32-bit buffer offsets
   if ((int64_t)w->K * w->N >= ((int64_t)1 << 31)) return QMOE_EUNSUPPORTED;
   const int64_t rows = (int64_t)T * k;
-  if (rows > QMOE_GEMV_MAX_ROWS) return QMOE_EUNSUPPORTED;
+  if (rows > (1 << 24)) return QMOE_EUNSUPPORTED;
   shape->rows = (int32_t)rows;
   shape->max_rows_per_expert = T;
   return QMOE_OK;

@@ -10,7 +10,9 @@
 // row covers CPR columns (1 for K >= 1536, 2 for K >= 768, else 4, so a lane
 // keeps up to 8 loads in flight even for short K), a wave 4 * CPR columns, a
 // workgroup of 8 waves 32 * CPR, over the whole K in passes (8 loads per lane
-// per pass): there is no split-K and no second launch.
+// per pass): there is no split-K and no second launch.  Rows go in passes of
+// up to 8 per workgroup, so any batch works; a prefill batch re-reads an
+// expert's columns (from L2) once per 8 rows.
 // The hardware FP8 -> bf16 conversion is exact; the k pairs meet the
 // activation pairs in dot2 instructions.  The 16 per-lane partial sums of a
 // column are added with a symmetric DPP butterfly inside the row, which
@@ -60,7 +62,6 @@ __global__ __launch_bounds__(kF8Waves * 64) void fp8_gemv_kernel(GemvArgs a) {
   const int slot = item / a.ntiles;
   const int tile = item - slot * a.ntiles;
 
-  const int p2e_l = (a.fc1 && lane < a.rows) ? a.p2e[lane] : 0;
   int row0 = 0, m = 0;
   const int e = find_slot_expert(a.offsets, a.E, slot, row0, m);
   if (e < 0) return;  // uniform over the workgroup
@@ -92,10 +93,9 @@ __global__ __launch_bounds__(kF8Waves * 64) void fp8_gemv_kernel(GemvArgs a) {
 #pragma unroll
       for (int r = 0; r < MRMAX; ++r) {
         const int p = row0 + rbase + r;
-        const int tok = __shfl(p2e_l, p & 63, 64) / a.topk;
         xv[r] = u32x4_t{0u, 0u, 0u, 0u};
         if (r < mr && tid * 8 < PASSK && kx < a.K) {
-          const int src = a.fc1 ? tok : p;
+          const int src = a.fc1 ? a.p2e[p] / a.topk : p;  // FC1 gathers x rows by token
           xv[r] = *(const u32x4_t *)(a.act + (size_t)src * a.K + kx);
         }
       }

@@ -184,7 +184,8 @@ def test_fp8_validation_and_workspace(q):
     assert fc1(W8(w=MIS)) == q.QMOE_EALIGN
     assert fc1(W8(K=200)) == q.QMOE_EUNSUPPORTED                 # K % 16
     assert fc1(W8(N=528)) == q.QMOE_EUNSUPPORTED                 # N % 32
-    assert fc1(W8(E=64), T=13, k=5) == q.QMOE_EUNSUPPORTED       # 65 rows: decode path only
+    assert fc1(W8(E=64), T=13, k=5) == q.QMOE_OK                 # 65 rows: row passes of 8
+    assert fc1(W8(E=64), T=(1 << 22) + 1, k=4) == q.QMOE_EUNSUPPORTED   # T*k > 2^24
     assert fc1(W8(E=300)) == q.QMOE_EUNSUPPORTED
     assert fc1(W8(), k=17) == q.QMOE_EINVAL                      # k > E
     assert fc1(W8(K=65536, N=32768)) == q.QMOE_EUNSUPPORTED      # one expert beyond 32-bit offsets

@@ -178,6 +178,8 @@ FP8_SMALL = [
     synth.shrink(synth.FP8_MTP4, E=37, T=7, k=5, H=320, I=144, seed=41),     # 35 rows, ragged N
     synth.shrink(synth.FP8_MTP4, E=8, T=2, k=2, H=2304, I=96, seed=42),      # K = 2304: two k passes
     synth.shrink(synth.FP8_MTP4, E=16, T=64, k=1, H=256, I=64, seed=43),     # up to 64 rows per expert
+    synth.shrink(synth.FP8_MTP4, E=24, T=48, k=4, H=512, I=256, seed=47),    # 192 rows: prefill-sized batch
+    synth.shrink(synth.FP8_MTP4, E=8, T=40, k=2, H=1024, I=160, seed=48),    # 80 rows, ragged N, 4 columns per lane row
     synth.with_rows(synth.FP8_MTP4, 1, "fp8_T1"),
     synth.FP8_MTP4,
     synth.with_rows(synth.FP8_MTP4, 8, "fp8_T8"),

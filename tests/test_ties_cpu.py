@@ -80,7 +80,14 @@ def test_large_value_set_to_zero_is_rejected(case):
 def test_two_ulps_at_a_tie_is_rejected(case):
     L, off, p2e, h_ref, u_ref, h32 = case
     hf, dh, floor = h_error_bound(L, u_ref, None, off, p2e)
-    i = tuple(np.argwhere((h32 != h_ref) & (np.abs(hf) > floor))[0])
+    # the differing (tie) element whose float32 bound is tightest against its
+    # bf16 ulp: the exact value lies within dh of the midpoint, so a value two
+    # ulps from the oracle's is >= 1.5 ulp - dh from it, outside the accepted
+    # dh + ulp/2 whenever dh < ulp/2
+    cand = np.argwhere((h32 != h_ref) & (np.abs(hf) > floor))
+    ulp = np.ldexp(1.0, np.frexp(codecs.bf16_to_f64(h_ref))[1] - 8)
+    i = tuple(min(cand, key=lambda c: dh[tuple(c)] / ulp[tuple(c)]))
+    assert dh[i] < 0.4 * ulp[i]
     bad = h32.copy()
     bad[i] = _step(h_ref[i], 2 * int(np.sign(bf16_order(h32[i]) - bf16_order(h_ref[i]))))
     with pytest.raises(AssertionError, match="rounding tie"):

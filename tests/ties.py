@@ -66,19 +66,22 @@ def h_error_bound(L, u_ref, oact, off, p2e):
 
 
 def h_roundings_differ_only_at_ties(L, g_h, h_ref, u_ref, oact, off, p2e):
-    """Every element where the GPU's h differs from the oracle's must be either a
-    rounding tie (one ulp away, the exact value within the float32 error bound of
-    the midpoint) or a float32 underflow (exact and GPU values both under the
-    floor of h_error_bound).  Returns the number of differing elements."""
+    """Every element where the GPU's h differs from the oracle's must be a
+    correct rounding of some float32 evaluation within the error bound: its
+    bf16 value within dh (the float32 bound of h_error_bound) plus half a bf16
+    ulp (the final rounding) of the exact value -- a rounding tie is the
+    common case, several ulps occur only where dh itself spans them (a linear
+    value that is a near-cancellation) -- or a float32 underflow (exact and
+    GPU values both under the floor of h_error_bound).  Returns the number of
+    differing elements."""
     diff = np.asarray(g_h) != np.asarray(h_ref)
     if not diff.any():
         return 0
     hf, dh, floor = h_error_bound(L, u_ref, oact, off, p2e)
     gv = codecs.bf16_to_f64(g_h)
-    one_ulp = np.abs(bf16_order(g_h) - bf16_order(h_ref)) == 1
-    mid = 0.5 * (gv + codecs.bf16_to_f64(h_ref))
-    tie = one_ulp & (np.abs(hf - mid) <= dh)
+    half_ulp = np.ldexp(1.0, np.frexp(np.where(gv == 0, 2.0 ** -133, gv))[1] - 9)   # half of bf16's 2^(e-8) spacing
+    within = np.abs(gv - hf) <= dh + half_ulp
     under = (np.abs(hf) <= floor) & (np.abs(gv) <= floor)
-    bad = diff & ~(tie | under)
+    bad = diff & ~(within | under)
     assert not bad.any(), ("h differs beyond a rounding tie", np.argwhere(bad)[:8].tolist())
     return int(diff.sum())
