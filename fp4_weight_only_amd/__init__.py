@@ -79,8 +79,8 @@ def _load():
         "qmoe_fp4_gemv_fc2_finalize": [P, I32, I32, W, P, P, P, P, P, SZ, I32, P],
         "qmoe_finalize": [P, P, P, I32, I32, I32, P, P],
         "qmoe_dequant_fp4": [W, P, P],
-        "qmoe_fp8_gemv_fc1_swiglu": [P, I32, I32, W8, P, P, ctypes.POINTER(SwigluC), P, P, SZ, P],
-        "qmoe_fp8_gemv_fc2": [P, I32, I32, W8, P, P, P, SZ, P],
+        "qmoe_fp8_gemv_fc1_swiglu": [P, I32, I32, W8, P, P, ctypes.POINTER(SwigluC), P, P, SZ, I32, P],
+        "qmoe_fp8_gemv_fc2": [P, I32, I32, W8, P, P, P, SZ, I32, P],
         "qmoe_dequant_fp8": [W8, P, P],
     }
     for name, args in sig.items():
@@ -214,35 +214,35 @@ def qmoe_dequant_fp4(w: FP4Weights, out, stream=None):
     _check("qmoe_dequant_fp4", lib.qmoe_dequant_fp4(ctypes.byref(wc), _ptr(out), _stream(stream)))
 
 
-def fp8_workspace_bytes(which: int, T: int, k: int, w: FP8Weights, act=None) -> int:
+def fp8_workspace_bytes(which: int, T: int, k: int, w: FP8Weights, act=None, path=QMOE_PATH_AUTO) -> int:
     """Workspace size of qmoe_fp8_gemv_fc1_swiglu (which=1, with its act) or qmoe_fp8_gemv_fc2 (which=2)."""
     n = ctypes.c_size_t(0)
     wc = w.c()
     dummy = 256
     if which == 1:
         st = lib.qmoe_fp8_gemv_fc1_swiglu(dummy, T, k, ctypes.byref(wc), dummy, dummy, _swiglu(act), dummy, None,
-                                          ctypes.byref(n), None)
+                                          ctypes.byref(n), path, None)
     else:
-        st = lib.qmoe_fp8_gemv_fc2(dummy, T, k, ctypes.byref(wc), dummy, dummy, None, ctypes.byref(n), None)
+        st = lib.qmoe_fp8_gemv_fc2(dummy, T, k, ctypes.byref(wc), dummy, dummy, None, ctypes.byref(n), path, None)
     _check("fp8_workspace_bytes", st)
     return n.value
 
 
 def qmoe_fp8_gemv_fc1_swiglu(x, k, w1: FP8Weights, expert_offsets, perm_to_expanded, h, ws, act=None,
-                             stream=None):
+                             path=QMOE_PATH_AUTO, stream=None):
     T = x.shape[0]
     wc = w1.c()
     n = ctypes.c_size_t(ws.numel() * ws.element_size())
     _check("qmoe_fp8_gemv_fc1_swiglu", lib.qmoe_fp8_gemv_fc1_swiglu(
         _ptr(x), T, k, ctypes.byref(wc), _ptr(expert_offsets), _ptr(perm_to_expanded), _swiglu(act), _ptr(h),
-        _ptr(ws), ctypes.byref(n), _stream(stream)))
+        _ptr(ws), ctypes.byref(n), path, _stream(stream)))
 
 
-def qmoe_fp8_gemv_fc2(h, T, k, w2: FP8Weights, expert_offsets, y_rows, ws, stream=None):
+def qmoe_fp8_gemv_fc2(h, T, k, w2: FP8Weights, expert_offsets, y_rows, ws, path=QMOE_PATH_AUTO, stream=None):
     wc = w2.c()
     n = ctypes.c_size_t(ws.numel() * ws.element_size())
     _check("qmoe_fp8_gemv_fc2", lib.qmoe_fp8_gemv_fc2(
-        _ptr(h), T, k, ctypes.byref(wc), _ptr(expert_offsets), _ptr(y_rows), _ptr(ws), ctypes.byref(n),
+        _ptr(h), T, k, ctypes.byref(wc), _ptr(expert_offsets), _ptr(y_rows), _ptr(ws), ctypes.byref(n), path,
         _stream(stream)))
 
 

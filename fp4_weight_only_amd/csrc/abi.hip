@@ -97,7 +97,8 @@ qmoe_status run_fc(GemvArgs &a, const qmoe_fp4_weights *w, int max_rows, qmoe_pa
 }
 
 qmoe_status check_fp8_fc(const qmoe_fp8_weights *w, int32_t T, int32_t k, const void *act, const void *offsets,
-                         const void *out, FcShape *shape) {
+                         const void *out, qmoe_path path, FcShape *shape, qmoe_path *resolved) {
+  if (path != QMOE_PATH_AUTO && path != QMOE_PATH_GEMV && path != QMOE_PATH_GROUPED) return QMOE_EINVAL;
   if (!w || !w->w || !w->gscale || !act || !offsets || !out) return QMOE_EINVAL;
   if (T < 1 || k < 1 || w->E < 1 || w->K < 1 || w->N < 1 || k > w->E) return QMOE_EINVAL;
   if (!aligned16(w->w) || !aligned16(w->gscale) || !aligned16(act) || !aligned16(offsets) || !aligned16(out))
@@ -110,11 +111,18 @@ qmoe_status check_fp8_fc(const qmoe_fp8_weights *w, int32_t T, int32_t k, const 
   if (rows > (1 << 24)) return QMOE_EUNSUPPORTED;
   shape->rows = (int32_t)rows;
   shape->max_rows_per_expert = T;
+  // AUTO: the grouped MFMA kernel beyond the decode window when K % 64 == 0
+  qmoe_path p = path;
+  if (p == QMOE_PATH_AUTO) p = (rows <= QMOE_GEMV_MAX_ROWS || w->K % 64 != 0) ? QMOE_PATH_GEMV : QMOE_PATH_GROUPED;
+  if (p == QMOE_PATH_GROUPED && w->K % 64 != 0) return QMOE_EUNSUPPORTED;
+  // the grouped kernel addresses the activations of a call in 32 bits
+  if (p == QMOE_PATH_GROUPED && rows * w->K * 2 >= ((int64_t)1 << 31)) return QMOE_EUNSUPPORTED;
+  *resolved = p;
   return QMOE_OK;
 }
 
-qmoe_status run_fp8(GemvArgs &a, const qmoe_fp8_weights *w, int max_rows, void *ws, size_t *ws_bytes,
-                    hipStream_t stream) {
+qmoe_status run_fp8(GemvArgs &a, const qmoe_fp8_weights *w, int max_rows, qmoe_path path, void *ws,
+                    size_t *ws_bytes, hipStream_t stream) {
   const size_t need = fp8_workspace_bytes(a.rows, w->N, a.concat != 0);
   if (!ws_bytes) return QMOE_EINVAL;
   if (!ws) {
@@ -128,6 +136,7 @@ qmoe_status run_fp8(GemvArgs &a, const qmoe_fp8_weights *w, int max_rows, void *
   a.E = w->E;
   a.K = w->K;
   a.N = w->N;
+  if (path == QMOE_PATH_GROUPED) return check_launch(launch_fp8_grouped(a, ws, stream));
   return check_launch(launch_fp8_gemv(a, max_rows, ws, stream));
 }
 
@@ -305,9 +314,10 @@ qmoe_status qmoe_dequant_fp4(const qmoe_fp4_weights *w, uint16_t *out, hipStream
 qmoe_status qmoe_fp8_gemv_fc1_swiglu(const uint16_t *x, int32_t T, int32_t k, const qmoe_fp8_weights *w1,
                                      const int32_t *expert_offsets, const int32_t *perm_to_expanded,
                                      const qmoe_swiglu *act, uint16_t *h, void *ws, size_t *ws_bytes,
-                                     hipStream_t stream) {
+                                     qmoe_path path, hipStream_t stream) {
   FcShape sh;
-  qmoe_status st = check_fp8_fc(w1, T, k, x, expert_offsets, h, &sh);
+  qmoe_path p;
+  qmoe_status st = check_fp8_fc(w1, T, k, x, expert_offsets, h, path, &sh, &p);
   if (st != QMOE_OK) return st;
   if (!perm_to_expanded) return QMOE_EINVAL;
   if (!aligned16(perm_to_expanded)) return QMOE_EALIGN;
@@ -325,14 +335,15 @@ qmoe_status qmoe_fp8_gemv_fc1_swiglu(const uint16_t *x, int32_t T, int32_t k, co
   if (fusion != 0 && fusion != QMOE_SWIGLU_INTERLEAVED && fusion != QMOE_SWIGLU_CONCAT) return QMOE_EINVAL;
   a.concat = fusion == QMOE_SWIGLU_CONCAT;
   a.out_bf16 = h;
-  return run_fp8(a, w1, sh.max_rows_per_expert, ws, ws_bytes, stream);
+  return run_fp8(a, w1, sh.max_rows_per_expert, p, ws, ws_bytes, stream);
 }
 
 qmoe_status qmoe_fp8_gemv_fc2(const uint16_t *h, int32_t T, int32_t k, const qmoe_fp8_weights *w2,
                               const int32_t *expert_offsets, float *y_rows, void *ws, size_t *ws_bytes,
-                              hipStream_t stream) {
+                              qmoe_path path, hipStream_t stream) {
   FcShape sh;
-  qmoe_status st = check_fp8_fc(w2, T, k, h, expert_offsets, y_rows, &sh);
+  qmoe_path p;
+  qmoe_status st = check_fp8_fc(w2, T, k, h, expert_offsets, y_rows, path, &sh, &p);
   if (st != QMOE_OK) return st;
   GemvArgs a = {};
   a.act = h;
@@ -341,7 +352,7 @@ qmoe_status qmoe_fp8_gemv_fc2(const uint16_t *h, int32_t T, int32_t k, const qmo
   a.rows = sh.rows;
   a.fc1 = 0;
   a.out_f32 = y_rows;
-  return run_fp8(a, w2, sh.max_rows_per_expert, ws, ws_bytes, stream);
+  return run_fp8(a, w2, sh.max_rows_per_expert, p, ws, ws_bytes, stream);
 }
 
 qmoe_status qmoe_dequant_fp8(const qmoe_fp8_weights *w, uint16_t *out, hipStream_t stream) {

@@ -137,6 +137,57 @@ __device__ __forceinline__ float swiglu(float gate, float lin, float alpha, floa
   return G / (1.0f + expf(-alpha * G)) * (L + beta);
 }
 
+// Finds the s-th (expert, m tile) item: experts in ascending order, each with
+// ceil(rows/BM) tiles.  Returns the expert (-1 past the last item) and the
+// tile index inside it.  Every lane gets the same answer.
+template <int BM>
+__device__ __forceinline__ int find_mtile(const int32_t *__restrict__ off, int E, int s, int &mt) {
+  const int lane = lane_id();
+  int o[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int e = 4 * lane + i;
+    o[i] = (e <= E) ? off[e] : 0;
+  }
+  int cnt[4], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    cnt[i] = (4 * lane + i < E) ? (o[i + 1] - o[i] + BM - 1) / BM : 0;
+    sum += cnt[i];
+  }
+  int incl = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
+  }
+  int run = incl - sum;
+  int found = -1, tile = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (s >= run && s < run + cnt[i]) {
+      found = 4 * lane + i;
+      tile = s - run;
+    }
+    run += cnt[i];
+  }
+  const unsigned long long fb = __ballot(found >= 0);
+  if (fb == 0ull) return -1;
+  const int src = __ffsll((long long)fb) - 1;
+  mt = __builtin_amdgcn_readlane(tile, src);
+  return __builtin_amdgcn_readlane(found, src);
+}
+
+// A wave-uniform pointer, moved to scalar registers (a buffer resource built
+// from it stays scalar; otherwise the compiler wraps every buffer load in a
+// waterfall loop).
+__device__ __forceinline__ void *uniform_ptr(const void *p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (void *)(((uint64_t)hi << 32) | lo);
+}
+
 // Workgroup barrier that orders LDS accesses only: __syncthreads() also
 // waits for the wave's outstanding global loads (its fence covers every
 // address space), which would stall on loads meant to stay in flight.

@@ -174,6 +174,188 @@ __global__ __launch_bounds__(kF8Waves * 64) void fp8_gemv_kernel(GemvArgs a) {
   }
 }
 
+// ---- prefill: grouped GEMM with bf16 MFMA ------------------------------------
+// Work item = (expert, 64-row m tile, 256-column n tile) as on the FP4
+// grouped path; 8 waves, wave w owns columns 32w..32w+31 (two 16-column MFMA
+// tiles) for every live 16-row sub-tile, v_mfma_f32_16x16x32_bf16, K in
+// 64-k slices.  The [N][K] layout gives each MFMA B operand (8 consecutive k
+// of one column) as 8 contiguous bytes: a column's 64 bytes of a slice are
+// copied into LDS (8-byte units XOR-swizzled by column), read back with one
+// ds_read_b64 per operand and converted with four exact FP8 -> bf16
+// conversions.  Global loads run two slices ahead in registers, LDS is
+// double buffered; the global scale multiplies the accumulator.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kF8BM = 64, kF8BN = 256, kF8BK = 64;
+constexpr int kF8GWaves = 8;
+
+struct F8GroupedSmem {
+  u32x4_t a[2][kF8BM][kF8BK / 8];   // activations, 16-byte chunk c of row r at c ^ (r & 7)
+  uint8_t b[2][kF8BN][kF8BK];       // weight bytes, 8-byte unit u of column n at u ^ (n & 7)
+};
+
+struct F8SliceRegs {
+  u32x4_t A;      // activation row ra, k = 8 * aq .. +7
+  u32x4_t B[2];   // columns cb and cb + 128, bytes 16 * bq .. +15 of the slice
+};
+
+__device__ __forceinline__ bf16x8_t fp8_operand(u32x2_t d) {
+  u32x4_t o;
+  o.x = fp8x2_lo(d.x);
+  o.y = fp8x2_hi(d.x);
+  o.z = fp8x2_lo(d.y);
+  o.w = fp8x2_hi(d.y);
+  return __builtin_bit_cast(bf16x8_t, o);
+}
+
+__global__ __launch_bounds__(kF8GWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void fp8_grouped_kernel(
+    GemvArgs a) {
+  __shared__ __attribute__((aligned(16))) F8GroupedSmem sm;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = lane_id();
+
+  // XCD-aware decode: the n tiles of one (expert, m tile) are consecutive
+  // items on one XCD
+  const int per = gridDim.x >> 3;
+  const int q = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  const int slot = q / a.ntiles;
+  const int ntile = q - slot * a.ntiles;
+  if (slot >= a.nslots) return;
+  int mt = 0;
+  const int ef = find_mtile<kF8BM>(a.offsets, a.E, slot, mt);
+  if (ef < 0) return;  // uniform over the workgroup
+  const int e = __builtin_amdgcn_readfirstlane(ef);
+  mt = __builtin_amdgcn_readfirstlane(mt);
+  const int row0 = a.offsets[e] + mt * kF8BM;
+  const int mrows = min(kF8BM, a.offsets[e + 1] - row0);
+  const int n0 = ntile * kF8BN;
+  const int steps = a.K / kF8BK;  // K % 64 == 0 on this path
+
+  // loaders (buffer loads; fixed vector offsets, the slice in the scalar offset)
+  const int ra = tid >> 3, aq = tid & 7;
+  const int act_rows = a.fc1 ? a.rows / a.topk : a.rows;
+  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+      uniform_ptr(a.act), (short)0, (int)((uint32_t)act_rows * (uint32_t)a.K * 2u), 0x00020000);
+  uint32_t avoff = kF8OutOfRange;
+  if (ra < mrows) {
+    const int p = row0 + ra;
+    const int src = a.fc1 ? (a.p2e[p] / a.topk) : p;
+    avoff = (uint32_t)src * (uint32_t)a.K * 2u + (uint32_t)(aq * 16);
+  }
+  const int cb = tid >> 2, bq = tid & 3;  // columns cb, cb + 128; 16 bytes bq of 64
+  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      uniform_ptr(a.w + (size_t)e * a.N * a.K), (short)0, (int)((uint32_t)a.N * (uint32_t)a.K), 0x00020000);
+  uint32_t bvoff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int col = n0 + cb + 128 * j;
+    bvoff[j] = col < a.N ? (uint32_t)col * (uint32_t)a.K + (uint32_t)(bq * 16) : kF8OutOfRange;
+  }
+  auto load_slice = [&](int s, F8SliceRegs &r) {
+    const int k0 = s * kF8BK;
+    r.A = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(arsrc, avoff, k0 * 2, 0));
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      r.B[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, bvoff[j], k0, 2));
+  };
+  auto store_slice = [&](int buf, const F8SliceRegs &r) {
+    sm.a[buf][ra][aq ^ (ra & 7)] = r.A;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = cb + 128 * j;
+      *(u32x2_t *)&sm.b[buf][n][8 * ((2 * bq) ^ (n & 7))] = u32x2_t{r.B[j].x, r.B[j].y};
+      *(u32x2_t *)&sm.b[buf][n][8 * ((2 * bq + 1) ^ (n & 7))] = u32x2_t{r.B[j].z, r.B[j].w};
+    }
+  };
+
+  // MFMA roles: lane (lk, li) -> column li of a 16-column tile, k 8 lk .. +7 of a 32-k group
+  const int li = lane & 15, lk = lane >> 4;
+  const int live = (mrows + 15) >> 4;
+  const bool wave_cols = n0 + wave * 32 < a.N;  // uniform (N % 32 == 0)
+  f32x4_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute_slice = [&](int buf) {
+    if (!wave_cols) return;
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg) {
+      const int unit = kg * 4 + lk;  // 8-byte unit of the column's 64 bytes
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int n = wave * 32 + t * 16 + li;
+        const bf16x8_t bv = fp8_operand(*(const u32x2_t *)&sm.b[buf][n][8 * (unit ^ (n & 7))]);
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms) {
+          if (ms >= live) break;  // uniform
+          const int r = ms * 16 + li;
+          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, sm.a[buf][r][unit ^ (r & 7)]);
+          acc[ms][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[ms][t], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  F8SliceRegs r0, r1;
+  load_slice(0, r0);
+  if (steps > 1) load_slice(1, r1);
+  for (int s = 0; s < steps; s += 2) {
+    store_slice(0, r0);
+    if (s + 2 < steps) load_slice(s + 2, r0);
+    __syncthreads();
+    compute_slice(0);
+    if (s + 1 >= steps) break;
+    store_slice(1, r1);
+    if (s + 3 < steps) load_slice(s + 3, r1);
+    __syncthreads();
+    compute_slice(1);
+  }
+
+  // epilogue: lane holds rows 4 lk + i, column li of each 16-column tile
+  if (!wave_cols) return;
+  const float gs = a.gscale[e];
+#pragma unroll
+  for (int ms = 0; ms < 4; ++ms) {
+    if (ms >= live) break;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int col = n0 + wave * 32 + t * 16 + li;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = ms * 16 + lk * 4 + i;
+        const float u = gs * acc[ms][t][i];
+        if (a.fc1 && !a.concat) {
+          const float partner = __uint_as_float(dpp_u32<kDppXor1>(__float_as_uint(u)));
+          if (r < mrows && (lane & 1) == 0)
+            a.out_bf16[(size_t)(row0 + r) * (a.N >> 1) + (col >> 1)] =
+                (uint16_t)bf16_rne(swiglu(u, partner, a.alpha, a.beta, a.limit));
+        } else if (r < mrows) {
+          a.out_f32[(size_t)(row0 + r) * a.N + col] = u;
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_fp8_grouped(GemvArgs &a, void *ws, hipStream_t s) {
+  const int erows = a.rows < a.E ? a.rows : a.E;
+  a.nslots = (a.rows + kF8BM - 1) / kF8BM + erows;  // worst-case (expert, m tile) count
+  a.ntiles = (a.N + kF8BN - 1) / kF8BN;
+  const int items = a.nslots * a.ntiles;
+  const dim3 grid((unsigned)(((items + 7) / 8) * 8));
+  if (a.concat) a.out_f32 = (float *)ws;
+  fp8_grouped_kernel<<<grid, kF8GWaves * 64, 0, s>>>(a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || !a.concat) return err;
+  a.partials = (float *)ws;
+  a.nchunks = 1;
+  return launch_splitk_epilogue(a, s);
+}
+
 size_t fp8_workspace_bytes(int32_t rows, int32_t N, bool concat) {
   const size_t u = concat ? (size_t)rows * N * sizeof(float) : 0;
   return u > 256 ? u : 256;

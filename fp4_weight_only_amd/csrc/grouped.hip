@@ -62,56 +62,6 @@ struct GroupedSmem {
   uint8_t sc[2][kBK / 16][kBN];     // block scales of the slice (B = 32 uses 4 rows)
 };
 
-// Finds the s-th (expert, m tile) item: experts in ascending order, each with
-// ceil(rows/64) tiles.  Returns the expert (-1 past the last item) and the
-// tile index inside it.  Every lane gets the same answer.
-__device__ __forceinline__ int find_mtile(const int32_t *__restrict__ off, int E, int s, int &mt) {
-  const int lane = lane_id();
-  int o[5];
-#pragma unroll
-  for (int i = 0; i < 5; ++i) {
-    const int e = 4 * lane + i;
-    o[i] = (e <= E) ? off[e] : 0;
-  }
-  int cnt[4], sum = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    cnt[i] = (4 * lane + i < E) ? (o[i + 1] - o[i] + kBM - 1) / kBM : 0;
-    sum += cnt[i];
-  }
-  int incl = sum;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int v = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += v;
-  }
-  int run = incl - sum;
-  int found = -1, tile = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (s >= run && s < run + cnt[i]) {
-      found = 4 * lane + i;
-      tile = s - run;
-    }
-    run += cnt[i];
-  }
-  const unsigned long long fb = __ballot(found >= 0);
-  if (fb == 0ull) return -1;
-  const int src = __ffsll((long long)fb) - 1;
-  mt = __builtin_amdgcn_readlane(tile, src);
-  return __builtin_amdgcn_readlane(found, src);
-}
-
-// A wave-uniform pointer, moved to scalar registers (a buffer resource built
-// from it stays scalar; otherwise the compiler wraps every buffer load in a
-// waterfall loop).
-__device__ __forceinline__ void *uniform_ptr(const void *p) {
-  const uint64_t v = (uint64_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (void *)(((uint64_t)hi << 32) | lo);
-}
-
 __device__ __forceinline__ float grouped_swiglu(float gate, float lin, float alpha, float beta, float limit) {
   const float G = fminf(gate, limit);
   const float L = fminf(fmaxf(lin, -limit), limit);
@@ -167,7 +117,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   const int ntile = q - slot * a.ntiles;
   if (slot >= a.nslots) return;
   int mt = 0;
-  const int ef = find_mtile(a.offsets, a.E, slot, mt);
+  const int ef = find_mtile<kBM>(a.offsets, a.E, slot, mt);
   if (ef < 0) return;  // uniform over the workgroup
   // the expert is wave-uniform; saying so keeps the buffer resources in
   // scalar registers (no per-load waterfall loops)

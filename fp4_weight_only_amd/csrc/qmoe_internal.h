@@ -48,6 +48,7 @@ hipError_t launch_grouped(GemvArgs &a, int fmt, hipStream_t s);
 // uses ws for float32 u rows) and dequant.
 size_t fp8_workspace_bytes(int32_t rows, int32_t N, bool concat);
 hipError_t launch_fp8_gemv(GemvArgs &a, int max_rows_per_expert, void *ws, hipStream_t s);
+hipError_t launch_fp8_grouped(GemvArgs &a, void *ws, hipStream_t s);  // K % 64 == 0
 hipError_t launch_fp8_dequant(const uint8_t *w, const float *g, int32_t E, int32_t K, int32_t N, uint16_t *out,
                               hipStream_t s);
 

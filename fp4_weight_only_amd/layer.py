@@ -3,7 +3,7 @@
 
 Buffers are allocated once per shape; run() enqueues the four calls on the
 current stream and allocates nothing.  The FC weights are FP4Weights
-(NVFP4/MXFP4) or FP8Weights (W8A16, decode path only).
+(NVFP4/MXFP4) or FP8Weights (W8A16).
 """
 from __future__ import annotations
 
@@ -31,7 +31,7 @@ class MoELayer:
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         self.fp8 = isinstance(w1, FP8Weights)
         if self.fp8:
-            need = max(fp8_workspace_bytes(1, T, k, w1, act), fp8_workspace_bytes(2, T, k, w2))
+            need = max(fp8_workspace_bytes(1, T, k, w1, act, path), fp8_workspace_bytes(2, T, k, w2, None, path))
         else:
             need = max(fc_workspace_bytes(1, T, k, w1, path, act), fc_workspace_bytes(2, T, k, w2, path),
                        fc_workspace_bytes(3, T, k, w2, path))
@@ -49,14 +49,15 @@ class MoELayer:
 
     def fc1(self, x):
         if self.fp8:
-            qmoe_fp8_gemv_fc1_swiglu(x, self.k, self.w1, self.offsets, self.p2e, self.h, self.ws, self.act)
+            qmoe_fp8_gemv_fc1_swiglu(x, self.k, self.w1, self.offsets, self.p2e, self.h, self.ws, self.act,
+                                     self.path)
         else:
             qmoe_fp4_gemv_fc1_swiglu(x, self.k, self.w1, self.offsets, self.p2e, self.h, self.ws, self.act,
                                      self.path)
 
     def fc2(self):
         if self.fp8:
-            qmoe_fp8_gemv_fc2(self.h, self.T, self.k, self.w2, self.offsets, self.y, self.ws)
+            qmoe_fp8_gemv_fc2(self.h, self.T, self.k, self.w2, self.offsets, self.y, self.ws, self.path)
         else:
             qmoe_fp4_gemv_fc2(self.h, self.T, self.k, self.w2, self.offsets, self.y, self.ws, self.path)
 

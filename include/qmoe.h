@@ -284,11 +284,12 @@ qmoe_status qmoe_dequant_fp4(const qmoe_fp4_weights *w, uint16_t *out, hipStream
  * Arguments, outputs and row order as qmoe_fp4_gemv_fc1_swiglu and
  * qmoe_fp4_gemv_fc2, with w1 (K = H, N = 2*I) or w2 (K = I, N = H) in the FP8
  * layout.  u[p][n] = gscale(e) * sum_k x[k] * e4m3(w[e][n][k]), accumulated in
- * float32.  One GEMV path for every batch (no path argument): rows go in
- * passes of up to 8 per expert, so prefill batches work but re-read an
- * expert's weights from cache once per 8 rows.  The workspace is needed only
- * for the concatenated SwiGLU layout (float32 u rows); the size query
- * convention is the FP4 calls'.
+ * float32.  path: GEMV (any batch; rows in passes of up to 8 per expert),
+ * GROUPED (bf16 MFMA grouped GEMM for prefill batches; K % 64 == 0 and
+ * T*k*K*2 < 2^31, else QMOE_EUNSUPPORTED) or AUTO (GEMV up to 64 rows or
+ * when K % 64 != 0, else GROUPED).  The workspace is needed only for the
+ * concatenated SwiGLU layout (float32 u rows); the size query convention is
+ * the FP4 calls'.
  * Limits: K % 16 == 0, N % 32 == 0, K*N < 2^31, E <= 256, k <= 8, T*k <= 2^24
  * (QMOE_EUNSUPPORTED); NULL w or gscale: QMOE_EINVAL.
  */
@@ -296,10 +297,10 @@ qmoe_status qmoe_fp8_gemv_fc1_swiglu(const uint16_t *x, int32_t T, int32_t k,
                                      const qmoe_fp8_weights *w1,
                                      const int32_t *expert_offsets, const int32_t *perm_to_expanded,
                                      const qmoe_swiglu *act, uint16_t *h,
-                                     void *ws, size_t *ws_bytes, hipStream_t stream);
+                                     void *ws, size_t *ws_bytes, qmoe_path path, hipStream_t stream);
 qmoe_status qmoe_fp8_gemv_fc2(const uint16_t *h, int32_t T, int32_t k,
                               const qmoe_fp8_weights *w2, const int32_t *expert_offsets,
-                              float *y_rows, void *ws, size_t *ws_bytes, hipStream_t stream);
+                              float *y_rows, void *ws, size_t *ws_bytes, qmoe_path path, hipStream_t stream);
 
 /*
  * qmoe_dequant_fp8 -- FP8 weights to bf16 (operator documentation section

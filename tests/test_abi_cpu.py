@@ -171,9 +171,11 @@ def test_fp8_validation_and_workspace(q):
     L = q.lib
     W8 = lambda E=16, K=256, N=512, w=A, g=A: q.Fp8WeightsC(w, g, E, K, N)
     n = ctypes.c_size_t(0)
-    fc1 = lambda wc, T=2, k=2, act=None, x=A, p2e=A: L.qmoe_fp8_gemv_fc1_swiglu(
-        x, T, k, ctypes.byref(wc), A, p2e, None if act is None else ctypes.byref(act), A, None, ctypes.byref(n), None)
-    fc2 = lambda wc, T=2, k=2, y=A: L.qmoe_fp8_gemv_fc2(A, T, k, ctypes.byref(wc), A, y, None, ctypes.byref(n), None)
+    fc1 = lambda wc, T=2, k=2, act=None, x=A, p2e=A, path=0: L.qmoe_fp8_gemv_fc1_swiglu(
+        x, T, k, ctypes.byref(wc), A, p2e, None if act is None else ctypes.byref(act), A, None, ctypes.byref(n),
+        path, None)
+    fc2 = lambda wc, T=2, k=2, y=A, path=0: L.qmoe_fp8_gemv_fc2(A, T, k, ctypes.byref(wc), A, y, None,
+                                                                  ctypes.byref(n), path, None)
     assert fc1(W8()) == q.QMOE_OK and n.value == 256             # interleaved: no workspace beyond the minimum
     assert fc1(W8(), act=q.SwigluC(1.0, 0.0, float("inf"), q.QMOE_SWIGLU_CONCAT)) == q.QMOE_OK
     assert n.value >= 4 * 512 * 4                                # concatenated: float32 u rows
@@ -191,6 +193,10 @@ def test_fp8_validation_and_workspace(q):
     assert fc1(W8(K=65536, N=32768)) == q.QMOE_EUNSUPPORTED      # one expert beyond 32-bit offsets
     assert fc2(W8(), y=None) == q.QMOE_EINVAL
     assert fc2(W8()) == q.QMOE_OK
+    assert fc1(W8(), path=7) == q.QMOE_EINVAL
+    assert fc1(W8(K=272), T=32, k=4, path=q.QMOE_PATH_GROUPED) == q.QMOE_EUNSUPPORTED   # K % 64
+    assert fc1(W8(K=272), T=32, k=4) == q.QMOE_OK                                      # AUTO falls back to the GEMV
+    assert fc1(W8(), T=32, k=4, path=q.QMOE_PATH_GROUPED) == q.QMOE_OK
     dq = lambda wc, out=A: L.qmoe_dequant_fp8(ctypes.byref(wc), out, None)
     assert dq(W8(g=0)) == q.QMOE_EINVAL
     assert dq(W8(), out=MIS) == q.QMOE_EALIGN

@@ -198,6 +198,30 @@ def test_fp8_concat_and_gptoss(act):
     check_layer(synth.layer_inputs(cfg), act=act)
 
 
+FP8_GROUPED = synth.shrink(synth.FP8_MTP4, E=24, T=48, k=4, H=512, I=256, seed=49)     # 192 rows
+
+
+@pytest.mark.parametrize("path", ["gemv", "grouped"])
+def test_fp8_same_shape_both_paths(path):
+    import fp4_weight_only_amd as q
+    p = q.QMOE_PATH_GEMV if path == "gemv" else q.QMOE_PATH_GROUPED
+    check_layer(synth.layer_inputs(FP8_GROUPED), path=p)
+
+
+@pytest.mark.parametrize("act", [STD, GPTOSS], ids=["std", "gptoss"])
+def test_fp8_grouped_concat_and_gptoss(act):
+    check_layer(synth.layer_inputs(FP8_GROUPED), act=act + (2,))
+    check_layer(synth.layer_inputs(FP8_GROUPED), act=act)
+
+
+def test_fp8_grouped_multi_tile():
+    # 1024 rows over 64 experts (several 64-row m tiles per expert), K = 1024:
+    # a K loop of 16 slices, N = 1024 and 1024: four n tiles
+    cfg = synth.dataclasses.replace(synth.shrink(synth.FP8_MTP4, E=64, T=256, k=4, H=1024, I=512, seed=50),
+                                    routing="zipf")
+    check_layer(synth.layer_inputs(cfg))
+
+
 def test_fp8_every_finite_byte_through_the_gemv():
     # every finite E4M3 byte at every lane position of a 16-byte load
     cfg = synth.shrink(synth.FP8_MTP4, E=2, T=2, k=1, H=512, I=128, seed=45)
