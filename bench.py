@@ -17,8 +17,9 @@ Other workloads (--workload): decode / mtp8 / mx_decode (same layer path),
 prefill (MXFP4 512 tokens, grouped-GEMM path; also reports TFLOP/s and the
 fraction of the bf16 MFMA peak), dequant (MXFP4 standalone dequant, GB/s on
 read + write bytes), fp8 (the MTP-verify layer with FP8 E4M3 W8A16 weights:
-qmoe_fp8_gemv_fc1_swiglu -> qmoe_fp8_gemv_fc2 -> qmoe_finalize), fp8_dequant
-(FP8 standalone dequant at the dequant workload's shape).  --calibrate-copy runs a plain device-to-device copy of
+qmoe_fp8_gemv_fc1_swiglu -> qmoe_fp8_gemv_fc2 -> qmoe_finalize), fp8_prefill
+(the prefill layer with FP8 weights, grouped MFMA path), fp8_dequant (FP8
+standalone dequant at the dequant workload's shape).  --calibrate-copy runs a plain device-to-device copy of
 known size, the reference kernel for scaling HBM traffic counters.
 
 roofline: the dominant kernel of the workload (FC1 for the layer workloads,
@@ -48,7 +49,7 @@ METRIC = "NVFP4 MoE decode GEMV µs/layer + achieved HBM GB/s (% of peak), 4–6
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 CSRC = os.path.join(ROOT, "fp4_weight_only_amd", "csrc")
-LAYER_WORKLOADS = ("mtp4", "mtp8", "decode", "mx_decode", "prefill", "fp8")
+LAYER_WORKLOADS = ("mtp4", "mtp8", "decode", "mx_decode", "prefill", "fp8", "fp8_prefill")
 
 
 def parse():
@@ -149,8 +150,8 @@ def bench_layer(args, torch, q, synth, np):
     from fp4_weight_only_amd.layer import MoELayer
 
     cfg = {"mtp4": synth.MTP4, "mtp8": synth.MTP8, "decode": synth.DECODE, "mx_decode": synth.MX_DECODE,
-           "prefill": synth.MX_PREFILL, "fp8": synth.FP8_MTP4}[args.workload]
-    prefill = args.workload == "prefill"
+           "prefill": synth.MX_PREFILL, "fp8": synth.FP8_MTP4, "fp8_prefill": synth.FP8_PREFILL}[args.workload]
+    prefill = args.workload in ("prefill", "fp8_prefill")
     fp8 = cfg.fmt == synth.FP8
     # distinct weight copies: > 256 MB Infinity Cache worth of selected experts
     layers = 40 if cfg.fmt == synth.NVFP4 else (2 if prefill else (16 if fp8 else 8))
@@ -210,7 +211,11 @@ def bench_layer(args, torch, q, synth, np):
     fc1_gbs = fc1_bytes / (fc1_ms * 1e-3) / 1e9
     layer.set_weights(*copies[0])
 
-    if prefill:
+    if prefill and fp8:
+        sources = ("fp8.hip", "device_common.h", "qmoe_internal.h")
+        kname, tname = "fp8_grouped_kernel (FC1+SwiGLU)", "fp8_grouped_fc1_prefill"
+        metric = "FP8 W8A16 MoE prefill layer µs/layer + achieved HBM GB/s on weight bytes"
+    elif prefill:
         sources = ("grouped.hip", "device_common.h", "qmoe_internal.h")
         kname, tname = "grouped_gemm_kernel (FC1+SwiGLU)", "grouped_fc1_prefill"
         metric = "MXFP4 MoE prefill layer µs/layer + achieved HBM GB/s on weight bytes"
@@ -369,9 +374,13 @@ def cpu_baseline_prefill(L, D, expert_bytes, budget_s):
             lo, hi = int(off[e]), int(off[e + 1])
             if lo == hi:
                 continue
-            u = x64[np.asarray(p2e[lo:hi]) // c.k] @ dequant.dequant_expert_f64(L.w1[e], L.s1[e], None, c.fmt)
+            s1 = None if L.s1 is None else L.s1[e]
+            s2 = None if L.s2 is None else L.s2[e]
+            g1 = None if L.g1 is None else L.g1[e]
+            g2 = None if L.g2 is None else L.g2[e]
+            u = x64[np.asarray(p2e[lo:hi]) // c.k] @ dequant.expert_weights_f64(L.w1[e], s1, g1, c.fmt)
             hb = moe.codecs.bf16_from_f64(moe.swiglu(u[:, 0::2], u[:, 1::2]))
-            moe.codecs.bf16_to_f64(hb) @ dequant.dequant_expert_f64(L.w2[e], L.s2[e], None, c.fmt)
+            moe.codecs.bf16_to_f64(hb) @ dequant.expert_weights_f64(L.w2[e], s2, g2, c.fmt)
             n, rows = n + 1, rows + hi - lo
             if time.perf_counter() - t0 >= budget_s:
                 break

@@ -83,7 +83,8 @@ _FP8_WEIGHT_BYTES = np.array([(s << 7) | (e << 3) | m for s in (0, 1) for e in r
 
 
 def fp8_weight_bytes(g: np.random.Generator, shape) -> np.ndarray:
-    return _FP8_WEIGHT_BYTES[g.integers(0, len(_FP8_WEIGHT_BYTES), size=shape)]
+    # uint8 table indices keep a prefill layer's 6.4 GB draw at one byte per weight
+    return _FP8_WEIGHT_BYTES[g.integers(0, len(_FP8_WEIGHT_BYTES), size=shape, dtype=np.uint8)]
 
 
 def global_scales(g: np.random.Generator, n: int) -> np.ndarray:
@@ -139,8 +140,10 @@ MX_PREFILL = LayerConfig("prefill_mxfp4_T512_E256_top8_H4096_I2048_zipf", MXFP4,
 
 # W8A16 decode at the NVFP4 MTP-verify shape (the pages' FP8 path, sections 6.4 and 10).
 FP8_MTP4 = LayerConfig("mtp_fp8_T4_E256_top8_H2048_I768_hot3", FP8, T=4, E=256, k=8, H=2048, I=768, routing="hot3")
+FP8_PREFILL = LayerConfig("prefill_fp8_T512_E256_top8_H4096_I2048_zipf", FP8, T=512, E=256, k=8, H=4096, I=2048,
+                          routing="zipf")
 
-LAYER_CONFIGS = {c.name: c for c in (TINY, DECODE, MTP4, MTP8, MX_DECODE, MX_PREFILL, FP8_MTP4)}
+LAYER_CONFIGS = {c.name: c for c in (TINY, DECODE, MTP4, MTP8, MX_DECODE, MX_PREFILL, FP8_MTP4, FP8_PREFILL)}
 
 HOT_BOOST = 6.0
 
