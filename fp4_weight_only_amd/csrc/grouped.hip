@@ -9,14 +9,14 @@
 // float32 y.  Same outputs as the decode GEMV.
 //
 // gfx950 design:
-// * Work item = (expert, 64-row m tile, 256-column n tile); a workgroup of 8
-//   waves steps through K in 128-k slices.  Wave w owns columns 32w..32w+31
+// * Work item = (expert, 64-row m tile, 512-column n tile); a workgroup of
+//   16 waves steps through K in 128-k slices.  Wave w owns columns 32w..32w+31
 //   (two 16-column MFMA tiles) for every live 16-row sub-tile of the m tile,
 //   with v_mfma_f32_16x16x32_bf16.  Most experts of a prefill batch hold a
 //   handful of rows, so the cost is streaming and decoding weights.
-// * Weights stay packed in LDS, copied as loaded: 128 k rows x 128 bytes per
-//   slice (eight lanes load a row's 128-byte line; 8-byte units XOR-swizzled
-//   by row in LDS).  gfx950's 4-bit transpose read
+// * Weights stay packed in LDS, copied as loaded: 128 k rows x 256 bytes per
+//   slice (sixteen lanes load a row's two 128-byte lines; 8-byte units
+//   XOR-swizzled by row in LDS).  gfx950's 4-bit transpose read
 //   (ds_read_b64_tr_b4) hands each lane of a 16-lane group one column's 16
 //   consecutive k codes from the rows its group points at, which is two
 //   K-paired MFMA B operands (k 16g..16g+7 and 16g+8..16g+15 of a 64-k
@@ -32,9 +32,11 @@
 // * Activations: 64 rows x 128 k bf16 per slice (rows gathered through the
 //   permutation for FC1), 16-byte chunks XOR-swizzled by row so the operand
 //   reads are conflict free.
-// * Pipeline: global loads two slices ahead in registers (up to 34 KB per
-//   workgroup per slice), LDS double buffered, one barrier per slice; two
-//   workgroups (16 waves, 128 VGPRs each) per CU.  16-row sub-tiles with no routed rows
+// * Pipeline: global loads two slices ahead in registers (up to 52 KB per
+//   workgroup per slice), LDS double buffered, one barrier per slice; one
+//   workgroup (16 waves, at most 128 VGPRs each) per CU.  The 512-column
+//   tile halves the activation re-reads of the n tiles (measured against 256
+//   columns on 8 waves).  16-row sub-tiles with no routed rows
 //   are skipped.  No weight element is decoded or read from LDS by more
 //   than one wave.
 // * Work items: the (expert, m tile) list is found on the device from
@@ -50,10 +52,10 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kBM = 64, kBN = 256, kBK = 128;
-constexpr int kWaves = 8;            // wave w owns columns 32w..32w+31
+constexpr int kBM = 64, kBN = 512, kBK = 128;
+constexpr int kWaves = 16;           // wave w owns columns 32w..32w+31
 constexpr int kAChunks = kBK / 8;    // 16-byte chunks per activation row of a slice
-constexpr int kBRow = kBN / 2;       // packed bytes per weight row of a slice (one 128-byte line)
+constexpr int kBRow = kBN / 2;       // packed bytes per weight row of a slice (two 128-byte lines)
 constexpr uint32_t kGOutOfRange = 0x80000000u;
 
 struct GroupedSmem {
@@ -70,7 +72,7 @@ __device__ __forceinline__ float grouped_swiglu(float gate, float lin, float alp
 
 // One slice's global loads for one thread.
 struct SliceRegs {
-  u32x4_t A[2];    // activation row ra, k = 16 * aq .. +15
+  u32x4_t A;       // activation row ra, k = 8 * aq .. +7
   u32x4_t B[2];    // packed weight rows rb and rb + 64, bytes 16 * bq .. +15
   uint32_t S;      // four block-scale bytes
 };
@@ -134,9 +136,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   // the whole kernel; the slice position rides in the scalar offset.  Rows
   // outside the data get an out-of-range vector offset (reads return 0).  A
   // ragged last slice (K % 128 == 64) is only read for its first 64 k.
-  // activations: thread -> (row ra, 16 k)
-  const int ra = tid >> 3;
-  const int aq = tid & 7;
+  // activations: thread -> (row ra, 8 k)
+  const int ra = tid >> 4;
+  const int aq = tid & 15;
   const int act_rows = a.fc1 ? a.rows / a.topk : a.rows;
   const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
       uniform_ptr(a.act), (short)0, (int)((uint32_t)act_rows * (uint32_t)a.K * 2u), 0x00020000);
@@ -144,33 +146,32 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   if (ra < mrows) {
     const int p = row0 + ra;
     const int src = a.fc1 ? (a.p2e[p] / a.topk) : p;
-    avoff = (uint32_t)src * (uint32_t)a.K * 2u + (uint32_t)(aq * 32);
+    avoff = (uint32_t)src * (uint32_t)a.K * 2u + (uint32_t)(aq * 16);
   }
-  // weights: thread -> (k rows rb, rb + 64; 16 bytes bq); eight lanes read a
-  // row's 128-byte line
-  const int rb = tid >> 3;
-  const int bq = tid & 7;
+  // weights: thread -> (k rows rb, rb + 64; 16 bytes bq); sixteen lanes read
+  // a row's 256 bytes (two 128-byte lines)
+  const int rb = tid >> 4;
+  const int bq = tid & 15;
   const uint32_t rowbytes = (uint32_t)(a.N >> 1);
   const int KB = a.K / B;
   const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
       uniform_ptr(a.w + (size_t)e * a.K * rowbytes), (short)0, (int)((uint32_t)a.K * rowbytes), 0x00020000);
   const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
       uniform_ptr(a.scales + (size_t)e * KB * a.N), (short)0, (int)((uint32_t)KB * a.N), 0x00020000);
-  // a last tile of 128 columns (N % 256 == 128) reads nothing past N
+  // a partial last tile (N % 512 != 0) reads nothing past N
   const bool bcols = n0 + 32 * bq + 32 <= a.N;
   const uint32_t bvoff0 = bcols ? (uint32_t)rb * rowbytes + (uint32_t)(n0 >> 1) + (uint32_t)(bq * 16) : kGOutOfRange;
   const uint32_t bvoff1 = bcols ? bvoff0 + 64u * rowbytes : kGOutOfRange;
   // scales: thread -> (block row sb, 4 columns sq)
-  const int sq = tid & 63;
-  const int sb = tid >> 6;
+  const int sq = tid & 127;
+  const int sb = tid >> 7;
   constexpr int kSBlocks = kBK / B;
   const uint32_t svoff = n0 + sq * 4 + 4 <= a.N ? (uint32_t)sb * (uint32_t)a.N + (uint32_t)(n0 + sq * 4) : kGOutOfRange;
 
   auto load_slice = [&](int s, SliceRegs &r) {
     const int k0 = s * kBK;
     const bool tail = ragged && s + 1 == steps;  // uniform
-    r.A[0] = __builtin_amdgcn_raw_buffer_load_b128(arsrc, avoff, k0 * 2, 0);
-    r.A[1] = __builtin_amdgcn_raw_buffer_load_b128(arsrc, avoff + 16u, k0 * 2, 0);
+    r.A = __builtin_amdgcn_raw_buffer_load_b128(arsrc, avoff, k0 * 2, 0);
     const int so = (int)((uint32_t)k0 * rowbytes);
     r.B[0] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, bvoff0, so, 2);
     r.B[1] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, tail ? kGOutOfRange : bvoff1, so, 2);
@@ -189,8 +190,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
     for (int h = 0; h < 2; ++h) bpos[j][h] = 8 * ((2 * bq + h) ^ ((rb + 64 * j) & 15));
 
   auto store_slice = [&](int buf, const SliceRegs &r) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) sm.a[buf][ra][(2 * aq + h) ^ (ra & 15)] = r.A[h];
+    sm.a[buf][ra][aq ^ (ra & 15)] = r.A;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       *(u32x2_t *)&sm.b[buf][rb + 64 * j][bpos[j][0]] = u32x2_t{r.B[j].x, r.B[j].y};
@@ -199,7 +199,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
     if (sb < kSBlocks) *(uint32_t *)&sm.sc[buf][sb][sq * 4] = r.S;
   };
 
-  // ---- MFMA roles: wave w owns columns 32w..32w+31 ----------------------------
+  // ---- MFMA roles: wave w owns columns 32w..32w+31 (unit T = 2w + t of a
+  // packed row; the row swizzle flips its low four bits only) ----------------
   const int li = lane & 15;
   const int lk = lane >> 4;
   const int live = (mrows + 15) >> 4;  // 16-row sub-tiles holding routed rows
@@ -297,7 +298,7 @@ size_t grouped_workspace_bytes(int32_t rows, int32_t N, bool concat) {
 hipError_t launch_grouped(GemvArgs &a, int fmt, hipStream_t s) {
   const int erows = a.rows < a.E ? a.rows : a.E;
   a.nslots = (a.rows + kBM - 1) / kBM + erows;  // worst-case (expert, m tile) count
-  a.ntiles = (a.N + kBN - 1) / kBN;  // N % 128 == 0: the last tile may hold 128 columns
+  a.ntiles = (a.N + kBN - 1) / kBN;  // N % 128 == 0: a partial last tile (whole 32-column waves)
   const int items = a.nslots * a.ntiles;
   const dim3 grid((unsigned)(((items + 7) / 8) * 8));
   if (fmt == 0)
