@@ -187,17 +187,27 @@ __global__ __launch_bounds__(kF8Waves * 64) void fp8_gemv_kernel(GemvArgs a) {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kF8BM = 64, kF8BN = 256, kF8BK = 64;
+constexpr int kF8BM = 64;
+constexpr int kF8BK = 128;                          // k per slice: one 128-byte line of a column
 constexpr int kF8GWaves = 8;
+constexpr int kF8BN = kF8GWaves * 32;               // columns per work item
+constexpr int kF8GThreads = kF8GWaves * 64;
+constexpr int kF8Units = kF8BK / 8;                 // 8-k units per slice (B: 8 bytes, A: 16 bytes)
+constexpr int kF8ALoads = (kF8BM * kF8Units + kF8GThreads - 1) / kF8GThreads;  // 16-byte A loads per thread
+constexpr int kF8AThreads = kF8BM * kF8Units / kF8ALoads;                   // threads that load A
+constexpr int kF8LPC = kF8BK / 16;                  // lanes per column (16 bytes each)
+constexpr int kF8CPP = kF8GThreads / kF8LPC;        // columns per load pass
+constexpr int kF8BLoads = kF8BN / kF8CPP;           // 16-byte B loads per thread
+static_assert(kF8AThreads % 64 == 0 && kF8BN % kF8CPP == 0 && (kF8Units & (kF8Units - 1)) == 0, "tile shape");
 
 struct F8GroupedSmem {
-  u32x4_t a[2][kF8BM][kF8BK / 8];   // activations, 16-byte chunk c of row r at c ^ (r & 7)
-  uint8_t b[2][kF8BN][kF8BK];       // weight bytes, 8-byte unit u of column n at u ^ (n & 7)
+  u32x4_t a[2][kF8BM][kF8Units];    // activations, 16-byte chunk c of row r at c ^ (r % units)
+  uint8_t b[2][kF8BN][kF8BK];       // weight bytes, 8-byte unit u of column n at u ^ (n % units)
 };
 
 struct F8SliceRegs {
-  u32x4_t A;      // activation row ra, k = 8 * aq .. +7
-  u32x4_t B[2];   // columns cb and cb + 128, bytes 16 * bq .. +15 of the slice
+  u32x4_t A[kF8ALoads];   // activation chunks
+  u32x4_t B[kF8BLoads];   // columns cb + j * kF8CPP, bytes 16 * bq .. +15 of the slice
 };
 
 __device__ __forceinline__ bf16x8_t fp8_operand(u32x2_t d) {
@@ -209,7 +219,7 @@ __device__ __forceinline__ bf16x8_t fp8_operand(u32x2_t d) {
   return __builtin_bit_cast(bf16x8_t, o);
 }
 
-__global__ __launch_bounds__(kF8GWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void fp8_grouped_kernel(
+__global__ __launch_bounds__(kF8GThreads) __attribute__((amdgpu_waves_per_eu(kF8GWaves / 4))) void fp8_grouped_kernel(
     GemvArgs a) {
   __shared__ __attribute__((aligned(16))) F8GroupedSmem sm;
   const int tid = threadIdx.x;
@@ -231,42 +241,67 @@ __global__ __launch_bounds__(kF8GWaves * 64) __attribute__((amdgpu_waves_per_eu(
   const int row0 = a.offsets[e] + mt * kF8BM;
   const int mrows = min(kF8BM, a.offsets[e + 1] - row0);
   const int n0 = ntile * kF8BN;
-  const int steps = a.K / kF8BK;  // K % 64 == 0 on this path
+  const int steps = (a.K + kF8BK - 1) / kF8BK;  // K % 64 == 0: the last slice may be half
+  const int ktail = a.K - (steps - 1) * kF8BK;  // k in the last slice
 
-  // loaders (buffer loads; fixed vector offsets, the slice in the scalar offset)
-  const int ra = tid >> 3, aq = tid & 7;
+  // loaders (buffer loads; fixed vector offsets, the slice in the scalar
+  // offset; chunks past K in a half last slice load as zero)
+  const bool aload = kF8AThreads == kF8GThreads || tid < kF8AThreads;  // uniform per wave
   const int act_rows = a.fc1 ? a.rows / a.topk : a.rows;
   const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
       uniform_ptr(a.act), (short)0, (int)((uint32_t)act_rows * (uint32_t)a.K * 2u), 0x00020000);
-  uint32_t avoff = kF8OutOfRange;
-  if (ra < mrows) {
-    const int p = row0 + ra;
-    const int src = a.fc1 ? (a.p2e[p] / a.topk) : p;
-    avoff = (uint32_t)src * (uint32_t)a.K * 2u + (uint32_t)(aq * 16);
+  int ar[kF8ALoads], aq[kF8ALoads];
+  uint32_t avoff[kF8ALoads];
+#pragma unroll
+  for (int i = 0; i < kF8ALoads; ++i) {
+    const int c = tid + i * kF8AThreads;
+    ar[i] = c / kF8Units;
+    aq[i] = c % kF8Units;
+    avoff[i] = kF8OutOfRange;
+    if (aload && ar[i] < mrows) {
+      const int p = row0 + ar[i];
+      const int src = a.fc1 ? (a.p2e[p] / a.topk) : p;
+      avoff[i] = (uint32_t)src * (uint32_t)a.K * 2u + (uint32_t)(aq[i] * 16);
+    }
   }
-  const int cb = tid >> 2, bq = tid & 3;  // columns cb, cb + 128; 16 bytes bq of 64
+  const int cb = tid / kF8LPC, bq = tid % kF8LPC;  // columns cb + j * kF8CPP; 16 bytes bq of the slice
   const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
       uniform_ptr(a.w + (size_t)e * a.N * a.K), (short)0, (int)((uint32_t)a.N * (uint32_t)a.K), 0x00020000);
-  uint32_t bvoff[2];
+  uint32_t bvoff[kF8BLoads];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int col = n0 + cb + 128 * j;
+  for (int j = 0; j < kF8BLoads; ++j) {
+    const int col = n0 + cb + kF8CPP * j;
     bvoff[j] = col < a.N ? (uint32_t)col * (uint32_t)a.K + (uint32_t)(bq * 16) : kF8OutOfRange;
   }
+  // Every thread issues the same loads for every slice, also past the last
+  // one (out-of-range offsets: no memory access, zeros), so the compiler's
+  // wait counts at the pipeline's join points stay exact.
   auto load_slice = [&](int s, F8SliceRegs &r) {
     const int k0 = s * kF8BK;
-    r.A = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(arsrc, avoff, k0 * 2, 0));
+    const bool dead = s >= steps;                         // uniform
+    const bool half = s == steps - 1 && ktail < kF8BK;    // uniform
+    const uint32_t kill = dead ? kF8OutOfRange : 0u;
+    const int ao = __builtin_amdgcn_readfirstlane(k0 * 2), bo = __builtin_amdgcn_readfirstlane(k0);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      r.B[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, bvoff[j], k0, 2));
+    for (int i = 0; i < kF8ALoads; ++i) {
+      const uint32_t off = (half && aq[i] * 8 >= ktail) ? kF8OutOfRange : avoff[i];
+      r.A[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(arsrc, off | kill, ao, 0));
+    }
+    const uint32_t bmask = ((half && bq * 16 >= ktail) ? kF8OutOfRange : 0u) | kill;
+#pragma unroll
+    for (int j = 0; j < kF8BLoads; ++j)
+      r.B[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, bvoff[j] | bmask, bo, 2));
   };
   auto store_slice = [&](int buf, const F8SliceRegs &r) {
-    sm.a[buf][ra][aq ^ (ra & 7)] = r.A;
+    if (aload) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = cb + 128 * j;
-      *(u32x2_t *)&sm.b[buf][n][8 * ((2 * bq) ^ (n & 7))] = u32x2_t{r.B[j].x, r.B[j].y};
-      *(u32x2_t *)&sm.b[buf][n][8 * ((2 * bq + 1) ^ (n & 7))] = u32x2_t{r.B[j].z, r.B[j].w};
+      for (int i = 0; i < kF8ALoads; ++i) sm.a[buf][ar[i]][aq[i] ^ (ar[i] & (kF8Units - 1))] = r.A[i];
+    }
+#pragma unroll
+    for (int j = 0; j < kF8BLoads; ++j) {
+      const int n = cb + kF8CPP * j;
+      *(u32x2_t *)&sm.b[buf][n][8 * ((2 * bq) ^ (n & (kF8Units - 1)))] = u32x2_t{r.B[j].x, r.B[j].y};
+      *(u32x2_t *)&sm.b[buf][n][8 * ((2 * bq + 1) ^ (n & (kF8Units - 1)))] = u32x2_t{r.B[j].z, r.B[j].w};
     }
   };
 
@@ -283,17 +318,17 @@ __global__ __launch_bounds__(kF8GWaves * 64) __attribute__((amdgpu_waves_per_eu(
   auto compute_slice = [&](int buf) {
     if (!wave_cols) return;
 #pragma unroll
-    for (int kg = 0; kg < 2; ++kg) {
-      const int unit = kg * 4 + lk;  // 8-byte unit of the column's 64 bytes
+    for (int kg = 0; kg < kF8BK / 32; ++kg) {
+      const int unit = kg * 4 + lk;  // 8-k unit of the slice
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int n = wave * 32 + t * 16 + li;
-        const bf16x8_t bv = fp8_operand(*(const u32x2_t *)&sm.b[buf][n][8 * (unit ^ (n & 7))]);
+        const bf16x8_t bv = fp8_operand(*(const u32x2_t *)&sm.b[buf][n][8 * (unit ^ (n & (kF8Units - 1)))]);
 #pragma unroll
         for (int ms = 0; ms < 4; ++ms) {
           if (ms >= live) break;  // uniform
           const int r = ms * 16 + li;
-          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, sm.a[buf][r][unit ^ (r & 7)]);
+          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, sm.a[buf][r][unit ^ (r & (kF8Units - 1))]);
           acc[ms][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[ms][t], 0, 0, 0);
         }
       }
@@ -302,17 +337,21 @@ __global__ __launch_bounds__(kF8GWaves * 64) __attribute__((amdgpu_waves_per_eu(
 
   F8SliceRegs r0, r1;
   load_slice(0, r0);
-  if (steps > 1) load_slice(1, r1);
+  // slice 0's loads stay ahead of slice 1's: the loop waits for the older
+  // register set only (memory returns in issue order)
+  __builtin_amdgcn_sched_barrier(0);
+  load_slice(1, r1);
+  // One exit, at the bottom: a break between the halves makes the compiler
+  // wait for both register sets at the top of the loop.
   for (int s = 0; s < steps; s += 2) {
     store_slice(0, r0);
-    if (s + 2 < steps) load_slice(s + 2, r0);
+    load_slice(s + 2, r0);
     __syncthreads();
     compute_slice(0);
-    if (s + 1 >= steps) break;
     store_slice(1, r1);
-    if (s + 3 < steps) load_slice(s + 3, r1);
+    load_slice(s + 3, r1);
     __syncthreads();
-    compute_slice(1);
+    if (s + 1 < steps) compute_slice(1);
   }
 
   // epilogue: lane holds rows 4 lk + i, column li of each 16-column tile
@@ -348,7 +387,7 @@ hipError_t launch_fp8_grouped(GemvArgs &a, void *ws, hipStream_t s) {
   const int items = a.nslots * a.ntiles;
   const dim3 grid((unsigned)(((items + 7) / 8) * 8));
   if (a.concat) a.out_f32 = (float *)ws;
-  fp8_grouped_kernel<<<grid, kF8GWaves * 64, 0, s>>>(a);
+  fp8_grouped_kernel<<<grid, kF8GThreads, 0, s>>>(a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !a.concat) return err;
   a.partials = (float *)ws;

@@ -228,10 +228,13 @@ __global__ __launch_bounds__(max_waves<MRMAX>() * 64) void fp4_gemv_kernel(GemvA
   const int kl = kc * KC + g * kGemvLaneK;  // first k row of this lane
   const uint32_t rowbytes = (uint32_t)(a.N >> 1);
   const int KB = a.K / B;
+  // uniform_ptr keeps the descriptors in scalar registers: the compiler may
+  // otherwise form the expert's base address on the vector ALU and wrap each
+  // load in a readfirstlane loop
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(a.w + (size_t)e * a.K * rowbytes), (short)0, (int)((uint32_t)a.K * rowbytes), 0x00020000);
+      uniform_ptr(a.w + (size_t)e * a.K * rowbytes), (short)0, (int)((uint32_t)a.K * rowbytes), 0x00020000);
   const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(a.scales + (size_t)e * KB * a.N), (short)0, (int)((uint32_t)KB * a.N), 0x00020000);
+      uniform_ptr(a.scales + (size_t)e * KB * a.N), (short)0, (int)((uint32_t)KB * a.N), 0x00020000);
   const bool col_ok = col0 < a.N;
   const uint32_t woff = col_ok ? (uint32_t)kl * rowbytes + (uint32_t)(col0 >> 1) : kOutOfRange;
   const uint32_t soff = col_ok ? (uint32_t)(kl / B) * (uint32_t)a.N + (uint32_t)col0 : kOutOfRange;

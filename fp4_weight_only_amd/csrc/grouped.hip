@@ -168,17 +168,23 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   constexpr int kSBlocks = kBK / B;
   const uint32_t svoff = n0 + sq * 4 + 4 <= a.N ? (uint32_t)sb * (uint32_t)a.N + (uint32_t)(n0 + sq * 4) : kGOutOfRange;
 
+  // Every thread issues the same loads for every slice, also past the last
+  // one (out-of-range offsets: no memory access, zeros), so the compiler's
+  // wait counts at the pipeline's join points stay exact.  The slice offsets
+  // go through readfirstlane: in a vector register they would force a
+  // readfirstlane loop around each load.
   auto load_slice = [&](int s, SliceRegs &r) {
     const int k0 = s * kBK;
-    const bool tail = ragged && s + 1 == steps;  // uniform
-    r.A = __builtin_amdgcn_raw_buffer_load_b128(arsrc, avoff, k0 * 2, 0);
-    const int so = (int)((uint32_t)k0 * rowbytes);
-    r.B[0] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, bvoff0, so, 2);
-    r.B[1] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, tail ? kGOutOfRange : bvoff1, so, 2);
-    r.S = 0u;
-    if (sb < kSBlocks)
-      r.S = __builtin_amdgcn_raw_buffer_load_b32(srsrc, (tail && sb >= kSBlocks / 2) ? kGOutOfRange : svoff,
-                                                 (int)((uint32_t)(k0 / B) * (uint32_t)a.N), 0);
+    const bool dead = s >= steps;                           // uniform
+    const bool tail = ragged && s + 1 == steps;             // uniform
+    const uint32_t kill = dead ? kGOutOfRange : 0u;
+    r.A = __builtin_amdgcn_raw_buffer_load_b128(arsrc, avoff | kill, __builtin_amdgcn_readfirstlane(k0 * 2), 0);
+    const int so = __builtin_amdgcn_readfirstlane((int)((uint32_t)k0 * rowbytes));
+    r.B[0] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, bvoff0 | kill, so, 2);
+    r.B[1] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, (tail ? kGOutOfRange : bvoff1) | kill, so, 2);
+    r.S = __builtin_amdgcn_raw_buffer_load_b32(
+        srsrc, ((tail && sb >= kSBlocks / 2) || sb >= kSBlocks ? kGOutOfRange : svoff) | kill,
+        __builtin_amdgcn_readfirstlane((int)((uint32_t)(k0 / B) * (uint32_t)a.N)), 0);
   };
 
   // LDS positions of this thread's stores (unit u of weight row r sits at
@@ -248,17 +254,21 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   // ---- pipeline: loads two slices ahead in registers, LDS double buffered ----
   SliceRegs r0, r1;
   load_slice(0, r0);
-  if (steps > 1) load_slice(1, r1);
+  // slice 0's loads stay ahead of slice 1's: the loop waits for the older
+  // register set only (memory returns in issue order)
+  __builtin_amdgcn_sched_barrier(0);
+  load_slice(1, r1);
+  // One exit, at the bottom: a break between the halves makes the compiler
+  // wait for both register sets at the top of the loop.
   for (int s = 0; s < steps; s += 2) {
     store_slice(0, r0);
-    if (s + 2 < steps) load_slice(s + 2, r0);
+    load_slice(s + 2, r0);
     __syncthreads();
     compute_slice(0, s);
-    if (s + 1 >= steps) break;
     store_slice(1, r1);
-    if (s + 3 < steps) load_slice(s + 3, r1);
+    load_slice(s + 3, r1);
     __syncthreads();
-    compute_slice(1, s + 1);
+    if (s + 1 < steps) compute_slice(1, s + 1);
   }
 
   // ---- epilogue: lane holds rows 4*(lane/16)+i, column lane%16 of each tile --

@@ -222,6 +222,16 @@ def test_fp8_grouped_multi_tile():
     check_layer(synth.layer_inputs(cfg))
 
 
+@pytest.mark.parametrize("act", [STD, GPTOSS], ids=["std", "gptoss"])
+def test_fp8_grouped_half_last_slice(act):
+    # K = 576 (FC1) and 192 (FC2): the last 128-k slice holds 64 k; N = 384
+    # and 576 end in part-filled n tiles
+    import fp4_weight_only_amd as q
+    cfg = synth.shrink(synth.FP8_MTP4, E=16, T=48, k=4, H=576, I=192, seed=51)
+    check_layer(synth.layer_inputs(cfg), path=q.QMOE_PATH_GROUPED, act=act)
+    check_layer(synth.layer_inputs(cfg), path=q.QMOE_PATH_GROUPED, act=act + (2,))
+
+
 def test_fp8_every_finite_byte_through_the_gemv():
     # every finite E4M3 byte at every lane position of a 16-byte load
     cfg = synth.shrink(synth.FP8_MTP4, E=2, T=2, k=1, H=512, I=128, seed=45)
