@@ -53,11 +53,10 @@ __global__ __launch_bounds__(kF8Waves * 64) void fp8_gemv_kernel(GemvArgs a) {
   const int wave = tid >> 6;
   const int lane = lane_id();
 
-  // Work item: consecutive column tiles of one slot on one XCD (its
-  // activation rows stay in that XCD's L2; the expert's columns are
-  // contiguous in memory).
-  const int per = gridDim.x >> 3;
-  const int item = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  // Work item: items are dealt to the 8 XCDs round-robin (workgroup order),
+  // so the idle slots past the batch's distinct-expert count, which sit at the
+  // end of the item range, are spread over all XCDs.
+  const int item = blockIdx.x;
   if (item >= a.nslots * a.ntiles) return;
   const int slot = item / a.ntiles;
   const int tile = item - slot * a.ntiles;
@@ -226,12 +225,13 @@ __global__ __launch_bounds__(kF8GThreads) __attribute__((amdgpu_waves_per_eu(kF8
   const int wave = tid >> 6;
   const int lane = lane_id();
 
-  // XCD-aware decode: the n tiles of one (expert, m tile) are consecutive
-  // items on one XCD
-  const int per = gridDim.x >> 3;
-  const int q = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  const int slot = q / a.ntiles;
-  const int ntile = q - slot * a.ntiles;
+  // XCD-aware decode: slot 8 i + x runs on XCD x (workgroups go to the XCDs
+  // round-robin), its n tiles back to back; idle slots past the live count
+  // are spread over all XCDs
+  const int local = blockIdx.x >> 3;
+  const int sl = local / a.ntiles;
+  const int ntile = local - sl * a.ntiles;
+  const int slot = sl * 8 + (blockIdx.x & 7);
   if (slot >= a.nslots) return;
   int mt = 0;
   const int ef = find_mtile<kF8BM>(a.offsets, a.E, slot, mt);
@@ -384,8 +384,7 @@ hipError_t launch_fp8_grouped(GemvArgs &a, void *ws, hipStream_t s) {
   const int erows = a.rows < a.E ? a.rows : a.E;
   a.nslots = (a.rows + kF8BM - 1) / kF8BM + erows;  // worst-case (expert, m tile) count
   a.ntiles = (a.N + kF8BN - 1) / kF8BN;
-  const int items = a.nslots * a.ntiles;
-  const dim3 grid((unsigned)(((items + 7) / 8) * 8));
+  const dim3 grid((unsigned)((a.nslots + 7) / 8 * 8 * a.ntiles));
   if (a.concat) a.out_f32 = (float *)ws;
   fp8_grouped_kernel<<<grid, kF8GThreads, 0, s>>>(a);
   hipError_t err = hipGetLastError();

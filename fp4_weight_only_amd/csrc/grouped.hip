@@ -60,8 +60,9 @@ constexpr uint32_t kGOutOfRange = 0x80000000u;
 
 struct GroupedSmem {
   u32x4_t a[2][kBM][kAChunks];      // activations, chunk c of row r at c ^ (r & 15)
-  uint8_t b[2][kBK][kBRow];         // packed codes, 8-byte unit u of row r at u ^ (r & 15)
-  uint8_t sc[2][kBK / 16][kBN];     // block scales of the slice (B = 32 uses 4 rows)
+  uint8_t b[2][kBK][kBRow];         // packed codes, 8-byte unit u of row r at u ^ (r & 31)
+  uint8_t sc[2][kBK / 16][kBN + 16];  // block scales of the slice (B = 32 uses 4 rows); the pad
+                                      // puts neighbouring block rows on other banks
 };
 
 __device__ __forceinline__ float grouped_swiglu(float gate, float lin, float alpha, float beta, float limit) {
@@ -110,13 +111,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   const int wave = tid >> 6;
   const int lane = lane_id();
 
-  // XCD-aware decode: consecutive logical items share an XCD, and the n
-  // tiles of one (expert, m tile) are consecutive items.
-  const int G = gridDim.x;
-  const int per = G >> 3;
-  const int q = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  const int slot = q / a.ntiles;
-  const int ntile = q - slot * a.ntiles;
+  // XCD-aware decode: workgroups go to the 8 XCDs round-robin; slot
+  // 8 i + x runs on XCD x, its n tiles back to back (the activation rows stay
+  // in that XCD's L2).  Dealing slots round-robin keeps the idle slots past
+  // the batch's live (expert, m tile) count spread over all XCDs.
+  const int local = blockIdx.x >> 3;
+  const int sl = local / a.ntiles;
+  const int ntile = local - sl * a.ntiles;
+  const int slot = sl * 8 + (blockIdx.x & 7);
   if (slot >= a.nslots) return;
   int mt = 0;
   const int ef = find_mtile<kBM>(a.offsets, a.E, slot, mt);
@@ -188,12 +190,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   };
 
   // LDS positions of this thread's stores (unit u of weight row r sits at
-  // u ^ (r & 15): the two 8-byte halves of a loaded chunk land separately)
+  // u ^ (r & 31): the two 8-byte halves of a loaded chunk land separately;
+  // the transpose reads of lane groups 16 rows apart then hit opposite bank
+  // halves)
   int bpos[2][2];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) bpos[j][h] = 8 * ((2 * bq + h) ^ ((rb + 64 * j) & 15));
+    for (int h = 0; h < 2; ++h) bpos[j][h] = 8 * ((2 * bq + h) ^ ((rb + 64 * j) & 31));
 
   auto store_slice = [&](int buf, const SliceRegs &r) {
     sm.a[buf][ra][aq ^ (ra & 15)] = r.A;
@@ -206,7 +210,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   };
 
   // ---- MFMA roles: wave w owns columns 32w..32w+31 (unit T = 2w + t of a
-  // packed row; the row swizzle flips its low four bits only) ----------------
+  // packed row; the row swizzle permutes the row's 32 units) ----------------
   const int li = lane & 15;
   const int lk = lane >> 4;
   const int live = (mrows + 15) >> 4;  // 16-row sub-tiles holding routed rows
@@ -232,7 +236,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
         const int T = wave * 2 + t;
         typedef int v2i_t __attribute__((ext_vector_type(2)));
         const v2i_t v = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
-            (__attribute__((address_space(3))) v2i_t *)(&sm.b[buf][row][8 * (T ^ (row & 15))]));
+            (__attribute__((address_space(3))) v2i_t *)(&sm.b[buf][row][8 * (T ^ (row & 31))]));
         const uint32_t sbyte = sm.sc[buf][blk][T * 16 + li];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -309,8 +313,7 @@ hipError_t launch_grouped(GemvArgs &a, int fmt, hipStream_t s) {
   const int erows = a.rows < a.E ? a.rows : a.E;
   a.nslots = (a.rows + kBM - 1) / kBM + erows;  // worst-case (expert, m tile) count
   a.ntiles = (a.N + kBN - 1) / kBN;  // N % 128 == 0: a partial last tile (whole 32-column waves)
-  const int items = a.nslots * a.ntiles;
-  const dim3 grid((unsigned)(((items + 7) / 8) * 8));
+  const dim3 grid((unsigned)((a.nslots + 7) / 8 * 8 * a.ntiles));
   if (fmt == 0)
     grouped_gemm_kernel<0><<<grid, kWaves * 64, 0, s>>>(a);
   else
