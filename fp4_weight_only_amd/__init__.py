@@ -25,7 +25,8 @@ QMOE_FMT_NVFP4, QMOE_FMT_MXFP4 = 0, 1
 QMOE_PATH_AUTO, QMOE_PATH_GEMV, QMOE_PATH_GROUPED = 0, 1, 2
 GEMV_MAX_ROWS = 64
 
-EXPORTS = ("qmoe_route_topk", "qmoe_route_topk_router_weights", "qmoe_fp4_gemv_fc1_swiglu", "qmoe_fp4_gemv_fc2", "qmoe_fp4_gemv_fc2_finalize",
+EXPORTS = ("qmoe_route_topk", "qmoe_route_topk_router_weights", "qmoe_fp4_gemv_fc1_swiglu",
+           "qmoe_fp4_route_fc1_swiglu", "qmoe_fp4_gemv_fc2", "qmoe_fp4_gemv_fc2_finalize",
            "qmoe_finalize",
            "qmoe_dequant_fp4", "qmoe_fp8_gemv_fc1_swiglu", "qmoe_fp8_gemv_fc2", "qmoe_dequant_fp8",
            "qmoe_status_str")
@@ -75,6 +76,7 @@ def _load():
         "qmoe_route_topk": [P, I32, I32, I32, P, P, P, P, P, P],
         "qmoe_route_topk_router_weights": [P, P, I32, I32, I32, P, P, P, P, P, P],
         "qmoe_fp4_gemv_fc1_swiglu": [P, I32, I32, W, P, P, ctypes.POINTER(SwigluC), P, P, SZ, I32, P],
+        "qmoe_fp4_route_fc1_swiglu": [P, P, P, I32, I32, W, ctypes.POINTER(SwigluC), P, P, P, P, P, P, P, SZ, P],
         "qmoe_fp4_gemv_fc2": [P, I32, I32, W, P, P, P, SZ, I32, P],
         "qmoe_fp4_gemv_fc2_finalize": [P, I32, I32, W, P, P, P, P, P, SZ, I32, P],
         "qmoe_finalize": [P, P, P, I32, I32, I32, P, P],
@@ -152,7 +154,8 @@ def qmoe_route_topk_router_weights(logits, router_weights, k, topk_idx, topk_w, 
 
 def fc_workspace_bytes(which: int, T: int, k: int, w: FP4Weights, path=QMOE_PATH_AUTO, act=None) -> int:
     """Workspace size of qmoe_fp4_gemv_fc1_swiglu (which=1, with its act), qmoe_fp4_gemv_fc2
-    (which=2) or qmoe_fp4_gemv_fc2_finalize (which=3)."""
+    (which=2), qmoe_fp4_gemv_fc2_finalize (which=3) or qmoe_fp4_route_fc1_swiglu (which=4,
+    with its act; path is ignored)."""
     n = ctypes.c_size_t(0)
     wc = w.c()
     dummy = 256  # aligned non-null placeholders: a size query launches nothing
@@ -161,6 +164,9 @@ def fc_workspace_bytes(which: int, T: int, k: int, w: FP4Weights, path=QMOE_PATH
                                           ctypes.byref(n), path, None)
     elif which == 2:
         st = lib.qmoe_fp4_gemv_fc2(dummy, T, k, ctypes.byref(wc), dummy, dummy, None, ctypes.byref(n), path, None)
+    elif which == 4:
+        st = lib.qmoe_fp4_route_fc1_swiglu(dummy, None, dummy, T, k, ctypes.byref(wc), _swiglu(act), dummy, dummy,
+                                           dummy, dummy, dummy, dummy, None, ctypes.byref(n), None)
     else:
         st = lib.qmoe_fp4_gemv_fc2_finalize(dummy, T, k, ctypes.byref(wc), dummy, dummy, dummy, dummy, None,
                                             ctypes.byref(n), path, None)
@@ -182,6 +188,17 @@ def qmoe_fp4_gemv_fc1_swiglu(x, k, w1: FP4Weights, expert_offsets, perm_to_expan
     _check("qmoe_fp4_gemv_fc1_swiglu", lib.qmoe_fp4_gemv_fc1_swiglu(
         _ptr(x), T, k, ctypes.byref(wc), _ptr(expert_offsets), _ptr(perm_to_expanded), a, _ptr(h), _ptr(ws),
         ctypes.byref(n), path, _stream(stream)))
+
+
+def qmoe_fp4_route_fc1_swiglu(logits, router_weights, x, k, w1: FP4Weights, topk_idx, topk_w, expert_offsets,
+                              perm_to_expanded, expanded_to_perm, h, ws, act=None, stream=None):
+    T = x.shape[0]
+    wc = w1.c()
+    n = ctypes.c_size_t(ws.numel() * ws.element_size())
+    _check("qmoe_fp4_route_fc1_swiglu", lib.qmoe_fp4_route_fc1_swiglu(
+        _ptr(logits), _ptr(router_weights), _ptr(x), T, k, ctypes.byref(wc), _swiglu(act), _ptr(topk_idx),
+        _ptr(topk_w), _ptr(expert_offsets), _ptr(perm_to_expanded), _ptr(expanded_to_perm), _ptr(h), _ptr(ws),
+        ctypes.byref(n), _stream(stream)))
 
 
 def qmoe_fp4_gemv_fc2(h, T, k, w2: FP4Weights, expert_offsets, y_rows, ws, path=QMOE_PATH_AUTO, stream=None):

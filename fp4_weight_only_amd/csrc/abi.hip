@@ -217,6 +217,44 @@ qmoe_status qmoe_fp4_gemv_fc1_swiglu(const uint16_t *x, int32_t T, int32_t k, co
   return run_fc(a, w1, sh.max_rows_per_expert, p, ws, ws_bytes, stream);
 }
 
+qmoe_status qmoe_fp4_route_fc1_swiglu(const float *logits, const float *router_weights, const uint16_t *x,
+                                      int32_t T, int32_t k, const qmoe_fp4_weights *w1, const qmoe_swiglu *act,
+                                      int32_t *topk_idx, float *topk_w, int32_t *expert_offsets,
+                                      int32_t *perm_to_expanded, int32_t *expanded_to_perm, uint16_t *h, void *ws,
+                                      size_t *ws_bytes, hipStream_t stream) {
+  if (!logits || !topk_idx || !topk_w || !expert_offsets || !perm_to_expanded || !expanded_to_perm)
+    return QMOE_EINVAL;
+  FcShape sh;
+  qmoe_status st = check_fc(w1, T, k, x, expert_offsets, h, QMOE_PATH_GEMV, &sh);
+  if (st != QMOE_OK) return st;
+  if (!aligned16(logits) || (router_weights && !aligned16(router_weights)) || !aligned16(topk_idx) ||
+      !aligned16(topk_w) || !aligned16(perm_to_expanded) || !aligned16(expanded_to_perm))
+    return QMOE_EALIGN;
+  // the maps of one call are ranked by one wave
+  if (sh.rows > QMOE_GEMV_MAX_ROWS) return QMOE_EUNSUPPORTED;
+  GemvArgs a = {};
+  a.act = x;
+  a.topk = k;
+  a.rows = sh.rows;
+  a.fc1 = 1;
+  a.alpha = act ? act->alpha : 1.0f;
+  a.beta = act ? act->beta : 0.0f;
+  a.limit = act ? act->limit : INFINITY;
+  const int32_t fusion = act ? act->fusion : QMOE_SWIGLU_INTERLEAVED;
+  if (fusion != 0 && fusion != QMOE_SWIGLU_INTERLEAVED && fusion != QMOE_SWIGLU_CONCAT) return QMOE_EINVAL;
+  a.concat = fusion == QMOE_SWIGLU_CONCAT;
+  a.out_bf16 = h;
+  a.route_logits = logits;
+  a.route_rw = router_weights;
+  a.route_T = T;
+  a.route_idx = topk_idx;
+  a.route_w = topk_w;
+  a.route_offsets = expert_offsets;
+  a.route_p2e = perm_to_expanded;
+  a.route_e2p = expanded_to_perm;
+  return run_fc(a, w1, sh.max_rows_per_expert, QMOE_PATH_GEMV, ws, ws_bytes, stream);
+}
+
 qmoe_status qmoe_fp4_gemv_fc2(const uint16_t *h, int32_t T, int32_t k, const qmoe_fp4_weights *w2,
                               const int32_t *expert_offsets, float *y_rows, void *ws, size_t *ws_bytes,
                               qmoe_path path, hipStream_t stream) {

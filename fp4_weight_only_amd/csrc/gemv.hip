@@ -35,6 +35,7 @@
 //   two rows (up to 3 tokens) or four rows.
 #include "device_common.h"
 #include "qmoe_internal.h"
+#include "route_device.h"
 
 namespace qmoe {
 
@@ -168,7 +169,50 @@ __device__ __forceinline__ void store_fc1(const GemvArgs &a, int p, int col, flo
 template <int MRMAX>
 constexpr int max_waves() { return kGemvMaxWaves; }
 
-template <int FMT, int MRMAX>
+// Routing state of the fused prologue (up to 64 expanded rows).
+struct RouteSmem {
+  int32_t sidx[64];   // selected expert of expanded row t*k + j
+  int32_t off[260];   // expert_offsets [E+1]
+  int32_t p2e[64];
+  int32_t e2p[64];
+  int32_t cnt[256];
+};
+
+// Fused routing prologue (operator documentation section 2; the pages'
+// fused routing + expert-map kernel, extended here to E <= 256 and up to 64
+// expanded rows): the waves take the tokens in turn (one wave per token, the
+// exact top-k of the routing kernels), then wave 0 ranks the rows by expert.
+// Every workgroup computes the same maps; workgroup 0 writes them out for
+// the later calls.
+__device__ __forceinline__ void route_prologue(const GemvArgs &a, RouteSmem &rs, int W, int wave, int lane) {
+  const int E = a.E, k = a.topk, T = a.route_T, R = a.rows;
+  const bool writer = blockIdx.x == 0;
+  for (int t = wave; t < T; t += W) {  // wave-uniform
+    int sel;
+    float wsel;
+    topk_token(a.route_logits + (size_t)t * E, a.route_rw ? a.route_rw + (size_t)t * E : nullptr, E, k, lane, sel,
+               wsel);
+    if (lane < k) {
+      rs.sidx[t * k + lane] = sel;
+      if (writer) {
+        a.route_idx[t * k + lane] = sel;
+        a.route_w[t * k + lane] = wsel;
+      }
+    }
+  }
+  lds_barrier();
+  if (wave == 0) build_maps_wave(rs.sidx, R, E, rs.off, rs.p2e, rs.e2p, rs.cnt);
+  lds_barrier();
+  if (writer) {
+    for (int i = threadIdx.x; i <= E; i += W * 64) a.route_offsets[i] = rs.off[i];
+    for (int i = threadIdx.x; i < R; i += W * 64) {
+      a.route_p2e[i] = rs.p2e[i];
+      a.route_e2p[i] = rs.e2p[i];
+    }
+  }
+}
+
+template <int FMT, int MRMAX, bool ROUTE>
 __global__ __launch_bounds__(max_waves<MRMAX>() * 64) void fp4_gemv_kernel(GemvArgs a) {
   constexpr int B = (FMT == 0) ? 16 : 32;
   constexpr int NBLK = kGemvLaneK / B;
@@ -189,11 +233,21 @@ __global__ __launch_bounds__(max_waves<MRMAX>() * 64) void fp4_gemv_kernel(GemvA
   const int slot = item / a.ntiles;
   const int tile = item - slot * a.ntiles;
 
+  // Routing: from the maps in memory, or computed here (fused prologue).
+  const int32_t *offs = a.offsets;
+  const int32_t *p2e = a.p2e;
+  if constexpr (ROUTE) {
+    __shared__ __attribute__((aligned(16))) RouteSmem rs;
+    route_prologue(a, rs, W, wave, lane);
+    offs = rs.off;
+    p2e = rs.p2e;
+  }
+
   // FC1 gathers its x rows through perm_to_expanded (at most 64 rows on this
   // path): fetch it together with the offsets, one lane per row.
-  const int p2e_l = (a.fc1 && lane < a.rows) ? a.p2e[lane] : 0;
+  const int p2e_l = (a.fc1 && lane < a.rows) ? p2e[lane] : 0;
   int row0 = 0, m = 0;
-  const int e = find_slot_expert(a.offsets, a.E, slot, row0, m);
+  const int e = find_slot_expert(offs, a.E, slot, row0, m);
   if (e < 0) return;  // uniform over the workgroup
 
   // ---- activation rows of the first pass, then the weights ---------------------
@@ -425,21 +479,28 @@ hipError_t launch_fp4_gemv(const GemvArgs &a, int fmt, int max_rows_per_expert, 
   // Rows per pass: one when no expert can hold more than one row (one
   // token), two for up to three tokens, else four.
   const int mr = max_rows_per_expert <= 1 ? 1 : (max_rows_per_expert <= 3 ? 2 : 4);
+#define QMOE_GEMV_LAUNCH(F, R)                                     \
+  if (mr == 1)                                                     \
+    fp4_gemv_kernel<F, 1, R><<<grid, block, 0, s>>>(a);            \
+  else if (mr == 2)                                                \
+    fp4_gemv_kernel<F, 2, R><<<grid, block, 0, s>>>(a);            \
+  else                                                             \
+    fp4_gemv_kernel<F, 4, R><<<grid, block, 0, s>>>(a);
+  const bool route = a.route_logits != nullptr;
   if (fmt == 0) {
-    if (mr == 1)
-      fp4_gemv_kernel<0, 1><<<grid, block, 0, s>>>(a);
-    else if (mr == 2)
-      fp4_gemv_kernel<0, 2><<<grid, block, 0, s>>>(a);
-    else
-      fp4_gemv_kernel<0, 4><<<grid, block, 0, s>>>(a);
+    if (route) {
+      QMOE_GEMV_LAUNCH(0, true)
+    } else {
+      QMOE_GEMV_LAUNCH(0, false)
+    }
   } else {
-    if (mr == 1)
-      fp4_gemv_kernel<1, 1><<<grid, block, 0, s>>>(a);
-    else if (mr == 2)
-      fp4_gemv_kernel<1, 2><<<grid, block, 0, s>>>(a);
-    else
-      fp4_gemv_kernel<1, 4><<<grid, block, 0, s>>>(a);
+    if (route) {
+      QMOE_GEMV_LAUNCH(1, true)
+    } else {
+      QMOE_GEMV_LAUNCH(1, false)
+    }
   }
+#undef QMOE_GEMV_LAUNCH
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.force_partials || (a.nchunks == 1 && !a.concat)) return err;
   return launch_splitk_epilogue(a, s);

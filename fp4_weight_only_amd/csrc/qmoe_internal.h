@@ -30,6 +30,18 @@ struct GemvArgs {
   uint16_t *out_bf16;      // FC1: h [rows][N/2]
   float *out_f32;          // FC2: y [rows][N]
   float *partials;         // [nchunks][rows][N] split-K partials (nchunks > 1)
+  // FC1 GEMV with fused routing (route_logits set, rows <= 64): every
+  // workgroup selects the top-k experts of all route_T tokens and builds the
+  // expert maps in LDS (offsets and p2e above are then not read); workgroup 0
+  // also writes them to the route_* outputs.
+  const float *route_logits;  // [route_T][E]
+  const float *route_rw;      // [route_T][E] router_weights, or null: softmax weights
+  int32_t route_T;
+  int32_t *route_idx;         // [route_T][topk]
+  float *route_w;             // [route_T][topk]
+  int32_t *route_offsets;     // [E+1]
+  int32_t *route_p2e;         // [rows]
+  int32_t *route_e2p;         // [rows]
 };
 
 size_t gemv_workspace_bytes(int32_t rows, int32_t max_rows_per_expert, int32_t E, int32_t K, int32_t N,

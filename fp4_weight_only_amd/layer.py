@@ -9,9 +9,10 @@ from __future__ import annotations
 
 import torch
 
-from . import (QMOE_PATH_AUTO, FP4Weights, FP8Weights, alloc_workspace, fc_workspace_bytes, fp8_workspace_bytes,
-               qmoe_finalize, qmoe_fp4_gemv_fc1_swiglu, qmoe_fp4_gemv_fc2, qmoe_fp4_gemv_fc2_finalize,
-               qmoe_fp8_gemv_fc1_swiglu, qmoe_fp8_gemv_fc2, qmoe_route_topk, qmoe_route_topk_router_weights)
+from . import (GEMV_MAX_ROWS, QMOE_PATH_AUTO, QMOE_PATH_GROUPED, FP4Weights, FP8Weights, alloc_workspace,
+               fc_workspace_bytes, fp8_workspace_bytes, qmoe_finalize, qmoe_fp4_gemv_fc1_swiglu, qmoe_fp4_gemv_fc2,
+               qmoe_fp4_gemv_fc2_finalize, qmoe_fp4_route_fc1_swiglu, qmoe_fp8_gemv_fc1_swiglu, qmoe_fp8_gemv_fc2,
+               qmoe_route_topk, qmoe_route_topk_router_weights)
 
 
 class MoELayer:
@@ -35,6 +36,14 @@ class MoELayer:
         else:
             need = max(fc_workspace_bytes(1, T, k, w1, path, act), fc_workspace_bytes(2, T, k, w2, path),
                        fc_workspace_bytes(3, T, k, w2, path))
+        # single-token decode: routing folded into the FC1 GEMV launch.  Every
+        # FC1 workgroup runs the routing; with more tokens (a wave routes
+        # several, or the grid takes more than one round of resident
+        # workgroups) that costs more than the launch it saves (measured:
+        # T=1 20.2 -> 19.2 us, T=4 32.3 -> 33.7 us, T=8 52.3 -> 62.9 us)
+        self.route_in_fc1 = not self.fp8 and path != QMOE_PATH_GROUPED and T == 1 and R <= GEMV_MAX_ROWS
+        if not self.fp8 and R <= GEMV_MAX_ROWS:  # route_fc1() is callable in the decode window
+            need = max(need, fc_workspace_bytes(4, T, k, w1, path, act))
         self.ws = alloc_workspace(need, dev)
 
     def set_weights(self, w1: FP4Weights, w2: FP4Weights):
@@ -55,6 +64,10 @@ class MoELayer:
             qmoe_fp4_gemv_fc1_swiglu(x, self.k, self.w1, self.offsets, self.p2e, self.h, self.ws, self.act,
                                      self.path)
 
+    def route_fc1(self, logits, x, router_weights=None):
+        qmoe_fp4_route_fc1_swiglu(logits, router_weights, x, self.k, self.w1, self.topk_idx, self.topk_w,
+                                  self.offsets, self.p2e, self.e2p, self.h, self.ws, self.act)
+
     def fc2(self):
         if self.fp8:
             qmoe_fp8_gemv_fc2(self.h, self.T, self.k, self.w2, self.offsets, self.y, self.ws, self.path)
@@ -69,11 +82,15 @@ class MoELayer:
                                    self.path)
 
     def run(self, logits, x, fused: bool = False, router_weights=None):
-        """route -> FC1+SwiGLU -> FC2 -> finalize; fused=True runs FC2 and the
-        finalize as one call (y is then not written); router_weights [T][E]
-        selects DeepSeek-style mixing weights."""
-        self.route(logits, router_weights)
-        self.fc1(x)
+        """route -> FC1+SwiGLU -> FC2 -> finalize; fused=True runs the routing
+        inside the FC1 launch (decode window, FP4) and FC2 and the finalize as
+        one call (y is then not written); router_weights [T][E] selects
+        DeepSeek-style mixing weights."""
+        if fused and self.route_in_fc1:
+            self.route_fc1(logits, x, router_weights)
+        else:
+            self.route(logits, router_weights)
+            self.fc1(x)
         if fused and not self.fp8:  # FP8 has no fused FC2 + finalize call
             self.fc2_finalize()
         else:

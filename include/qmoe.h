@@ -202,6 +202,34 @@ qmoe_status qmoe_fp4_gemv_fc1_swiglu(const uint16_t *x, int32_t T, int32_t k,
                                      hipStream_t stream);
 
 /*
+ * qmoe_fp4_route_fc1_swiglu -- routing and FC1 + SwiGLU in one launch (decode).
+ *
+ * Passages: PR 29919 (fused routing and expert maps in one kernel for
+ * single-token decode), extended here to E <= 256 and up to 64 expanded
+ * rows and folded into the FC1 GEMV's prologue; operator documentation
+ * section 2 (routing, input 14 router_weights) and the passages of
+ * qmoe_fp4_gemv_fc1_swiglu.
+ *
+ * Equals qmoe_route_topk (router_weights NULL) or
+ * qmoe_route_topk_router_weights, followed by qmoe_fp4_gemv_fc1_swiglu with
+ * path GEMV, bit for bit: every workgroup of the GEMV selects the top-k
+ * experts of all T tokens and ranks the rows by expert in LDS, so it finds
+ * its expert without reading maps written by another launch.
+ *
+ * logits, router_weights (may be NULL), T, k, topk_idx, topk_w,
+ * expert_offsets, perm_to_expanded, expanded_to_perm: as qmoe_route_topk /
+ * qmoe_route_topk_router_weights (E = w1->E; the map and weight outputs are
+ * written by the call).  x, w1, act, h, ws, ws_bytes: as
+ * qmoe_fp4_gemv_fc1_swiglu (query the workspace size with ws == NULL).
+ * Limits: T*k <= 64 (QMOE_EUNSUPPORTED beyond), and those of both calls.
+ */
+qmoe_status qmoe_fp4_route_fc1_swiglu(const float *logits, const float *router_weights, const uint16_t *x,
+                                      int32_t T, int32_t k, const qmoe_fp4_weights *w1, const qmoe_swiglu *act,
+                                      int32_t *topk_idx, float *topk_w, int32_t *expert_offsets,
+                                      int32_t *perm_to_expanded, int32_t *expanded_to_perm, uint16_t *h, void *ws,
+                                      size_t *ws_bytes, hipStream_t stream);
+
+/*
  * qmoe_fp4_gemv_fc2 -- FC2 of every routed row.
  *
  * Passages: PR 31159 (the plain FP4 decode GEMV, "moe_gemv_kernel"); operator

@@ -143,6 +143,35 @@ def test_route_router_weights_validation(q):
     assert call(E=257) == q.QMOE_EUNSUPPORTED
 
 
+def test_route_fc1_validation_and_workspace(q):
+    L = q.lib
+    wc = weights(q, E=16, K=256, N=512)
+    n = ctypes.c_size_t(0)
+
+    def call(lg=A, rw=None, x=A, T=4, k=2, w=wc, idx=A, tw=A, off=A, p2e=A, e2p=A, h=A):
+        n.value = 0
+        return L.qmoe_fp4_route_fc1_swiglu(lg, rw, x, T, k, ctypes.byref(w), None, idx, tw, off, p2e, e2p, h, None,
+                                           ctypes.byref(n), None)
+
+    assert call() == q.QMOE_OK
+    fused = n.value
+    n2 = ctypes.c_size_t(0)
+    assert L.qmoe_fp4_gemv_fc1_swiglu(A, 4, 2, ctypes.byref(wc), A, A, None, A, None, ctypes.byref(n2),
+                                      q.QMOE_PATH_GEMV, None) == q.QMOE_OK
+    assert fused == n2.value                      # the same GEMV workspace
+    assert call(rw=A) == q.QMOE_OK                # router_weights is optional
+    for kw in ("lg", "x", "idx", "tw", "off", "p2e", "e2p", "h"):
+        assert call(**{kw: None}) == q.QMOE_EINVAL, kw
+    for kw in ("lg", "rw", "x", "idx", "tw", "off", "p2e", "e2p", "h"):
+        assert call(**{kw: MIS}) == q.QMOE_EALIGN, kw
+    assert call(T=8, k=8) == q.QMOE_OK            # 64 rows: the one-wave maps' limit
+    assert call(T=33, k=2) == q.QMOE_EUNSUPPORTED  # 66 rows
+    assert call(T=0) == q.QMOE_EINVAL
+    assert call(k=17) == q.QMOE_EINVAL            # k > E
+    assert call(w=weights(q, E=300, K=256, N=512), k=9) == q.QMOE_EUNSUPPORTED
+    assert call(w=weights(q, E=16, K=250, N=512)) == q.QMOE_EUNSUPPORTED   # K % 16
+
+
 def fc1_act(q, wc, act, T=1, k=2, path=0):
     n = ctypes.c_size_t(0)
     st = q.lib.qmoe_fp4_gemv_fc1_swiglu(A, T, k, ctypes.byref(wc), A, A, ctypes.byref(act), A, None,

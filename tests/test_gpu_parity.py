@@ -418,6 +418,46 @@ def test_fc2_finalize_fused_equals_separate_calls(cfg):
     assert np.array_equal(bf16_host(layer.out), ref)
 
 
+ROUTE_FC1 = [
+    synth.shrink(synth.TINY, seed=0),
+    synth.shrink(synth.DECODE, E=37, T=7, k=5, H=320, I=144, seed=1),      # 35 rows; two tokens per wave
+    synth.shrink(synth.DECODE, E=20, T=5, k=3, H=128, I=64, seed=22),      # K = 128: two waves per workgroup
+    synth.shrink(synth.MTP8, E=64, T=8, k=8, H=512, I=272, seed=2),        # 64 rows (the limit)
+    synth.shrink(synth.DECODE, E=16, T=64, k=1, H=256, I=64, seed=4),      # 64 tokens, k = 1, one k chunk
+    synth.shrink(synth.MX_DECODE, E=40, T=8, k=8, H=544, I=160, seed=3),   # MXFP4
+    synth.shrink(synth.MTP4, T=16, k=4, H=512, I=128, seed=23),            # E = 256, 16 tokens
+    synth.DECODE,
+    synth.MTP4,
+]
+
+
+@pytest.mark.parametrize("mode", ["softmax", "router_weights", "gptoss_concat"])
+@pytest.mark.parametrize("cfg", ROUTE_FC1, ids=lambda c: c.name)
+def test_route_fc1_equals_separate_calls(cfg, mode):
+    """qmoe_fp4_route_fc1_swiglu runs the routing of all tokens in every FC1
+    workgroup: every output (selections, weights, maps, h) must equal the
+    separate routing and FC1 GEMV calls bit for bit (those are checked against
+    the oracle by the layer tests)."""
+    import fp4_weight_only_amd as q
+    L = synth.layer_inputs(cfg)
+    act = GPTOSS + (q.QMOE_SWIGLU_CONCAT,) if mode == "gptoss_concat" else None
+    layer, logits, x = layer_dev(L, act=act, path=q.QMOE_PATH_GEMV)
+    rw = to_dev(synth.router_weights(cfg)) if mode == "router_weights" else None
+    print_case("route+fc1", cfg.name, mode)
+    outs = (layer.topk_idx, layer.topk_w, layer.offsets, layer.p2e, layer.e2p, layer.h)
+    layer.route(logits, rw)
+    layer.fc1(x)
+    torch.cuda.synchronize()
+    ref = [t.view(torch.int32 if t.element_size() == 4 else torch.int16).cpu().numpy().copy() for t in outs]
+    for t in outs:                                   # poison every output
+        t.view(torch.int32 if t.element_size() == 4 else torch.int16).fill_(-7)
+    layer.route_fc1(logits, x, rw)
+    torch.cuda.synchronize()
+    for name, t, r in zip(("idx", "w", "offsets", "p2e", "e2p", "h"), outs, ref):
+        got = t.view(torch.int32 if t.element_size() == 4 else torch.int16).cpu().numpy()
+        assert np.array_equal(got, r), name
+
+
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "mxfp4_g"])
 def test_dequant_small_exhaustive_scales(fmt):
     """Every scale byte (NaN bytes aside) with random codes; MXFP4 with and
