@@ -223,6 +223,10 @@ def bench_layer(args, torch, q, synth, np):
         sources = ("fp8.hip", "device_common.h", "qmoe_internal.h")
         kname, tname = "fp8_gemv_kernel (FC1+SwiGLU)", "fp8_gemv_fc1_mtp4"
         metric = "FP8 W8A16 MoE decode µs/layer + achieved HBM GB/s on weight bytes"
+    elif q.qmoe_fp4_resolve_path(cfg.T, cfg.k, copies[0][0]) == q.QMOE_PATH_GROUPED:
+        sources = ("grouped.hip", "device_common.h", "qmoe_internal.h")
+        kname, tname = "grouped_gemm_kernel (FC1+SwiGLU)", f"grouped_fc1_{args.workload}"
+        metric = METRIC
     else:
         sources = ("gemv.hip", "device_common.h", "qmoe_internal.h")
         kname, tname = "fp4_gemv_kernel + splitk_epilogue_kernel (FC1+SwiGLU)", f"gemv_fc1_{args.workload}"

@@ -25,7 +25,7 @@ QMOE_FMT_NVFP4, QMOE_FMT_MXFP4 = 0, 1
 QMOE_PATH_AUTO, QMOE_PATH_GEMV, QMOE_PATH_GROUPED = 0, 1, 2
 GEMV_MAX_ROWS = 64
 
-EXPORTS = ("qmoe_route_topk", "qmoe_route_topk_router_weights", "qmoe_fp4_gemv_fc1_swiglu",
+EXPORTS = ("qmoe_route_topk", "qmoe_route_topk_router_weights", "qmoe_fp4_resolve_path", "qmoe_fp4_gemv_fc1_swiglu",
            "qmoe_fp4_route_fc1_swiglu", "qmoe_fp4_gemv_fc2", "qmoe_fp4_gemv_fc2_finalize",
            "qmoe_finalize",
            "qmoe_dequant_fp4", "qmoe_fp8_gemv_fc1_swiglu", "qmoe_fp8_gemv_fc2", "qmoe_dequant_fp8",
@@ -76,6 +76,7 @@ def _load():
         "qmoe_route_topk": [P, I32, I32, I32, P, P, P, P, P, P],
         "qmoe_route_topk_router_weights": [P, P, I32, I32, I32, P, P, P, P, P, P],
         "qmoe_fp4_gemv_fc1_swiglu": [P, I32, I32, W, P, P, ctypes.POINTER(SwigluC), P, P, SZ, I32, P],
+        "qmoe_fp4_resolve_path": [I32, I32, W, I32, ctypes.POINTER(ctypes.c_int)],
         "qmoe_fp4_route_fc1_swiglu": [P, P, P, I32, I32, W, ctypes.POINTER(SwigluC), P, P, P, P, P, P, P, SZ, P],
         "qmoe_fp4_gemv_fc2": [P, I32, I32, W, P, P, P, SZ, I32, P],
         "qmoe_fp4_gemv_fc2_finalize": [P, I32, I32, W, P, P, P, P, P, SZ, I32, P],
@@ -172,6 +173,14 @@ def fc_workspace_bytes(which: int, T: int, k: int, w: FP4Weights, path=QMOE_PATH
                                             ctypes.byref(n), path, None)
     _check("fc_workspace_bytes", st)
     return n.value
+
+
+def qmoe_fp4_resolve_path(T: int, k: int, w: FP4Weights, path=QMOE_PATH_AUTO) -> int:
+    """The path (QMOE_PATH_GEMV or QMOE_PATH_GROUPED) an FC call with these arguments takes."""
+    out = ctypes.c_int(-1)
+    wc = w.c()
+    _check("qmoe_fp4_resolve_path", lib.qmoe_fp4_resolve_path(T, k, ctypes.byref(wc), path, ctypes.byref(out)))
+    return out.value
 
 
 def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:

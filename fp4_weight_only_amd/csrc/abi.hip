@@ -52,9 +52,21 @@ qmoe_status check_fc(const qmoe_fp4_weights *w, int32_t T, int32_t k, const void
 }
 
 // Resolves AUTO and checks the row window and tile shape of each path.
-qmoe_status resolve_path(qmoe_path path, int32_t rows, const qmoe_fp4_weights *w, qmoe_path *out) {
+// AUTO: the grouped MFMA kernel above the GEMV's 64-row window, and inside
+// it when an expert can hold more than four rows (the GEMV then runs several
+// row passes of VALU dot products) and N spans at least four of the grouped
+// kernel's 512-column tiles (enough workgroups without split-K).  Measured
+// on MI355X: MXFP4 T=8 (H=4096, I=2048) FC1 122 -> 100 us, FC2 64 -> 57 us;
+// NVFP4 T=8 FC2 (N=2048) 27 -> 23 us; NVFP4 T=8 FC1 (N=1536, three tiles)
+// and every T=4 shape stay faster on the GEMV.
+qmoe_status resolve_path(qmoe_path path, int32_t rows, int32_t max_rows_per_expert, const qmoe_fp4_weights *w,
+                         qmoe_path *out) {
   qmoe_path p = path;
-  if (p == QMOE_PATH_AUTO) p = rows <= QMOE_GEMV_MAX_ROWS ? QMOE_PATH_GEMV : QMOE_PATH_GROUPED;
+  if (p == QMOE_PATH_AUTO) {
+    const bool grouped_ok = w->K % 64 == 0 && w->N % 128 == 0;
+    const bool many_rows = max_rows_per_expert > 4 && (w->N + 511) / 512 >= 4;
+    p = rows > QMOE_GEMV_MAX_ROWS || (grouped_ok && many_rows) ? QMOE_PATH_GROUPED : QMOE_PATH_GEMV;
+  }
   if (p == QMOE_PATH_GEMV && rows > QMOE_GEMV_MAX_ROWS) return QMOE_EUNSUPPORTED;
   if (p == QMOE_PATH_GROUPED && (w->K % 64 != 0 || w->N % 128 != 0)) return QMOE_EUNSUPPORTED;
   // buffer resources address the activations of a call in 32 bits
@@ -188,6 +200,21 @@ qmoe_status qmoe_route_topk_router_weights(const float *logits, const float *rou
                                    perm_to_expanded, expanded_to_perm, stream));
 }
 
+qmoe_status qmoe_fp4_resolve_path(int32_t T, int32_t k, const qmoe_fp4_weights *w, qmoe_path path,
+                                  qmoe_path *resolved) {
+  if (!resolved) return QMOE_EINVAL;
+  if (T < 1 || k < 1) return QMOE_EINVAL;
+  qmoe_status st = check_weights(w);
+  if (st != QMOE_OK) return st;
+  if (k > w->E) return QMOE_EINVAL;
+  if (path != QMOE_PATH_AUTO && path != QMOE_PATH_GEMV && path != QMOE_PATH_GROUPED) return QMOE_EINVAL;
+  if (w->E > QMOE_MAX_EXPERTS || k > QMOE_MAX_TOPK) return QMOE_EUNSUPPORTED;
+  if (w->N % 32 != 0) return QMOE_EUNSUPPORTED;
+  const int64_t rows = (int64_t)T * k;
+  if (rows > (1 << 24)) return QMOE_EUNSUPPORTED;
+  return resolve_path(path, (int32_t)rows, T, w, resolved);
+}
+
 qmoe_status qmoe_fp4_gemv_fc1_swiglu(const uint16_t *x, int32_t T, int32_t k, const qmoe_fp4_weights *w1,
                                      const int32_t *expert_offsets, const int32_t *perm_to_expanded,
                                      const qmoe_swiglu *act, uint16_t *h, void *ws, size_t *ws_bytes,
@@ -198,7 +225,7 @@ qmoe_status qmoe_fp4_gemv_fc1_swiglu(const uint16_t *x, int32_t T, int32_t k, co
   if (!perm_to_expanded) return QMOE_EINVAL;
   if (!aligned16(perm_to_expanded)) return QMOE_EALIGN;
   qmoe_path p;
-  st = resolve_path(path, sh.rows, w1, &p);
+  st = resolve_path(path, sh.rows, sh.max_rows_per_expert, w1, &p);
   if (st != QMOE_OK) return st;
   GemvArgs a = {};
   a.act = x;
@@ -262,7 +289,7 @@ qmoe_status qmoe_fp4_gemv_fc2(const uint16_t *h, int32_t T, int32_t k, const qmo
   qmoe_status st = check_fc(w2, T, k, h, expert_offsets, y_rows, path, &sh);
   if (st != QMOE_OK) return st;
   qmoe_path p;
-  st = resolve_path(path, sh.rows, w2, &p);
+  st = resolve_path(path, sh.rows, sh.max_rows_per_expert, w2, &p);
   if (st != QMOE_OK) return st;
   GemvArgs a = {};
   a.act = h;
@@ -285,7 +312,7 @@ qmoe_status qmoe_fp4_gemv_fc2_finalize(const uint16_t *h, int32_t T, int32_t k, 
   if (!aligned16(topk_w) || !aligned16(expanded_to_perm)) return QMOE_EALIGN;
   if (w2->N % 8 != 0) return QMOE_EUNSUPPORTED;
   qmoe_path p;
-  st = resolve_path(path, sh.rows, w2, &p);
+  st = resolve_path(path, sh.rows, sh.max_rows_per_expert, w2, &p);
   if (st != QMOE_OK) return st;
   GemvArgs a = {};
   a.act = h;

@@ -82,7 +82,9 @@ typedef enum {
 } qmoe_fmt;
 
 typedef enum {
-  QMOE_PATH_AUTO = 0,     /* GEMV for T*k <= 64 expanded rows, GROUPED above                   */
+  QMOE_PATH_AUTO = 0,     /* GEMV for T*k <= 64 expanded rows, GROUPED above; inside the GEMV
+                             window GROUPED when T > 4 and N > 1536 (at least four 512-column
+                             tiles) and the grouped shape limits hold                          */
   QMOE_PATH_GEMV = 1,     /* FP4 decode GEMV; rejects T*k > 64 with QMOE_EUNSUPPORTED          */
   QMOE_PATH_GROUPED = 2   /* MFMA bf16 grouped GEMM over LDS-dequantised weight tiles          */
 } qmoe_path;
@@ -165,6 +167,21 @@ qmoe_status qmoe_route_topk_router_weights(const float *logits, const float *rou
                                            int32_t *topk_idx, float *topk_w, int32_t *expert_offsets,
                                            int32_t *perm_to_expanded, int32_t *expanded_to_perm,
                                            hipStream_t stream);
+
+/*
+ * qmoe_fp4_resolve_path -- the kernel path an FC call with these arguments takes.
+ *
+ * Passage: operator documentation section 4.3 (the decode GEMV for small
+ * batches, the grouped GEMM otherwise); the AUTO rule is that of qmoe_path.
+ *
+ * T, k, w, path: as for qmoe_fp4_gemv_fc1_swiglu / qmoe_fp4_gemv_fc2 /
+ * qmoe_fp4_gemv_fc2_finalize with the same weights.  *resolved (host) out:
+ * QMOE_PATH_GEMV or QMOE_PATH_GROUPED.  Returns the status those calls'
+ * shape checks return (QMOE_EUNSUPPORTED for a path the shape cannot take);
+ * nothing is launched and no device memory is read.
+ */
+qmoe_status qmoe_fp4_resolve_path(int32_t T, int32_t k, const qmoe_fp4_weights *w, qmoe_path path,
+                                  qmoe_path *resolved);
 
 /*
  * qmoe_fp4_gemv_fc1_swiglu -- FC1 of every routed row with fused SwiGLU.

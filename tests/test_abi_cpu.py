@@ -143,6 +143,41 @@ def test_route_router_weights_validation(q):
     assert call(E=257) == q.QMOE_EUNSUPPORTED
 
 
+def test_auto_path_rule(q):
+    """AUTO inside the 64-row window: the grouped kernel when T > 4 and N
+    spans more than three 512-column tiles, else the GEMV (seen through the
+    workspace size each path asks for)."""
+    n = ctypes.c_size_t(0)
+
+    def size(T, k, K, N, path):
+        wc = weights(q, E=256, K=K, N=N)
+        assert q.lib.qmoe_fp4_gemv_fc2(A, T, k, ctypes.byref(wc), A, A, None, ctypes.byref(n), path,
+                                       None) == q.QMOE_OK
+        return n.value
+
+    G, V, AU = q.QMOE_PATH_GROUPED, q.QMOE_PATH_GEMV, q.QMOE_PATH_AUTO
+    res = ctypes.c_int(-1)
+
+    def resolved(T, k, K, N, path=AU):
+        wc = weights(q, E=256, K=K, N=N)
+        st = q.lib.qmoe_fp4_resolve_path(T, k, ctypes.byref(wc), path, ctypes.byref(res))
+        return st, res.value
+
+    assert resolved(8, 8, 768, 2048) == (q.QMOE_OK, G)
+    assert resolved(8, 8, 2048, 1536) == (q.QMOE_OK, V)
+    assert resolved(4, 8, 768, 2048) == (q.QMOE_OK, V)
+    assert resolved(8, 8, 784, 2048) == (q.QMOE_OK, V)
+    assert resolved(9, 8, 2048, 1536) == (q.QMOE_OK, G)             # 72 rows
+    assert resolved(9, 8, 2048, 1536, V)[0] == q.QMOE_EUNSUPPORTED  # past the GEMV window
+    assert resolved(8, 8, 784, 2048, G)[0] == q.QMOE_EUNSUPPORTED   # K % 64
+    assert q.lib.qmoe_fp4_resolve_path(1, 1, ctypes.byref(weights(q)), AU, None) == q.QMOE_EINVAL
+    assert size(8, 8, 768, 2048, G) != size(8, 8, 768, 2048, V)
+    assert size(8, 8, 768, 2048, AU) == size(8, 8, 768, 2048, G)      # T = 8, four n tiles
+    assert size(8, 8, 2048, 1536, AU) == size(8, 8, 2048, 1536, V)    # three n tiles
+    assert size(4, 8, 768, 2048, AU) == size(4, 8, 768, 2048, V)      # T = 4
+    assert size(8, 8, 784, 2048, AU) == size(8, 8, 784, 2048, V)      # K % 64 != 0: no grouped path
+
+
 def test_route_fc1_validation_and_workspace(q):
     L = q.lib
     wc = weights(q, E=16, K=256, N=512)
