@@ -26,7 +26,8 @@ QMOE_PATH_AUTO, QMOE_PATH_GEMV, QMOE_PATH_GROUPED = 0, 1, 2
 GEMV_MAX_ROWS = 64
 
 EXPORTS = ("qmoe_route_topk", "qmoe_route_topk_router_weights", "qmoe_fp4_resolve_path", "qmoe_fp4_gemv_fc1_swiglu",
-           "qmoe_fp4_route_fc1_swiglu", "qmoe_fp4_gemv_fc2", "qmoe_fp4_gemv_fc2_finalize",
+           "qmoe_fp4_route_fc1_swiglu", "qmoe_fp4_moe_layer_decode", "qmoe_fp4_gemv_fc2",
+           "qmoe_fp4_gemv_fc2_finalize",
            "qmoe_finalize",
            "qmoe_dequant_fp4", "qmoe_fp8_gemv_fc1_swiglu", "qmoe_fp8_gemv_fc2", "qmoe_dequant_fp8",
            "qmoe_status_str")
@@ -77,6 +78,8 @@ def _load():
         "qmoe_route_topk_router_weights": [P, P, I32, I32, I32, P, P, P, P, P, P],
         "qmoe_fp4_gemv_fc1_swiglu": [P, I32, I32, W, P, P, ctypes.POINTER(SwigluC), P, P, SZ, I32, P],
         "qmoe_fp4_resolve_path": [I32, I32, W, I32, ctypes.POINTER(ctypes.c_int)],
+        "qmoe_fp4_moe_layer_decode": [P, P, P, I32, I32, W, W, ctypes.POINTER(SwigluC), I32, P, P, P, P, P, P, P,
+                                      SZ, P],
         "qmoe_fp4_route_fc1_swiglu": [P, P, P, I32, I32, W, ctypes.POINTER(SwigluC), P, P, P, P, P, P, P, SZ, P],
         "qmoe_fp4_gemv_fc2": [P, I32, I32, W, P, P, P, SZ, I32, P],
         "qmoe_fp4_gemv_fc2_finalize": [P, I32, I32, W, P, P, P, P, P, SZ, I32, P],
@@ -183,6 +186,17 @@ def qmoe_fp4_resolve_path(T: int, k: int, w: FP4Weights, path=QMOE_PATH_AUTO) ->
     return out.value
 
 
+def layer_decode_workspace_bytes(T: int, k: int, w1: FP4Weights, w2: FP4Weights, act=None) -> int:
+    """Workspace size of qmoe_fp4_moe_layer_decode."""
+    n = ctypes.c_size_t(0)
+    c1, c2 = w1.c(), w2.c()
+    d = 256
+    _check("layer_decode_workspace_bytes", lib.qmoe_fp4_moe_layer_decode(
+        d, None, d, T, k, ctypes.byref(c1), ctypes.byref(c2), _swiglu(act), 0, d, d, d, d, d, d, None,
+        ctypes.byref(n), None))
+    return n.value
+
+
 def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
     """Workspace of at least nbytes (scratch: its contents do not matter)."""
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -208,6 +222,18 @@ def qmoe_fp4_route_fc1_swiglu(logits, router_weights, x, k, w1: FP4Weights, topk
         _ptr(logits), _ptr(router_weights), _ptr(x), T, k, ctypes.byref(wc), _swiglu(act), _ptr(topk_idx),
         _ptr(topk_w), _ptr(expert_offsets), _ptr(perm_to_expanded), _ptr(expanded_to_perm), _ptr(h), _ptr(ws),
         ctypes.byref(n), _stream(stream)))
+
+
+def qmoe_fp4_moe_layer_decode(logits, router_weights, x, k, w1: FP4Weights, w2: FP4Weights, topk_idx, topk_w,
+                              expert_offsets, perm_to_expanded, expanded_to_perm, out, ws, act=None,
+                              route_in_fc1=False, stream=None):
+    T = x.shape[0]
+    c1, c2 = w1.c(), w2.c()
+    n = ctypes.c_size_t(ws.numel() * ws.element_size())
+    _check("qmoe_fp4_moe_layer_decode", lib.qmoe_fp4_moe_layer_decode(
+        _ptr(logits), _ptr(router_weights), _ptr(x), T, k, ctypes.byref(c1), ctypes.byref(c2), _swiglu(act),
+        1 if route_in_fc1 else 0, _ptr(topk_idx), _ptr(topk_w), _ptr(expert_offsets), _ptr(perm_to_expanded),
+        _ptr(expanded_to_perm), _ptr(out), _ptr(ws), ctypes.byref(n), _stream(stream)))
 
 
 def qmoe_fp4_gemv_fc2(h, T, k, w2: FP4Weights, expert_offsets, y_rows, ws, path=QMOE_PATH_AUTO, stream=None):

@@ -282,6 +282,100 @@ qmoe_status qmoe_fp4_route_fc1_swiglu(const float *logits, const float *router_w
   return run_fc(a, w1, sh.max_rows_per_expert, QMOE_PATH_GEMV, ws, ws_bytes, stream);
 }
 
+qmoe_status qmoe_fp4_moe_layer_decode(const float *logits, const float *router_weights, const uint16_t *x,
+                                      int32_t T, int32_t k, const qmoe_fp4_weights *w1, const qmoe_fp4_weights *w2,
+                                      const qmoe_swiglu *act, int32_t route_in_fc1, int32_t *topk_idx, float *topk_w,
+                                      int32_t *expert_offsets, int32_t *perm_to_expanded, int32_t *expanded_to_perm,
+                                      uint16_t *out, void *ws, size_t *ws_bytes, hipStream_t stream) {
+  if (!logits || !topk_idx || !topk_w || !expert_offsets || !perm_to_expanded || !expanded_to_perm)
+    return QMOE_EINVAL;
+  if (route_in_fc1 != 0 && route_in_fc1 != 1) return QMOE_EINVAL;
+  FcShape sh;
+  qmoe_status st = check_fc(w1, T, k, x, expert_offsets, out, QMOE_PATH_GEMV, &sh);
+  if (st != QMOE_OK) return st;
+  st = check_weights(w2);
+  if (st != QMOE_OK) return st;
+  if (w2->E != w1->E || w1->N != 2 * w2->K || w2->N != w1->K) return QMOE_EINVAL;
+  if (!aligned16(logits) || (router_weights && !aligned16(router_weights)) || !aligned16(topk_idx) ||
+      !aligned16(topk_w) || !aligned16(perm_to_expanded) || !aligned16(expanded_to_perm))
+    return QMOE_EALIGN;
+  if (sh.rows > QMOE_GEMV_MAX_ROWS || w2->N % 32 != 0 || w2->N % 8 != 0) return QMOE_EUNSUPPORTED;
+  const int32_t fusion = act ? act->fusion : QMOE_SWIGLU_INTERLEAVED;
+  if (fusion != 0 && fusion != QMOE_SWIGLU_INTERLEAVED && fusion != QMOE_SWIGLU_CONCAT) return QMOE_EINVAL;
+  // workspace: FC1's split-K partials (u, g applied), then FC2's
+  const size_t p1 = (gemv_workspace_bytes(sh.rows, sh.max_rows_per_expert, w1->E, w1->K, w1->N, true) + 255) &
+                    ~(size_t)255;
+  const size_t p2 = gemv_workspace_bytes(sh.rows, sh.max_rows_per_expert, w2->E, w2->K, w2->N, true);
+  // FC2's staging addresses FC1's partial planes with 32-bit buffer offsets
+  if (p1 >= ((size_t)1 << 31)) return QMOE_EUNSUPPORTED;
+  if (!ws_bytes) return QMOE_EINVAL;
+  if (!ws) {
+    *ws_bytes = p1 + p2;
+    return QMOE_OK;
+  }
+  if (*ws_bytes < p1 + p2) return QMOE_EWORKSPACE;
+  if (!aligned16(ws)) return QMOE_EALIGN;
+  const int E = w1->E;
+  if (!route_in_fc1) {
+    st = check_launch(launch_route(logits, router_weights, T, E, k, topk_idx, topk_w, expert_offsets,
+                                   perm_to_expanded, expanded_to_perm, stream));
+    if (st != QMOE_OK) return st;
+  }
+  GemvArgs a1 = {};
+  a1.act = x;
+  a1.p2e = perm_to_expanded;
+  a1.offsets = expert_offsets;
+  a1.w = w1->w;
+  a1.scales = w1->scales;
+  a1.gscale = w1->gscale;
+  a1.E = E;
+  a1.K = w1->K;
+  a1.N = w1->N;
+  a1.topk = k;
+  a1.rows = sh.rows;
+  a1.fc1 = 1;
+  a1.force_partials = 1;  // SwiGLU runs in FC2's staging
+  a1.concat = fusion == QMOE_SWIGLU_CONCAT;
+  if (route_in_fc1) {
+    a1.route_logits = logits;
+    a1.route_rw = router_weights;
+    a1.route_T = T;
+    a1.route_idx = topk_idx;
+    a1.route_w = topk_w;
+    a1.route_offsets = expert_offsets;
+    a1.route_p2e = perm_to_expanded;
+    a1.route_e2p = expanded_to_perm;
+  }
+  gemv_plan(a1, sh.max_rows_per_expert, ws);
+  st = check_launch(launch_fp4_gemv(a1, w1->fmt == QMOE_FMT_NVFP4 ? 0 : 1, sh.max_rows_per_expert, stream));
+  if (st != QMOE_OK) return st;
+  GemvArgs a2 = {};
+  a2.offsets = expert_offsets;
+  a2.w = w2->w;
+  a2.scales = w2->scales;
+  a2.gscale = w2->gscale;
+  a2.E = E;
+  a2.K = w2->K;
+  a2.N = w2->N;
+  a2.topk = k;
+  a2.rows = sh.rows;
+  a2.fc1 = 0;
+  a2.force_partials = 1;  // the finalize sums FC2's planes
+  a2.h_partials = (const float *)ws;
+  a2.h_nchunks = a1.nchunks;
+  a2.h_concat = a1.concat;
+  a2.h_alpha = act ? act->alpha : 1.0f;
+  a2.h_beta = act ? act->beta : 0.0f;
+  a2.h_limit = act ? act->limit : INFINITY;
+  float *ws2 = (float *)((char *)ws + p1);
+  gemv_plan(a2, sh.max_rows_per_expert, ws2);
+  st = check_launch(launch_fp4_gemv(a2, w2->fmt == QMOE_FMT_NVFP4 ? 0 : 1, sh.max_rows_per_expert, stream));
+  if (st != QMOE_OK) return st;
+  const size_t plane = (size_t)sh.rows * w2->N;
+  return check_launch(
+      launch_finalize(ws2, a2.nchunks, plane, topk_w, expanded_to_perm, T, k, w2->N, out, stream));
+}
+
 qmoe_status qmoe_fp4_gemv_fc2(const uint16_t *h, int32_t T, int32_t k, const qmoe_fp4_weights *w2,
                               const int32_t *expert_offsets, float *y_rows, void *ws, size_t *ws_bytes,
                               qmoe_path path, hipStream_t stream) {

@@ -212,7 +212,70 @@ __device__ __forceinline__ void route_prologue(const GemvArgs &a, RouteSmem &rs,
   }
 }
 
-template <int FMT, int MRMAX, bool ROUTE>
+// FC1's SwiGLU folded into FC2's staging: a thread forms 4 h values of one
+// row from the FC1 partial planes it holds (8 floats per plane: the gate and
+// linear values), summing the planes in order from -0 as the split-K epilogue
+// does (planes past h_nchunks add -0), then SwiGLU and bf16 RNE.
+constexpr int kHPlanes = 8;  // planes loaded per round
+
+struct HPart {
+  float4 v[kHPlanes][2];
+};
+
+__device__ __forceinline__ void load_h_planes(const GemvArgs &a, int c0, int p, int kabs, bool live_row,
+                                              HPart &hp) {
+  // buffer loads: rows past the expert's count and planes past h_nchunks use
+  // an out-of-range offset (no memory access, zeros) while every load is
+  // still issued unconditionally
+  const uint32_t plane = (uint32_t)a.rows * (uint32_t)(2 * a.K) * 4u;
+  const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
+      uniform_ptr(a.h_partials), (short)0, (int)(plane * (uint32_t)a.h_nchunks), 0x00020000);
+  const uint32_t row = (uint32_t)p * (uint32_t)(2 * a.K) * 4u;
+  const uint32_t o0 = row + 4u * (uint32_t)(a.h_concat ? kabs : 2 * kabs);
+  const uint32_t o1 = row + 4u * (uint32_t)(a.h_concat ? a.K + kabs : 2 * kabs + 4);
+#pragma unroll
+  for (int g = 0; g < kHPlanes; ++g) {
+    const bool on = live_row && c0 + g < a.h_nchunks;
+    const uint32_t base = (uint32_t)(c0 + g) * plane;
+    hp.v[g][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(hr, on ? base + o0 : kOutOfRange, 0, 0));
+    hp.v[g][1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(hr, on ? base + o1 : kOutOfRange, 0, 0));
+  }
+}
+
+__device__ __forceinline__ void add_h_planes(const GemvArgs &a, int c0, const HPart &hp, float4 &s0, float4 &s1) {
+#pragma unroll
+  for (int g = 0; g < kHPlanes; ++g) {
+    const bool live = c0 + g < a.h_nchunks;
+    s0.x += live ? hp.v[g][0].x : -0.f;
+    s0.y += live ? hp.v[g][0].y : -0.f;
+    s0.z += live ? hp.v[g][0].z : -0.f;
+    s0.w += live ? hp.v[g][0].w : -0.f;
+    s1.x += live ? hp.v[g][1].x : -0.f;
+    s1.y += live ? hp.v[g][1].y : -0.f;
+    s1.z += live ? hp.v[g][1].z : -0.f;
+    s1.w += live ? hp.v[g][1].w : -0.f;
+  }
+}
+
+// Four bf16 h values (packed) from the summed planes.
+__device__ __forceinline__ u32x2_t h_from_sums(const GemvArgs &a, float4 s0, float4 s1) {
+  float gt[4], ln[4];
+  if (a.h_concat) {
+    gt[0] = s0.x; gt[1] = s0.y; gt[2] = s0.z; gt[3] = s0.w;
+    ln[0] = s1.x; ln[1] = s1.y; ln[2] = s1.z; ln[3] = s1.w;
+  } else {
+    gt[0] = s0.x; ln[0] = s0.y; gt[1] = s0.z; ln[1] = s0.w;
+    gt[2] = s1.x; ln[2] = s1.y; gt[3] = s1.z; ln[3] = s1.w;
+  }
+  uint32_t h[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) h[i] = bf16_rne(swiglu(gt[i], ln[i], a.h_alpha, a.h_beta, a.h_limit));
+  return u32x2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+}
+
+// MODE 0: plain; 1: fused routing prologue (FC1); 2: h formed from FC1's
+// partials while staging (FC2).
+template <int FMT, int MRMAX, int MODE>
 __global__ __launch_bounds__(max_waves<MRMAX>() * 64) void fp4_gemv_kernel(GemvArgs a) {
   constexpr int B = (FMT == 0) ? 16 : 32;
   constexpr int NBLK = kGemvLaneK / B;
@@ -236,7 +299,7 @@ __global__ __launch_bounds__(max_waves<MRMAX>() * 64) void fp4_gemv_kernel(GemvA
   // Routing: from the maps in memory, or computed here (fused prologue).
   const int32_t *offs = a.offsets;
   const int32_t *p2e = a.p2e;
-  if constexpr (ROUTE) {
+  if constexpr (MODE == 1) {
     __shared__ __attribute__((aligned(16))) RouteSmem rs;
     route_prologue(a, rs, W, wave, lane);
     offs = rs.off;
@@ -267,12 +330,23 @@ __global__ __launch_bounds__(max_waves<MRMAX>() * 64) void fp4_gemv_kernel(GemvA
     const int kabs = kc * KC + kk;
     const int p = row0 + r;
     const int tok = __shfl(p2e_l, p & 63, 64) / a.topk;
-    if (xon0 && r < mr0 && kabs < a.K) {
+    if (MODE != 2 && xon0 && r < mr0 && kabs < a.K) {
       const int src = a.fc1 ? tok : p;
       xv0 = *(const u32x4_t *)(a.act + (size_t)src * a.K + kabs);
     }
     xr0 = r;
     xk0 = kk;
+  }
+  // MODE 2: this thread's FC1 partial planes of the first pass (4 h values of
+  // one row), issued before the weights
+  const int per_row4 = KC / 4;
+  const bool hon0 = MODE == 2 && tid < MRMAX * per_row4;
+  const int hr0 = hon0 ? tid / per_row4 : 0;
+  const int hk0 = (tid - hr0 * per_row4) * 4;
+  HPart hp0;
+  if constexpr (MODE == 2) {
+    const int kabs = kc * KC + hk0;
+    load_h_planes(a, 0, row0 + hr0, kabs, hon0 && hr0 < mr0 && kabs < a.K, hp0);
   }
 
   // ---- weight and scale loads of this lane ----------------------------------
@@ -311,7 +385,23 @@ __global__ __launch_bounds__(max_waves<MRMAX>() * 64) void fp4_gemv_kernel(GemvA
     const int mr = rem < MRMAX ? rem : MRMAX;
     // Stage the chunk's activation rows (rows past mr as zeros): one thread
     // per 8 values; the first pass's load was issued with the weights.
-    if (rbase == 0) {
+    if constexpr (MODE == 2) {
+      // h from FC1's partial planes (rows past mr and columns past K: zeros)
+      const int r = hr0;
+      const int kabs = kc * KC + hk0;
+      const bool on = hon0 && r < mr && kabs < a.K;
+      float4 s0 = make_float4(-0.f, -0.f, -0.f, -0.f), s1 = s0;
+      for (int c0 = 0; c0 < a.h_nchunks; c0 += kHPlanes) {
+        HPart hp;
+        if (rbase == 0 && c0 == 0) {
+          hp = hp0;
+        } else {
+          load_h_planes(a, c0, row0 + rbase + r, kabs, on, hp);
+        }
+        add_h_planes(a, c0, hp, s0, s1);
+      }
+      if (hon0) *(u32x2_t *)&sm.xs[r][hk0] = on ? h_from_sums(a, s0, s1) : u32x2_t{0u, 0u};
+    } else if (rbase == 0) {
       if (xon0) *(u32x4_t *)&sm.xs[xr0][xk0] = xv0;
     } else {
       const int i = tid;
@@ -479,25 +569,29 @@ hipError_t launch_fp4_gemv(const GemvArgs &a, int fmt, int max_rows_per_expert, 
   // Rows per pass: one when no expert can hold more than one row (one
   // token), two for up to three tokens, else four.
   const int mr = max_rows_per_expert <= 1 ? 1 : (max_rows_per_expert <= 3 ? 2 : 4);
-#define QMOE_GEMV_LAUNCH(F, R)                                     \
+#define QMOE_GEMV_LAUNCH(F, M)                                     \
   if (mr == 1)                                                     \
-    fp4_gemv_kernel<F, 1, R><<<grid, block, 0, s>>>(a);            \
+    fp4_gemv_kernel<F, 1, M><<<grid, block, 0, s>>>(a);            \
   else if (mr == 2)                                                \
-    fp4_gemv_kernel<F, 2, R><<<grid, block, 0, s>>>(a);            \
+    fp4_gemv_kernel<F, 2, M><<<grid, block, 0, s>>>(a);            \
   else                                                             \
-    fp4_gemv_kernel<F, 4, R><<<grid, block, 0, s>>>(a);
-  const bool route = a.route_logits != nullptr;
+    fp4_gemv_kernel<F, 4, M><<<grid, block, 0, s>>>(a);
+  const int mode = a.route_logits ? 1 : (a.h_partials ? 2 : 0);
   if (fmt == 0) {
-    if (route) {
-      QMOE_GEMV_LAUNCH(0, true)
+    if (mode == 1) {
+      QMOE_GEMV_LAUNCH(0, 1)
+    } else if (mode == 2) {
+      QMOE_GEMV_LAUNCH(0, 2)
     } else {
-      QMOE_GEMV_LAUNCH(0, false)
+      QMOE_GEMV_LAUNCH(0, 0)
     }
   } else {
-    if (route) {
-      QMOE_GEMV_LAUNCH(1, true)
+    if (mode == 1) {
+      QMOE_GEMV_LAUNCH(1, 1)
+    } else if (mode == 2) {
+      QMOE_GEMV_LAUNCH(1, 2)
     } else {
-      QMOE_GEMV_LAUNCH(1, false)
+      QMOE_GEMV_LAUNCH(1, 0)
     }
   }
 #undef QMOE_GEMV_LAUNCH

@@ -42,6 +42,14 @@ struct GemvArgs {
   int32_t *route_offsets;     // [E+1]
   int32_t *route_p2e;         // [rows]
   int32_t *route_e2p;         // [rows]
+  // FC2 with FC1's SwiGLU folded into the activation staging (h_partials
+  // set): h[p][j] is formed from FC1's split-K partials exactly as the FC1
+  // epilogue forms it (planes summed in order from -0, SwiGLU, bf16 RNE);
+  // act is not read.
+  const float *h_partials;    // [h_nchunks][rows][2*K] FC1 u (g applied)
+  int32_t h_nchunks;
+  int32_t h_concat;           // FC1 pairing: gate j / linear K + j (else 2j, 2j + 1)
+  float h_alpha, h_beta, h_limit;
 };
 
 size_t gemv_workspace_bytes(int32_t rows, int32_t max_rows_per_expert, int32_t E, int32_t K, int32_t N,

@@ -9,10 +9,11 @@ from __future__ import annotations
 
 import torch
 
-from . import (GEMV_MAX_ROWS, QMOE_PATH_AUTO, QMOE_PATH_GROUPED, FP4Weights, FP8Weights, alloc_workspace,
-               fc_workspace_bytes, fp8_workspace_bytes, qmoe_finalize, qmoe_fp4_gemv_fc1_swiglu, qmoe_fp4_gemv_fc2,
-               qmoe_fp4_gemv_fc2_finalize, qmoe_fp4_route_fc1_swiglu, qmoe_fp8_gemv_fc1_swiglu, qmoe_fp8_gemv_fc2,
-               qmoe_route_topk, qmoe_route_topk_router_weights)
+from . import (GEMV_MAX_ROWS, QMOE_PATH_AUTO, QMOE_PATH_GEMV, QMOE_PATH_GROUPED, FP4Weights, FP8Weights,
+               alloc_workspace, fc_workspace_bytes, fp8_workspace_bytes, layer_decode_workspace_bytes,
+               qmoe_finalize, qmoe_fp4_gemv_fc1_swiglu, qmoe_fp4_gemv_fc2, qmoe_fp4_gemv_fc2_finalize,
+               qmoe_fp4_moe_layer_decode, qmoe_fp4_resolve_path, qmoe_fp4_route_fc1_swiglu,
+               qmoe_fp8_gemv_fc1_swiglu, qmoe_fp8_gemv_fc2, qmoe_route_topk, qmoe_route_topk_router_weights)
 
 
 class MoELayer:
@@ -42,8 +43,17 @@ class MoELayer:
         # workgroups) that costs more than the launch it saves (measured:
         # T=1 20.2 -> 19.2 us, T=4 32.3 -> 33.7 us, T=8 52.3 -> 62.9 us)
         self.route_in_fc1 = not self.fp8 and path != QMOE_PATH_GROUPED and T == 1 and R <= GEMV_MAX_ROWS
-        if not self.fp8 and R <= GEMV_MAX_ROWS:  # route_fc1() is callable in the decode window
+        # decode window with both FCs on the GEMV: the whole layer in one call
+        # (FC1's SwiGLU folded into FC2's staging, h not written)
+        fits = (not self.fp8 and R <= GEMV_MAX_ROWS and w2.w.shape[0] == w1.w.shape[0]
+                and w2.w.shape[1] == w1.w.shape[2] and 2 * w2.w.shape[2] == w1.w.shape[1])
+        self.layer_decode = (fits and path != QMOE_PATH_GROUPED
+                             and qmoe_fp4_resolve_path(T, k, w1, path) == QMOE_PATH_GEMV
+                             and qmoe_fp4_resolve_path(T, k, w2, path) == QMOE_PATH_GEMV)
+        if not self.fp8 and R <= GEMV_MAX_ROWS:  # route_fc1() is callable
             need = max(need, fc_workspace_bytes(4, T, k, w1, path, act))
+        if fits:  # decode_layer() is callable
+            need = max(need, layer_decode_workspace_bytes(T, k, w1, w2, act))
         self.ws = alloc_workspace(need, dev)
 
     def set_weights(self, w1: FP4Weights, w2: FP4Weights):
@@ -68,6 +78,12 @@ class MoELayer:
         qmoe_fp4_route_fc1_swiglu(logits, router_weights, x, self.k, self.w1, self.topk_idx, self.topk_w,
                                   self.offsets, self.p2e, self.e2p, self.h, self.ws, self.act)
 
+    def decode_layer(self, logits, x, router_weights=None, route_in_fc1=None):
+        """The whole layer by qmoe_fp4_moe_layer_decode (h and y are not written)."""
+        rin = self.route_in_fc1 if route_in_fc1 is None else route_in_fc1
+        qmoe_fp4_moe_layer_decode(logits, router_weights, x, self.k, self.w1, self.w2, self.topk_idx, self.topk_w,
+                                  self.offsets, self.p2e, self.e2p, self.out, self.ws, self.act, rin)
+
     def fc2(self):
         if self.fp8:
             qmoe_fp8_gemv_fc2(self.h, self.T, self.k, self.w2, self.offsets, self.y, self.ws, self.path)
@@ -82,10 +98,14 @@ class MoELayer:
                                    self.path)
 
     def run(self, logits, x, fused: bool = False, router_weights=None):
-        """route -> FC1+SwiGLU -> FC2 -> finalize; fused=True runs the routing
-        inside the FC1 launch (decode window, FP4) and FC2 and the finalize as
-        one call (y is then not written); router_weights [T][E] selects
-        DeepSeek-style mixing weights."""
+        """route -> FC1+SwiGLU -> FC2 -> finalize; fused=True runs the decode
+        window's layer as one call (routing inside FC1 at T = 1, SwiGLU inside
+        FC2's staging, FC2 + finalize fused: h and y are not written), else
+        FC2 and the finalize as one call (y not written); router_weights [T][E]
+        selects DeepSeek-style mixing weights."""
+        if fused and self.layer_decode:
+            self.decode_layer(logits, x, router_weights)
+            return self.out
         if fused and self.route_in_fc1:
             self.route_fc1(logits, x, router_weights)
         else:

@@ -247,6 +247,40 @@ qmoe_status qmoe_fp4_route_fc1_swiglu(const float *logits, const float *router_w
                                       size_t *ws_bytes, hipStream_t stream);
 
 /*
+ * qmoe_fp4_moe_layer_decode -- the whole decode MoE layer: routing, FC1,
+ * SwiGLU, FC2 and the weighted un-permute, h never written.
+ *
+ * Passages: operator documentation section 1 (the chain), section 12.1
+ * (split-K SwiGLU: partial sums first, SwiGLU on the reduced sum) and
+ * section 9.8 (epilogue fusion); PR 31159 (the decode GEMV and its 64-row
+ * window); PR 29919 (routing fused into the path) for route_in_fc1.
+ *
+ * FC1 writes only its split-K partial sums; every FC2 workgroup forms the
+ * bf16 h values its k chunk needs from them (planes summed in order, SwiGLU,
+ * round to nearest even, as qmoe_fp4_gemv_fc1_swiglu's epilogue does) while
+ * staging its activations, and FC2's split-K planes go to the finalize.  out
+ * equals qmoe_route_topk[_router_weights] + qmoe_fp4_gemv_fc1_swiglu (GEMV)
+ * + qmoe_fp4_gemv_fc2_finalize (GEMV) bit for bit, as do the routing outputs.
+ *
+ * logits, router_weights (may be NULL: softmax weights), topk_idx, topk_w,
+ * expert_offsets, perm_to_expanded, expanded_to_perm: as qmoe_route_topk /
+ * qmoe_route_topk_router_weights (written by the call).  x, w1, act: as
+ * qmoe_fp4_gemv_fc1_swiglu; w2: FC2 weights (w2->E == w1->E, w2->K == w1->N/2,
+ * w2->N == w1->K).  out [T][H] bf16.
+ * route_in_fc1  0: routing runs as its own launch first; 1: inside the FC1
+ *            launch (as qmoe_fp4_route_fc1_swiglu).  Anything else: QMOE_EINVAL.
+ * ws, ws_bytes  as for the FC calls (query with ws == NULL): both layers'
+ *            float32 split-K partials.
+ * Limits: T*k <= 64 (QMOE_EUNSUPPORTED beyond), H % 32 == 0, and those of
+ * the separate calls; mismatched w1 / w2 shapes: QMOE_EINVAL.
+ */
+qmoe_status qmoe_fp4_moe_layer_decode(const float *logits, const float *router_weights, const uint16_t *x,
+                                      int32_t T, int32_t k, const qmoe_fp4_weights *w1, const qmoe_fp4_weights *w2,
+                                      const qmoe_swiglu *act, int32_t route_in_fc1, int32_t *topk_idx, float *topk_w,
+                                      int32_t *expert_offsets, int32_t *perm_to_expanded, int32_t *expanded_to_perm,
+                                      uint16_t *out, void *ws, size_t *ws_bytes, hipStream_t stream);
+
+/*
  * qmoe_fp4_gemv_fc2 -- FC2 of every routed row.
  *
  * Passages: PR 31159 (the plain FP4 decode GEMV, "moe_gemv_kernel"); operator

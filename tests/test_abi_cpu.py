@@ -207,6 +207,36 @@ def test_route_fc1_validation_and_workspace(q):
     assert call(w=weights(q, E=16, K=250, N=512)) == q.QMOE_EUNSUPPORTED   # K % 16
 
 
+def test_layer_decode_validation_and_workspace(q):
+    L = q.lib
+    w1 = weights(q, E=16, K=512, N=512)      # H = 512, 2I = 512
+    w2 = weights(q, E=16, K=256, N=512)      # I = 256, H = 512
+    n = ctypes.c_size_t(0)
+
+    def call(lg=A, rw=None, x=A, T=4, k=2, a=w1, b=w2, rin=0, idx=A, tw=A, off=A, p2e=A, e2p=A, out=A):
+        n.value = 0
+        return L.qmoe_fp4_moe_layer_decode(lg, rw, x, T, k, ctypes.byref(a), ctypes.byref(b), None, rin, idx, tw,
+                                           off, p2e, e2p, out, None, ctypes.byref(n), None)
+
+    assert call() == q.QMOE_OK and n.value > 0
+    both = n.value
+    n1 = ctypes.c_size_t(0)
+    assert L.qmoe_fp4_gemv_fc1_swiglu(A, 4, 2, ctypes.byref(w1), A, A, None, A, None, ctypes.byref(n1),
+                                      q.QMOE_PATH_GEMV, None) == q.QMOE_OK
+    assert both >= n1.value                       # both layers' partial sums
+    assert call(rin=1) == q.QMOE_OK and n.value == both
+    assert call(rin=2) == q.QMOE_EINVAL
+    for kw in ("lg", "x", "idx", "tw", "off", "p2e", "e2p", "out"):
+        assert call(**{kw: None}) == q.QMOE_EINVAL, kw
+    for kw in ("lg", "rw", "x", "idx", "tw", "off", "p2e", "e2p", "out"):
+        assert call(**{kw: MIS}) == q.QMOE_EALIGN, kw
+    assert call(b=weights(q, E=16, K=128, N=512)) == q.QMOE_EINVAL   # FC2 K != FC1 N / 2
+    assert call(b=weights(q, E=16, K=256, N=256)) == q.QMOE_EINVAL   # FC2 N != FC1 K
+    assert call(b=weights(q, E=8, K=256, N=512)) == q.QMOE_EINVAL    # expert counts differ
+    assert call(T=8, k=8) == q.QMOE_OK
+    assert call(T=33, k=2) == q.QMOE_EUNSUPPORTED                     # 66 rows
+
+
 def fc1_act(q, wc, act, T=1, k=2, path=0):
     n = ctypes.c_size_t(0)
     st = q.lib.qmoe_fp4_gemv_fc1_swiglu(A, T, k, ctypes.byref(wc), A, A, ctypes.byref(act), A, None,

@@ -458,6 +458,40 @@ def test_route_fc1_equals_separate_calls(cfg, mode):
         assert np.array_equal(got, r), name
 
 
+LAYER_DECODE = ROUTE_FC1 + [
+    synth.shrink(synth.DECODE, E=8, T=2, k=2, H=2304, I=96, seed=24),      # FC1 in 9 k chunks; FC2 K = 96 < its chunk
+    synth.shrink(synth.MX_DECODE, E=12, T=16, k=4, H=1024, I=256, seed=25),  # MXFP4, experts with > 4 rows
+]
+
+
+@pytest.mark.parametrize("route_in_fc1", [0, 1])
+@pytest.mark.parametrize("mode", ["softmax", "router_weights", "gptoss_concat"])
+@pytest.mark.parametrize("cfg", LAYER_DECODE, ids=lambda c: c.name)
+def test_layer_decode_equals_separate_calls(cfg, mode, route_in_fc1):
+    """qmoe_fp4_moe_layer_decode forms h inside FC2's staging from FC1's
+    partial sums: the routing outputs and out must equal the separate routing,
+    FC1 (GEMV) and fused FC2 + finalize (GEMV) calls bit for bit."""
+    import fp4_weight_only_amd as q
+    L = synth.layer_inputs(cfg)
+    act = GPTOSS + (q.QMOE_SWIGLU_CONCAT,) if mode == "gptoss_concat" else None
+    layer, logits, x = layer_dev(L, act=act, path=q.QMOE_PATH_GEMV)
+    rw = to_dev(synth.router_weights(cfg)) if mode == "router_weights" else None
+    print_case("layer decode", cfg.name, mode, "route_in_fc1", route_in_fc1)
+    outs = (layer.topk_idx, layer.topk_w, layer.offsets, layer.p2e, layer.e2p, layer.out)
+    layer.route(logits, rw)
+    layer.fc1(x)
+    layer.fc2_finalize()
+    torch.cuda.synchronize()
+    ref = [t.view(torch.int32 if t.element_size() == 4 else torch.int16).cpu().numpy().copy() for t in outs]
+    for t in outs:                                   # poison every output
+        t.view(torch.int32 if t.element_size() == 4 else torch.int16).fill_(-7)
+    layer.decode_layer(logits, x, rw, route_in_fc1=bool(route_in_fc1))
+    torch.cuda.synchronize()
+    for name, t, r in zip(("idx", "w", "offsets", "p2e", "e2p", "out"), outs, ref):
+        got = t.view(torch.int32 if t.element_size() == 4 else torch.int16).cpu().numpy()
+        assert np.array_equal(got, r), name
+
+
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "mxfp4_g"])
 def test_dequant_small_exhaustive_scales(fmt):
     """Every scale byte (NaN bytes aside) with random codes; MXFP4 with and
