@@ -320,17 +320,20 @@ __global__ __launch_bounds__(kF8GThreads) __attribute__((amdgpu_waves_per_eu(kF8
 #pragma unroll
     for (int kg = 0; kg < kF8BK / 32; ++kg) {
       const int unit = kg * 4 + lk;  // 8-k unit of the slice
+      // both column tiles' operands first: one activation read feeds two MFMAs
+      bf16x8_t bv[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int n = wave * 32 + t * 16 + li;
-        const bf16x8_t bv = fp8_operand(*(const u32x2_t *)&sm.b[buf][n][8 * (unit ^ (n & (kF8Units - 1)))]);
+        bv[t] = fp8_operand(*(const u32x2_t *)&sm.b[buf][n][8 * (unit ^ (n & (kF8Units - 1)))]);
+      }
 #pragma unroll
-        for (int ms = 0; ms < 4; ++ms) {
-          if (ms >= live) break;  // uniform
-          const int r = ms * 16 + li;
-          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, sm.a[buf][r][unit ^ (r & (kF8Units - 1))]);
-          acc[ms][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[ms][t], 0, 0, 0);
-        }
+      for (int ms = 0; ms < 4; ++ms) {
+        if (ms >= live) break;  // uniform
+        const int r = ms * 16 + li;
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, sm.a[buf][r][unit ^ (r & (kF8Units - 1))]);
+        acc[ms][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[0], acc[ms][0], 0, 0, 0);
+        acc[ms][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[1], acc[ms][1], 0, 0, 0);
       }
     }
   };

@@ -231,25 +231,31 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
       // the transpose returns column li's codes of rows kg*64 + 16*lk + 0..15
       const int row = kg * 64 + lk * 16 + li;
       const int blk = (kg * 64 + lk * 16) / B;
+      // both column tiles' operands of this k group first, so one activation
+      // read feeds two MFMAs
+      typedef int v2i_t __attribute__((ext_vector_type(2)));
+      v2i_t v[2];
+      uint32_t sbyte[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int T = wave * 2 + t;
-        typedef int v2i_t __attribute__((ext_vector_type(2)));
-        const v2i_t v = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+        v[t] = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
             (__attribute__((address_space(3))) v2i_t *)(&sm.b[buf][row][8 * (T ^ (row & 31))]));
-        const uint32_t sbyte = sm.sc[buf][blk][T * 16 + li];
+        sbyte[t] = sm.sc[buf][blk][T * 16 + li];
+      }
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          // decoded just before its MFMAs: one operand live at a time
-          const bf16x8_t bv = decode_operand<FMT>(h ? (uint32_t)v.y : (uint32_t)v.x, sbyte);
-          const int chunk = kg * 8 + lk * 2 + h;  // k = kg*64 + 16*lk + 8*h .. +7
+      for (int h = 0; h < 2; ++h) {
+        // decoded just before their MFMAs: two operands live at a time
+        const bf16x8_t bv0 = decode_operand<FMT>(h ? (uint32_t)v[0].y : (uint32_t)v[0].x, sbyte[0]);
+        const bf16x8_t bv1 = decode_operand<FMT>(h ? (uint32_t)v[1].y : (uint32_t)v[1].x, sbyte[1]);
+        const int chunk = kg * 8 + lk * 2 + h;  // k = kg*64 + 16*lk + 8*h .. +7
 #pragma unroll
-          for (int ms = 0; ms < 4; ++ms) {
-            if (ms >= live) break;  // uniform
-            const int r = ms * 16 + li;
-            const bf16x8_t av = __builtin_bit_cast(bf16x8_t, sm.a[buf][r][chunk ^ (r & 15)]);
-            acc[ms][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[ms][t], 0, 0, 0);
-          }
+        for (int ms = 0; ms < 4; ++ms) {
+          if (ms >= live) break;  // uniform
+          const int r = ms * 16 + li;
+          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, sm.a[buf][r][chunk ^ (r & 15)]);
+          acc[ms][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv0, acc[ms][0], 0, 0, 0);
+          acc[ms][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv1, acc[ms][1], 0, 0, 0);
         }
       }
     }
