@@ -53,7 +53,13 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kBM = 64, kBN = 512, kBK = 128;
-constexpr int kWaves = 16;           // wave w owns columns 32w..32w+31
+constexpr int kCT = 2;                     // 16-column MFMA tiles per wave
+constexpr int kWaves = kBN / (16 * kCT);   // wave w owns columns 16 kCT w .. 16 kCT (w + 1) - 1
+constexpr int kThreads = kWaves * 64;
+constexpr int kALoads = kBM * (kBK / 8) / kThreads;   // 16-byte activation chunks per thread per slice
+constexpr int kBLoads = kBK * 16 / kThreads;          // 16-byte weight chunks per thread per slice
+constexpr int kBRowStep = kThreads / 16;              // k rows between a thread's weight chunks
+static_assert(kALoads >= 1 && kBLoads >= 1 && kBN % (16 * kCT) == 0, "tile shape");
 constexpr int kAChunks = kBK / 8;    // 16-byte chunks per activation row of a slice
 constexpr int kBRow = kBN / 2;       // packed bytes per weight row of a slice (two 128-byte lines)
 constexpr uint32_t kGOutOfRange = 0x80000000u;
@@ -72,10 +78,11 @@ __device__ __forceinline__ float grouped_swiglu(float gate, float lin, float alp
 }
 
 // One slice's global loads for one thread.
+template <int NS>
 struct SliceRegs {
-  u32x4_t A;       // activation row ra, k = 8 * aq .. +7
-  u32x4_t B[2];    // packed weight rows rb and rb + 64, bytes 16 * bq .. +15
-  uint32_t S;      // four block-scale bytes
+  u32x4_t A[kALoads];
+  u32x4_t B[kBLoads];
+  uint32_t S[NS];
 };
 
 // MFMA B operand of one lane: 8 consecutive k codes of its column (one
@@ -104,7 +111,7 @@ __device__ __forceinline__ bf16x8_t decode_operand(uint32_t d, uint32_t sbyte) {
 }
 
 template <int FMT>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void grouped_gemm_kernel(GemvArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4))) void grouped_gemm_kernel(GemvArgs a) {
   constexpr int B = (FMT == 0) ? 16 : 32;
   __shared__ __attribute__((aligned(16))) GroupedSmem sm;
   const int tid = threadIdx.x;
@@ -138,20 +145,25 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   // the whole kernel; the slice position rides in the scalar offset.  Rows
   // outside the data get an out-of-range vector offset (reads return 0).  A
   // ragged last slice (K % 128 == 64) is only read for its first 64 k.
-  // activations: thread -> (row ra, 8 k)
-  const int ra = tid >> 4;
+  // activations: thread -> 16-byte chunk aq (8 k) of rows ra[i]
   const int aq = tid & 15;
   const int act_rows = a.fc1 ? a.rows / a.topk : a.rows;
   const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
       uniform_ptr(a.act), (short)0, (int)((uint32_t)act_rows * (uint32_t)a.K * 2u), 0x00020000);
-  uint32_t avoff = kGOutOfRange;
-  if (ra < mrows) {
-    const int p = row0 + ra;
-    const int src = a.fc1 ? (a.p2e[p] / a.topk) : p;
-    avoff = (uint32_t)src * (uint32_t)a.K * 2u + (uint32_t)(aq * 16);
+  int ra[kALoads];
+  uint32_t avoff[kALoads];
+#pragma unroll
+  for (int i = 0; i < kALoads; ++i) {
+    ra[i] = (tid >> 4) + i * (kThreads / 16);
+    avoff[i] = kGOutOfRange;
+    if (ra[i] < mrows) {
+      const int p = row0 + ra[i];
+      const int src = a.fc1 ? (a.p2e[p] / a.topk) : p;
+      avoff[i] = (uint32_t)src * (uint32_t)a.K * 2u + (uint32_t)(aq * 16);
+    }
   }
-  // weights: thread -> (k rows rb, rb + 64; 16 bytes bq); sixteen lanes read
-  // a row's 256 bytes (two 128-byte lines)
+  // weights: thread -> 16 bytes bq of k rows rb + j * kBRowStep; sixteen
+  // lanes read a row's 256 bytes (two 128-byte lines)
   const int rb = tid >> 4;
   const int bq = tid & 15;
   const uint32_t rowbytes = (uint32_t)(a.N >> 1);
@@ -162,64 +174,81 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
       uniform_ptr(a.scales + (size_t)e * KB * a.N), (short)0, (int)((uint32_t)KB * a.N), 0x00020000);
   // a partial last tile (N % 512 != 0) reads nothing past N
   const bool bcols = n0 + 32 * bq + 32 <= a.N;
-  const uint32_t bvoff0 = bcols ? (uint32_t)rb * rowbytes + (uint32_t)(n0 >> 1) + (uint32_t)(bq * 16) : kGOutOfRange;
-  const uint32_t bvoff1 = bcols ? bvoff0 + 64u * rowbytes : kGOutOfRange;
-  // scales: thread -> (block row sb, 4 columns sq)
-  const int sq = tid & 127;
-  const int sb = tid >> 7;
+  const uint32_t bvoff0 = (uint32_t)rb * rowbytes + (uint32_t)(n0 >> 1) + (uint32_t)(bq * 16);
+  // scales: thread -> 4 columns sq of block rows sb[i]
   constexpr int kSBlocks = kBK / B;
-  const uint32_t svoff = n0 + sq * 4 + 4 <= a.N ? (uint32_t)sb * (uint32_t)a.N + (uint32_t)(n0 + sq * 4) : kGOutOfRange;
+  constexpr int kSLoads = (kSBlocks * (kBN / 4) + kThreads - 1) / kThreads;
+  const int sq = tid & 127;
+  const bool scols = n0 + sq * 4 + 4 <= a.N;
 
   // Every thread issues the same loads for every slice, also past the last
   // one (out-of-range offsets: no memory access, zeros), so the compiler's
   // wait counts at the pipeline's join points stay exact.  The slice offsets
   // go through readfirstlane: in a vector register they would force a
   // readfirstlane loop around each load.
-  auto load_slice = [&](int s, SliceRegs &r) {
+  using Regs = SliceRegs<kSLoads>;
+  auto load_slice = [&](int s, Regs &r) {
     const int k0 = s * kBK;
     const bool dead = s >= steps;                           // uniform
     const bool tail = ragged && s + 1 == steps;             // uniform
     const uint32_t kill = dead ? kGOutOfRange : 0u;
-    r.A = __builtin_amdgcn_raw_buffer_load_b128(arsrc, avoff | kill, __builtin_amdgcn_readfirstlane(k0 * 2), 0);
+    const int ao = __builtin_amdgcn_readfirstlane(k0 * 2);
+#pragma unroll
+    for (int i = 0; i < kALoads; ++i) r.A[i] = __builtin_amdgcn_raw_buffer_load_b128(arsrc, avoff[i] | kill, ao, 0);
     const int so = __builtin_amdgcn_readfirstlane((int)((uint32_t)k0 * rowbytes));
-    r.B[0] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, bvoff0 | kill, so, 2);
-    r.B[1] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, (tail ? kGOutOfRange : bvoff1) | kill, so, 2);
-    r.S = __builtin_amdgcn_raw_buffer_load_b32(
-        srsrc, ((tail && sb >= kSBlocks / 2) || sb >= kSBlocks ? kGOutOfRange : svoff) | kill,
-        __builtin_amdgcn_readfirstlane((int)((uint32_t)(k0 / B) * (uint32_t)a.N)), 0);
+#pragma unroll
+    for (int j = 0; j < kBLoads; ++j) {
+      const bool on = bcols && !(tail && rb + j * kBRowStep >= kBK / 2);
+      r.B[j] = __builtin_amdgcn_raw_buffer_load_b128(
+          wrsrc, (on ? bvoff0 + (uint32_t)(j * kBRowStep) * rowbytes : kGOutOfRange) | kill, so, 2);
+    }
+    const int sso = __builtin_amdgcn_readfirstlane((int)((uint32_t)(k0 / B) * (uint32_t)a.N));
+#pragma unroll
+    for (int i = 0; i < kSLoads; ++i) {
+      const int sb = (tid >> 7) + i * (kThreads / 128);
+      const bool on = scols && sb < kSBlocks && !(tail && sb >= kSBlocks / 2);
+      r.S[i] = __builtin_amdgcn_raw_buffer_load_b32(
+          srsrc, (on ? (uint32_t)sb * (uint32_t)a.N + (uint32_t)(n0 + sq * 4) : kGOutOfRange) | kill, sso, 0);
+    }
   };
 
   // LDS positions of this thread's stores (unit u of weight row r sits at
   // u ^ (r & 31): the two 8-byte halves of a loaded chunk land separately;
   // the transpose reads of lane groups 16 rows apart then hit opposite bank
   // halves)
-  int bpos[2][2];
+  int bpos[kBLoads][2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < kBLoads; ++j)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) bpos[j][h] = 8 * ((2 * bq + h) ^ ((rb + 64 * j) & 31));
+    for (int h = 0; h < 2; ++h) bpos[j][h] = 8 * ((2 * bq + h) ^ ((rb + j * kBRowStep) & 31));
 
-  auto store_slice = [&](int buf, const SliceRegs &r) {
-    sm.a[buf][ra][aq ^ (ra & 15)] = r.A;
+  auto store_slice = [&](int buf, const Regs &r) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      *(u32x2_t *)&sm.b[buf][rb + 64 * j][bpos[j][0]] = u32x2_t{r.B[j].x, r.B[j].y};
-      *(u32x2_t *)&sm.b[buf][rb + 64 * j][bpos[j][1]] = u32x2_t{r.B[j].z, r.B[j].w};
+    for (int i = 0; i < kALoads; ++i) sm.a[buf][ra[i]][aq ^ (ra[i] & 15)] = r.A[i];
+#pragma unroll
+    for (int j = 0; j < kBLoads; ++j) {
+      const int row = rb + j * kBRowStep;
+      *(u32x2_t *)&sm.b[buf][row][bpos[j][0]] = u32x2_t{r.B[j].x, r.B[j].y};
+      *(u32x2_t *)&sm.b[buf][row][bpos[j][1]] = u32x2_t{r.B[j].z, r.B[j].w};
     }
-    if (sb < kSBlocks) *(uint32_t *)&sm.sc[buf][sb][sq * 4] = r.S;
+#pragma unroll
+    for (int i = 0; i < kSLoads; ++i) {
+      const int sb = (tid >> 7) + i * (kThreads / 128);
+      if (sb < kSBlocks) *(uint32_t *)&sm.sc[buf][sb][sq * 4] = r.S[i];
+    }
   };
 
-  // ---- MFMA roles: wave w owns columns 32w..32w+31 (unit T = 2w + t of a
-  // packed row; the row swizzle permutes the row's 32 units) ----------------
+  // ---- MFMA roles: wave w owns units T = kCT w + t of a packed row (16
+  // columns each; the row swizzle permutes the row's 32 units) ---------------
   const int li = lane & 15;
   const int lk = lane >> 4;
   const int live = (mrows + 15) >> 4;  // 16-row sub-tiles holding routed rows
-  const bool wave_cols = n0 + wave * 32 < a.N;  // uniform: this wave's columns exist
-  f32x4_t acc[4][2];
+  const bool wave_cols = n0 + wave * 16 * kCT < a.N;  // uniform: this wave's columns exist
+  f32x4_t acc[4][kCT];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kCT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   auto compute_slice = [&](int buf, int s) {
     if (!wave_cols) return;
@@ -231,38 +260,40 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
       // the transpose returns column li's codes of rows kg*64 + 16*lk + 0..15
       const int row = kg * 64 + lk * 16 + li;
       const int blk = (kg * 64 + lk * 16) / B;
-      // both column tiles' operands of this k group first, so one activation
-      // read feeds two MFMAs
+      // every column tile's operands of this k group first, so one
+      // activation read feeds kCT MFMAs
       typedef int v2i_t __attribute__((ext_vector_type(2)));
-      v2i_t v[2];
-      uint32_t sbyte[2];
+      v2i_t v[kCT];
+      uint32_t sbyte[kCT];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int T = wave * 2 + t;
+      for (int t = 0; t < kCT; ++t) {
+        const int T = wave * kCT + t;
         v[t] = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
             (__attribute__((address_space(3))) v2i_t *)(&sm.b[buf][row][8 * (T ^ (row & 31))]));
         sbyte[t] = sm.sc[buf][blk][T * 16 + li];
       }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        // decoded just before their MFMAs: two operands live at a time
-        const bf16x8_t bv0 = decode_operand<FMT>(h ? (uint32_t)v[0].y : (uint32_t)v[0].x, sbyte[0]);
-        const bf16x8_t bv1 = decode_operand<FMT>(h ? (uint32_t)v[1].y : (uint32_t)v[1].x, sbyte[1]);
+        // decoded just before their MFMAs: kCT operands live at a time
+        bf16x8_t bv[kCT];
+#pragma unroll
+        for (int t = 0; t < kCT; ++t) bv[t] = decode_operand<FMT>(h ? (uint32_t)v[t].y : (uint32_t)v[t].x, sbyte[t]);
         const int chunk = kg * 8 + lk * 2 + h;  // k = kg*64 + 16*lk + 8*h .. +7
 #pragma unroll
         for (int ms = 0; ms < 4; ++ms) {
           if (ms >= live) break;  // uniform
           const int r = ms * 16 + li;
           const bf16x8_t av = __builtin_bit_cast(bf16x8_t, sm.a[buf][r][chunk ^ (r & 15)]);
-          acc[ms][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv0, acc[ms][0], 0, 0, 0);
-          acc[ms][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv1, acc[ms][1], 0, 0, 0);
+#pragma unroll
+          for (int t = 0; t < kCT; ++t)
+            acc[ms][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[t], acc[ms][t], 0, 0, 0);
         }
       }
     }
   };
 
   // ---- pipeline: loads two slices ahead in registers, LDS double buffered ----
-  SliceRegs r0, r1;
+  Regs r0, r1;
   load_slice(0, r0);
   // slice 0's loads stay ahead of slice 1's: the loop waits for the older
   // register set only (memory returns in issue order)
@@ -288,8 +319,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   for (int ms = 0; ms < 4; ++ms) {
     if (ms >= live) break;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int col = n0 + wave * 32 + t * 16 + li;
+    for (int t = 0; t < kCT; ++t) {
+      const int col = n0 + wave * 16 * kCT + t * 16 + li;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = ms * 16 + lk * 4 + i;
@@ -318,12 +349,12 @@ size_t grouped_workspace_bytes(int32_t rows, int32_t N, bool concat) {
 hipError_t launch_grouped(GemvArgs &a, int fmt, hipStream_t s) {
   const int erows = a.rows < a.E ? a.rows : a.E;
   a.nslots = (a.rows + kBM - 1) / kBM + erows;  // worst-case (expert, m tile) count
-  a.ntiles = (a.N + kBN - 1) / kBN;  // N % 128 == 0: a partial last tile (whole 32-column waves)
+  a.ntiles = (a.N + kBN - 1) / kBN;  // N % 128 == 0: a partial last tile (whole 16 kCT-column waves)
   const dim3 grid((unsigned)((a.nslots + 7) / 8 * 8 * a.ntiles));
   if (fmt == 0)
-    grouped_gemm_kernel<0><<<grid, kWaves * 64, 0, s>>>(a);
+    grouped_gemm_kernel<0><<<grid, kThreads, 0, s>>>(a);
   else
-    grouped_gemm_kernel<1><<<grid, kWaves * 64, 0, s>>>(a);
+    grouped_gemm_kernel<1><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
