@@ -70,13 +70,20 @@ __global__ __launch_bounds__(kF8Waves * 64) void fp8_gemv_kernel(GemvArgs a) {
   const int col0 = (tile * kF8Waves + wave) * 4 * CPR + (lane >> 4);
   const int q = lane & 15;
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(a.w + (size_t)e * a.N * a.K), (short)0, (int)((uint32_t)a.N * (uint32_t)a.K), 0x00020000);
+      uniform_ptr(a.w + (size_t)e * a.N * a.K), (short)0, (int)((uint32_t)a.N * (uint32_t)a.K), 0x00020000);
   const float gs = a.gscale[e];
 
 #pragma nounroll
   for (int rbase = 0; rbase < m; rbase += MRMAX) {
     const int rem = m - rbase;
     const int mr = rem < MRMAX ? rem : MRMAX;
+    // source rows of the pass: FC1 gathers x by token through
+    // perm_to_expanded, one lane per row, one memory round trip
+    const int pl = row0 + rbase + (lane < mr ? lane : 0);
+    const int srcl = a.fc1 ? a.p2e[pl] / a.topk : pl;
+    int src[MRMAX];
+#pragma unroll
+    for (int r = 0; r < MRMAX; ++r) src[r] = __shfl(srcl, r < mr ? r : 0, 64);
     float acc[CPR][MRMAX];
 #pragma unroll
     for (int j = 0; j < CPR; ++j)
@@ -87,17 +94,20 @@ __global__ __launch_bounds__(kF8Waves * 64) void fp8_gemv_kernel(GemvArgs a) {
     for (int k0 = 0; k0 < a.K; k0 += PASSK) {
       // activation rows of the pass first (memory returns in issue order),
       // then this lane's weight bytes
+      // every load unconditional (clamped address; rows past mr and k past
+      // K zeroed afterwards), so none waits for another
       const int kx = k0 + tid * 8;
+      const bool xon = tid * 8 < PASSK && kx < a.K;
+      const int kxc = kx < a.K ? kx : a.K - 8;
       u32x4_t xv[MRMAX];
 #pragma unroll
-      for (int r = 0; r < MRMAX; ++r) {
-        const int p = row0 + rbase + r;
-        xv[r] = u32x4_t{0u, 0u, 0u, 0u};
-        if (r < mr && tid * 8 < PASSK && kx < a.K) {
-          const int src = a.fc1 ? a.p2e[p] / a.topk : p;  // FC1 gathers x rows by token
-          xv[r] = *(const u32x4_t *)(a.act + (size_t)src * a.K + kx);
-        }
-      }
+      for (int r = 0; r < MRMAX; ++r) xv[r] = *(const u32x4_t *)(a.act + (size_t)src[r] * a.K + kxc);
+#pragma unroll
+      for (int r = 0; r < MRMAX; ++r)
+        if (!(xon && r < mr)) xv[r] = u32x4_t{0u, 0u, 0u, 0u};
+      // keep the activation loads ahead of the weights: staging then waits
+      // for them alone
+      __builtin_amdgcn_sched_barrier(0);
       u32x4_t W[CPR][NLD];
 #pragma unroll
       for (int j = 0; j < CPR; ++j)
