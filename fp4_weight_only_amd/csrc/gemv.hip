@@ -33,6 +33,11 @@
 //   ballots); grids are sized for the worst case and idle slots exit.  Rows
 //   of an expert are processed in passes of one row (single-token batches),
 //   two rows (up to 3 tokens) or four rows.
+// * Two fused modes (template MODE): 1, every workgroup of an FC1 launch
+//   first runs the routing of all tokens (top-k per wave, one-wave expert
+//   maps in LDS) and takes its expert from LDS; 2, FC2 stages its bf16
+//   activations from FC1's split-K partial sums (planes in order, SwiGLU,
+//   round to nearest even), so FC1 needs no epilogue launch.
 #include "device_common.h"
 #include "qmoe_internal.h"
 #include "route_device.h"
