@@ -279,9 +279,12 @@ __device__ __forceinline__ u32x2_t h_from_sums(const GemvArgs &a, float4 s0, flo
 }
 
 // MODE 0: plain; 1: fused routing prologue (FC1); 2: h formed from FC1's
-// partials while staging (FC2).
+// partials while staging (FC2).  Modes 0 and 1 are held to 128 VGPRs (four
+// waves per SIMD): the four-row body then spills a few registers but the FC1
+// call at T=4 runs faster (16.1 -> 15.5 us); mode 2 keeps its registers
+// (capped it spills far more and FC2 slows down).
 template <int FMT, int MRMAX, int MODE>
-__global__ __launch_bounds__(max_waves<MRMAX>() * 64) void fp4_gemv_kernel(GemvArgs a) {
+__global__ __launch_bounds__(max_waves<MRMAX>() * 64) __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 1 : 4))) void fp4_gemv_kernel(GemvArgs a) {
   constexpr int B = (FMT == 0) ? 16 : 32;
   constexpr int NBLK = kGemvLaneK / B;
   __shared__ __attribute__((aligned(16))) Smem<MRMAX> sm;
