@@ -18,9 +18,16 @@
  *
  *   qmoe_fp8_gemv_fc1_swiglu, qmoe_fp8_gemv_fc2, qmoe_dequant_fp8
  *
- * and one fused call for the decode layer's tail:
+ * Fused calls for decode-sized batches (bit-identical to the calls they
+ * replace):
  *
  *   qmoe_fp4_gemv_fc2_finalize  FC2 + weighted un-permute without y_rows
+ *   qmoe_fp4_route_fc1_swiglu   routing inside the FC1 launch
+ *   qmoe_fp4_moe_layer_decode   the whole layer: routing, FC1, SwiGLU inside
+ *                               FC2's staging, FC2 + finalize (h, y not written)
+ *
+ * and one host-only query: qmoe_fp4_resolve_path (the kernel path an FC call
+ * takes).
  *
  * Conventions shared by every call
  * --------------------------------
