@@ -71,12 +71,6 @@ struct GroupedSmem {
                                       // puts neighbouring block rows on other banks
 };
 
-__device__ __forceinline__ float grouped_swiglu(float gate, float lin, float alpha, float beta, float limit) {
-  const float G = fminf(gate, limit);
-  const float L = fminf(fmaxf(lin, -limit), limit);
-  return G / (1.0f + expf(-alpha * G)) * (L + beta);
-}
-
 // One slice's global loads for one thread.
 template <int NS>
 struct SliceRegs {
@@ -329,7 +323,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
           const float partner = __uint_as_float(dpp_u32<kDppXor1>(__float_as_uint(u)));
           if (r < mrows && (lane & 1) == 0)
             a.out_bf16[(size_t)(row0 + r) * (a.N >> 1) + (col >> 1)] =
-                (uint16_t)bf16_rne(grouped_swiglu(u, partner, a.alpha, a.beta, a.limit));
+                (uint16_t)bf16_rne(swiglu(u, partner, a.alpha, a.beta, a.limit));
         } else if (r < mrows) {
           a.out_f32[(size_t)(row0 + r) * a.N + col] = u;
         }
