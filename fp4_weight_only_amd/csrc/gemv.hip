@@ -279,12 +279,14 @@ __device__ __forceinline__ u32x2_t h_from_sums(const GemvArgs &a, float4 s0, flo
 }
 
 // MODE 0: plain; 1: fused routing prologue (FC1); 2: h formed from FC1's
-// partials while staging (FC2).  Modes 0 and 1 are held to 128 VGPRs (four
-// waves per SIMD): the four-row body then spills a few registers but the FC1
-// call at T=4 runs faster (16.1 -> 15.5 us); mode 2 keeps its registers
-// (capped it spills far more and FC2 slows down).
-template <int FMT, int MRMAX, int MODE>
-__global__ __launch_bounds__(max_waves<MRMAX>() * 64) __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 1 : 4))) void fp4_gemv_kernel(GemvArgs a) {
+// partials while staging (FC2).  The plain single-pass variants are held to
+// 128 VGPRs (four waves per SIMD), which the four-row body fits without
+// spilling once its weight registers may die as they are decoded (FC1 call
+// at T=4 16.1 -> 15.5 us); the other variants would spill under that cap.
+// MULTI: an expert may hold more than MRMAX rows (several row passes); the
+// single-pass variants let the weight registers die as they are decoded.
+template <int FMT, int MRMAX, int MODE, bool MULTI>
+__global__ __launch_bounds__(max_waves<MRMAX>() * 64) __attribute__((amdgpu_waves_per_eu(MODE == 0 && !MULTI ? 4 : 1))) void fp4_gemv_kernel(GemvArgs a) {
   constexpr int B = (FMT == 0) ? 16 : 32;
   constexpr int NBLK = kGemvLaneK / B;
   __shared__ __attribute__((aligned(16))) Smem<MRMAX> sm;
@@ -437,10 +439,12 @@ __global__ __launch_bounds__(max_waves<MRMAX>() * 64) __attribute__((amdgpu_wave
     // Opaque to the optimiser: a later pass sees the weights as new values,
     // so their decode stays inside each pass (hoisted out of the loop it would
     // keep all 128 decoded registers live).
+    if constexpr (MULTI) {
 #pragma unroll
-    for (int i = 0; i < kGemvLaneK; ++i) asm volatile("" : "+v"(A[i]));
+      for (int i = 0; i < kGemvLaneK; ++i) asm volatile("" : "+v"(A[i]));
 #pragma unroll
-    for (int b = 0; b < 2; ++b) asm volatile("" : "+v"(SB[b]));
+      for (int b = 0; b < 2; ++b) asm volatile("" : "+v"(SB[b]));
+    }
     lds_barrier();
 
     // ---- reduce the W waves (fixed order); one thread per column ------------
@@ -462,10 +466,12 @@ __global__ __launch_bounds__(max_waves<MRMAX>() * 64) __attribute__((amdgpu_wave
     }
   };
   pass(0);
+  if constexpr (MULTI) {
 #pragma nounroll
-  for (int rbase = MRMAX; rbase < m; rbase += MRMAX) {
-    lds_barrier();  // the previous pass's reduction has read sm.red
-    pass(rbase);
+    for (int rbase = MRMAX; rbase < m; rbase += MRMAX) {
+      lds_barrier();  // the previous pass's reduction has read sm.red
+      pass(rbase);
+    }
   }
 }
 
@@ -577,13 +583,20 @@ hipError_t launch_fp4_gemv(const GemvArgs &a, int fmt, int max_rows_per_expert, 
   // Rows per pass: one when no expert can hold more than one row (one
   // token), two for up to three tokens, else four.
   const int mr = max_rows_per_expert <= 1 ? 1 : (max_rows_per_expert <= 3 ? 2 : 4);
+  // an expert holds at most max_rows_per_expert rows (a token selects it at
+  // most once): one pass when that fits the pass size
+  const bool multi = max_rows_per_expert > mr;
 #define QMOE_GEMV_LAUNCH(F, M)                                     \
   if (mr == 1)                                                     \
-    fp4_gemv_kernel<F, 1, M><<<grid, block, 0, s>>>(a);            \
+    fp4_gemv_kernel<F, 1, M, false><<<grid, block, 0, s>>>(a);     \
+  else if (mr == 2 && !multi)                                      \
+    fp4_gemv_kernel<F, 2, M, false><<<grid, block, 0, s>>>(a);     \
   else if (mr == 2)                                                \
-    fp4_gemv_kernel<F, 2, M><<<grid, block, 0, s>>>(a);            \
+    fp4_gemv_kernel<F, 2, M, true><<<grid, block, 0, s>>>(a);      \
+  else if (!multi)                                                 \
+    fp4_gemv_kernel<F, 4, M, false><<<grid, block, 0, s>>>(a);     \
   else                                                             \
-    fp4_gemv_kernel<F, 4, M><<<grid, block, 0, s>>>(a);
+    fp4_gemv_kernel<F, 4, M, true><<<grid, block, 0, s>>>(a);
   const int mode = a.route_logits ? 1 : (a.h_partials ? 2 : 0);
   if (fmt == 0) {
     if (mode == 1) {
