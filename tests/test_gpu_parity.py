@@ -35,6 +35,8 @@ SMALL = [
     synth.shrink(synth.MX_DECODE, E=40, T=8, k=8, H=544, I=160, seed=3),      # MXFP4, ragged
     synth.shrink(synth.DECODE, E=16, T=64, k=1, H=256, I=64, seed=4),         # m up to 64 per expert
     synth.shrink(synth.MX_DECODE, E=4, T=16, k=4, H=1024, I=512, seed=5),     # every expert has 16 rows
+    synth.shrink(synth.MTP4, E=32, T=2, k=8, H=512, I=192, seed=26),          # T=2: one two-row pass
+    synth.shrink(synth.MTP4, E=32, T=3, k=8, H=512, I=192, seed=27),          # T=3: two-row passes, 3-row experts
 ]
 FULL = [synth.TINY, synth.DECODE, synth.MTP4, synth.MTP8]
 
@@ -458,7 +460,7 @@ def test_route_fc1_equals_separate_calls(cfg, mode):
         assert np.array_equal(got, r), name
 
 
-LAYER_DECODE = ROUTE_FC1 + [
+LAYER_DECODE = ROUTE_FC1 + SMALL[-2:] + [
     synth.shrink(synth.DECODE, E=8, T=2, k=2, H=2304, I=96, seed=24),      # FC1 in 9 k chunks; FC2 K = 96 < its chunk
     synth.shrink(synth.MX_DECODE, E=12, T=16, k=4, H=1024, I=256, seed=25),  # MXFP4, experts with > 4 rows
 ]
