@@ -9,7 +9,7 @@
 // column and each lane loads 16 consecutive k with one 16-byte load.  A lane
 // row covers CPR columns (1 for K >= 1536, 2 for K >= 768, else 4, so a lane
 // keeps up to 8 loads in flight even for short K), a wave 4 * CPR columns, a
-// workgroup of 8 waves 32 * CPR, over the whole K in passes (8 loads per lane
+// workgroup of 4 waves 16 * CPR, over the whole K in passes (8 loads per lane
 // per pass): there is no split-K and no second launch.  Rows go in passes of
 // up to 8 per workgroup, so any batch works; a prefill batch re-reads an
 // expert's columns (from L2) once per 8 rows.
@@ -22,10 +22,11 @@
 
 namespace qmoe {
 
-constexpr int kF8Waves = 8;
+constexpr int kF8Waves = 4;                          // measured against 8 and 16 (fewer, larger workgroups: slower)
 constexpr int kF8Loads = 8;                          // 16-byte loads per lane per pass
 constexpr int kF8PassK = 16 * 16 * kF8Loads;         // 2048 k per pass (CPR = 1)
-constexpr int kF8TileN1 = kF8Waves * 4;              // 32 columns per workgroup and column per lane row
+constexpr int kF8TileN1 = kF8Waves * 4;              // 16 columns per workgroup and column per lane row
+static_assert(kF8Waves * 64 * 8 >= kF8PassK, "one 8-value staging load per thread covers a pass");
 constexpr uint32_t kF8OutOfRange = 0x80000000u;
 
 __device__ __forceinline__ float row16_sum(float v) {
