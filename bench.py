@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=80)
     ap.add_argument("--eager", action="store_true")
+    ap.add_argument("--path", default="auto", choices=("auto", "gemv", "grouped"),
+                    help="FC kernel path of the layer workloads (auto: the library's AUTO rule)")
     ap.add_argument("--workload", default="mtp4", choices=LAYER_WORKLOADS + ("dequant", "fp8_dequant"))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -175,7 +177,8 @@ def bench_layer(args, torch, q, synth, np):
             copies.append((q.FP4Weights(t[0], t[1], t[2], fmt), q.FP4Weights(t[3], t[4], t[5], fmt)))
     logits = to_dev(L.logits)
     x = to_dev(L.x.view(np.int16)).view(torch.bfloat16)
-    layer = MoELayer(cfg.T, cfg.E, cfg.k, cfg.H, cfg.I, copies[0][0], copies[0][1], device=dev)
+    path = {"auto": q.QMOE_PATH_AUTO, "gemv": q.QMOE_PATH_GEMV, "grouped": q.QMOE_PATH_GROUPED}[args.path]
+    layer = MoELayer(cfg.T, cfg.E, cfg.k, cfg.H, cfg.I, copies[0][0], copies[0][1], path=path, device=dev)
     layer.run(logits, x)
     torch.cuda.synchronize()
     offsets = layer.offsets.cpu().numpy()
@@ -223,7 +226,7 @@ def bench_layer(args, torch, q, synth, np):
         sources = ("fp8.hip", "device_common.h", "qmoe_internal.h")
         kname, tname = "fp8_gemv_kernel (FC1+SwiGLU)", "fp8_gemv_fc1_mtp4"
         metric = "FP8 W8A16 MoE decode µs/layer + achieved HBM GB/s on weight bytes"
-    elif q.qmoe_fp4_resolve_path(cfg.T, cfg.k, copies[0][0]) == q.QMOE_PATH_GROUPED:
+    elif q.qmoe_fp4_resolve_path(cfg.T, cfg.k, copies[0][0], path) == q.QMOE_PATH_GROUPED:
         sources = ("grouped.hip", "device_common.h", "qmoe_internal.h")
         kname, tname = "grouped_gemm_kernel (FC1+SwiGLU)", f"grouped_fc1_{args.workload}"
         metric = METRIC
@@ -232,7 +235,7 @@ def bench_layer(args, torch, q, synth, np):
         kname, tname = "fp4_gemv_kernel + splitk_epilogue_kernel (FC1+SwiGLU)", f"gemv_fc1_{args.workload}"
         metric = METRIC
     config = {"workload": cfg.name, "rows": R, "distinct_experts": D, "layer_copies": layers,
-              "launch": "eager" if args.eager else "hip_graph"}
+              "path": args.path, "launch": "eager" if args.eager else "hip_graph"}
     result = base_result(metric, value, "GB/s", args, ms, config)
     result.update({"us_per_layer": round(ms * 1e3, 3), "hbm_frac_weight_bytes": round(value / HBM_PEAK_GBS, 4),
                    "weight_bytes_per_layer": weight_bytes})

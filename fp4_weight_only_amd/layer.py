@@ -47,7 +47,10 @@ class MoELayer:
         # (FC1's SwiGLU folded into FC2's staging, h not written)
         fits = (not self.fp8 and R <= GEMV_MAX_ROWS and w2.w.shape[0] == w1.w.shape[0]
                 and w2.w.shape[1] == w1.w.shape[2] and 2 * w2.w.shape[2] == w1.w.shape[1])
-        self.layer_decode = (fits and path != QMOE_PATH_GROUPED
+        # used where measured to pay: T <= 4 and FC1 in at most eight k chunks
+        # (H <= 2048), so FC2's staging reads every plane ahead of its weights
+        # (MXFP4 T=8, H=4096 on the GEMV path: 169 us separate, 193 us fused)
+        self.layer_decode = (fits and path != QMOE_PATH_GROUPED and T <= 4 and H <= 2048
                              and qmoe_fp4_resolve_path(T, k, w1, path) == QMOE_PATH_GEMV
                              and qmoe_fp4_resolve_path(T, k, w2, path) == QMOE_PATH_GEMV)
         if not self.fp8 and R <= GEMV_MAX_ROWS:  # route_fc1() is callable

@@ -107,12 +107,16 @@ def test_layer_full(cfg):
     check_layer(synth.layer_inputs(cfg))
 
 
-def test_layer_mxfp4_decode_full_sampled():
+@pytest.mark.parametrize("path", ["gemv", "auto"])
+def test_layer_mxfp4_decode_full_sampled(path):
+    # the 8-token MXFP4 decode at full size on the GEMV path, and as AUTO
+    # runs it (the grouped kernel for T > 4 at this N)
+    import fp4_weight_only_amd as q
     L = synth.layer_inputs(synth.MX_DECODE)
     rng = np.random.default_rng(0)
     cols1 = np.sort(rng.choice(L.cfg.I, 160, replace=False))
     cols2 = np.sort(rng.choice(L.cfg.H, 320, replace=False))
-    check_layer(L, cols1=cols1, cols2=cols2)
+    check_layer(L, cols1=cols1, cols2=cols2, path=q.QMOE_PATH_GEMV if path == "gemv" else None)
 
 
 # Variants: concatenated SwiGLU columns (swiglu_fusion=2), MXFP4 with
