@@ -52,21 +52,15 @@ qmoe_status check_fc(const qmoe_fp4_weights *w, int32_t T, int32_t k, const void
 }
 
 // Resolves AUTO and checks the row window and tile shape of each path.
-// AUTO: the grouped MFMA kernel above the GEMV's 64-row window, and inside
-// it when an expert can hold more than four rows (the GEMV then runs several
-// row passes of VALU dot products) and N spans at least four of the grouped
-// kernel's 512-column tiles (enough workgroups without split-K).  Measured
-// on MI355X: MXFP4 T=8 (H=4096, I=2048) FC1 122 -> 100 us, FC2 64 -> 57 us;
-// NVFP4 T=8 FC2 (N=2048) 27 -> 23 us; NVFP4 T=8 FC1 (N=1536, three tiles)
-// and every T=4 shape stay faster on the GEMV.
+// AUTO follows the decode GEMV's 64-row window: the GEMV up to 64 expanded
+// rows, the grouped MFMA GEMM (the dense contraction of prefill) above.  The
+// grouped kernel also takes multi-row decode shapes when asked for
+// explicitly (MXFP4 T=8 layer: 143 us grouped against 171 us GEMV).
 qmoe_status resolve_path(qmoe_path path, int32_t rows, int32_t max_rows_per_expert, const qmoe_fp4_weights *w,
                          qmoe_path *out) {
+  (void)max_rows_per_expert;
   qmoe_path p = path;
-  if (p == QMOE_PATH_AUTO) {
-    const bool grouped_ok = w->K % 64 == 0 && w->N % 128 == 0;
-    const bool many_rows = max_rows_per_expert > 4 && (w->N + 511) / 512 >= 4;
-    p = rows > QMOE_GEMV_MAX_ROWS || (grouped_ok && many_rows) ? QMOE_PATH_GROUPED : QMOE_PATH_GEMV;
-  }
+  if (p == QMOE_PATH_AUTO) p = rows <= QMOE_GEMV_MAX_ROWS ? QMOE_PATH_GEMV : QMOE_PATH_GROUPED;
   if (p == QMOE_PATH_GEMV && rows > QMOE_GEMV_MAX_ROWS) return QMOE_EUNSUPPORTED;
   if (p == QMOE_PATH_GROUPED && (w->K % 64 != 0 || w->N % 128 != 0)) return QMOE_EUNSUPPORTED;
   // buffer resources address the activations of a call in 32 bits

@@ -89,9 +89,7 @@ typedef enum {
 } qmoe_fmt;
 
 typedef enum {
-  QMOE_PATH_AUTO = 0,     /* GEMV for T*k <= 64 expanded rows, GROUPED above; inside the GEMV
-                             window GROUPED when T > 4 and N > 1536 (at least four 512-column
-                             tiles) and the grouped shape limits hold                          */
+  QMOE_PATH_AUTO = 0,     /* GEMV for T*k <= 64 expanded rows, GROUPED above                   */
   QMOE_PATH_GEMV = 1,     /* FP4 decode GEMV; rejects T*k > 64 with QMOE_EUNSUPPORTED          */
   QMOE_PATH_GROUPED = 2   /* MFMA bf16 grouped GEMM over LDS-dequantised weight tiles          */
 } qmoe_path;

@@ -144,9 +144,9 @@ def test_route_router_weights_validation(q):
 
 
 def test_auto_path_rule(q):
-    """AUTO inside the 64-row window: the grouped kernel when T > 4 and N
-    spans more than three 512-column tiles, else the GEMV (seen through the
-    workspace size each path asks for)."""
+    """AUTO: the GEMV up to 64 expanded rows, the grouped kernel above (seen
+    through qmoe_fp4_resolve_path and the workspace size each path asks for);
+    the grouped kernel serves the decode window when asked for explicitly."""
     n = ctypes.c_size_t(0)
 
     def size(T, k, K, N, path):
@@ -163,19 +163,16 @@ def test_auto_path_rule(q):
         st = q.lib.qmoe_fp4_resolve_path(T, k, ctypes.byref(wc), path, ctypes.byref(res))
         return st, res.value
 
-    assert resolved(8, 8, 768, 2048) == (q.QMOE_OK, G)
-    assert resolved(8, 8, 2048, 1536) == (q.QMOE_OK, V)
-    assert resolved(4, 8, 768, 2048) == (q.QMOE_OK, V)
-    assert resolved(8, 8, 784, 2048) == (q.QMOE_OK, V)
+    assert resolved(8, 8, 768, 2048) == (q.QMOE_OK, V)              # 64 rows: the GEMV window
+    assert resolved(1, 8, 2048, 1536) == (q.QMOE_OK, V)
     assert resolved(9, 8, 2048, 1536) == (q.QMOE_OK, G)             # 72 rows
+    assert resolved(8, 8, 768, 2048, G) == (q.QMOE_OK, G)           # explicit grouped inside the window
     assert resolved(9, 8, 2048, 1536, V)[0] == q.QMOE_EUNSUPPORTED  # past the GEMV window
     assert resolved(8, 8, 784, 2048, G)[0] == q.QMOE_EUNSUPPORTED   # K % 64
     assert q.lib.qmoe_fp4_resolve_path(1, 1, ctypes.byref(weights(q)), AU, None) == q.QMOE_EINVAL
     assert size(8, 8, 768, 2048, G) != size(8, 8, 768, 2048, V)
-    assert size(8, 8, 768, 2048, AU) == size(8, 8, 768, 2048, G)      # T = 8, four n tiles
-    assert size(8, 8, 2048, 1536, AU) == size(8, 8, 2048, 1536, V)    # three n tiles
-    assert size(4, 8, 768, 2048, AU) == size(4, 8, 768, 2048, V)      # T = 4
-    assert size(8, 8, 784, 2048, AU) == size(8, 8, 784, 2048, V)      # K % 64 != 0: no grouped path
+    assert size(8, 8, 768, 2048, AU) == size(8, 8, 768, 2048, V)
+    assert size(9, 8, 768, 2048, AU) == size(9, 8, 768, 2048, G)
 
 
 def test_route_fc1_validation_and_workspace(q):
