@@ -30,8 +30,8 @@ byte count per launch measured with FETCH_SIZE + WRITE_SIZE counters and
 scaled by the copy calibration, read from profiles/ and reported only while
 the kernel source it was taken on is unchanged (else null).
 
-cpu_baseline: the CPU oracle (test infrastructure, float64 numpy, one
-thread) timed on a bounded sample of the same workload.
+cpu_baseline: the C++ CPU oracle (test infrastructure, float64, single-
+threaded) timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -287,7 +287,8 @@ def bench_dequant(args, torch, q, synth, np):
                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                           "traffic": traffic, "avg_us": round(ms * 1e3, 3), "bytes_per_launch": rd + wr}
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline_dequant(w, s, g, cfg, args.cpu_seconds)
+        per = w[0].nbytes + s[0].nbytes + cfg.N * cfg.K * 2
+        result["cpu_baseline"] = cpu_baseline_dequant(w, s, g, cfg.fmt, cfg.E, per, cfg.name, args.cpu_seconds)
     return result
 
 
@@ -316,18 +317,8 @@ def bench_fp8_dequant(args, torch, q, synth, np):
                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                           "traffic": None, "avg_us": round(ms * 1e3, 3), "bytes_per_launch": rd + wr}
     if not args.no_cpu_baseline:
-        from threadpoolctl import threadpool_limits
-
-        from oracle import dequant
-        with threadpool_limits(limits=1):
-            n, t0 = 0, time.perf_counter()
-            while time.perf_counter() - t0 < args.cpu_seconds and n < c.E:
-                dequant.dequant_fp8_bf16(w[n:n + 1], g[n:n + 1])
-                n += 1
-            el = time.perf_counter() - t0
-        result["cpu_baseline"] = {"value": round(n * (w[0].nbytes * 3) / el / 1e9, 4), "unit": "GB/s", "cores": 1,
-                                  "kind": "oracle", "sample": f"{n} of {c.E} experts, float64 numpy, {el:.1f} s",
-                                  "host_cores_total": os.cpu_count()}
+        result["cpu_baseline"] = cpu_baseline_dequant(w, None, g, "fp8", c.E, w[0].nbytes * 3, cfg.name,
+                                                      args.cpu_seconds)
     return result
 
 
@@ -345,73 +336,64 @@ def calibrate_copy(args, torch):
 
 
 def cpu_baseline_layer(L, weight_bytes, budget_s):
-    """The oracle as it stands, one thread, on the same layer (bounded sample)."""
-    from threadpoolctl import threadpool_limits
-
-    from oracle import moe
-    with threadpool_limits(limits=1):
-        n, t0 = 0, time.perf_counter()
-        while True:
-            moe.layer(L)
-            n += 1
-            el = time.perf_counter() - t0
-            if el >= budget_s or n >= 20:
-                break
+    """The C++ oracle as it stands (single-threaded, float64) on whole layers of the same workload."""
+    from oracle import cpp
+    cpp.lib()
+    n, t0 = 0, time.perf_counter()
+    while True:
+        cpp.layer(L)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 20:
+            break
     per_layer = el / n
     return {"value": round(weight_bytes / per_layer / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} full layers of {L.cfg.name} (route, FC1+SwiGLU, FC2, finalize), float64 numpy, "
+            "sample": f"{n} full layers of {L.cfg.name} (route, FC1+SwiGLU, FC2, finalize), C++ float64 oracle, "
                       f"{per_layer * 1e3:.1f} ms/layer",
             "host_cores_total": os.cpu_count()}
 
 
 def cpu_baseline_prefill(L, D, expert_bytes, budget_s):
-    """The oracle's FC1+SwiGLU and FC2 on the rows of the first experts (in expert order) until the
-    budget runs out; GB/s on the weight bytes of the experts processed."""
+    """The C++ oracle's FC1+SwiGLU and FC2 on the rows of the first routed experts (in expert order), one
+    expert per call, until the budget runs out; GB/s on the weight bytes of the experts processed."""
     import numpy as np
-    from threadpoolctl import threadpool_limits
 
-    from oracle import dequant, moe, route
+    from oracle import cpp
     c = L.cfg
-    with threadpool_limits(limits=1):
-        idx, _ = route.route_topk(L.logits, c.k)
-        off, p2e, _ = route.expert_maps(idx, c.E)
-        x64 = moe.codecs.bf16_to_f64(L.x)
-        n, rows, t0 = 0, 0, time.perf_counter()
-        for e in range(c.E):
-            lo, hi = int(off[e]), int(off[e + 1])
-            if lo == hi:
-                continue
-            s1 = None if L.s1 is None else L.s1[e]
-            s2 = None if L.s2 is None else L.s2[e]
-            g1 = None if L.g1 is None else L.g1[e]
-            g2 = None if L.g2 is None else L.g2[e]
-            u = x64[np.asarray(p2e[lo:hi]) // c.k] @ dequant.expert_weights_f64(L.w1[e], s1, g1, c.fmt)
-            hb = moe.codecs.bf16_from_f64(moe.swiglu(u[:, 0::2], u[:, 1::2]))
-            moe.codecs.bf16_to_f64(hb) @ dequant.expert_weights_f64(L.w2[e], s2, g2, c.fmt)
-            n, rows = n + 1, rows + hi - lo
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        el = time.perf_counter() - t0
+    cpp.lib()
+    idx, _ = cpp.route_topk(L.logits, c.k)
+    off, p2e, _ = cpp.expert_maps(idx, c.E)
+    n, rows, t0 = 0, 0, time.perf_counter()
+    for e in range(c.E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if lo == hi:
+            continue
+        # maps of a batch that holds only expert e's rows
+        sub = np.where(np.arange(c.E + 1) <= e, 0, hi - lo).astype(np.int32)
+        h, _ = cpp.fc1_swiglu(L.x, c.k, L.w1, L.s1, L.g1, c.fmt, sub, p2e[lo:hi], want_u=False)
+        cpp.fc2(h, L.w2, L.s2, L.g2, c.fmt, sub)
+        n, rows = n + 1, rows + hi - lo
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
     return {"value": round(n * expert_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"FC1+SwiGLU and FC2 of {n} of {D} routed experts ({rows} of {c.rows} rows) of {c.name}, "
-                      f"float64 numpy, {el:.1f} s", "host_cores_total": os.cpu_count()}
+                      f"C++ float64 oracle, {el:.1f} s", "host_cores_total": os.cpu_count()}
 
 
-def cpu_baseline_dequant(w, s, g, cfg, budget_s):
-    from threadpoolctl import threadpool_limits
-
-    from oracle import dequant
-    with threadpool_limits(limits=1):
-        n, t0 = 0, time.perf_counter()
-        while n < cfg.E:
-            dequant.dequant_bf16(w[n:n + 1], s[n:n + 1], None if g is None else g[n:n + 1], cfg.fmt)
-            n += 1
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        el = time.perf_counter() - t0
-    per = (w[0].nbytes + s[0].nbytes + cfg.N * cfg.K * 2)
-    return {"value": round(n * per / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} of {cfg.E} experts of {cfg.name}, float64 numpy, {el:.1f} s",
+def cpu_baseline_dequant(w, s, g, fmt, E, per_expert_bytes, name, budget_s):
+    """The C++ oracle's dequant, one expert per call, until the budget runs out."""
+    from oracle import cpp
+    cpp.lib()
+    n, t0 = 0, time.perf_counter()
+    while n < E:
+        cpp.dequant_bf16(w[n:n + 1], None if s is None else s[n:n + 1], None if g is None else g[n:n + 1], fmt)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(n * per_expert_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} of {E} experts of {name}, C++ float64 oracle, {el:.1f} s",
             "host_cores_total": os.cpu_count()}
 
 

@@ -6,8 +6,10 @@ and the CPU-baseline leg of the benchmark may import it.  The product path
 (the HIP library and its Python binding) never imports, calls or links it,
 and it shares no code with that path.
 
-Arithmetic is numpy float64.  Every function cites the passage of the pages
-it follows:
+It holds two independent definitions: the numpy float64 modules below, and
+a plain single-threaded C++17 float64 oracle (qmoe_oracle.cpp, loaded by
+cpp.py through ctypes) that shares no code with them.  Every function cites
+the passage of the pages it follows:
 
   * "[CUDA] Speed up the NVFP4 QMoE decode GEMV and enable it for MTP verify"
     (onnxruntime PR 31159) -- the decode GEMV, expanded rows up to 64;
@@ -20,5 +22,6 @@ it follows:
 
 Modules: codecs (E2M1, E4M3FN, E8M0, bfloat16 rounding), dequant, route
 (softmax top-k and expert maps), moe (FC1+SwiGLU, FC2, finalize, layer),
-tolerance (the floating-point comparison rule).
+tolerance (the floating-point comparison rule), cpp (the C++ oracle: the
+same steps, same call names as route / moe).
 """

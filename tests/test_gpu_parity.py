@@ -14,7 +14,7 @@ import torch
 import synth
 from gpu_util import bf16_dev, bf16_host, layer_dev, print_case, to_dev, weights_dev
 from ties import h_roundings_differ_only_at_ties
-from oracle import codecs, dequant, moe, route, tolerance
+from oracle import codecs, cpp, dequant, moe, route, tolerance
 
 pytestmark = pytest.mark.gpu
 
@@ -58,34 +58,36 @@ def assert_close(name, gpu, ref):
     assert ok, (name, rep)
 
 
-def check_layer(L, act=None, cols1=None, cols2=None, path=None, rw=None):
-    """act: (alpha, beta, limit[, fusion]); rw: router_weights [T][E] or None."""
+def check_layer(L, act=None, cols1=None, cols2=None, path=None, rw=None, orc="numpy"):
+    """act: (alpha, beta, limit[, fusion]); rw: router_weights [T][E] or None;
+    orc: "numpy" (oracle.route / oracle.moe) or "cpp" (the C++ oracle, same calls)."""
     c = L.cfg
+    R, M = (route, moe) if orc == "numpy" else (cpp, cpp)
     g = run_gpu_layer(L, act, path, rw)
     oact = None if act is None else dict(alpha=act[0], beta=act[1], limit=act[2],
                                          fusion=act[3] if len(act) > 3 else 1)
     # routing and maps: bit-exact
     if rw is None:
-        idx, wts = route.route_topk(L.logits, c.k)
+        idx, wts = R.route_topk(L.logits, c.k)
     else:
-        idx, wts = route.route_topk_router_weights(L.logits, rw, c.k)
+        idx, wts = R.route_topk_router_weights(L.logits, rw, c.k)
         assert np.array_equal(g["w"], wts)     # a gather: exact
-    off, p2e, e2p = route.expert_maps(idx, c.E)
+    off, p2e, e2p = R.expert_maps(idx, c.E)
     assert np.array_equal(g["idx"], idx)
     assert np.array_equal(g["offsets"], off)
     assert np.array_equal(g["p2e"], p2e)
     assert np.array_equal(g["e2p"], e2p)
     assert_close("topk_w", g["w"], wts)
     # FC1 stage (inputs identical to the oracle's)
-    h_ref, u_ref = moe.fc1_swiglu(L.x, c.k, L.w1, L.s1, L.g1, c.fmt, off, p2e, oact, cols=cols1)
+    h_ref, u_ref = M.fc1_swiglu(L.x, c.k, L.w1, L.s1, L.g1, c.fmt, off, p2e, oact, cols=cols1)
     hsel = slice(None) if cols1 is None else cols1
     assert_close("h", codecs.bf16_to_f64(g["h"])[:, hsel], codecs.bf16_to_f64(h_ref)[:, hsel])
     # FC2 stage, fed the GPU's h
-    y_ref = moe.fc2(g["h"], L.w2, L.s2, L.g2, c.fmt, off, cols=cols2)
+    y_ref = M.fc2(g["h"], L.w2, L.s2, L.g2, c.fmt, off, cols=cols2)
     ysel = slice(None) if cols2 is None else cols2
     assert_close("y", g["y"][:, ysel], y_ref)
     # finalize stage, fed the GPU's y and weights
-    out_ref = moe.finalize(g["y"], g["w"], g["e2p"], c.T, c.k)
+    out_ref = M.finalize(g["y"], g["w"], g["e2p"], c.T, c.k)
     assert_close("out(stage)", g["out"], out_ref)
     # end to end: the oracle chain from the inputs, with h's rounding taken the
     # GPU's way only where it is a tie (see h_roundings_differ_only_at_ties)
@@ -93,7 +95,7 @@ def check_layer(L, act=None, cols1=None, cols2=None, path=None, rw=None):
         # (after the tie check the GPU's h is that chain's h, so y_ref is its y)
         ties = h_roundings_differ_only_at_ties(L, g["h"], h_ref, u_ref, oact, off, p2e)
         print("h rounding ties", ties, flush=True)
-        assert_close("out(e2e)", g["out"], moe.finalize(y_ref, wts, e2p, c.T, c.k))
+        assert_close("out(e2e)", g["out"], M.finalize(y_ref, wts, e2p, c.T, c.k))
     return g
 
 
@@ -640,3 +642,36 @@ def test_determinism_and_poisoned_buffers():
         again = [bf16_host(layer.h), layer.y.cpu().numpy(), bf16_host(layer.out)]
         for a, b in zip(first, again):
             assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+# The same layers against the C++ oracle (plain single-threaded float64,
+# written independently of the numpy oracle): the full decode, MTP-verify
+# and FP8 layers, a grouped-path batch, the prefill layer on sampled columns
+# and the full standalone dequant.
+CPP_LAYERS = [synth.TINY, synth.DECODE, synth.MTP4, synth.MTP8, synth.FP8_MTP4, GROUPED[0], GROUPED[3]]
+
+
+@pytest.mark.parametrize("cfg", CPP_LAYERS, ids=lambda c: c.name)
+def test_layer_against_cpp_oracle(cfg):
+    check_layer(synth.layer_inputs(cfg), orc="cpp")
+
+
+def test_prefill_full_sampled_against_cpp_oracle():
+    L = synth.layer_inputs(synth.MX_PREFILL)
+    rng = np.random.default_rng(2)
+    cols1 = np.sort(rng.choice(L.cfg.I, 48, replace=False))
+    cols2 = np.sort(rng.choice(L.cfg.H, 64, replace=False))
+    check_layer(L, cols1=cols1, cols2=cols2, orc="cpp")
+
+
+def test_dequant_full_config_against_cpp_oracle():
+    import fp4_weight_only_amd as q
+    c = synth.DEQUANT
+    w, s, g = synth.dequant_inputs(c)
+    out = torch.empty((c.E, c.N, c.K), dtype=torch.bfloat16, device="cuda")
+    print_case("dequant full (C++ oracle)", c.name)
+    q.qmoe_dequant_fp4(weights_dev(w, s, g, c.fmt), out)
+    torch.cuda.synchronize()
+    got = bf16_host(out)
+    for e in range(c.E):
+        assert np.array_equal(got[e], cpp.dequant_bf16(w[e:e + 1], s[e:e + 1], None, c.fmt)[0]), e
