@@ -129,6 +129,54 @@ __device__ __forceinline__ int find_slot_expert(const int32_t *__restrict__ off,
   return __builtin_amdgcn_readlane(found, src);
 }
 
+// Slot s when every expert's rows are dealt out in groups of at most G: an
+// expert with m rows owns ceil(m / G) consecutive slots (experts in
+// ascending order, its groups in row order).  Returns the expert, the
+// group's first row and row count (every lane the same answer), or -1 when
+// s is past the last group.  A lane covers experts 4*lane .. 4*lane + 3
+// (E <= 256); a wave prefix sum of the per-lane group counts locates s.
+__device__ __forceinline__ int find_slot_group(const int32_t *__restrict__ off, int E, int s, int G, int &row0,
+                                               int &m) {
+  const int lane = lane_id();
+  int o[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int e = 4 * lane + i;
+    o[i] = (e <= E) ? off[e] : 0;
+  }
+  int cnt[4], grp[4], local = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    cnt[i] = (4 * lane + i < E) ? o[i + 1] - o[i] : 0;
+    grp[i] = (cnt[i] + G - 1) / G;
+    local += grp[i];
+  }
+  int incl = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
+  }
+  int found = -1, r0 = 0, rc = 0;
+  int run = incl - local;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (found < 0 && s >= run && s < run + grp[i]) {
+      const int q = s - run;
+      found = 4 * lane + i;
+      r0 = o[i] + q * G;
+      rc = (cnt[i] - q * G) < G ? (cnt[i] - q * G) : G;
+    }
+    run += grp[i];
+  }
+  const unsigned long long fb = __ballot(found >= 0);
+  if (fb == 0ull) return -1;
+  const int src = __ffsll((long long)fb) - 1;
+  row0 = __builtin_amdgcn_readlane(r0, src);
+  m = __builtin_amdgcn_readlane(rc, src);
+  return __builtin_amdgcn_readlane(found, src);
+}
+
 // SwiGLU(G, L) = G * sigmoid(alpha G) * (L + beta), G = min(gate, limit),
 // L = clamp(lin, -limit, limit) (operator documentation section 8).
 __device__ __forceinline__ float swiglu(float gate, float lin, float alpha, float beta, float limit) {

@@ -30,9 +30,11 @@
 // * Work items (expert slot, column tile) are spread round-robin over the 8
 //   XCDs and all k chunks of an item land on the same XCD.
 // * The routed experts are found on the device from expert_offsets (wave
-//   ballots); grids are sized for the worst case and idle slots exit.  Rows
-//   of an expert are processed in passes of one row (single-token batches),
-//   two rows (up to 3 tokens) or four rows.
+//   ballots); grids are sized for the worst case and idle slots exit.  A
+//   workgroup runs one pass over at most one row (single-token batches), two
+//   rows (up to 3 tokens) or four rows; an expert holding more rows is dealt
+//   out over several slots of at most a pass each (a wave prefix sum of the
+//   per-expert group counts), so no workgroup runs longer than one pass.
 // * Two fused modes (template MODE): 1, every workgroup of an FC1 launch
 //   first runs the routing of all tokens (top-k per wave, one-wave expert
 //   maps in LDS) and takes its expert from LDS; 2, FC2 stages its bf16
@@ -283,10 +285,11 @@ __device__ __forceinline__ u32x2_t h_from_sums(const GemvArgs &a, float4 s0, flo
 // 128 VGPRs (four waves per SIMD), which the four-row body fits without
 // spilling once its weight registers may die as they are decoded (FC1 call
 // at T=4 16.1 -> 15.5 us); the other variants would spill under that cap.
-// MULTI: an expert may hold more than MRMAX rows (several row passes); the
-// single-pass variants let the weight registers die as they are decoded.
-template <int FMT, int MRMAX, int MODE, bool MULTI>
-__global__ __launch_bounds__(max_waves<MRMAX>() * 64) __attribute__((amdgpu_waves_per_eu(MODE == 0 && !MULTI ? 4 : 1))) void fp4_gemv_kernel(GemvArgs a) {
+// A workgroup runs one pass of at most MRMAX rows: an expert with more rows
+// is dealt out over several slots (gemv_plan), so the weight registers die
+// as they are decoded.
+template <int FMT, int MRMAX, int MODE>
+__global__ __launch_bounds__(max_waves<MRMAX>() * 64) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? 4 : 1))) void fp4_gemv_kernel(GemvArgs a) {
   constexpr int B = (FMT == 0) ? 16 : 32;
   constexpr int NBLK = kGemvLaneK / B;
   __shared__ __attribute__((aligned(16))) Smem<MRMAX> sm;
@@ -320,7 +323,8 @@ __global__ __launch_bounds__(max_waves<MRMAX>() * 64) __attribute__((amdgpu_wave
   // path): fetch it together with the offsets, one lane per row.
   const int p2e_l = (a.fc1 && lane < a.rows) ? p2e[lane] : 0;
   int row0 = 0, m = 0;
-  const int e = find_slot_expert(offs, a.E, slot, row0, m);
+  const int e = a.split_rows > 0 ? find_slot_group(offs, a.E, slot, a.split_rows, row0, m)
+                                 : find_slot_expert(offs, a.E, slot, row0, m);
   if (e < 0) return;  // uniform over the workgroup
 
   // ---- activation rows of the first pass, then the weights ---------------------
@@ -436,15 +440,6 @@ __global__ __launch_bounds__(max_waves<MRMAX>() * 64) __attribute__((amdgpu_wave
       lane_dot<FMT, 2, MRMAX>(sm, A, SB, g, wave, lane);
     else
       lane_dot<FMT, 4, MRMAX>(sm, A, SB, g, wave, lane);  // 3 or 4 rows
-    // Opaque to the optimiser: a later pass sees the weights as new values,
-    // so their decode stays inside each pass (hoisted out of the loop it would
-    // keep all 128 decoded registers live).
-    if constexpr (MULTI) {
-#pragma unroll
-      for (int i = 0; i < kGemvLaneK; ++i) asm volatile("" : "+v"(A[i]));
-#pragma unroll
-      for (int b = 0; b < 2; ++b) asm volatile("" : "+v"(SB[b]));
-    }
     lds_barrier();
 
     // ---- reduce the W waves (fixed order); one thread per column ------------
@@ -466,13 +461,6 @@ __global__ __launch_bounds__(max_waves<MRMAX>() * 64) __attribute__((amdgpu_wave
     }
   };
   pass(0);
-  if constexpr (MULTI) {
-#pragma nounroll
-    for (int rbase = MRMAX; rbase < m; rbase += MRMAX) {
-      lds_barrier();  // the previous pass's reduction has read sm.red
-      pass(rbase);
-    }
-  }
 }
 
 // Split-K epilogue: sums the k-chunk partials of every (row, column) in chunk
@@ -569,8 +557,20 @@ size_t gemv_workspace_bytes(int32_t rows, int32_t max_rows_per_expert, int32_t E
   return part > 256 ? part : 256;
 }
 
+// Rows per pass: one when no expert can hold more than one row (one
+// token), two for up to three tokens, else four.
+static int rows_per_pass(int max_rows_per_expert) {
+  return max_rows_per_expert <= 1 ? 1 : (max_rows_per_expert <= 3 ? 2 : 4);
+}
+
 void gemv_plan(GemvArgs &a, int max_rows_per_expert, void *ws) {
-  a.nslots = a.rows < a.E ? a.rows : a.E;
+  // An expert that may hold more rows than a pass is dealt out over several
+  // slots of at most a pass each (workgroups of equal length; no pass loop).
+  // Slots needed: sum_e ceil(m_e / G) <= (rows + min(E, rows) * (G - 1)) / G.
+  const int mr = rows_per_pass(max_rows_per_expert);
+  const int nexp = a.rows < a.E ? a.rows : a.E;
+  a.split_rows = max_rows_per_expert > mr ? mr : 0;
+  a.nslots = a.split_rows ? (a.rows + nexp * (mr - 1)) / mr : nexp;
   a.ntiles = (a.N + kGemvTileN - 1) / kGemvTileN;
   plan_chunks(a.nslots * a.ntiles, a.K, plan_max_waves(max_rows_per_expert), a.nchunks, a.waves);
   a.partials = (float *)ws;
@@ -580,23 +580,17 @@ hipError_t launch_fp4_gemv(const GemvArgs &a, int fmt, int max_rows_per_expert, 
   const int items = a.nslots * a.ntiles;
   const dim3 grid((unsigned)(((items + 7) / 8) * 8 * a.nchunks));
   const dim3 block((unsigned)(a.waves * 64));
-  // Rows per pass: one when no expert can hold more than one row (one
-  // token), two for up to three tokens, else four.
-  const int mr = max_rows_per_expert <= 1 ? 1 : (max_rows_per_expert <= 3 ? 2 : 4);
-  // an expert holds at most max_rows_per_expert rows (a token selects it at
-  // most once): one pass when that fits the pass size
-  const bool multi = max_rows_per_expert > mr;
-#define QMOE_GEMV_LAUNCH(F, M)                                     \
-  if (mr == 1)                                                     \
-    fp4_gemv_kernel<F, 1, M, false><<<grid, block, 0, s>>>(a);     \
-  else if (mr == 2 && !multi)                                      \
-    fp4_gemv_kernel<F, 2, M, false><<<grid, block, 0, s>>>(a);     \
-  else if (mr == 2)                                                \
-    fp4_gemv_kernel<F, 2, M, true><<<grid, block, 0, s>>>(a);      \
-  else if (!multi)                                                 \
-    fp4_gemv_kernel<F, 4, M, false><<<grid, block, 0, s>>>(a);     \
-  else                                                             \
-    fp4_gemv_kernel<F, 4, M, true><<<grid, block, 0, s>>>(a);
+  // one pass of at most mr rows per workgroup: an expert holding more rows
+  // (a token selects an expert at most once, so at most max_rows_per_expert)
+  // was split over slots by gemv_plan
+  const int mr = rows_per_pass(max_rows_per_expert);
+#define QMOE_GEMV_LAUNCH(F, M)                               \
+  if (mr == 1)                                               \
+    fp4_gemv_kernel<F, 1, M><<<grid, block, 0, s>>>(a);      \
+  else if (mr == 2)                                          \
+    fp4_gemv_kernel<F, 2, M><<<grid, block, 0, s>>>(a);      \
+  else                                                       \
+    fp4_gemv_kernel<F, 4, M><<<grid, block, 0, s>>>(a);
   const int mode = a.route_logits ? 1 : (a.h_partials ? 2 : 0);
   if (fmt == 0) {
     if (mode == 1) {

@@ -22,6 +22,7 @@ struct GemvArgs {
   const float *gscale;     // may be null
   int32_t E, K, N, topk, rows;
   int32_t nslots, ntiles, nchunks;
+  int32_t split_rows;      // 0: a slot is one routed expert; G > 0: a group of at most G rows of one expert
   int32_t waves;           // waves per block; the k chunk is waves * 64 rows
   int32_t fc1;             // 1: act rows gathered by token, SwiGLU epilogue, bf16 out
   int32_t force_partials;  // GEMV: write g * partial sums even for one k chunk, run no epilogue
