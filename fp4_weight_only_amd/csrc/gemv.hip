@@ -391,9 +391,11 @@ __global__ __launch_bounds__(max_waves<MRMAX>() * 64) __attribute__((amdgpu_wave
     A[i] = __builtin_amdgcn_raw_buffer_load_b32(wr, woff, i * (int)rowbytes, kBufNontemporal);
   const float gs = a.gscale ? a.gscale[e] : 1.0f;
 
-  // ---- passes of up to MRMAX rows -----------------------------------------------
-  // The first pass is peeled out of the loop: in straight-line code each dot
-  // product waits only for its own weight rows.
+  // ---- the pass over the slot's rows (at most MRMAX) ----------------------------
+  // Straight-line code: each dot product waits only for its own weight rows.
+  // The body stays a lambda taking the first row (called once, with 0): the
+  // same body written inline compiled to a slower schedule (T=4 decode layer
+  // 30.8 -> 32.4 us, measured A/B on one box).
   auto pass = [&](const int rbase) {
     const int rem = m - rbase;
     const int mr = rem < MRMAX ? rem : MRMAX;
