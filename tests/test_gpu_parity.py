@@ -36,7 +36,7 @@ SMALL = [
     synth.shrink(synth.DECODE, E=16, T=64, k=1, H=256, I=64, seed=4),         # m up to 64 per expert
     synth.shrink(synth.MX_DECODE, E=4, T=16, k=4, H=1024, I=512, seed=5),     # every expert has 16 rows
     synth.shrink(synth.MTP4, E=32, T=2, k=8, H=512, I=192, seed=26),          # T=2: one two-row pass
-    synth.shrink(synth.MTP4, E=32, T=3, k=8, H=512, I=192, seed=27),          # T=3: two-row passes, 3-row experts
+    synth.shrink(synth.MTP4, E=32, T=3, k=8, H=512, I=192, seed=27),          # T=3: 3-row experts over two-row slots (2 + 1)
 ]
 FULL = [synth.TINY, synth.DECODE, synth.MTP4, synth.MTP8]
 
