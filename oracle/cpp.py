@@ -28,7 +28,7 @@ _lib = None
 
 
 def build() -> str:
-    tmp = LIB + ".tmp"
+    tmp = f"{LIB}.tmp{os.getpid()}"  # one temporary per process: concurrent builds do not collide
     cmd = ["g++", "-O2", "-std=c++17", "-Wall", "-Wextra", "-Werror", "-ffp-contract=off",
            "-shared", "-fPIC", SRC, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
