@@ -313,9 +313,10 @@ def bench_fp8_dequant(args, torch, q, synth, np):
               "launch": "eager" if args.eager else "hip_graph"}
     result = base_result("FP8 standalone dequant GB/s (read + write bytes)", gbs, "GB/s", args, ms, config,
                          dtype="u8")
+    traffic = measured_traffic("fp8_dequant", ("fp8.hip", "device_common.h", "qmoe_internal.h"))
     result["roofline"] = {"bound": "hbm", "kernel": "fp8_dequant_kernel", "achieved": round(gbs, 2),
                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                          "traffic": None, "avg_us": round(ms * 1e3, 3), "bytes_per_launch": rd + wr}
+                          "traffic": traffic, "avg_us": round(ms * 1e3, 3), "bytes_per_launch": rd + wr}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_dequant(w, None, g, "fp8", c.E, w[0].nbytes * 3, cfg.name,
                                                       args.cpu_seconds)

@@ -445,35 +445,40 @@ hipError_t launch_fp8_gemv(GemvArgs &a, int max_rows_per_expert, void *ws, hipSt
 }
 
 // Dequant: out[e][n][k] = bf16(float32(e4m3(w[e][n][k]) * g[e])), the same
-// [E][N][K] layout as the input, so a thread converts 16 consecutive bytes
-// into 32 consecutive output bytes.
+// [E][N][K] layout as the input.  A wave converts 1 KB of input as two
+// 512-byte halves, 8 bytes per lane each, so every load instruction reads
+// and every store instruction writes one contiguous run (a lane's 16 output
+// bytes sit next to its neighbours').
 __global__ __launch_bounds__(256) void fp8_dequant_kernel(const uint8_t *__restrict__ w,
                                                           const float *__restrict__ g, size_t per_expert,
                                                           uint16_t *__restrict__ out) {
   const int e = blockIdx.y;
-  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 16;
-  if (i >= per_expert) return;
+  const int lane = threadIdx.x & 63;
+  const size_t base = (size_t)blockIdx.x * 4096 + (size_t)(threadIdx.x >> 6) * 1024 + (size_t)lane * 8;
   const float ge = g[e];
-  const size_t off = (size_t)e * per_expert + i;
-  const u32x4_t v = __builtin_nontemporal_load((const u32x4_t *)(w + off));
-  const uint32_t vs[4] = {v.x, v.y, v.z, v.w};
-  uint32_t o[8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const f32x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(vs[j], 1.0f, false);
-    const f32x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(vs[j], 1.0f, true);
-    o[2 * j] = pack_bf16x2_rne(lo.x * ge, lo.y * ge);
-    o[2 * j + 1] = pack_bf16x2_rne(hi.x * ge, hi.y * ge);
+  for (int h = 0; h < 2; ++h) {
+    const size_t i = base + (size_t)h * 512;
+    if (i >= per_expert) continue;  // per_expert % 16 == 0: a lane's 8 bytes are all in or all out
+    const size_t off = (size_t)e * per_expert + i;
+    const u32x2_t v = __builtin_nontemporal_load((const u32x2_t *)(w + off));
+    const uint32_t vs[2] = {v.x, v.y};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const f32x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(vs[j], 1.0f, false);
+      const f32x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(vs[j], 1.0f, true);
+      o[2 * j] = pack_bf16x2_rne(lo.x * ge, lo.y * ge);
+      o[2 * j + 1] = pack_bf16x2_rne(hi.x * ge, hi.y * ge);
+    }
+    __builtin_nontemporal_store(u32x4_t{o[0], o[1], o[2], o[3]}, (u32x4_t *)(out + off));
   }
-  u32x4_t* dst = (u32x4_t *)(out + off);
-  __builtin_nontemporal_store(u32x4_t{o[0], o[1], o[2], o[3]}, dst);
-  __builtin_nontemporal_store(u32x4_t{o[4], o[5], o[6], o[7]}, dst + 1);
 }
 
 hipError_t launch_fp8_dequant(const uint8_t *w, const float *g, int32_t E, int32_t K, int32_t N, uint16_t *out,
                               hipStream_t s) {
   const size_t per = (size_t)N * K;
-  const dim3 grid((unsigned)((per / 16 + 255) / 256), (unsigned)E);
+  const dim3 grid((unsigned)((per + 4095) / 4096), (unsigned)E);
   fp8_dequant_kernel<<<grid, 256, 0, s>>>(w, g, per, out);
   return hipGetLastError();
 }
