@@ -283,7 +283,7 @@ def bench_dequant(args, torch, q, synth, np):
     result = base_result("MXFP4 standalone dequant GB/s (read + write bytes)", gbs, "GB/s", args, ms, config,
                          dtype="u8")
     traffic = measured_traffic("dequant", ("dequant.hip", "device_common.h", "qmoe_internal.h"))
-    result["roofline"] = {"bound": "hbm", "kernel": "dequant_kernel<MXFP4>", "achieved": round(gbs, 2),
+    result["roofline"] = {"bound": "hbm", "kernel": "dequant_lds_kernel<MXFP4>", "achieved": round(gbs, 2),
                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                           "traffic": traffic, "avg_us": round(ms * 1e3, 3), "bytes_per_launch": rd + wr}
     if not args.no_cpu_baseline:

@@ -158,6 +158,83 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
   }
 }
 
+// Staged variant for K % 256 == 0 and N % 256 == 0: a workgroup first
+// copies a 256 k x 256 n packed tile into LDS with full-line reads (8
+// threads per 128-byte row; 4-byte units XOR-swizzled by row / 8 so the
+// k-major reads below spread over the banks), then its lanes run along k: 32
+// lanes x 8 k cover one column block's 256 k, so every store instruction
+// writes 512 contiguous bytes of an output row (the direct kernel's stores
+// write 256-byte runs of four rows).  Same decode and rounding per column.
+constexpr int kLdsKT = 256, kLdsNT = 256;
+
+template <int FMT, bool POW2>
+__global__ __launch_bounds__(256) void dequant_lds_kernel(const uint8_t *__restrict__ w, const uint8_t *__restrict__ s,
+                                                          const float *__restrict__ g, int K, int N,
+                                                          uint16_t *__restrict__ out) {
+  constexpr int B = (FMT == 0) ? 16 : 32;
+  constexpr int KL = kLdsKT / 8;        // lanes along k per column block
+  constexpr int BPW = 64 / KL;           // column blocks per wave and pass
+  constexpr int PASSES = (kLdsNT / 8) / (4 * BPW);
+  __shared__ uint32_t tile[kLdsKT * 32];  // 256 rows x 128 bytes
+  const int e = blockIdx.z;
+  const int k0 = blockIdx.x * kLdsKT;
+  const int n0 = blockIdx.y * kLdsNT;
+  const int tid = threadIdx.x;
+  const size_t rowbytes = (size_t)(N >> 1);
+  {
+    const int c = tid & 7;
+#pragma unroll
+    for (int i = 0; i < kLdsKT / 32; ++i) {
+      const int r = (tid >> 3) + 32 * i;
+      const u32x4_t v = __builtin_nontemporal_load(
+          (const u32x4_t *)(w + ((size_t)e * K + k0 + r) * rowbytes + (n0 >> 1) + 16 * c));
+      const int sw = (r >> 3) & 31;
+      tile[r * 32 + ((4 * c + 0) ^ sw)] = v.x;
+      tile[r * 32 + ((4 * c + 1) ^ sw)] = v.y;
+      tile[r * 32 + ((4 * c + 2) ^ sw)] = v.z;
+      tile[r * 32 + ((4 * c + 3) ^ sw)] = v.w;
+    }
+  }
+  __syncthreads();
+  const bool has_g = g != nullptr;
+  const float gs = has_g ? g[e] : 1.0f;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int kl = lane % KL;
+  const int sub = lane / KL;
+  const int kk = k0 + 8 * kl;  // this lane's 8 k rows (inside one scale block)
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int cb = (p * 4 + wave) * BPW + sub;  // block of 8 columns = dword cb of a packed row
+    uint32_t A[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 8 * kl + i;
+      A[i] = tile[r * 32 + (cb ^ ((r >> 3) & 31))];
+    }
+    const uint2 sv = *(const uint2 *)(s + ((size_t)e * (K / B) + kk / B) * N + n0 + 8 * cb);
+    uint32_t ev[4], od[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ev[q] = (A[2 * q] & 0x0F0F0F0Fu) | ((A[2 * q + 1] << 4) & 0xF0F0F0F0u);
+      od[q] = ((A[2 * q] >> 4) & 0x0F0F0F0Fu) | (A[2 * q + 1] & 0xF0F0F0F0u);
+    }
+    uint16_t *op = out + ((size_t)e * N + n0 + 8 * cb) * K + kk;
+#define QMOE_DQL_COL(C)                                                                                  \
+  __builtin_nontemporal_store(                                                                           \
+      dequant_col<C, FMT, POW2>(ev, od, (((C) < 4 ? sv.x : sv.y) >> (8 * ((C) & 3))) & 0xFFu, gs, has_g), \
+      (u32x4_t *)(op + (size_t)(C)*K))
+    QMOE_DQL_COL(0);
+    QMOE_DQL_COL(1);
+    QMOE_DQL_COL(2);
+    QMOE_DQL_COL(3);
+    QMOE_DQL_COL(4);
+    QMOE_DQL_COL(5);
+    QMOE_DQL_COL(6);
+    QMOE_DQL_COL(7);
+#undef QMOE_DQL_COL
+  }
+}
+
 template <int KT, int CW>
 static void launch_shape(const uint8_t *w, const uint8_t *scales, const float *g, int32_t E, int32_t K, int32_t N,
                          int fmt, uint16_t *out, hipStream_t s) {
@@ -178,7 +255,17 @@ hipError_t launch_dequant(const uint8_t *w, const uint8_t *scales, const float *
   // write 256 contiguous bytes of an output row) ran 48.7 us against 61 us
   // for 64 x 256 with 8 columns per thread.  Smaller shapes cover K or N
   // that the large tile does not divide.
-  if (K % 128 == 0 && N % 512 == 0)
+  // Staged through LDS when the 256 x 256 tile divides the shape (MXFP4,
+  // E=32, K=2048, N=1536: 43.7 us against 49.6 us for the direct kernel).
+  if (K % kLdsKT == 0 && N % kLdsNT == 0) {
+    const dim3 grid((unsigned)(K / kLdsKT), (unsigned)(N / kLdsNT), (unsigned)E);
+    if (fmt == 0)
+      dequant_lds_kernel<0, false><<<grid, 256, 0, s>>>(w, scales, g, K, N, out);
+    else if (g == nullptr)
+      dequant_lds_kernel<1, true><<<grid, 256, 0, s>>>(w, scales, g, K, N, out);
+    else
+      dequant_lds_kernel<1, false><<<grid, 256, 0, s>>>(w, scales, g, K, N, out);
+  } else if (K % 128 == 0 && N % 512 == 0)
     launch_shape<128, 32>(w, scales, g, E, K, N, fmt, out, s);
   else if (N % 512 == 0)
     launch_shape<64, 16>(w, scales, g, E, K, N, fmt, out, s);
