@@ -251,8 +251,12 @@ def bench_layer(args, torch, q, synth, np):
                           "unit": "GB/s", "frac": round(fc1_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                           "avg_us": round(fc1_ms * 1e3, 3), "bytes_per_launch": fc1_bytes}
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = (cpu_baseline_prefill(L, D, fc1_w + fc2_w, args.cpu_seconds) if prefill
-                                  else cpu_baseline_layer(L, weight_bytes, args.cpu_seconds))
+        restore = pin_one_core()
+        try:
+            result["cpu_baseline"] = (cpu_baseline_prefill(L, D, fc1_w + fc2_w, args.cpu_seconds) if prefill
+                                      else cpu_baseline_layer(L, weight_bytes, args.cpu_seconds))
+        finally:
+            restore()
     return result
 
 
@@ -287,8 +291,12 @@ def bench_dequant(args, torch, q, synth, np):
                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                           "traffic": traffic, "avg_us": round(ms * 1e3, 3), "bytes_per_launch": rd + wr}
     if not args.no_cpu_baseline:
-        per = w[0].nbytes + s[0].nbytes + cfg.N * cfg.K * 2
-        result["cpu_baseline"] = cpu_baseline_dequant(w, s, g, cfg.fmt, cfg.E, per, cfg.name, args.cpu_seconds)
+        restore = pin_one_core()
+        try:
+            per = w[0].nbytes + s[0].nbytes + cfg.N * cfg.K * 2
+            result["cpu_baseline"] = cpu_baseline_dequant(w, s, g, cfg.fmt, cfg.E, per, cfg.name, args.cpu_seconds)
+        finally:
+            restore()
     return result
 
 
@@ -318,8 +326,12 @@ def bench_fp8_dequant(args, torch, q, synth, np):
                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                           "traffic": traffic, "avg_us": round(ms * 1e3, 3), "bytes_per_launch": rd + wr}
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline_dequant(w, None, g, "fp8", c.E, w[0].nbytes * 3, cfg.name,
-                                                      args.cpu_seconds)
+        restore = pin_one_core()
+        try:
+            result["cpu_baseline"] = cpu_baseline_dequant(w, None, g, "fp8", c.E, w[0].nbytes * 3, cfg.name,
+                                                          args.cpu_seconds)
+        finally:
+            restore()
     return result
 
 
@@ -336,6 +348,19 @@ def calibrate_copy(args, torch):
             "avg_us": round(ms * 1e3, 3), "gbs": round(2 * n / (ms * 1e-3) / 1e9, 2)}
 
 
+def pin_one_core():
+    """Pins this process to one host core for the CPU baseline (the oracle is
+    single-threaded; the pin makes `cores` = 1 a measured fact) and returns a
+    function that restores the previous affinity."""
+    prev = os.sched_getaffinity(0)
+    os.sched_setaffinity(0, {min(prev)})
+    return lambda: os.sched_setaffinity(0, prev)
+
+
+def cpu_cores_used():
+    return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline_layer(L, weight_bytes, budget_s):
     """The C++ oracle as it stands (single-threaded, float64) on whole layers of the same workload."""
     from oracle import cpp
@@ -348,7 +373,7 @@ def cpu_baseline_layer(L, weight_bytes, budget_s):
         if el >= budget_s or n >= 20:
             break
     per_layer = el / n
-    return {"value": round(weight_bytes / per_layer / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": round(weight_bytes / per_layer / 1e9, 4), "unit": "GB/s", "cores": cpu_cores_used(), "kind": "oracle",
             "sample": f"{n} full layers of {L.cfg.name} (route, FC1+SwiGLU, FC2, finalize), C++ float64 oracle, "
                       f"{per_layer * 1e3:.1f} ms/layer",
             "host_cores_total": os.cpu_count()}
@@ -377,7 +402,7 @@ def cpu_baseline_prefill(L, D, expert_bytes, budget_s):
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
-    return {"value": round(n * expert_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": round(n * expert_bytes / el / 1e9, 4), "unit": "GB/s", "cores": cpu_cores_used(), "kind": "oracle",
             "sample": f"FC1+SwiGLU and FC2 of {n} of {D} routed experts ({rows} of {c.rows} rows) of {c.name}, "
                       f"C++ float64 oracle, {el:.1f} s", "host_cores_total": os.cpu_count()}
 
@@ -393,7 +418,7 @@ def cpu_baseline_dequant(w, s, g, fmt, E, per_expert_bytes, name, budget_s):
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
-    return {"value": round(n * per_expert_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": round(n * per_expert_bytes / el / 1e9, 4), "unit": "GB/s", "cores": cpu_cores_used(), "kind": "oracle",
             "sample": f"{n} of {E} experts of {name}, C++ float64 oracle, {el:.1f} s",
             "host_cores_total": os.cpu_count()}
 

@@ -99,6 +99,34 @@ def check_layer(L, act=None, cols1=None, cols2=None, path=None, rw=None, orc="nu
     return g
 
 
+_ORACLE_FC1 = {}
+
+
+def oracle_e2e(L, gpu_h, act=None, rw=None, orc="numpy", key=None):
+    """The oracle's layer output from the inputs alone (numpy or C++ oracle),
+    taking h's bf16 rounding the GPU's way only where the tests/ties rule
+    shows a float32 rounding tie; returns (out float64 [T][H], h_ref bits).
+    key: cache key for the oracle's routing and FC1 (they depend on the
+    inputs only)."""
+    c = L.cfg
+    R, M = (route, moe) if orc == "numpy" else (cpp, cpp)
+    oact = None if act is None else dict(alpha=act[0], beta=act[1], limit=act[2],
+                                         fusion=act[3] if len(act) > 3 else 1)
+    ck = None if key is None else (key, orc)
+    if ck is not None and ck in _ORACLE_FC1:
+        idx, wts, off, p2e, e2p, h_ref, u_ref = _ORACLE_FC1[ck]
+    else:
+        idx, wts = R.route_topk(L.logits, c.k) if rw is None else R.route_topk_router_weights(L.logits, rw, c.k)
+        off, p2e, e2p = R.expert_maps(idx, c.E)
+        h_ref, u_ref = M.fc1_swiglu(L.x, c.k, L.w1, L.s1, L.g1, c.fmt, off, p2e, oact)
+        if ck is not None:
+            _ORACLE_FC1[ck] = (idx, wts, off, p2e, e2p, h_ref, u_ref)
+    ties = h_roundings_differ_only_at_ties(L, gpu_h, h_ref, u_ref, oact, off, p2e)
+    print("h rounding ties", ties, flush=True)
+    y_ref = M.fc2(gpu_h, L.w2, L.s2, L.g2, c.fmt, off)
+    return M.finalize(y_ref, wts, e2p, c.T, c.k), h_ref
+
+
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
 def test_layer_small(cfg):
     check_layer(synth.layer_inputs(cfg))
@@ -109,16 +137,16 @@ def test_layer_full(cfg):
     check_layer(synth.layer_inputs(cfg))
 
 
-@pytest.mark.parametrize("path", ["gemv", "auto"])
+@pytest.mark.parametrize("path", ["gemv", "grouped"])
 def test_layer_mxfp4_decode_full_sampled(path):
-    # the 8-token MXFP4 decode at full size on the GEMV path, and as AUTO
-    # runs it (the grouped kernel for T > 4 at this N)
+    # the 8-token MXFP4 decode at full size on the GEMV path (AUTO's choice
+    # at 64 rows) and on the grouped MFMA kernel (path = GROUPED)
     import fp4_weight_only_amd as q
     L = synth.layer_inputs(synth.MX_DECODE)
     rng = np.random.default_rng(0)
     cols1 = np.sort(rng.choice(L.cfg.I, 160, replace=False))
     cols2 = np.sort(rng.choice(L.cfg.H, 320, replace=False))
-    check_layer(L, cols1=cols1, cols2=cols2, path=q.QMOE_PATH_GEMV if path == "gemv" else None)
+    check_layer(L, cols1=cols1, cols2=cols2, path=q.QMOE_PATH_GEMV if path == "gemv" else q.QMOE_PATH_GROUPED)
 
 
 # Variants: concatenated SwiGLU columns (swiglu_fusion=2), MXFP4 with
@@ -398,6 +426,88 @@ def test_every_code_in_every_nibble_through_the_gemv(fmt):
     assert np.count_nonzero(diff) <= 2, np.nonzero(diff)
 
 
+def _scale_exponent(fmt, byte):
+    """floor(log2 |scale|) of a scale byte, from the oracle's codec."""
+    v = (codecs.e4m3fn_value if fmt == "nvfp4" else codecs.e8m0_value)(np.array([byte]))[0]
+    return 0 if v == 0 else int(np.floor(np.log2(abs(v))))     # E4M3 0x00 / 0x80: a zero scale
+
+
+def _scale_byte_case(fmt, path, K, N, seed):
+    """Weights with one nonzero code per column n (row n of K) whose block
+    scale is the byte under test; every scale byte of the codec appears in
+    some column (NaN bytes excepted).  The activation of row n is a power of
+    two that brings x * code * scale near 1, so products stay exact and
+    normal in float32.  On the grouped path (weights formed in bf16) the
+    codes at E8M0 bytes 253 and 254 are kept small enough for bf16's range."""
+    B = 16 if fmt == "nvfp4" else 32
+    rng = np.random.default_rng(seed)
+    if fmt == "nvfp4":
+        bytes_ = np.array([b for b in range(256) if (b & 0x7F) != 0x7F])
+    else:
+        bytes_ = np.arange(255)
+    assert K >= N
+    col_byte = bytes_[(np.arange(N) * 7 + seed) % len(bytes_)]
+    assert set(col_byte) == set(bytes_) or N < len(bytes_)
+    nonzero = np.array([c for c in range(16) if c not in (0, 8)])
+    codes = nonzero[rng.integers(0, len(nonzero), N)]
+    if fmt == "mxfp4" and path == "grouped":
+        small3 = np.array([1, 2, 3, 4, 5, 9, 10, 11, 12, 13])     # |value| <= 3
+        small15 = np.array([1, 2, 3, 9, 10, 11])                  # |value| <= 1.5
+        m253, m254 = col_byte == 253, col_byte == 254
+        codes[m253] = small3[rng.integers(0, len(small3), m253.sum())]
+        codes[m254] = small15[rng.integers(0, len(small15), m254.sum())]
+    w = np.zeros((1, K, N // 2), np.uint8)
+    s = np.full((1, K // B, N), 0x38 if fmt == "nvfp4" else 127, np.uint8)
+    xexp = np.zeros(K, np.int64)
+    for n in range(N):
+        w[0, n, n // 2] |= np.uint8(codes[n] << (4 * (n % 2)))
+        s[0, n // B, n] = col_byte[n]
+        xexp[n] = int(np.clip(-_scale_exponent(fmt, col_byte[n]) + rng.integers(-2, 3), -120, 120))
+    sign = np.where(rng.random(K) < 0.5, -1.0, 1.0)
+    act = synth.to_bf16_bits((sign * np.ldexp(1.0, xexp)).astype(np.float32))[None, :]
+    g = np.array([0.75], np.float32) if fmt == "nvfp4" else None
+    return w, s, g, act, col_byte
+
+
+@pytest.mark.parametrize("path", ["gemv", "grouped"])
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_every_scale_byte_through_fc1_and_fc2(fmt, path):
+    """Every E4M3 byte but the NaN pair (subnormals included) and every E8M0
+    byte 0..254 reach FC1 and FC2 as block scales, on the GEMV and the grouped
+    kernel, against the oracle; FC2 with one product per output is exact."""
+    import fp4_weight_only_amd as q
+    p = q.QMOE_PATH_GEMV if path == "gemv" else q.QMOE_PATH_GROUPED
+    offsets = to_dev(np.array([0, 1], np.int32))
+    p2e = to_dev(np.array([0], np.int32))
+    # FC1: K = 512, N = 512 (I = 256): h = SwiGLU(u[2j], u[2j+1])
+    K1, N1 = 512, 512
+    w1, s1, g1, x, b1 = _scale_byte_case(fmt, path, K1, N1, seed=71)
+    wd1 = weights_dev(w1, s1, g1, fmt)
+    h = torch.empty((1, N1 // 2), dtype=torch.bfloat16, device="cuda")
+    ws = q.alloc_workspace(max(q.fc_workspace_bytes(1, 1, 1, wd1, p), 1 << 16))
+    print_case("scale bytes fc1", fmt, path)
+    q.qmoe_fp4_gemv_fc1_swiglu(bf16_dev(x), 1, wd1, offsets, p2e, h, ws, path=p)
+    torch.cuda.synchronize()
+    h_ref, _ = moe.fc1_swiglu(x, 1, w1, s1, g1, fmt, np.array([0, 1]), np.array([0]))
+    assert_close("h (every scale byte)", codecs.bf16_to_f64(bf16_host(h)), codecs.bf16_to_f64(h_ref))
+    # FC2: K = I = 512 rows, N = H = 256 columns; the input row plays x's part
+    K2, N2 = 512, 256
+    w2, s2, g2, hin, b2 = _scale_byte_case(fmt, path, K2, N2, seed=72)
+    wd2 = weights_dev(w2, s2, g2, fmt)
+    y = torch.empty((1, N2), dtype=torch.float32, device="cuda")
+    ws2 = q.alloc_workspace(max(q.fc_workspace_bytes(2, 1, 1, wd2, p), 1 << 16))
+    print_case("scale bytes fc2", fmt, path)
+    q.qmoe_fp4_gemv_fc2(bf16_dev(hin), 1, 1, wd2, offsets, y, ws2, path=p)
+    torch.cuda.synchronize()
+    y_ref = moe.fc2(hin, w2, s2, g2, fmt, np.array([0, 1]))
+    got = y.cpu().numpy().astype(np.float64)
+    bad = np.nonzero(got != y_ref)[1]
+    assert bad.size == 0, [(int(n), int(b2[n]), got[0, n], y_ref[0, n]) for n in bad[:8]]
+    seen = set(b1) | set(b2)
+    expect = set(range(255)) if fmt == "mxfp4" else {b for b in range(256) if (b & 0x7F) != 0x7F}
+    assert seen == expect
+
+
 FUSED = [
     synth.TINY,
     synth.shrink(synth.DECODE, E=37, T=7, k=5, H=320, I=144, seed=1),      # ragged K/N, several k chunks
@@ -412,18 +522,24 @@ FUSED = [
 def test_fc2_finalize_fused_equals_separate_calls(cfg):
     """qmoe_fp4_gemv_fc2_finalize adds FC2's partial sums per routed row in the
     order the split-K epilogue does, then weights them as qmoe_finalize does:
-    the output must equal the separate calls bit for bit (the separate path is
-    checked against the oracle by the layer tests)."""
+    the output must equal the separate calls bit for bit, with its output and
+    workspace poisoned first, and match the oracle's end-to-end output."""
     L = synth.layer_inputs(cfg)
     layer, logits, x = layer_dev(L)
     print_case("fused fc2+finalize", cfg.name)
     layer.run(logits, x)
     torch.cuda.synchronize()
     ref = bf16_host(layer.out).copy()
+    gpu_h = bf16_host(layer.h).copy()
     layer.out.view(torch.int16).fill_(0x7FC1)   # poison
+    layer.ws.view(torch.int16).fill_(0x7FC1)
     layer.run(logits, x, fused=True)
     torch.cuda.synchronize()
-    assert np.array_equal(bf16_host(layer.out), ref)
+    got = bf16_host(layer.out)
+    assert np.array_equal(got, ref)
+    # and the fused output itself against the oracle's end-to-end output
+    out_ref, _ = oracle_e2e(L, gpu_h)
+    assert_close("fused out vs oracle", codecs.bf16_to_f64(got), out_ref)
 
 
 ROUTE_FC1 = [
@@ -444,8 +560,8 @@ ROUTE_FC1 = [
 def test_route_fc1_equals_separate_calls(cfg, mode):
     """qmoe_fp4_route_fc1_swiglu runs the routing of all tokens in every FC1
     workgroup: every output (selections, weights, maps, h) must equal the
-    separate routing and FC1 GEMV calls bit for bit (those are checked against
-    the oracle by the layer tests)."""
+    separate routing and FC1 GEMV calls bit for bit, and h must match the
+    oracle's FC1."""
     import fp4_weight_only_amd as q
     L = synth.layer_inputs(cfg)
     act = GPTOSS + (q.QMOE_SWIGLU_CONCAT,) if mode == "gptoss_concat" else None
@@ -464,6 +580,13 @@ def test_route_fc1_equals_separate_calls(cfg, mode):
     for name, t, r in zip(("idx", "w", "offsets", "p2e", "e2p", "h"), outs, ref):
         got = t.view(torch.int32 if t.element_size() == 4 else torch.int16).cpu().numpy()
         assert np.array_equal(got, r), name
+    # the fused call's h against the oracle's FC1 (routing compared bit for bit)
+    rwh = None if rw is None else synth.router_weights(cfg)
+    idx, _ = (route.route_topk(L.logits, cfg.k) if rwh is None
+              else route.route_topk_router_weights(L.logits, rwh, cfg.k))
+    assert np.array_equal(layer.topk_idx.cpu().numpy(), idx)
+    _, h_ref = oracle_e2e(L, bf16_host(layer.h), act, rwh, key=(cfg.name, mode))
+    assert_close("fused h vs oracle", codecs.bf16_to_f64(bf16_host(layer.h)), codecs.bf16_to_f64(h_ref))
 
 
 LAYER_DECODE = ROUTE_FC1 + SMALL[-2:] + [
@@ -478,7 +601,9 @@ LAYER_DECODE = ROUTE_FC1 + SMALL[-2:] + [
 def test_layer_decode_equals_separate_calls(cfg, mode, route_in_fc1):
     """qmoe_fp4_moe_layer_decode forms h inside FC2's staging from FC1's
     partial sums: the routing outputs and out must equal the separate routing,
-    FC1 (GEMV) and fused FC2 + finalize (GEMV) calls bit for bit."""
+    FC1 (GEMV) and fused FC2 + finalize (GEMV) calls bit for bit (outputs and
+    workspace poisoned first), and out must match the oracle's end-to-end
+    output."""
     import fp4_weight_only_amd as q
     L = synth.layer_inputs(cfg)
     act = GPTOSS + (q.QMOE_SWIGLU_CONCAT,) if mode == "gptoss_concat" else None
@@ -491,24 +616,32 @@ def test_layer_decode_equals_separate_calls(cfg, mode, route_in_fc1):
     layer.fc2_finalize()
     torch.cuda.synchronize()
     ref = [t.view(torch.int32 if t.element_size() == 4 else torch.int16).cpu().numpy().copy() for t in outs]
-    for t in outs:                                   # poison every output
+    gpu_h = bf16_host(layer.h).copy()
+    for t in outs:                                   # poison every output and the workspace
         t.view(torch.int32 if t.element_size() == 4 else torch.int16).fill_(-7)
+    layer.ws.view(torch.int16).fill_(0x7FC1)
     layer.decode_layer(logits, x, rw, route_in_fc1=bool(route_in_fc1))
     torch.cuda.synchronize()
     for name, t, r in zip(("idx", "w", "offsets", "p2e", "e2p", "out"), outs, ref):
         got = t.view(torch.int32 if t.element_size() == 4 else torch.int16).cpu().numpy()
         assert np.array_equal(got, r), name
+    # the whole-layer call's output against the oracle's end-to-end output
+    rwh = None if rw is None else synth.router_weights(cfg)
+    out_ref, _ = oracle_e2e(L, gpu_h, act, rwh, key=(cfg.name, mode))
+    assert_close("layer decode out vs oracle", codecs.bf16_to_f64(bf16_host(layer.out)), out_ref)
 
 
+@pytest.mark.parametrize("K", [512, 384], ids=["lds_tile", "direct_128x512"])
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "mxfp4_g"])
-def test_dequant_small_exhaustive_scales(fmt):
+def test_dequant_small_exhaustive_scales(fmt, K):
     """Every scale byte (NaN bytes aside) with random codes; MXFP4 with and
-    without a global scale (the two take different conversion paths)."""
+    without a global scale (the two take different conversion paths); K = 512
+    runs the LDS-staged kernel, K = 384 the direct kernel's 128 x 512 tile."""
     import fp4_weight_only_amd as q
     with_g = fmt == "mxfp4_g"
     fmt = "mxfp4" if with_g else fmt
     B = 16 if fmt == "nvfp4" else 32
-    E, K, N = 2, 64 * 8, 256 * 2
+    E, N = 2, 256 * 2
     rng = np.random.default_rng(12)
     w = synth.packed_codes(synth.stream(1, 2), (E, K, N // 2))
     s = (np.arange(E * (K // B) * N) % 256).astype(np.uint8).reshape(E, K // B, N)   # every scale byte
@@ -529,9 +662,11 @@ def test_dequant_small_exhaustive_scales(fmt):
 
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
-@pytest.mark.parametrize("K,N", [(320, 512), (320, 256), (512, 256)])
+@pytest.mark.parametrize("K,N", [(512, 256), (384, 512), (320, 512), (384, 256), (320, 256)])
 def test_dequant_tile_shapes(fmt, K, N):
-    """Shapes the largest dequant tile does not divide (K % 128, N % 512)."""
+    """One shape per dequant kernel branch: the LDS-staged 256 x 256 tile (K %
+    256 == 0), then the direct kernel's tiles 128 k x 512 n (K % 128 == 0, N %
+    512 == 0), 64 x 512 (N % 512 == 0), 128 x 256 (K % 128 == 0) and 64 x 256."""
     import fp4_weight_only_amd as q
     B = 16 if fmt == "nvfp4" else 32
     E = 3
@@ -610,8 +745,7 @@ def test_same_shape_both_paths(cfg):
     g1 = check_layer(L, path=q.QMOE_PATH_GEMV)
     g2 = check_layer(L, path=q.QMOE_PATH_GROUPED)
     assert np.array_equal(g1["idx"], g2["idx"])
-    ok, rep = tolerance.check(g2["out"], g1["out"])
-    print("gemv vs grouped", rep)
+    assert_close("gemv vs grouped", g2["out"], g1["out"])
 
 
 def test_prefill_full_sampled():
@@ -623,25 +757,67 @@ def test_prefill_full_sampled():
     check_layer(L, cols1=cols1, cols2=cols2)
 
 
-def test_determinism_and_poisoned_buffers():
-    cfg = synth.shrink(synth.MTP8, E=48, T=8, k=8, H=512, I=384, seed=13)
+POISON_CFGS = [
+    synth.shrink(synth.MTP8, E=48, T=8, k=8, H=512, I=384, seed=13),      # hot experts, 64 rows
+    synth.shrink(synth.DECODE, E=37, T=7, k=5, H=320, I=144, seed=14),    # ragged K/N, most experts empty
+    synth.shrink(synth.MTP4, E=256, T=3, k=8, H=512, I=192, seed=15),     # E = 256: 232+ zero-count experts
+]
+
+
+def _poison_patterns(n_random=24):
+    """Float patterns (NaN, +-inf, +-1e30, +-0, float max) and random byte
+    patterns, as 32-bit words."""
+    vals = np.array([np.nan, np.inf, -np.inf, 1e30, -1e30, 0.0, -0.0, 3.4e38], np.float32).view(np.uint32)
+    rng = np.random.default_rng(99)
+    return [int(v) for v in vals] + [int(v) for v in rng.integers(0, 2 ** 32, n_random, dtype=np.uint64)]
+
+
+@pytest.mark.parametrize("cfg", POISON_CFGS, ids=lambda c: c.name)
+def test_determinism_and_poisoned_buffers(cfg):
+    """Every output and the whole workspace filled with 32 patterns (NaN,
+    +-inf, +-1e30, signed zeros, float max, random bytes) before each run: the
+    separate calls and the fused calls must reproduce their first results bit
+    for bit, on hot, ragged and zero-count expert shapes."""
     L = synth.layer_inputs(cfg)
     layer, logits, x = layer_dev(L)
     print_case("determinism", cfg.name)
+    bufs = (layer.topk_idx, layer.topk_w, layer.offsets, layer.p2e, layer.e2p, layer.h, layer.y, layer.out,
+            layer.ws)
+
+    def snap():
+        return [t.view(torch.uint8).cpu().numpy().copy() for t in bufs[:-1]]
+
     layer.run(logits, x)
     torch.cuda.synchronize()
-    first = [bf16_host(layer.h).copy(), layer.y.cpu().numpy().copy(), bf16_host(layer.out).copy()]
-    poison = [float("nan"), float("inf"), -float("inf"), 1e30]
-    for pv in poison:
-        layer.h.fill_(pv)
-        layer.y.fill_(pv)
-        layer.out.fill_(pv)
-        layer.ws.view(torch.float32).fill_(pv)      # the workspace is pure scratch
-        layer.run(logits, x)
-        torch.cuda.synchronize()
-        again = [bf16_host(layer.h), layer.y.cpu().numpy(), bf16_host(layer.out)]
-        for a, b in zip(first, again):
-            assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    first = snap()
+    layer.run(logits, x, fused=True)
+    torch.cuda.synchronize()
+    first_fused = bf16_host(layer.out).copy()
+    assert np.array_equal(first_fused, bf16_host_from(first[7]))
+    for pat in _poison_patterns():
+        for fused in (False, True):
+            for t in bufs:
+                fill_pattern(t, pat)
+            layer.run(logits, x, fused=fused)
+            torch.cuda.synchronize()
+            if fused:   # h and y are not written by the fused calls
+                assert np.array_equal(bf16_host(layer.out), first_fused), hex(pat)
+                assert np.array_equal(layer.topk_idx.view(torch.uint8).cpu().numpy(), first[0]), hex(pat)
+            else:
+                for i, (a, b) in enumerate(zip(first, snap())):
+                    assert np.array_equal(a, b), (hex(pat), i)
+
+
+def bf16_host_from(u8):
+    return np.ascontiguousarray(u8).view(np.uint16)
+
+
+def fill_pattern(t, pat):
+    """Fills a device tensor's bytes with the 32-bit word pat repeated."""
+    u8 = t.view(torch.uint8).view(-1)
+    n = u8.numel()
+    rep = np.tile(np.frombuffer(np.uint32(pat).tobytes(), np.uint8), (n + 3) // 4)[:n]
+    u8.copy_(torch.from_numpy(np.ascontiguousarray(rep)))
 
 
 # The same layers against the C++ oracle (plain single-threaded float64,
