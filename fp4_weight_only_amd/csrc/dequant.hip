@@ -37,17 +37,16 @@ __device__ __forceinline__ u32x4_t dequant_col(const uint32_t (&ev)[4], const ui
   constexpr int J = C >> 1;
   u32x4_t o;
   if constexpr (POW2) {
-    // E8M0 without a global scale: code * 2^(b-127) is the output value
-    // exactly, and the scaled FP4 -> bf16 conversion computes it (the scale's
-    // exponent is the block exponent).  Scales whose products could leave the
-    // normal bf16 range take the float32 path below.
-    if (sbyte >= 2u && sbyte <= 252u) {
-      const float sc = __uint_as_float(sbyte << 23);
+    // E8M0 without a global scale: the output is bf16_rne(code * 2^(b-127)),
+    // which the scaled FP4 -> bf16 conversion computes for every byte: it
+    // takes the scale operand's exponent field as an E8M0 value (field 0 is
+    // 2^-127, giving bf16 subnormals; 255 is NaN; past bf16's range +-inf),
+    // checked for all 256 bytes x 16 codes.
+    const float sc = __uint_as_float(sbyte << 23);
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        o[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((C & 1) ? od[q] : ev[q], sc, J));
-      return o;
-    }
+    for (int q = 0; q < 4; ++q)
+      o[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((C & 1) ? od[q] : ev[q], sc, J));
+    return o;
   }
   float sf;
   if constexpr (FMT == 0)

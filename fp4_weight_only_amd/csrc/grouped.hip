@@ -80,12 +80,20 @@ struct SliceRegs {
 };
 
 // MFMA B operand of one lane: 8 consecutive k codes of its column (one
-// dword, low nibble first), decoded to bf16 with the block scale.
+// dword, low nibble first), decoded to bf16 with the block scale.  The
+// weights are bf16 values code * scale, rounded to nearest even: exact for
+// every finite E4M3 byte and for E8M0 bytes 0..252 (bf16 subnormals at 0
+// and 1); at E8M0 bytes 253 and 254 a product past bf16's range is +-inf,
+// and byte 255 (NaN) gives NaN.  The scaled FP4 conversion takes the
+// scale operand's exponent field as an E8M0 value (field 0 is 2^-127, 255
+// NaN): checked for all 256 bytes x 16 codes against round-to-nearest-even
+// of the exact product, so the byte shifted into the exponent field is the
+// whole decode.
 template <int FMT>
 __device__ __forceinline__ bf16x8_t decode_operand(uint32_t d, uint32_t sbyte) {
   u32x4_t o;
   if constexpr (FMT == 1) {
-    const float sc = __uint_as_float(sbyte << 23);  // E8M0 as the conversion exponent
+    const float sc = __uint_as_float(sbyte << 23);  // E8M0 byte as the conversion's scale exponent
     o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 0));
     o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 1));
     o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 2));
