@@ -26,7 +26,8 @@ QMOE_PATH_AUTO, QMOE_PATH_GEMV, QMOE_PATH_GROUPED = 0, 1, 2
 GEMV_MAX_ROWS = 64
 
 EXPORTS = ("qmoe_route_topk", "qmoe_route_topk_router_weights", "qmoe_fp4_resolve_path", "qmoe_fp4_gemv_fc1_swiglu",
-           "qmoe_fp4_route_fc1_swiglu", "qmoe_fp4_moe_layer_decode", "qmoe_fp4_gemv_fc2",
+           "qmoe_fp4_route_fc1_swiglu", "qmoe_fp4_moe_layer_decode", "qmoe_fp4_moe_layer_decode_noalloc",
+           "qmoe_fp4_gemv_fc2",
            "qmoe_fp4_gemv_fc2_finalize",
            "qmoe_finalize",
            "qmoe_dequant_fp4", "qmoe_fp8_gemv_fc1_swiglu", "qmoe_fp8_gemv_fc2", "qmoe_dequant_fp8",
@@ -80,6 +81,8 @@ def _load():
         "qmoe_fp4_resolve_path": [I32, I32, W, I32, ctypes.POINTER(ctypes.c_int)],
         "qmoe_fp4_moe_layer_decode": [P, P, P, I32, I32, W, W, ctypes.POINTER(SwigluC), I32, P, P, P, P, P, P, P,
                                       SZ, P],
+        "qmoe_fp4_moe_layer_decode_noalloc": [P, P, P, I32, I32, W, W, ctypes.POINTER(SwigluC), I32, P, P, P, P,
+                                              P, P, P],
         "qmoe_fp4_route_fc1_swiglu": [P, P, P, I32, I32, W, ctypes.POINTER(SwigluC), P, P, P, P, P, P, P, SZ, P],
         "qmoe_fp4_gemv_fc2": [P, I32, I32, W, P, P, P, SZ, I32, P],
         "qmoe_fp4_gemv_fc2_finalize": [P, I32, I32, W, P, P, P, P, P, SZ, I32, P],
@@ -234,6 +237,21 @@ def qmoe_fp4_moe_layer_decode(logits, router_weights, x, k, w1: FP4Weights, w2: 
         _ptr(logits), _ptr(router_weights), _ptr(x), T, k, ctypes.byref(c1), ctypes.byref(c2), _swiglu(act),
         1 if route_in_fc1 else 0, _ptr(topk_idx), _ptr(topk_w), _ptr(expert_offsets), _ptr(perm_to_expanded),
         _ptr(expanded_to_perm), _ptr(out), _ptr(ws), ctypes.byref(n), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def qmoe_fp4_moe_layer_decode_noalloc(logits, router_weights, x, k, w1: FP4Weights, w2: FP4Weights, topk_idx,
+                                      topk_w, expert_offsets, perm_to_expanded, expanded_to_perm, out, act=None,
+                                      route_in_fc1=False, stream=None):
+    """qmoe_fp4_moe_layer_decode with the library's fixed device scratch (no workspace argument)."""
+    T = x.shape[0]
+    c1, c2 = w1.c(), w2.c()
+    _check("qmoe_fp4_moe_layer_decode_noalloc", lib.qmoe_fp4_moe_layer_decode_noalloc(
+        _ptr(logits), _ptr(router_weights), _ptr(x), T, k, ctypes.byref(c1), ctypes.byref(c2), _swiglu(act),
+        1 if route_in_fc1 else 0, _ptr(topk_idx), _ptr(topk_w), _ptr(expert_offsets), _ptr(perm_to_expanded),
+        _ptr(expanded_to_perm), _ptr(out), _stream(stream)))
 
 
 def qmoe_fp4_gemv_fc2(h, T, k, w2: FP4Weights, expert_offsets, y_rows, ws, path=QMOE_PATH_AUTO, stream=None):

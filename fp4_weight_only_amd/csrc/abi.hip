@@ -2,6 +2,8 @@
 // dispatch to the gfx950 kernels.
 #include <math.h>
 
+#include <mutex>
+
 #include "qmoe.h"
 #include "qmoe_internal.h"
 
@@ -146,6 +148,43 @@ qmoe_status run_fp8(GemvArgs &a, const qmoe_fp8_weights *w, int max_rows, qmoe_p
   return check_launch(launch_fp8_gemv(a, max_rows, ws, stream));
 }
 
+qmoe_status layer_decode(const float *logits, const float *router_weights, const uint16_t *x, int32_t T, int32_t k,
+                         const qmoe_fp4_weights *w1, const qmoe_fp4_weights *w2, const qmoe_swiglu *act,
+                         int32_t route_in_fc1, int32_t *topk_idx, float *topk_w, int32_t *expert_offsets,
+                         int32_t *perm_to_expanded, int32_t *expanded_to_perm, uint16_t *out, void *ws,
+                         size_t *ws_bytes, hipStream_t stream);
+
+}  // namespace
+
+// Scratch of qmoe_fp4_moe_layer_decode_noalloc: both layers' split-K partial
+// sums live here instead of in a caller's workspace.  A file-scope device
+// array: every GPU the library runs on holds its own copy (zero-initialised
+// when the code object loads) until the process ends.  In host code the name
+// `scratch` is only a stand-in; device_scratch() resolves the current
+// device's address once and every launch takes that address.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[QMOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch`, resolved with hipGetSymbolAddress
+// on the first call on that device (with the device current) and kept.
+qmoe_status device_scratch(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QMOE_ELAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return QMOE_ELAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return QMOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -281,6 +320,39 @@ qmoe_status qmoe_fp4_moe_layer_decode(const float *logits, const float *router_w
                                       const qmoe_swiglu *act, int32_t route_in_fc1, int32_t *topk_idx, float *topk_w,
                                       int32_t *expert_offsets, int32_t *perm_to_expanded, int32_t *expanded_to_perm,
                                       uint16_t *out, void *ws, size_t *ws_bytes, hipStream_t stream) {
+  return layer_decode(logits, router_weights, x, T, k, w1, w2, act, route_in_fc1, topk_idx, topk_w, expert_offsets,
+                      perm_to_expanded, expanded_to_perm, out, ws, ws_bytes, stream);
+}
+
+qmoe_status qmoe_fp4_moe_layer_decode_noalloc(const float *logits, const float *router_weights, const uint16_t *x,
+                                              int32_t T, int32_t k, const qmoe_fp4_weights *w1,
+                                              const qmoe_fp4_weights *w2, const qmoe_swiglu *act,
+                                              int32_t route_in_fc1, int32_t *topk_idx, float *topk_w,
+                                              int32_t *expert_offsets, int32_t *perm_to_expanded,
+                                              int32_t *expanded_to_perm, uint16_t *out, hipStream_t stream) {
+  // the argument checks and the scratch size, with nothing launched
+  size_t need = 0;
+  qmoe_status st = layer_decode(logits, router_weights, x, T, k, w1, w2, act, route_in_fc1, topk_idx, topk_w,
+                                expert_offsets, perm_to_expanded, expanded_to_perm, out, nullptr, &need, stream);
+  if (st != QMOE_OK) return st;
+  if (need > (size_t)QMOE_NOALLOC_SCRATCH_BYTES) return QMOE_EWORKSPACE;
+  void *ptr = nullptr;
+  st = device_scratch(&ptr);
+  if (st != QMOE_OK) return st;
+  size_t have = (size_t)QMOE_NOALLOC_SCRATCH_BYTES;
+  return layer_decode(logits, router_weights, x, T, k, w1, w2, act, route_in_fc1, topk_idx, topk_w, expert_offsets,
+                      perm_to_expanded, expanded_to_perm, out, ptr, &have, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+qmoe_status layer_decode(const float *logits, const float *router_weights, const uint16_t *x, int32_t T, int32_t k,
+                         const qmoe_fp4_weights *w1, const qmoe_fp4_weights *w2, const qmoe_swiglu *act,
+                         int32_t route_in_fc1, int32_t *topk_idx, float *topk_w, int32_t *expert_offsets,
+                         int32_t *perm_to_expanded, int32_t *expanded_to_perm, uint16_t *out, void *ws,
+                         size_t *ws_bytes, hipStream_t stream) {
   if (!logits || !topk_idx || !topk_w || !expert_offsets || !perm_to_expanded || !expanded_to_perm)
     return QMOE_EINVAL;
   if (route_in_fc1 != 0 && route_in_fc1 != 1) return QMOE_EINVAL;
@@ -369,6 +441,10 @@ qmoe_status qmoe_fp4_moe_layer_decode(const float *logits, const float *router_w
   return check_launch(
       launch_finalize(ws2, a2.nchunks, plane, topk_w, expanded_to_perm, T, k, w2->N, out, stream));
 }
+
+}  // namespace
+
+extern "C" {
 
 qmoe_status qmoe_fp4_gemv_fc2(const uint16_t *h, int32_t T, int32_t k, const qmoe_fp4_weights *w2,
                               const int32_t *expert_offsets, float *y_rows, void *ws, size_t *ws_bytes,

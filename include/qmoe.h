@@ -286,6 +286,31 @@ qmoe_status qmoe_fp4_moe_layer_decode(const float *logits, const float *router_w
                                       uint16_t *out, void *ws, size_t *ws_bytes, hipStream_t stream);
 
 /*
+ * qmoe_fp4_moe_layer_decode_noalloc -- qmoe_fp4_moe_layer_decode without a
+ * workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).
+ *
+ * Arguments and results as qmoe_fp4_moe_layer_decode; the split-K partial
+ * sums go to a fixed device array inside the library instead: one copy per
+ * GPU it runs on, QMOE_NOALLOC_SCRATCH_BYTES long, held until the process
+ * ends (the copy of the current device is used; stream must belong to it).
+ * The call allocates nothing and needs no zeroed memory.  A shape whose
+ * partial sums exceed the array returns QMOE_EWORKSPACE before any launch
+ * (e.g. 64 rows of a hidden 4096 / intermediate 2048 layer need 25.2 MB).
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (concurrent streams, other threads) race and must be ordered by the
+ * caller.  QMOE_ELAUNCH also covers a failure to resolve the array's address.
+ */
+#define QMOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+qmoe_status qmoe_fp4_moe_layer_decode_noalloc(const float *logits, const float *router_weights, const uint16_t *x,
+                                              int32_t T, int32_t k, const qmoe_fp4_weights *w1,
+                                              const qmoe_fp4_weights *w2, const qmoe_swiglu *act,
+                                              int32_t route_in_fc1, int32_t *topk_idx, float *topk_w,
+                                              int32_t *expert_offsets, int32_t *perm_to_expanded,
+                                              int32_t *expanded_to_perm, uint16_t *out, hipStream_t stream);
+
+/*
  * qmoe_fp4_gemv_fc2 -- FC2 of every routed row.
  *
  * Passages: PR 31159 (the plain FP4 decode GEMV, "moe_gemv_kernel"); operator

@@ -234,6 +234,28 @@ def test_layer_decode_validation_and_workspace(q):
     assert call(T=33, k=2) == q.QMOE_EUNSUPPORTED                     # 66 rows
 
 
+def test_layer_decode_noalloc_validation(q):
+    """The allocation-free layer call runs the same checks before touching the
+    device, and refuses a shape whose partial sums exceed its fixed scratch."""
+    L = q.lib
+    w1 = weights(q, E=16, K=512, N=512)
+    w2 = weights(q, E=16, K=256, N=512)
+
+    def call(lg=A, x=A, T=4, k=2, a=w1, b=w2, rin=0, out=A):
+        return L.qmoe_fp4_moe_layer_decode_noalloc(lg, None, x, T, k, ctypes.byref(a), ctypes.byref(b), None, rin,
+                                                   A, A, A, A, A, out, None)
+
+    assert call(rin=2) == q.QMOE_EINVAL
+    assert call(lg=None) == q.QMOE_EINVAL
+    assert call(out=MIS) == q.QMOE_EALIGN
+    assert call(b=weights(q, E=16, K=128, N=512)) == q.QMOE_EINVAL
+    assert call(T=33, k=2) == q.QMOE_EUNSUPPORTED
+    big1 = weights(q, E=8, K=8192, N=8192)
+    big2 = weights(q, E=8, K=4096, N=8192)
+    assert call(T=8, k=8, a=big1, b=big2) == q.QMOE_EWORKSPACE      # 67 MB of partial sums
+    assert q.NOALLOC_SCRATCH_BYTES == 32 << 20
+
+
 def fc1_act(q, wc, act, T=1, k=2, path=0):
     n = ctypes.c_size_t(0)
     st = q.lib.qmoe_fp4_gemv_fc1_swiglu(A, T, k, ctypes.byref(wc), A, A, ctypes.byref(act), A, None,
