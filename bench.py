@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--path", default="auto", choices=("auto", "gemv", "grouped"),
                     help="FC kernel path of the layer workloads (auto: the library's AUTO rule)")
     ap.add_argument("--workload", default="mtp4", choices=LAYER_WORKLOADS + ("dequant", "fp8_dequant"))
+    ap.add_argument("--layer-call", default="auto", choices=("auto", "multi"),
+                    help="decode layer: auto = one kernel launch where the shape allows "
+                         "(qmoe_fp4_moe_layer_persistent), multi = the multi-launch fused calls")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -179,6 +182,8 @@ def bench_layer(args, torch, q, synth, np):
     x = to_dev(L.x.view(np.int16)).view(torch.bfloat16)
     path = {"auto": q.QMOE_PATH_AUTO, "gemv": q.QMOE_PATH_GEMV, "grouped": q.QMOE_PATH_GROUPED}[args.path]
     layer = MoELayer(cfg.T, cfg.E, cfg.k, cfg.H, cfg.I, copies[0][0], copies[0][1], path=path, device=dev)
+    if args.layer_call == "multi":
+        layer.layer_persistent = False
     layer.run(logits, x)
     torch.cuda.synchronize()
     offsets = layer.offsets.cpu().numpy()
@@ -235,7 +240,8 @@ def bench_layer(args, torch, q, synth, np):
         kname, tname = "fp4_gemv_kernel + splitk_epilogue_kernel (FC1+SwiGLU)", f"gemv_fc1_{args.workload}"
         metric = METRIC
     config = {"workload": cfg.name, "rows": R, "distinct_experts": D, "layer_copies": layers,
-              "path": args.path, "launch": "eager" if args.eager else "hip_graph"}
+              "path": args.path, "launch": "eager" if args.eager else "hip_graph",
+              "layer_call": "one launch" if layer.layer_persistent else "multi-launch"}
     result = base_result(metric, value, "GB/s", args, ms, config)
     result.update({"us_per_layer": round(ms * 1e3, 3), "hbm_frac_weight_bytes": round(value / HBM_PEAK_GBS, 4),
                    "weight_bytes_per_layer": weight_bytes})

@@ -26,7 +26,8 @@ QMOE_PATH_AUTO, QMOE_PATH_GEMV, QMOE_PATH_GROUPED = 0, 1, 2
 GEMV_MAX_ROWS = 64
 
 EXPORTS = ("qmoe_route_topk", "qmoe_route_topk_router_weights", "qmoe_fp4_resolve_path", "qmoe_fp4_gemv_fc1_swiglu",
-           "qmoe_fp4_route_fc1_swiglu", "qmoe_fp4_moe_layer_decode", "qmoe_fp4_moe_layer_decode_noalloc",
+           "qmoe_fp4_route_fc1_swiglu", "qmoe_fp4_moe_layer_decode", "qmoe_fp4_moe_layer_persistent",
+           "qmoe_fp4_moe_layer_decode_noalloc",
            "qmoe_fp4_gemv_fc2",
            "qmoe_fp4_gemv_fc2_finalize",
            "qmoe_finalize",
@@ -81,6 +82,8 @@ def _load():
         "qmoe_fp4_resolve_path": [I32, I32, W, I32, ctypes.POINTER(ctypes.c_int)],
         "qmoe_fp4_moe_layer_decode": [P, P, P, I32, I32, W, W, ctypes.POINTER(SwigluC), I32, P, P, P, P, P, P, P,
                                       SZ, P],
+        "qmoe_fp4_moe_layer_persistent": [P, P, P, I32, I32, W, W, ctypes.POINTER(SwigluC), P, P, P, P, P, P, P,
+                                          SZ, P],
         "qmoe_fp4_moe_layer_decode_noalloc": [P, P, P, I32, I32, W, W, ctypes.POINTER(SwigluC), I32, P, P, P, P,
                                               P, P, P],
         "qmoe_fp4_route_fc1_swiglu": [P, P, P, I32, I32, W, ctypes.POINTER(SwigluC), P, P, P, P, P, P, P, SZ, P],
@@ -237,6 +240,43 @@ def qmoe_fp4_moe_layer_decode(logits, router_weights, x, k, w1: FP4Weights, w2: 
         _ptr(logits), _ptr(router_weights), _ptr(x), T, k, ctypes.byref(c1), ctypes.byref(c2), _swiglu(act),
         1 if route_in_fc1 else 0, _ptr(topk_idx), _ptr(topk_w), _ptr(expert_offsets), _ptr(perm_to_expanded),
         _ptr(expanded_to_perm), _ptr(out), _ptr(ws), ctypes.byref(n), _stream(stream)))
+
+
+LAYER_SYNC_BYTES = 69888   # QMOE_LAYER_SYNC_BYTES: counters at the start of the persistent layer's workspace
+
+
+def layer_persistent_workspace_bytes(T: int, k: int, w1: FP4Weights, w2: FP4Weights, act=None) -> int:
+    """Workspace size of qmoe_fp4_moe_layer_persistent."""
+    n = ctypes.c_size_t(0)
+    c1, c2 = w1.c(), w2.c()
+    d = 256
+    _check("layer_persistent_workspace_bytes", lib.qmoe_fp4_moe_layer_persistent(
+        d, None, d, T, k, ctypes.byref(c1), ctypes.byref(c2), _swiglu(act), d, d, d, d, d, d, None,
+        ctypes.byref(n), None))
+    return n.value
+
+
+def alloc_layer_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """Workspace of qmoe_fp4_moe_layer_persistent: zero-filled once here (its counters must start at
+    zero; every completed call leaves them zero)."""
+    return torch.zeros(max(nbytes, LAYER_SYNC_BYTES), dtype=torch.uint8, device=device)
+
+
+def layer_error_word(ws: torch.Tensor) -> int:
+    """The persistent layer's error word (bytes 0..3 of its workspace): nonzero after a wait ran out."""
+    return int(ws[:4].view(torch.int32).item())
+
+
+def qmoe_fp4_moe_layer_persistent(logits, router_weights, x, k, w1: FP4Weights, w2: FP4Weights, topk_idx, topk_w,
+                                  expert_offsets, perm_to_expanded, expanded_to_perm, out, ws, act=None,
+                                  stream=None):
+    T = x.shape[0]
+    c1, c2 = w1.c(), w2.c()
+    n = ctypes.c_size_t(ws.numel() * ws.element_size())
+    _check("qmoe_fp4_moe_layer_persistent", lib.qmoe_fp4_moe_layer_persistent(
+        _ptr(logits), _ptr(router_weights), _ptr(x), T, k, ctypes.byref(c1), ctypes.byref(c2), _swiglu(act),
+        _ptr(topk_idx), _ptr(topk_w), _ptr(expert_offsets), _ptr(perm_to_expanded), _ptr(expanded_to_perm),
+        _ptr(out), _ptr(ws), ctypes.byref(n), _stream(stream)))
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20

@@ -324,6 +324,81 @@ qmoe_status qmoe_fp4_moe_layer_decode(const float *logits, const float *router_w
                       perm_to_expanded, expanded_to_perm, out, ws, ws_bytes, stream);
 }
 
+qmoe_status qmoe_fp4_moe_layer_persistent(const float *logits, const float *router_weights, const uint16_t *x,
+                                          int32_t T, int32_t k, const qmoe_fp4_weights *w1, const qmoe_fp4_weights *w2,
+                                          const qmoe_swiglu *act, int32_t *topk_idx, float *topk_w,
+                                          int32_t *expert_offsets, int32_t *perm_to_expanded,
+                                          int32_t *expanded_to_perm, uint16_t *out, void *ws, size_t *ws_bytes,
+                                          hipStream_t stream) {
+  if (!logits || !topk_idx || !topk_w || !expert_offsets || !perm_to_expanded || !expanded_to_perm)
+    return QMOE_EINVAL;
+  FcShape sh;
+  qmoe_status st = check_fc(w1, T, k, x, expert_offsets, out, QMOE_PATH_GEMV, &sh);
+  if (st != QMOE_OK) return st;
+  st = check_weights(w2);
+  if (st != QMOE_OK) return st;
+  if (w2->E != w1->E || w1->N != 2 * w2->K || w2->N != w1->K || w2->fmt != w1->fmt) return QMOE_EINVAL;
+  if (!aligned16(logits) || (router_weights && !aligned16(router_weights)) || !aligned16(topk_idx) ||
+      !aligned16(topk_w) || !aligned16(perm_to_expanded) || !aligned16(expanded_to_perm))
+    return QMOE_EALIGN;
+  const int32_t fusion = act ? act->fusion : QMOE_SWIGLU_INTERLEAVED;
+  if (fusion != 0 && fusion != QMOE_SWIGLU_INTERLEAVED && fusion != QMOE_SWIGLU_CONCAT) return QMOE_EINVAL;
+  const int32_t H = w1->K, I = w2->K;
+  if (sh.rows > QMOE_GEMV_MAX_ROWS || H % 32 != 0) return QMOE_EUNSUPPORTED;
+  if (I > 256 * kLayerMaxHChunks || H > 256 * kLayerMaxTiles2) return QMOE_EUNSUPPORTED;
+  if (fusion == QMOE_SWIGLU_CONCAT && I % 256 != 0) return QMOE_EUNSUPPORTED;
+  LayerArgs a = {};
+  a.logits = logits;
+  a.rw = router_weights;
+  a.x = x;
+  a.w1 = w1->w;
+  a.s1 = w1->scales;
+  a.g1 = w1->gscale;
+  a.w2 = w2->w;
+  a.s2 = w2->scales;
+  a.g2 = w2->gscale;
+  a.T = T;
+  a.E = w1->E;
+  a.k = k;
+  a.H = H;
+  a.I = I;
+  a.concat = fusion == QMOE_SWIGLU_CONCAT;
+  a.alpha = act ? act->alpha : 1.0f;
+  a.beta = act ? act->beta : 0.0f;
+  a.limit = act ? act->limit : INFINITY;
+  a.idx = topk_idx;
+  a.wts = topk_w;
+  a.offsets = expert_offsets;
+  a.p2e = perm_to_expanded;
+  a.e2p = expanded_to_perm;
+  a.out = out;
+  a.rows = sh.rows;
+  a.nch1 = (H + 255) / 256;
+  a.nch2 = (I + 255) / 256;
+  a.ntiles1 = (2 * I + 255) / 256;
+  a.ntiles2 = (H + 255) / 256;
+  a.max_polls = 1 << 18;
+  // workspace: counters, FC1 partial sums, FC2 partial sums (256-byte aligned parts)
+  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  static_assert(((kLayerSyncBytes + 255) & ~(size_t)255) == QMOE_LAYER_SYNC_BYTES, "counter region");
+  const size_t b_sync = QMOE_LAYER_SYNC_BYTES;
+  const size_t b_p1 = up((size_t)a.nch1 * sh.rows * (2 * I) * sizeof(float));
+  const size_t b_p2 = up((size_t)a.nch2 * sh.rows * H * sizeof(float));
+  if (b_p1 >= ((size_t)1 << 31) || b_p2 >= ((size_t)1 << 31)) return QMOE_EUNSUPPORTED;
+  if (!ws_bytes) return QMOE_EINVAL;
+  if (!ws) {
+    *ws_bytes = b_sync + b_p1 + b_p2;
+    return QMOE_OK;
+  }
+  if (*ws_bytes < b_sync + b_p1 + b_p2) return QMOE_EWORKSPACE;
+  if (!aligned16(ws)) return QMOE_EALIGN;
+  char *base = (char *)ws;
+  a.sync = (int32_t *)base;
+  a.part1 = (float *)(base + b_sync);
+  a.part2 = (float *)(base + b_sync + b_p1);
+  return check_launch(launch_fp4_layer(a, w1->fmt == QMOE_FMT_NVFP4 ? 0 : 1, stream));
+}
+
 qmoe_status qmoe_fp4_moe_layer_decode_noalloc(const float *logits, const float *router_weights, const uint16_t *x,
                                               int32_t T, int32_t k, const qmoe_fp4_weights *w1,
                                               const qmoe_fp4_weights *w2, const qmoe_swiglu *act,

@@ -53,6 +53,45 @@ struct GemvArgs {
   float h_alpha, h_beta, h_limit;
 };
 
+// The whole decode layer in one launch (layer.hip): routing, FC1 + SwiGLU,
+// FC2 and the weighted un-permute, workgroups handing results to each other
+// through the workspace and counters.
+struct LayerArgs {
+  const float *logits;      // [T][E]
+  const float *rw;          // [T][E] router_weights, or null: softmax weights
+  const uint16_t *x;        // [T][H] bf16
+  const uint8_t *w1, *s1;   // FC1: K = H, N = N1 = 2I
+  const float *g1;          // may be null (MXFP4)
+  const uint8_t *w2, *s2;   // FC2: K = I, N = H
+  const float *g2;
+  int32_t T, E, k, H, I;
+  int32_t concat;           // FC1 pairing: gate j / linear I + j (else 2j, 2j + 1)
+  float alpha, beta, limit;
+  int32_t *idx;             // [T][k]
+  float *wts;               // [T][k]
+  int32_t *offsets;         // [E+1]
+  int32_t *p2e, *e2p;       // [T*k]
+  uint16_t *out;            // [T][H] bf16
+  int32_t *sync;            // counters (zero on entry, zero again on exit) and the error word
+  float *part1;             // [nch1][rows][2I] FC1 split-K partial sums (g applied)
+  float *part2;             // [nch2][rows][H] FC2 split-K partial sums (g applied)
+  int32_t rows;             // T*k (<= 64)
+  int32_t nch1, nch2;       // k chunks of 256 rows: ceil(H / 256), ceil(I / 256)
+  int32_t ntiles1, ntiles2; // 256-column tiles: ceil(2I / 256), ceil(H / 256)
+  int32_t max_polls;        // bound on every wait (then the error word is set and the wait ends)
+};
+
+constexpr int kLayerMaxHChunks = 16;   // I <= 4096
+constexpr int kLayerMaxTiles2 = 64;    // H <= 16384
+constexpr int kLayerSyncStride = 16;   // int32 per counter: one 64-byte segment each
+constexpr size_t kLayerSyncBytes =
+    (size_t)(2 + kLayerMaxTiles2 + 64 * kLayerMaxHChunks) * kLayerSyncStride * sizeof(int32_t);
+// rows per workgroup pass of the layer (1 for one token, 2 up to 3 tokens, else 4)
+int layer_rows_per_pass(int T);
+// upper bound of the work items of one call (every slot live)
+int layer_max_items(const LayerArgs &a);
+hipError_t launch_fp4_layer(const LayerArgs &a, int fmt, hipStream_t s);
+
 size_t gemv_workspace_bytes(int32_t rows, int32_t max_rows_per_expert, int32_t E, int32_t K, int32_t N,
                             bool force_partials = false);
 void gemv_plan(GemvArgs &a, int max_rows_per_expert, void *ws);

@@ -9,10 +9,11 @@ from __future__ import annotations
 
 import torch
 
-from . import (GEMV_MAX_ROWS, QMOE_PATH_AUTO, QMOE_PATH_GEMV, QMOE_PATH_GROUPED, FP4Weights, FP8Weights,
-               alloc_workspace, fc_workspace_bytes, fp8_workspace_bytes, layer_decode_workspace_bytes,
-               qmoe_finalize, qmoe_fp4_gemv_fc1_swiglu, qmoe_fp4_gemv_fc2, qmoe_fp4_gemv_fc2_finalize,
-               qmoe_fp4_moe_layer_decode, qmoe_fp4_resolve_path, qmoe_fp4_route_fc1_swiglu,
+from . import (GEMV_MAX_ROWS, QMOE_PATH_AUTO, QMOE_PATH_GEMV, QMOE_PATH_GROUPED, QMOE_SWIGLU_CONCAT, FP4Weights,
+               FP8Weights, alloc_layer_workspace, alloc_workspace, fc_workspace_bytes, fp8_workspace_bytes,
+               layer_decode_workspace_bytes, layer_persistent_workspace_bytes, qmoe_finalize,
+               qmoe_fp4_gemv_fc1_swiglu, qmoe_fp4_gemv_fc2, qmoe_fp4_gemv_fc2_finalize, qmoe_fp4_moe_layer_decode,
+               qmoe_fp4_moe_layer_persistent, qmoe_fp4_resolve_path, qmoe_fp4_route_fc1_swiglu,
                qmoe_fp8_gemv_fc1_swiglu, qmoe_fp8_gemv_fc2, qmoe_route_topk, qmoe_route_topk_router_weights)
 
 
@@ -53,6 +54,13 @@ class MoELayer:
         self.layer_decode = (fits and path != QMOE_PATH_GROUPED and T <= 4 and H <= 2048
                              and qmoe_fp4_resolve_path(T, k, w1, path) == QMOE_PATH_GEMV
                              and qmoe_fp4_resolve_path(T, k, w2, path) == QMOE_PATH_GEMV)
+        # the whole layer in one kernel launch (qmoe_fp4_moe_layer_persistent)
+        concat = act is not None and len(tuple(act)) > 3 and tuple(act)[3] == QMOE_SWIGLU_CONCAT
+        self.layer_persistent = (fits and path != QMOE_PATH_GROUPED and H % 32 == 0 and H <= 16384 and I <= 4096
+                                 and (not concat or I % 256 == 0) and w1.fmt == w2.fmt
+                                 and qmoe_fp4_resolve_path(T, k, w1, path) == QMOE_PATH_GEMV)
+        self.ws_layer = (alloc_layer_workspace(layer_persistent_workspace_bytes(T, k, w1, w2, act), dev)
+                         if self.layer_persistent else None)
         if not self.fp8 and R <= GEMV_MAX_ROWS:  # route_fc1() is callable
             need = max(need, fc_workspace_bytes(4, T, k, w1, path, act))
         if fits:  # decode_layer() is callable
@@ -87,6 +95,12 @@ class MoELayer:
         qmoe_fp4_moe_layer_decode(logits, router_weights, x, self.k, self.w1, self.w2, self.topk_idx, self.topk_w,
                                   self.offsets, self.p2e, self.e2p, self.out, self.ws, self.act, rin)
 
+    def persistent_layer(self, logits, x, router_weights=None):
+        """The whole layer by qmoe_fp4_moe_layer_persistent (one kernel launch; h and y are not written)."""
+        qmoe_fp4_moe_layer_persistent(logits, router_weights, x, self.k, self.w1, self.w2, self.topk_idx,
+                                      self.topk_w, self.offsets, self.p2e, self.e2p, self.out, self.ws_layer,
+                                      self.act)
+
     def fc2(self):
         if self.fp8:
             qmoe_fp8_gemv_fc2(self.h, self.T, self.k, self.w2, self.offsets, self.y, self.ws, self.path)
@@ -102,10 +116,14 @@ class MoELayer:
 
     def run(self, logits, x, fused: bool = False, router_weights=None):
         """route -> FC1+SwiGLU -> FC2 -> finalize; fused=True runs the decode
-        window's layer as one call (routing inside FC1 at T = 1, SwiGLU inside
-        FC2's staging, FC2 + finalize fused: h and y are not written), else
-        FC2 and the finalize as one call (y not written); router_weights [T][E]
-        selects DeepSeek-style mixing weights."""
+        window's layer in one kernel launch where it can (the persistent
+        layer), else as one call of a few launches (routing inside FC1 at
+        T = 1, SwiGLU inside FC2's staging, FC2 + finalize fused: h and y are
+        not written), else FC2 and the finalize as one call (y not written);
+        router_weights [T][E] selects DeepSeek-style mixing weights."""
+        if fused and self.layer_persistent:
+            self.persistent_layer(logits, x, router_weights)
+            return self.out
         if fused and self.layer_decode:
             self.decode_layer(logits, x, router_weights)
             return self.out

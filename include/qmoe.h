@@ -25,6 +25,8 @@
  *   qmoe_fp4_route_fc1_swiglu   routing inside the FC1 launch
  *   qmoe_fp4_moe_layer_decode   the whole layer: routing, FC1, SwiGLU inside
  *                               FC2's staging, FC2 + finalize (h, y not written)
+ *   qmoe_fp4_moe_layer_persistent  the whole layer in one kernel launch
+ *   qmoe_fp4_moe_layer_decode_noalloc  the whole layer without a workspace
  *
  * and one host-only query: qmoe_fp4_resolve_path (the kernel path an FC call
  * takes).
@@ -284,6 +286,44 @@ qmoe_status qmoe_fp4_moe_layer_decode(const float *logits, const float *router_w
                                       const qmoe_swiglu *act, int32_t route_in_fc1, int32_t *topk_idx, float *topk_w,
                                       int32_t *expert_offsets, int32_t *perm_to_expanded, int32_t *expanded_to_perm,
                                       uint16_t *out, void *ws, size_t *ws_bytes, hipStream_t stream);
+
+/*
+ * qmoe_fp4_moe_layer_persistent -- the whole decode MoE layer in one kernel
+ * launch: routing, FC1 + SwiGLU, FC2 and the weighted un-permute.
+ *
+ * Passages: operator documentation section 1 (the chain) and section 12.1
+ * (split-K SwiGLU); PR 31159 (the decode GEMV, up to 64 rows); PR 31156 and
+ * the fused single-token routing kernel it builds on (PR 29919), which this
+ * call extends from the routing prologue to the whole layer.
+ *
+ * Every output equals qmoe_fp4_moe_layer_decode's (routing outputs and out)
+ * bit for bit: the same partial sums, summation orders and roundings.  The
+ * kernel's workgroups hand FC1 sums, h and FC2 sums to each other through the
+ * workspace and counters in it; it launches no more workgroups than the GPU
+ * holds at once (an occupancy query), and every wait in it is bounded.
+ *
+ * Arguments as qmoe_fp4_moe_layer_decode (without route_in_fc1; w1 and w2
+ * share the format).  Workspace (query its size with ws == NULL): its first
+ * QMOE_LAYER_SYNC_BYTES bytes are counters that MUST BE ZERO before the first
+ * call on this workspace (hipMemset once after allocating it); every
+ * completed call leaves them zero again, so calls on one stream need no
+ * clearing in between.
+ * Bytes 0..3 are an error word: a call that finds a wait run out (possible
+ * only if other work keeps some of its workgroups off the GPU) ORs 1 into it,
+ * its outputs are then invalid and the counters must be zeroed again; the
+ * call never clears the word.  Calls that share a workspace must be ordered
+ * (same stream).
+ * Limits: T*k <= 64, H % 32 == 0, H <= 16384, I <= 4096, concatenated SwiGLU
+ * only with I % 256 == 0 (QMOE_EUNSUPPORTED); w1 / w2 shapes or formats that
+ * do not match: QMOE_EINVAL; and the limits of the separate calls.
+ */
+#define QMOE_LAYER_SYNC_BYTES 69888
+qmoe_status qmoe_fp4_moe_layer_persistent(const float *logits, const float *router_weights, const uint16_t *x,
+                                          int32_t T, int32_t k, const qmoe_fp4_weights *w1, const qmoe_fp4_weights *w2,
+                                          const qmoe_swiglu *act, int32_t *topk_idx, float *topk_w,
+                                          int32_t *expert_offsets, int32_t *perm_to_expanded,
+                                          int32_t *expanded_to_perm, uint16_t *out, void *ws, size_t *ws_bytes,
+                                          hipStream_t stream);
 
 /*
  * qmoe_fp4_moe_layer_decode_noalloc -- qmoe_fp4_moe_layer_decode without a

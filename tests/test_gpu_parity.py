@@ -533,7 +533,7 @@ def test_fc2_finalize_fused_equals_separate_calls(cfg):
     gpu_h = bf16_host(layer.h).copy()
     layer.out.view(torch.int16).fill_(0x7FC1)   # poison
     layer.ws.view(torch.int16).fill_(0x7FC1)
-    layer.run(logits, x, fused=True)
+    layer.fc2_finalize()
     torch.cuda.synchronize()
     got = bf16_host(layer.out)
     assert np.array_equal(got, ref)
@@ -629,6 +629,85 @@ def test_layer_decode_equals_separate_calls(cfg, mode, route_in_fc1):
     rwh = None if rw is None else synth.router_weights(cfg)
     out_ref, _ = oracle_e2e(L, gpu_h, act, rwh, key=(cfg.name, mode))
     assert_close("layer decode out vs oracle", codecs.bf16_to_f64(bf16_host(layer.out)), out_ref)
+
+
+PERSISTENT = LAYER_DECODE + [synth.MTP8, synth.shrink(synth.MX_DECODE, E=32, T=8, k=8, H=1024, I=512, seed=28),
+                             synth.shrink(synth.MTP4, E=64, T=6, k=8, H=2304, I=1280, seed=29)]
+
+
+@pytest.mark.parametrize("mode", ["softmax", "router_weights", "gptoss_concat"])
+@pytest.mark.parametrize("cfg", PERSISTENT, ids=lambda c: c.name)
+def test_layer_persistent(cfg, mode):
+    """qmoe_fp4_moe_layer_persistent runs the whole layer in one launch: the
+    routing outputs and out must equal the separate routing, FC1 (GEMV) and
+    fused FC2 + finalize (GEMV) calls bit for bit, on two calls in a row with
+    outputs and the non-counter workspace poisoned before each; the counters
+    must be back at zero with the error word clear; and out must match the
+    oracle's end-to-end output."""
+    import fp4_weight_only_amd as q
+    L = synth.layer_inputs(cfg)
+    act = GPTOSS + (q.QMOE_SWIGLU_CONCAT,) if mode == "gptoss_concat" else None
+    layer, logits, x = layer_dev(L, act=act, path=q.QMOE_PATH_GEMV)
+    rw = to_dev(synth.router_weights(cfg)) if mode == "router_weights" else None
+    print_case("layer persistent", cfg.name, mode)
+    if mode == "gptoss_concat" and cfg.I % 256 != 0:
+        assert not layer.layer_persistent
+        with pytest.raises(q.QmoeError) as ei:
+            q.layer_persistent_workspace_bytes(cfg.T, cfg.k, layer.w1, layer.w2, act)
+        assert ei.value.status == q.QMOE_EUNSUPPORTED
+        return
+    assert layer.layer_persistent
+    outs = (layer.topk_idx, layer.topk_w, layer.offsets, layer.p2e, layer.e2p, layer.out)
+    layer.route(logits, rw)
+    layer.fc1(x)
+    layer.fc2_finalize()
+    torch.cuda.synchronize()
+    ref = [t.view(torch.int32 if t.element_size() == 4 else torch.int16).cpu().numpy().copy() for t in outs]
+    gpu_h = bf16_host(layer.h).copy()
+    for rep in range(2):
+        for t in outs:
+            t.view(torch.int32 if t.element_size() == 4 else torch.int16).fill_(-7)
+        fill_pattern(layer.ws_layer[q.LAYER_SYNC_BYTES:], 0x7FC00001 + rep)
+        layer.persistent_layer(logits, x, rw)
+        torch.cuda.synchronize()
+        for name, t, r in zip(("idx", "w", "offsets", "p2e", "e2p", "out"), outs, ref):
+            got = t.view(torch.int32 if t.element_size() == 4 else torch.int16).cpu().numpy()
+            assert np.array_equal(got, r), (rep, name)
+        assert layer_sync_clean(layer.ws_layer), rep
+    rwh = None if rw is None else synth.router_weights(cfg)
+    out_ref, _ = oracle_e2e(L, gpu_h, act, rwh, key=(cfg.name, mode))
+    assert_close("persistent out vs oracle", codecs.bf16_to_f64(bf16_host(layer.out)), out_ref)
+
+
+def test_layer_persistent_mxfp4_decode_full():
+    """The 8-token MXFP4 layer (E=256, hidden 4096, intermediate 2048) in one
+    launch: bit for bit the separate GEMV calls; FC2 + finalize against the
+    oracle on sampled columns, fed the GPU's h (the separate FC1 call's h is
+    checked against the oracle by test_layer_mxfp4_decode_full_sampled)."""
+    import fp4_weight_only_amd as q
+    L = synth.layer_inputs(synth.MX_DECODE)
+    c = L.cfg
+    layer, logits, x = layer_dev(L, path=q.QMOE_PATH_GEMV)
+    print_case("layer persistent", c.name)
+    assert layer.layer_persistent
+    layer.route(logits)
+    layer.fc1(x)
+    layer.fc2_finalize()
+    torch.cuda.synchronize()
+    ref = bf16_host(layer.out).copy()
+    gpu_h = bf16_host(layer.h).copy()
+    layer.out.view(torch.int16).fill_(-7)
+    layer.persistent_layer(logits, x)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_host(layer.out), ref)
+    assert layer_sync_clean(layer.ws_layer)
+    rng = np.random.default_rng(3)
+    cols = np.sort(rng.choice(c.H, 256, replace=False))
+    idx, wts = route.route_topk(L.logits, c.k)
+    off, p2e, e2p = route.expert_maps(idx, c.E)
+    y_ref = moe.fc2(gpu_h, L.w2, L.s2, L.g2, c.fmt, off, cols=cols)
+    assert_close("persistent out vs oracle (sampled)", codecs.bf16_to_f64(ref)[:, cols],
+                 moe.finalize(y_ref, wts, e2p, c.T, c.k))
 
 
 @pytest.mark.parametrize("K", [512, 384], ids=["lds_tile", "direct_128x512"])
@@ -790,26 +869,48 @@ def test_determinism_and_poisoned_buffers(cfg):
     layer.run(logits, x)
     torch.cuda.synchronize()
     first = snap()
-    layer.run(logits, x, fused=True)
-    torch.cuda.synchronize()
-    first_fused = bf16_host(layer.out).copy()
-    assert np.array_equal(first_fused, bf16_host_from(first[7]))
+    first_out = bf16_host_from(first[7])
+
+    def fc2_finalize():
+        layer.route(logits)
+        layer.fc1(x)
+        layer.fc2_finalize()
+
+    variants = [("separate", lambda: layer.run(logits, x)), ("fc2+finalize", fc2_finalize)]
+    if layer.layer_decode:
+        variants.append(("layer decode", lambda: layer.decode_layer(logits, x)))
+    if layer.layer_persistent:
+        variants.append(("persistent", lambda: layer.persistent_layer(logits, x)))
     for pat in _poison_patterns():
-        for fused in (False, True):
+        for name, run in variants:
             for t in bufs:
                 fill_pattern(t, pat)
-            layer.run(logits, x, fused=fused)
+            if layer.ws_layer is not None:   # everything past the counters (they must stay zero)
+                fill_pattern(layer.ws_layer[q_layer_sync_bytes():], pat)
+            run()
             torch.cuda.synchronize()
-            if fused:   # h and y are not written by the fused calls
-                assert np.array_equal(bf16_host(layer.out), first_fused), hex(pat)
-                assert np.array_equal(layer.topk_idx.view(torch.uint8).cpu().numpy(), first[0]), hex(pat)
-            else:
+            if name == "separate":
                 for i, (a, b) in enumerate(zip(first, snap())):
-                    assert np.array_equal(a, b), (hex(pat), i)
+                    assert np.array_equal(a, b), (hex(pat), name, i)
+            else:   # h and y are not all written by the fused calls
+                assert np.array_equal(bf16_host(layer.out), first_out), (hex(pat), name)
+                assert np.array_equal(layer.topk_idx.view(torch.uint8).cpu().numpy(), first[0]), (hex(pat), name)
+                if name == "persistent":
+                    assert layer_sync_clean(layer.ws_layer), (hex(pat), name)
 
 
 def bf16_host_from(u8):
     return np.ascontiguousarray(u8).view(np.uint16)
+
+
+def q_layer_sync_bytes():
+    import fp4_weight_only_amd as q
+    return q.LAYER_SYNC_BYTES
+
+
+def layer_sync_clean(ws):
+    """The persistent layer's counters are back at zero and its error word is 0."""
+    return not bool(ws[:q_layer_sync_bytes()].any().item())
 
 
 def fill_pattern(t, pat):
