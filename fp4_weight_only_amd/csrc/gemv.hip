@@ -318,12 +318,7 @@ __global__ __launch_bounds__(max_waves<MRMAX>() * 64) __attribute__((amdgpu_wave
     }
     lds_barrier();
 
-    if (MRMAX == 1 || mr == 1)
-      lane_dot<FMT, 1, MRMAX>(sm, A, SB, g, wave, lane);
-    else if (MRMAX == 2 || mr == 2)
-      lane_dot<FMT, 2, MRMAX>(sm, A, SB, g, wave, lane);
-    else
-      lane_dot<FMT, 4, MRMAX>(sm, A, SB, g, wave, lane);  // 3 or 4 rows
+    lane_pass<FMT, MRMAX>(sm, A, SB, g, wave, lane, 0, mr);
     lds_barrier();
 
     // ---- reduce the W waves (fixed order); one thread per column ------------

@@ -131,4 +131,92 @@ __device__ __forceinline__ void lane_dot(Smem<MRMAX> &sm, const uint32_t (&A)[kG
   }
 }
 
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Columns 4 GRP .. 4 GRP + 3 of two E2M1 rows as bf16 K pairs (the
+// matching half of e2m1_kpair_cvt's output).
+template <int GRP>
+__device__ __forceinline__ void e2m1_kpair_cvt_half(uint32_t a, uint32_t b, uint32_t (&w)[4]) {
+  const uint32_t ev = (a & 0x0F0F0F0Fu) | ((b << 4) & 0xF0F0F0F0u);
+  const uint32_t od = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+  w[0] = fp4_byte_to_bf16x2<2 * GRP>(ev);
+  w[1] = fp4_byte_to_bf16x2<2 * GRP>(od);
+  w[2] = fp4_byte_to_bf16x2<2 * GRP + 1>(ev);
+  w[3] = fp4_byte_to_bf16x2<2 * GRP + 1>(od);
+}
+
+// Two to four staged rows r0 .. r0 + mr - 1 through the matrix cores, over
+// the same lane layout as lane_dot: 4x4x4 bf16 blocks, sixteen per
+// instruction.  Block b is lanes 4b .. 4b + 3; lane 4b + i brings activation
+// row r0 + i (zeros past mr) and lane 4b + j one of its own weight columns,
+// each over a k quad (4 of the lane's 32 k rows); the result is the lane's
+// column for all four rows.  Per column and scale block the k quads
+// accumulate in fp32 from +0, and the block scale multiplies the block sum
+// into the lane's running sum (fma), the dot2 path's order of operations.
+// Columns go in two groups of four to bound the live accumulators.
+template <int FMT, int MRMAX, int GRP>
+__device__ __forceinline__ void lane_mfma_group(Smem<MRMAX> &sm, const uint32_t (&A)[kGemvLaneK],
+                                                const u32x2_t (&SB)[2], int g, int wave, int lane, int r0, int mr) {
+  constexpr int B = (FMT == 0) ? 16 : 32;
+  constexpr int NBLK = kGemvLaneK / B;
+  constexpr int QPB = B / 4;  // k quads per scale block
+  const int i = lane & 3;
+  const bool xon = i < mr;
+  const uint16_t *xrow = &sm.xs[xon ? r0 + i : 0][g * kGemvLaneK];
+  float acc[4][4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[c][r] = 0.f;
+#pragma unroll
+  for (int b = 0; b < NBLK; ++b) {
+    f32x4_t bacc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) bacc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < QPB; ++q) {
+      const int kq = b * QPB + q;
+      const u32x2_t xa = xon ? *(const u32x2_t *)(xrow + 4 * kq) : u32x2_t{0u, 0u};
+      uint32_t w0[4], w1[4];
+      e2m1_kpair_cvt_half<GRP>(A[4 * kq], A[4 * kq + 1], w0);
+      e2m1_kpair_cvt_half<GRP>(A[4 * kq + 2], A[4 * kq + 3], w1);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        bacc[c] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(s16x4_t, xa),
+                                                        __builtin_bit_cast(s16x4_t, u32x2_t{w0[c], w1[c]}),
+                                                        bacc[c], 0, 0, 0);
+    }
+    float sc[8];
+    decode_scales<FMT>(SB[b], sc);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[c][r] = fmaf(sc[4 * GRP + c], bacc[c][r], acc[c][r]);
+  }
+  const int nl = lane & 31;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (r < mr) {  // uniform
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c][r] = acc[c][r] + __shfl_xor(acc[c][r], 32);  // lower half + upper half
+      if (lane < 32)
+        *(float4 *)&sm.red[wave][r0 + r][nl * 8 + 4 * GRP] = make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
+    }
+  }
+}
+
+// One pass over mr <= MRMAX staged rows starting at r0: one row on the dot2
+// path, two to four on the matrix cores.
+template <int FMT, int MRMAX>
+__device__ __forceinline__ void lane_pass(Smem<MRMAX> &sm, const uint32_t (&A)[kGemvLaneK], const u32x2_t (&SB)[2],
+                                          int g, int wave, int lane, int r0, int mr) {
+  if (MRMAX == 1 || mr == 1) {
+    lane_dot<FMT, 1, MRMAX>(sm, A, SB, g, wave, lane, r0);
+  } else {
+    lane_mfma_group<FMT, MRMAX, 0>(sm, A, SB, g, wave, lane, r0, mr);
+    lane_mfma_group<FMT, MRMAX, 1>(sm, A, SB, g, wave, lane, r0, mr);
+  }
+}
+
 }  // namespace qmoe

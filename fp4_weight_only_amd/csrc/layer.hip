@@ -235,28 +235,7 @@ __device__ __forceinline__ void item_dot_store(const LayerArgs &a, S &sm, const 
                                                int tile, int kc, int K, int N, float *part, int tid, int wave,
                                                int lane) {
   const int g = wave * 2 + (lane >> 5);
-  // Three or four rows run as two passes over the same weight registers:
-  // one four-row pass needs more than the 128 registers a wave has here, and
-  // its spills would wait on the weight loads.
-  if (MRMAX == 1 || m == 1) {
-    lane_dot<FMT, 1, MRMAX>(sm.g, L.A, L.SB, g, wave, lane);
-  } else {
-    lane_dot<FMT, 2, MRMAX>(sm.g, L.A, L.SB, g, wave, lane);
-    if (MRMAX == 4 && m > 2) {
-      // the same registers, made opaque so the second pass decodes weights and
-      // scales again rather than keeping the first pass's decoded values live
-      uint32_t A[kGemvLaneK];
-#pragma unroll
-      for (int i = 0; i < kGemvLaneK; ++i) {
-        A[i] = L.A[i];
-        asm volatile("" : "+v"(A[i]));
-      }
-      u32x2_t SB[2] = {L.SB[0], L.SB[1]};
-#pragma unroll
-      for (int b = 0; b < 2; ++b) asm volatile("" : "+v"(SB[b]));
-      lane_dot<FMT, 2, MRMAX>(sm.g, A, SB, g, wave, lane, 2);  // m = 3: row 3 is staged as zeros, never stored
-    }
-  }
+  lane_pass<FMT, MRMAX>(sm.g, L.A, L.SB, g, wave, lane, 0, m);
   lds_barrier();
   const int W = K >= kKC ? kGemvMaxWaves : (K + kGemvWaveK - 1) / kGemvWaveK;
   const uint32_t plane = (uint32_t)a.rows * (uint32_t)N * 4u;
