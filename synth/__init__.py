@@ -135,6 +135,8 @@ DEQUANT = DequantConfig("dequant_mxfp4_E32_K2048_N1536", MXFP4, E=32, K=2048, N=
 DECODE = LayerConfig("decode_nvfp4_T1_E256_top8_H2048_I768", NVFP4, T=1, E=256, k=8, H=2048, I=768)
 MTP4 = LayerConfig("mtp_nvfp4_T4_E256_top8_H2048_I768_hot3", NVFP4, T=4, E=256, k=8, H=2048, I=768, routing="hot3")
 MTP8 = LayerConfig("mtp_nvfp4_T8_E256_top8_H2048_I768_hot3", NVFP4, T=8, E=256, k=8, H=2048, I=768, routing="hot3")
+# the same layer at 2 tokens (16 rows): the middle of the decode GEMV's 4-64 row range
+MTP2 = LayerConfig("mtp_nvfp4_T2_E256_top8_H2048_I768_hot3", NVFP4, T=2, E=256, k=8, H=2048, I=768, routing="hot3")
 MX_DECODE = LayerConfig("decode_mxfp4_T8_E256_top8_H4096_I2048", MXFP4, T=8, E=256, k=8, H=4096, I=2048)
 MX_PREFILL = LayerConfig("prefill_mxfp4_T512_E256_top8_H4096_I2048_zipf", MXFP4, T=512, E=256, k=8, H=4096, I=2048, routing="zipf")
 
@@ -143,7 +145,7 @@ FP8_MTP4 = LayerConfig("mtp_fp8_T4_E256_top8_H2048_I768_hot3", FP8, T=4, E=256, 
 FP8_PREFILL = LayerConfig("prefill_fp8_T512_E256_top8_H4096_I2048_zipf", FP8, T=512, E=256, k=8, H=4096, I=2048,
                           routing="zipf")
 
-LAYER_CONFIGS = {c.name: c for c in (TINY, DECODE, MTP4, MTP8, MX_DECODE, MX_PREFILL, FP8_MTP4, FP8_PREFILL)}
+LAYER_CONFIGS = {c.name: c for c in (TINY, DECODE, MTP2, MTP4, MTP8, MX_DECODE, MX_PREFILL, FP8_MTP4, FP8_PREFILL)}
 
 HOT_BOOST = 6.0
 
