@@ -313,6 +313,7 @@ def bench_layer(args, torch, q, synth, np):
     value = rig.weight_bytes / (ms * 1e-3) / 1e9
     fc1_ms = rig.time_fc1(args.eager)
     fc1_gbs = rig.fc1_bytes / (fc1_ms * 1e-3) / 1e9
+    fc2_ms = None if (prefill or fp8) else rig.time_fc2(args.eager)
     one_launch = layer.one_launch
 
     if prefill and fp8:
@@ -364,6 +365,9 @@ def bench_layer(args, torch, q, synth, np):
                               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(fc1_gbs / HBM_PEAK_GBS, 4),
                               "traffic": traffic, "avg_us": round(fc1_ms * 1e3, 3),
                               "bytes_per_launch": rig.fc1_bytes}
+    if fc2_ms is not None:   # the FC2 + finalize call on its own (GEMV + finalize launches)
+        result["fc2_finalize"] = {"us": round(fc2_ms * 1e3, 3), "bytes_per_call": rig.fc2_bytes,
+                                  "frac": round(rig.fc2_bytes / (fc2_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     if args.workload == "mtp4" and not args.no_sweep:
         # the metric's whole row range, T = 1, 2, 4, 8 (8..64 expanded rows)
         sweep = []
