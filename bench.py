@@ -79,9 +79,10 @@ def parse():
     ap.add_argument("--path", default="auto", choices=("auto", "gemv", "grouped"),
                     help="FC kernel path of the layer workloads (auto: the library's AUTO rule)")
     ap.add_argument("--workload", default="mtp4", choices=LAYER_WORKLOADS + ("dequant", "fp8_dequant"))
-    ap.add_argument("--layer-call", default="auto", choices=("auto", "multi"),
-                    help="decode layer: auto = one kernel launch where the shape allows "
-                         "(qmoe_fp4_moe_layer_persistent), multi = the multi-launch fused calls")
+    ap.add_argument("--layer-call", default="auto", choices=("auto", "multi", "one"),
+                    help="decode layer: auto = the library's default (one kernel launch, "
+                         "qmoe_fp4_moe_layer_persistent, up to four tokens), multi = the multi-launch calls, "
+                         "one = one launch wherever the shape allows")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true",
                     help="mtp4: skip the T = 1, 2, 4, 8 sweep and the dequant figures of the default line")
@@ -207,6 +208,8 @@ class LayerRig:
         self.one_launch_default = layer.one_launch      # and run(fused=True) takes it
         if layer_call == "multi":
             layer.one_launch = False
+        elif layer_call == "one":
+            layer.one_launch = layer.layer_persistent
         layer.run(self.logits, self.x)
         torch.cuda.synchronize()
         offsets = layer.offsets.cpu().numpy()
