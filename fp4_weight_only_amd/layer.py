@@ -61,12 +61,14 @@ class MoELayer:
                                  and qmoe_fp4_resolve_path(T, k, w1, path) == QMOE_PATH_GEMV)
         self.ws_layer = (alloc_layer_workspace(layer_persistent_workspace_bytes(T, k, w1, w2, act), dev)
                          if self.layer_persistent else None)
-        # run(fused=True) takes the one-launch layer up to four tokens, where
-        # it measured faster than the multi-launch calls (NVFP4 E=256,
-        # H=2048, I=768, same box: T=1 17.2 vs 17.5 us, T=2 22.0 vs 23.7,
-        # T=4 27.6 vs 30.2); at T=8 its three rounds of resident workgroups
-        # measured 42.7 against 41.3 us
-        self.one_launch = self.layer_persistent and T <= 4
+        # run(fused=True) takes the one-launch layer at two to four tokens,
+        # where it measured faster than the multi-launch calls (NVFP4 E=256,
+        # H=2048, I=768, same box: T=2 22.0 vs 23.7 us, T=4 27.6 vs 30.2); at
+        # T=1 the three launches with routing inside FC1 measured 17.45
+        # against 18.19 us (four repetitions each, one box), and at T=8 the
+        # one-launch layer's three rounds of resident workgroups 42.4 against
+        # 41.3 us
+        self.one_launch = self.layer_persistent and 2 <= T <= 4
         if not self.fp8 and R <= GEMV_MAX_ROWS:  # route_fc1() is callable
             need = max(need, fc_workspace_bytes(4, T, k, w1, path, act))
         if fits:  # decode_layer() is callable
