@@ -7,6 +7,8 @@
 #include "qmoe.h"
 #include "qmoe_internal.h"
 
+#include <cstdlib>
+
 using namespace qmoe;
 
 namespace {
@@ -378,6 +380,11 @@ qmoe_status qmoe_fp4_moe_layer_persistent(const float *logits, const float *rout
   a.ntiles1 = (2 * I + 255) / 256;
   a.ntiles2 = (H + 255) / 256;
   a.max_polls = 1 << 18;
+  // a smaller bound from the environment exercises the error path (tests)
+  if (const char *env = getenv("QMOE_LAYER_MAX_POLLS")) {
+    const long v = strtol(env, nullptr, 10);
+    if (v >= 0 && v < a.max_polls) a.max_polls = (int32_t)v;
+  }
   // workspace: counters, FC1 partial sums, FC2 partial sums (256-byte aligned parts)
   auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
   static_assert(((kLayerSyncBytes + 255) & ~(size_t)255) == QMOE_LAYER_SYNC_BYTES, "counter region");

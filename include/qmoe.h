@@ -312,7 +312,9 @@ qmoe_status qmoe_fp4_moe_layer_decode(const float *logits, const float *router_w
  * only if other work keeps some of its workgroups off the GPU) ORs 1 into it,
  * its outputs are then invalid and the counters must be zeroed again; the
  * call never clears the word.  Calls that share a workspace must be ordered
- * (same stream).
+ * (same stream).  Every wait polls at most 2^18 times; the environment
+ * variable QMOE_LAYER_MAX_POLLS, read at each call, may lower that bound
+ * (tests use a bound of 0 to take the error path on purpose).
  * Limits: T*k <= 64, H % 32 == 0, H <= 16384, I <= 4096, concatenated SwiGLU
  * only with I % 256 == 0 (QMOE_EUNSUPPORTED); w1 / w2 shapes or formats that
  * do not match: QMOE_EINVAL; and the limits of the separate calls.

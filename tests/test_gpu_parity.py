@@ -679,6 +679,88 @@ def test_layer_persistent(cfg, mode):
     assert_close("persistent out vs oracle", codecs.bf16_to_f64(bf16_host(layer.out)), out_ref)
 
 
+def test_layer_persistent_graph_replay():
+    """The one-launch layer captured in a HIP graph over two weight copies
+    (the bench's launch path) and replayed three times, with eager calls and
+    synchronisations in between: every replay's outputs equal the eager calls'
+    bit for bit, and the counters stay at zero."""
+    import fp4_weight_only_amd as q
+    cfg = synth.shrink(synth.MTP4, E=64, T=4, k=8, H=512, I=256, seed=41)
+    L = synth.layer_inputs(cfg)
+    layer, logits, x = layer_dev(L, path=q.QMOE_PATH_GEMV)
+    print_case("layer persistent graph", cfg.name)
+    assert layer.layer_persistent
+    wa = (layer.w1, layer.w2)
+    wb = tuple(q.FP4Weights(w.w.clone(), w.scales.clone(), None if w.gscale is None else w.gscale * 0.5, w.fmt)
+               for w in wa)
+    refs = []
+    for w in (wa, wb):
+        layer.set_weights(*w)
+        layer.persistent_layer(logits, x)
+        torch.cuda.synchronize()
+        refs.append(bf16_host(layer.out).copy())
+    assert not np.array_equal(refs[0], refs[1])
+    outs = [torch.empty_like(layer.out) for _ in range(2)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+
+    def body():
+        for i, w in enumerate((wa, wb)):
+            layer.set_weights(*w)
+            layer.persistent_layer(logits, x)
+            outs[i].copy_(layer.out)
+
+    with torch.cuda.stream(s):
+        body()   # warm-up outside the capture
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        body()
+    for rep in range(3):
+        for o in outs:
+            o.view(torch.int16).fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert np.array_equal(bf16_host(outs[i]), refs[i]), (rep, i)
+        assert layer_sync_clean(layer.ws_layer), rep
+        layer.set_weights(*wa)      # eager work between replays
+        layer.route(logits)
+        layer.fc1(x)
+        layer.fc2_finalize()
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_host(layer.out), refs[0]), rep
+
+
+def test_layer_persistent_wait_bound(monkeypatch):
+    """A wait that runs out sets the error word and the call still completes:
+    with the bound lowered to 0 (QMOE_LAYER_MAX_POLLS), the FC2 items of a
+    one-round layer poll before FC1 has finished and give up at once.  After
+    the workspace is zeroed again the next call is exact."""
+    import fp4_weight_only_amd as q
+    L = synth.layer_inputs(synth.TINY)
+    layer, logits, x = layer_dev(L, path=q.QMOE_PATH_GEMV)
+    print_case("layer persistent wait bound", L.cfg.name)
+    layer.route(logits)
+    layer.fc1(x)
+    layer.fc2_finalize()
+    torch.cuda.synchronize()
+    ref = bf16_host(layer.out).copy()
+    monkeypatch.setenv("QMOE_LAYER_MAX_POLLS", "0")
+    layer.persistent_layer(logits, x)
+    torch.cuda.synchronize()
+    assert q.layer_error_word(layer.ws_layer) & 1
+    monkeypatch.delenv("QMOE_LAYER_MAX_POLLS")
+    layer.ws_layer.zero_()
+    layer.out.view(torch.int16).fill_(-7)
+    layer.persistent_layer(logits, x)
+    torch.cuda.synchronize()
+    assert q.layer_error_word(layer.ws_layer) == 0
+    assert np.array_equal(bf16_host(layer.out), ref)
+    assert layer_sync_clean(layer.ws_layer)
+
+
 def test_layer_persistent_mxfp4_decode_full():
     """The 8-token MXFP4 layer (E=256, hidden 4096, intermediate 2048) in one
     launch: bit for bit the separate GEMV calls; FC2 + finalize against the
