@@ -48,10 +48,12 @@ class MoELayer:
         # (FC1's SwiGLU folded into FC2's staging, h not written)
         fits = (not self.fp8 and R <= GEMV_MAX_ROWS and w2.w.shape[0] == w1.w.shape[0]
                 and w2.w.shape[1] == w1.w.shape[2] and 2 * w2.w.shape[2] == w1.w.shape[1])
-        # used where measured to pay: T <= 4 and FC1 in at most eight k chunks
+        # used where measured to pay: T <= 2 and FC1 in at most eight k chunks
         # (H <= 2048), so FC2's staging reads every plane ahead of its weights
-        # (MXFP4 T=8, H=4096 on the GEMV path: 169 us separate, 193 us fused)
-        self.layer_decode = (fits and path != QMOE_PATH_GROUPED and T <= 4 and H <= 2048
+        # (NVFP4 E=256, H=2048, I=768, one box, against the separate calls:
+        # T=1 17.3 vs 18.8 us, T=2 23.8 vs 24.4, T=4 29.8 vs 29.2, T=8 43.2
+        # vs 40.8; MXFP4 T=8, H=4096: 193 vs 169 us)
+        self.layer_decode = (fits and path != QMOE_PATH_GROUPED and T <= 2 and H <= 2048
                              and qmoe_fp4_resolve_path(T, k, w1, path) == QMOE_PATH_GEMV
                              and qmoe_fp4_resolve_path(T, k, w2, path) == QMOE_PATH_GEMV)
         # the whole layer in one kernel launch (qmoe_fp4_moe_layer_persistent)
@@ -71,6 +73,7 @@ class MoELayer:
         self.one_launch = self.layer_persistent and 2 <= T <= 4
         if not self.fp8 and R <= GEMV_MAX_ROWS:  # route_fc1() is callable
             need = max(need, fc_workspace_bytes(4, T, k, w1, path, act))
+        self.decode_layer_callable = fits
         if fits:  # decode_layer() is callable
             need = max(need, layer_decode_workspace_bytes(T, k, w1, w2, act))
         self.ws = alloc_workspace(need, dev)

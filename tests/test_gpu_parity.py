@@ -959,7 +959,7 @@ def test_determinism_and_poisoned_buffers(cfg):
         layer.fc2_finalize()
 
     variants = [("separate", lambda: layer.run(logits, x)), ("fc2+finalize", fc2_finalize)]
-    if layer.layer_decode:
+    if layer.decode_layer_callable:
         variants.append(("layer decode", lambda: layer.decode_layer(logits, x)))
     if layer.layer_persistent:
         variants.append(("persistent", lambda: layer.persistent_layer(logits, x)))
