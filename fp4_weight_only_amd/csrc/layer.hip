@@ -27,9 +27,10 @@
 //   relaxed device-scope atomic counters, one per 64-byte segment; a wave
 //   waits for its own stores (s_waitcnt vmcnt(0)) before its workgroup
 //   counts.  No release/acquire fences: measured on MI355X, an agent-scope
-//   release costs 6-30 ns of serialised L2 write-back per workgroup, this
-//   scheme about nothing; counters are spread so that no address takes many
-//   increments (same-address atomics serialise at about 10 ns each).
+//   release fence costs about 100 ns of serialised L2 write-back per
+//   workgroup (a release atomic 19-30 ns), this scheme about nothing;
+//   counters are spread so that no address takes many increments
+//   (same-address atomics serialise at about 10 ns each).
 //   - FC1 item: writes its g * partial plane and counts on (slot, h chunk)
 //     without waiting for the counter's value.
 //   - FC2 item: issues its weight loads, waits until the 2 x nch1 FC1 items
