@@ -36,15 +36,22 @@
 //   workgroup per slice), LDS double buffered, one barrier per slice; one
 //   workgroup (16 waves, at most 128 VGPRs each) per CU.  The 512-column
 //   tile halves the activation re-reads of the n tiles (measured against 256
-//   columns on 8 waves).  16-row sub-tiles with no routed rows
-//   are skipped.  No weight element is decoded or read from LDS by more
-//   than one wave.
-// * Work items: the (expert, m tile) list is found on the device from
-//   expert_offsets; the grid covers the worst case (rows/64 + experts tiles)
-//   and idle items exit.  The n tiles of one (expert, m tile) run back to
-//   back on one XCD: its activation rows stay in that L2 for all n tiles.
+//   columns on 8 waves).  16-row sub-tiles with no routed rows are skipped.
+//   No weight element is decoded or read from LDS by more than one wave.
+// * Persistent work items: one workgroup per CU takes a fixed list of
+//   (expert, 64-row m tile, n tile) items and streams their slices as one
+//   sequence, so the next item's first loads are in flight while the
+//   current one finishes and writes its tile (with one workgroup per item,
+//   a CU idled about 3 us between items and again while its first slices
+//   arrived).  The lists are built on the device from expert_offsets: m
+//   tiles ordered by class (live 16-row sub-tiles, heaviest first), dealt
+//   over the workgroups in a snake so the per-workgroup work evens out; the
+//   n tiles of one m tile land on one XCD (its activation rows stay in that
+//   L2).  Each slice's loads are branch-free (item-dependent offsets formed
+//   once per item) so the compiler waits for exactly the older register set.
 #include "device_common.h"
 #include "qmoe_internal.h"
+#include "qmoe.h"
 
 namespace qmoe {
 
@@ -64,11 +71,19 @@ constexpr int kAChunks = kBK / 8;    // 16-byte chunks per activation row of a s
 constexpr int kBRow = kBN / 2;       // packed bytes per weight row of a slice (two 128-byte lines)
 constexpr uint32_t kGOutOfRange = 0x80000000u;
 
+constexpr int kMaxItems = 32;        // work items per workgroup (LDS tables)
+constexpr int kClasses = 4;          // m-tile classes: 16-row sub-tiles holding routed rows
+constexpr int kPreE = QMOE_MAX_EXPERTS;
+
 struct GroupedSmem {
   u32x4_t a[2][kBM][kAChunks];      // activations, chunk c of row r at c ^ (r & 15)
   uint8_t b[2][kBK][kBRow];         // packed codes, 8-byte unit u of row r at u ^ (r & 31)
   uint8_t sc[2][kBK / 16][kBN + 16];  // block scales of the slice (B = 32 uses 4 rows); the pad
                                       // puts neighbouring block rows on other banks
+  int32_t pre[kClasses][kPreE + 1];   // per class (4, 3, 2, 1): its slots in the experts before e
+  int32_t item[kMaxItems][4];         // this workgroup's items in order: expert, first row, rows, first column
+  int32_t src[kMaxItems][kBM];        // activation row of each m-tile row, -1 past the expert's rows
+  float gsc[kMaxItems];               // the item's global scale (1 without one)
 };
 
 // One slice's global loads for one thread.
@@ -112,6 +127,73 @@ __device__ __forceinline__ bf16x8_t decode_operand(uint32_t d, uint32_t sbyte) {
   return __builtin_bit_cast(bf16x8_t, o);
 }
 
+// ---- work items --------------------------------------------------------------
+// A slot is one (expert, 64-row m tile); its class is the number of 16-row
+// sub-tiles holding routed rows (1..4), which sets its MFMA and LDS work.  An
+// expert with R rows has R / 64 full tiles (class 4) and, when R % 64 != 0, one
+// tile of class ceil((R % 64) / 16).  Slots are ordered by class, heaviest
+// first (experts ascending within a class); a work item is (slot, n tile).
+// pre[w][e] counts the class-(4 - w) slots of the experts before e.
+__device__ __forceinline__ void class_prefix(const int32_t *__restrict__ off, int E, GroupedSmem &sm, int wave,
+                                             int lane) {
+  if (wave >= kClasses) return;  // uniform
+  const int c = kClasses - wave;
+  int o[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int e = 4 * lane + i;
+    o[i] = (e <= E) ? off[e] : 0;
+  }
+  int cnt[4], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int R = (4 * lane + i < E) ? o[i + 1] - o[i] : 0;
+    cnt[i] = (((R & (kBM - 1)) + 15) >> 4) == c ? 1 : 0;
+    if (c == kClasses) cnt[i] += R / kBM;
+    sum += cnt[i];
+  }
+  int incl = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
+  }
+  int run = incl - sum;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sm.pre[wave][4 * lane + i] = run;
+    run += cnt[i];
+  }
+  if (lane == 63) sm.pre[wave][kPreE] = run;
+}
+
+// Slot q of the class order -> expert and m tile.
+__device__ __forceinline__ void slot_of(const int32_t *__restrict__ off, int E, const GroupedSmem &sm, int q, int &e,
+                                        int &mt) {
+  int w = 0, base = 0;
+  while (w < kClasses - 1 && q >= base + sm.pre[w][kPreE]) {
+    base += sm.pre[w][kPreE];
+    ++w;
+  }
+  const int u = q - base;
+  int lo = 0, hi = E;  // pre[w][lo] <= u < pre[w][hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (sm.pre[w][mid] <= u)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  e = lo;
+  mt = (w == 0) ? u - sm.pre[0][lo] : (off[lo + 1] - off[lo]) / kBM;
+}
+
+// Persistent grouped GEMM: G workgroups (one per CU or as many as the item
+// tables need), workgroup g takes the items at positions g, 2G - 1 - g,
+// 2G + g, ... of the class order (a snake over the rounds, so the heavy
+// items spread evenly), and streams them as one sequence of 128-k slices: the
+// loads for the next item's first slices are in flight while the current
+// item finishes and writes its tile.
 template <int FMT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4))) void grouped_gemm_kernel(GemvArgs a) {
   constexpr int B = (FMT == 0) ? 16 : 32;
@@ -119,98 +201,152 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = lane_id();
+  const int G = gridDim.x;
+  const int g = blockIdx.x;
+  const int NT = a.ntiles;
 
-  // XCD-aware decode: workgroups go to the 8 XCDs round-robin; slot
-  // 8 i + x runs on XCD x, its n tiles back to back (the activation rows stay
-  // in that XCD's L2).  Dealing slots round-robin keeps the idle slots past
-  // the batch's live (expert, m tile) count spread over all XCDs.
-  const int local = blockIdx.x >> 3;
-  const int sl = local / a.ntiles;
-  const int ntile = local - sl * a.ntiles;
-  const int slot = sl * 8 + (blockIdx.x & 7);
-  if (slot >= a.nslots) return;
-  int mt = 0;
-  const int ef = find_mtile<kBM>(a.offsets, a.E, slot, mt);
-  if (ef < 0) return;  // uniform over the workgroup
-  // the expert is wave-uniform; saying so keeps the buffer resources in
-  // scalar registers (no per-load waterfall loops)
-  const int e = __builtin_amdgcn_readfirstlane(ef);
-  mt = __builtin_amdgcn_readfirstlane(mt);
-  const int row0 = a.offsets[e] + mt * kBM;
-  const int mrows = min(kBM, a.offsets[e + 1] - row0);
-  const int n0 = ntile * kBN;
+  // ---- this workgroup's items -------------------------------------------------
+  class_prefix(a.offsets, a.E, sm, wave, lane);
+  __syncthreads();
+  int S = 0;
+#pragma unroll
+  for (int w = 0; w < kClasses; ++w) S += sm.pre[w][kPreE];
+  const int NI = S * NT;
+  int nt = 0;
+  while (nt < kMaxItems) {
+    const int j = nt * G + ((nt & 1) ? G - 1 - g : g);
+    if (j >= NI) break;
+    ++nt;
+  }
+  if (nt == 0) return;  // uniform
+  // The items of one slot sit 8 positions apart (blocks of 8 slots x NT
+  // tiles), so they run on one XCD and share its L2 copy of the activation
+  // rows.  Workgroups start their lists at an offset set by the XCD, so at
+  // any time each XCD works on a different mix of classes.
+  const int rot = ((g & 7) * nt) >> 3;
+  if (tid < nt) {
+    const int t = tid;
+    const int j = t * G + ((t & 1) ? G - 1 - g : g);
+    const int bsz = 8 * NT;
+    const int b = j / bsz;
+    const int p = j - b * bsz;
+    const int sb = min(8, S - 8 * b);
+    const int q = 8 * b + p % sb;
+    const int ntile = p / sb;
+    int e, mt;
+    slot_of(a.offsets, a.E, sm, q, e, mt);
+    const int row0 = a.offsets[e] + mt * kBM;
+    int tt = t - rot;
+    if (tt < 0) tt += nt;
+    sm.item[tt][0] = e;
+    sm.item[tt][1] = row0;
+    sm.item[tt][2] = min(kBM, a.offsets[e + 1] - row0);
+    sm.item[tt][3] = ntile * kBN;
+    sm.gsc[tt] = a.gscale ? a.gscale[e] : 1.0f;
+  }
+  __syncthreads();
+  for (int x = tid; x < nt * kBM; x += kThreads) {
+    const int t = x / kBM, r = x - (x / kBM) * kBM;
+    const int row0 = sm.item[t][1], mrows = sm.item[t][2];
+    int src = -1;
+    if (r < mrows) src = a.fc1 ? a.p2e[row0 + r] / a.topk : row0 + r;
+    sm.src[t][r] = src;
+  }
+  __syncthreads();
+
   const int steps = (a.K + kBK - 1) / kBK;
-  const bool ragged = (a.K % kBK) != 0;  // the last slice holds 64 valid k rows
+  const bool ragged = (a.K % kBK) != 0;  // the last slice of an item holds 64 valid k rows
+  const uint32_t rowbytes = (uint32_t)(a.N >> 1);
+  const int KB = a.K / B;
 
   // ---- loader roles ----------------------------------------------------------
-  // Every load is a buffer load whose vector offset is fixed per thread for
-  // the whole kernel; the slice position rides in the scalar offset.  Rows
-  // outside the data get an out-of-range vector offset (reads return 0).  A
-  // ragged last slice (K % 128 == 64) is only read for its first 64 k.
-  // activations: thread -> 16-byte chunk aq (8 k) of rows ra[i]
+  // Every load is a buffer load; rows and columns outside the data, and
+  // slices past the last item, get an out-of-range vector offset (reads
+  // return 0, no memory access).  A ragged last slice (K % 128 == 64) is only
+  // read for its first 64 k.
+  // activations: thread -> 16-byte chunk aq (8 k) of m-tile rows ra[i]
   const int aq = tid & 15;
+  int ra[kALoads];
+#pragma unroll
+  for (int i = 0; i < kALoads; ++i) ra[i] = (tid >> 4) + i * (kThreads / 16);
   const int act_rows = a.fc1 ? a.rows / a.topk : a.rows;
   const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
       uniform_ptr(a.act), (short)0, (int)((uint32_t)act_rows * (uint32_t)a.K * 2u), 0x00020000);
-  int ra[kALoads];
-  uint32_t avoff[kALoads];
-#pragma unroll
-  for (int i = 0; i < kALoads; ++i) {
-    ra[i] = (tid >> 4) + i * (kThreads / 16);
-    avoff[i] = kGOutOfRange;
-    if (ra[i] < mrows) {
-      const int p = row0 + ra[i];
-      const int src = a.fc1 ? (a.p2e[p] / a.topk) : p;
-      avoff[i] = (uint32_t)src * (uint32_t)a.K * 2u + (uint32_t)(aq * 16);
-    }
-  }
   // weights: thread -> 16 bytes bq of k rows rb + j * kBRowStep; sixteen
   // lanes read a row's 256 bytes (two 128-byte lines)
   const int rb = tid >> 4;
   const int bq = tid & 15;
-  const uint32_t rowbytes = (uint32_t)(a.N >> 1);
-  const int KB = a.K / B;
-  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      uniform_ptr(a.w + (size_t)e * a.K * rowbytes), (short)0, (int)((uint32_t)a.K * rowbytes), 0x00020000);
-  const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
-      uniform_ptr(a.scales + (size_t)e * KB * a.N), (short)0, (int)((uint32_t)KB * a.N), 0x00020000);
-  // a partial last tile (N % 512 != 0) reads nothing past N
-  const bool bcols = n0 + 32 * bq + 32 <= a.N;
-  const uint32_t bvoff0 = (uint32_t)rb * rowbytes + (uint32_t)(n0 >> 1) + (uint32_t)(bq * 16);
-  // scales: thread -> 4 columns sq of block rows sb[i]
+
+  // Loads are issued for the slice sequence of all items in order; (lt, lks)
+  // is the next slice to load.  Every thread issues the same loads for every
+  // slice, also past the last one, so the compiler's wait counts at the
+  // pipeline's join points stay exact.  Offsets that are uniform go through
+  // readfirstlane: in a vector register they would force a readfirstlane
+  // loop around each load.
+  // The item-dependent part of the offsets is formed once per item, when
+  // the loader reaches the item's first slice; a slice's loads then differ
+  // only by uniform masks, so the load sequence has no branches (a branch
+  // around a load leaves the compiler's wait counts conservative, and the
+  // pipeline's waits would then include the next slice's first loads).
+  // Out-of-range offsets stay out of range when a row step is added.
   constexpr int kSBlocks = kBK / B;
   constexpr int kSLoads = (kSBlocks * (kBN / 4) + kThreads - 1) / kThreads;
-  const int sq = tid & 127;
-  const bool scols = n0 + sq * 4 + 4 <= a.N;
-
-  // Every thread issues the same loads for every slice, also past the last
-  // one (out-of-range offsets: no memory access, zeros), so the compiler's
-  // wait counts at the pipeline's join points stay exact.  The slice offsets
-  // go through readfirstlane: in a vector register they would force a
-  // readfirstlane loop around each load.
+  const int sq = tid & 127;  // scales: thread -> 4 columns sq of block rows sb[i]
+  uint32_t btail[kBLoads], stail[kSLoads];  // rows past the first 64 k of a ragged slice
+#pragma unroll
+  for (int j = 0; j < kBLoads; ++j) btail[j] = (rb + j * kBRowStep >= kBK / 2) ? kGOutOfRange : 0u;
+#pragma unroll
+  for (int i = 0; i < kSLoads; ++i) stail[i] = ((tid >> 7) + i * (kThreads / 128) >= kSBlocks / 2) ? kGOutOfRange : 0u;
+  int lt = 0, lks = 0;
+  int e = 0;
+  uint32_t avoff[kALoads], boff = kGOutOfRange, soff[kSLoads];
+#pragma unroll
+  for (int i = 0; i < kALoads; ++i) avoff[i] = kGOutOfRange;
+#pragma unroll
+  for (int i = 0; i < kSLoads; ++i) soff[i] = kGOutOfRange;
   using Regs = SliceRegs<kSLoads>;
-  auto load_slice = [&](int s, Regs &r) {
-    const int k0 = s * kBK;
-    const bool dead = s >= steps;                           // uniform
-    const bool tail = ragged && s + 1 == steps;             // uniform
-    const uint32_t kill = dead ? kGOutOfRange : 0u;
+  auto load_slice = [&](Regs &r) {
+    const bool dead = lt >= nt;  // uniform
+    if (lks == 0 && !dead) {     // uniform
+      e = __builtin_amdgcn_readfirstlane(sm.item[lt][0]);
+      const int n0 = __builtin_amdgcn_readfirstlane(sm.item[lt][3]);
+#pragma unroll
+      for (int i = 0; i < kALoads; ++i) {
+        const int srow = sm.src[lt][ra[i]];
+        avoff[i] = srow >= 0 ? (uint32_t)srow * (uint32_t)a.K * 2u + (uint32_t)(aq * 16) : kGOutOfRange;
+      }
+      // a partial last tile (N % 512 != 0) reads nothing past N
+      boff = n0 + 32 * bq + 32 <= a.N ? (uint32_t)rb * rowbytes + (uint32_t)(n0 >> 1) + (uint32_t)(bq * 16)
+                                      : kGOutOfRange;
+#pragma unroll
+      for (int i = 0; i < kSLoads; ++i) {
+        const int sb = (tid >> 7) + i * (kThreads / 128);
+        soff[i] = (n0 + sq * 4 + 4 <= a.N && sb < kSBlocks) ? (uint32_t)sb * (uint32_t)a.N + (uint32_t)(n0 + sq * 4)
+                                                           : kGOutOfRange;
+      }
+    }
+    const int k0 = lks * kBK;
+    const uint32_t tailm = (ragged && lks + 1 == steps) ? ~0u : 0u;  // uniform
+    const uint32_t kill = dead ? kGOutOfRange : 0u;                  // uniform
     const int ao = __builtin_amdgcn_readfirstlane(k0 * 2);
 #pragma unroll
     for (int i = 0; i < kALoads; ++i) r.A[i] = __builtin_amdgcn_raw_buffer_load_b128(arsrc, avoff[i] | kill, ao, 0);
+    const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(a.w + (size_t)e * a.K * rowbytes), (short)0, (int)((uint32_t)a.K * rowbytes), 0x00020000);
     const int so = __builtin_amdgcn_readfirstlane((int)((uint32_t)k0 * rowbytes));
 #pragma unroll
-    for (int j = 0; j < kBLoads; ++j) {
-      const bool on = bcols && !(tail && rb + j * kBRowStep >= kBK / 2);
+    for (int j = 0; j < kBLoads; ++j)
       r.B[j] = __builtin_amdgcn_raw_buffer_load_b128(
-          wrsrc, (on ? bvoff0 + (uint32_t)(j * kBRowStep) * rowbytes : kGOutOfRange) | kill, so, 2);
-    }
+          wrsrc, (boff + (uint32_t)(j * kBRowStep) * rowbytes) | kill | (btail[j] & tailm), so, 2);
+    const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(a.scales + (size_t)e * KB * a.N), (short)0, (int)((uint32_t)KB * a.N), 0x00020000);
     const int sso = __builtin_amdgcn_readfirstlane((int)((uint32_t)(k0 / B) * (uint32_t)a.N));
 #pragma unroll
-    for (int i = 0; i < kSLoads; ++i) {
-      const int sb = (tid >> 7) + i * (kThreads / 128);
-      const bool on = scols && sb < kSBlocks && !(tail && sb >= kSBlocks / 2);
-      r.S[i] = __builtin_amdgcn_raw_buffer_load_b32(
-          srsrc, (on ? (uint32_t)sb * (uint32_t)a.N + (uint32_t)(n0 + sq * 4) : kGOutOfRange) | kill, sso, 0);
+    for (int i = 0; i < kSLoads; ++i)
+      r.S[i] = __builtin_amdgcn_raw_buffer_load_b32(srsrc, soff[i] | kill | (stail[i] & tailm), sso, 0);
+    if (++lks == steps) {
+      lks = 0;
+      ++lt;
     }
   };
 
@@ -244,17 +380,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   // columns each; the row swizzle permutes the row's 32 units) ---------------
   const int li = lane & 15;
   const int lk = lane >> 4;
-  const int live = (mrows + 15) >> 4;  // 16-row sub-tiles holding routed rows
-  const bool wave_cols = n0 + wave * 16 * kCT < a.N;  // uniform: this wave's columns exist
+  // the item being computed: (ct, cks) is its next slice
+  int ct = 0, cks = 0;
+  int c_live = 0, c_row0 = 0, c_mrows = 0, c_n0 = 0;
+  // the epilogue makes no global load: one issued behind the next item's
+  // slice loads would wait for all of them
+  auto load_citem = [&]() {
+    c_row0 = __builtin_amdgcn_readfirstlane(sm.item[ct][1]);
+    c_mrows = __builtin_amdgcn_readfirstlane(sm.item[ct][2]);
+    c_n0 = __builtin_amdgcn_readfirstlane(sm.item[ct][3]);
+    c_live = (c_mrows + 15) >> 4;  // 16-row sub-tiles holding routed rows
+  };
+  load_citem();
   f32x4_t acc[4][kCT];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < kCT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute_slice = [&](int buf, int s) {
-    if (!wave_cols) return;
-    const int nkg = (ragged && s + 1 == steps) ? 1 : 2;  // 64-k groups below K
+  auto compute_slice = [&](int buf) {
+    if (c_n0 + wave * 16 * kCT >= a.N) return;  // uniform: this wave's columns do not exist
+    const int nkg = (ragged && cks + 1 == steps) ? 1 : 2;  // 64-k groups below K
 #pragma unroll
     for (int kg = 0; kg < 2; ++kg) {
       if (kg >= nkg) break;
@@ -283,7 +429,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         const int chunk = kg * 8 + lk * 2 + h;  // k = kg*64 + 16*lk + 8*h .. +7
 #pragma unroll
         for (int ms = 0; ms < 4; ++ms) {
-          if (ms >= live) break;  // uniform
+          if (ms >= c_live) break;  // uniform
           const int r = ms * 16 + li;
           const bf16x8_t av = __builtin_bit_cast(bf16x8_t, sm.a[buf][r][chunk ^ (r & 15)]);
 #pragma unroll
@@ -294,48 +440,68 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     }
   };
 
+  // ---- epilogue of the item being computed: lane holds rows 4*(lane/16)+i,
+  // column lane%16 of each tile; then the accumulators restart for the next
+  auto finish_item = [&]() {
+    if (c_n0 + wave * 16 * kCT < a.N) {  // uniform
+      const float gs = sm.gsc[ct];
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms) {
+        if (ms >= c_live) break;
+#pragma unroll
+        for (int t = 0; t < kCT; ++t) {
+          const int col = c_n0 + wave * 16 * kCT + t * 16 + li;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = ms * 16 + lk * 4 + i;
+            const float u = gs * acc[ms][t][i];
+            if (a.fc1 && !a.concat) {
+              const float partner = __uint_as_float(dpp_u32<kDppXor1>(__float_as_uint(u)));
+              if (r < c_mrows && (lane & 1) == 0)
+                a.out_bf16[(size_t)(c_row0 + r) * (a.N >> 1) + (col >> 1)] =
+                    (uint16_t)bf16_rne(swiglu(u, partner, a.alpha, a.beta, a.limit));
+            } else if (r < c_mrows) {
+              a.out_f32[(size_t)(c_row0 + r) * a.N + col] = u;
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < kCT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (++ct < nt) load_citem();
+  };
+  auto advance_compute = [&]() {
+    if (++cks == steps) {  // uniform: the item's last slice is done
+      cks = 0;
+      finish_item();
+    }
+  };
+
   // ---- pipeline: loads two slices ahead in registers, LDS double buffered ----
   Regs r0, r1;
-  load_slice(0, r0);
+  load_slice(r0);
   // slice 0's loads stay ahead of slice 1's: the loop waits for the older
   // register set only (memory returns in issue order)
   __builtin_amdgcn_sched_barrier(0);
-  load_slice(1, r1);
+  load_slice(r1);
+  const int total = nt * steps;
   // One exit, at the bottom: a break between the halves makes the compiler
   // wait for both register sets at the top of the loop.
-  for (int s = 0; s < steps; s += 2) {
+  for (int s = 0; s < total; s += 2) {
     store_slice(0, r0);
-    load_slice(s + 2, r0);
+    load_slice(r0);
     __syncthreads();
-    compute_slice(0, s);
+    compute_slice(0);
+    advance_compute();
     store_slice(1, r1);
-    load_slice(s + 3, r1);
+    load_slice(r1);
     __syncthreads();
-    if (s + 1 < steps) compute_slice(1, s + 1);
-  }
-
-  // ---- epilogue: lane holds rows 4*(lane/16)+i, column lane%16 of each tile --
-  if (!wave_cols) return;
-  const float gs = a.gscale ? a.gscale[e] : 1.0f;
-#pragma unroll
-  for (int ms = 0; ms < 4; ++ms) {
-    if (ms >= live) break;
-#pragma unroll
-    for (int t = 0; t < kCT; ++t) {
-      const int col = n0 + wave * 16 * kCT + t * 16 + li;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = ms * 16 + lk * 4 + i;
-        const float u = gs * acc[ms][t][i];
-        if (a.fc1 && !a.concat) {
-          const float partner = __uint_as_float(dpp_u32<kDppXor1>(__float_as_uint(u)));
-          if (r < mrows && (lane & 1) == 0)
-            a.out_bf16[(size_t)(row0 + r) * (a.N >> 1) + (col >> 1)] =
-                (uint16_t)bf16_rne(swiglu(u, partner, a.alpha, a.beta, a.limit));
-        } else if (r < mrows) {
-          a.out_f32[(size_t)(row0 + r) * a.N + col] = u;
-        }
-      }
+    if (s + 1 < total) {
+      compute_slice(1);
+      advance_compute();
     }
   }
 }
@@ -352,11 +518,20 @@ hipError_t launch_grouped(GemvArgs &a, int fmt, hipStream_t s) {
   const int erows = a.rows < a.E ? a.rows : a.E;
   a.nslots = (a.rows + kBM - 1) / kBM + erows;  // worst-case (expert, m tile) count
   a.ntiles = (a.N + kBN - 1) / kBN;  // N % 128 == 0: a partial last tile (whole 16 kCT-column waves)
-  const dim3 grid((unsigned)((a.nslots + 7) / 8 * 8 * a.ntiles));
+  // one workgroup per CU, more when a workgroup's item table would overflow
+  int dev = 0, cus = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return err;
+  if (cus < 1) return hipErrorInvalidConfiguration;
+  const long items = (long)a.nslots * a.ntiles;
+  long grid = (cus + 7) / 8 * 8;
+  const long need = (items + kMaxItems - 1) / kMaxItems;
+  if (grid < need) grid = (need + 7) / 8 * 8;
   if (fmt == 0)
-    grouped_gemm_kernel<0><<<grid, kThreads, 0, s>>>(a);
+    grouped_gemm_kernel<0><<<dim3((unsigned)grid), kThreads, 0, s>>>(a);
   else
-    grouped_gemm_kernel<1><<<grid, kThreads, 0, s>>>(a);
+    grouped_gemm_kernel<1><<<dim3((unsigned)grid), kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
