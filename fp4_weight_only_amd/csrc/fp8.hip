@@ -19,6 +19,7 @@
 // leaves the same value in all 16 lanes.
 #include "device_common.h"
 #include "qmoe_internal.h"
+#include "grouped_sched.h"
 
 namespace qmoe {
 
@@ -188,12 +189,14 @@ __global__ __launch_bounds__(kF8Waves * 64) void fp8_gemv_kernel(GemvArgs a) {
 // Work item = (expert, 64-row m tile, 256-column n tile) as on the FP4
 // grouped path; 8 waves, wave w owns columns 32w..32w+31 (two 16-column MFMA
 // tiles) for every live 16-row sub-tile, v_mfma_f32_16x16x32_bf16, K in
-// 64-k slices.  The [N][K] layout gives each MFMA B operand (8 consecutive k
-// of one column) as 8 contiguous bytes: a column's 64 bytes of a slice are
-// copied into LDS (8-byte units XOR-swizzled by column), read back with one
-// ds_read_b64 per operand and converted with four exact FP8 -> bf16
+// 128-k slices.  The [N][K] layout gives each MFMA B operand (8 consecutive
+// k of one column) as 8 contiguous bytes: a column's 128 bytes of a slice
+// are copied into LDS (8-byte units XOR-swizzled by column), read back with
+// one ds_read_b64 per operand and converted with four exact FP8 -> bf16
 // conversions.  Global loads run two slices ahead in registers, LDS is
-// double buffered; the global scale multiplies the accumulator.
+// double buffered; the global scale multiplies the accumulator.  Persistent
+// workgroups (one per CU) stream fixed item lists as on the FP4 path
+// (grouped_sched.h): the next item's loads overlap the current item's tail.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -209,10 +212,13 @@ constexpr int kF8LPC = kF8BK / 16;                  // lanes per column (16 byte
 constexpr int kF8CPP = kF8GThreads / kF8LPC;        // columns per load pass
 constexpr int kF8BLoads = kF8BN / kF8CPP;           // 16-byte B loads per thread
 static_assert(kF8AThreads % 64 == 0 && kF8BN % kF8CPP == 0 && (kF8Units & (kF8Units - 1)) == 0, "tile shape");
+static_assert(kF8BM == kGBM, "m tile of the item lists");
 
 struct F8GroupedSmem {
   u32x4_t a[2][kF8BM][kF8Units];    // activations, 16-byte chunk c of row r at c ^ (r % units)
   uint8_t b[2][kF8BN][kF8BK];       // weight bytes, 8-byte unit u of column n at u ^ (n % units)
+  GroupedPre pre;                   // set-up only
+  GroupedItems it;                  // this workgroup's items
 };
 
 struct F8SliceRegs {
@@ -236,72 +242,72 @@ __global__ __launch_bounds__(kF8GThreads) __attribute__((amdgpu_waves_per_eu(kF8
   const int wave = tid >> 6;
   const int lane = lane_id();
 
-  // XCD-aware decode: slot 8 i + x runs on XCD x (workgroups go to the XCDs
-  // round-robin), its n tiles back to back; idle slots past the live count
-  // are spread over all XCDs
-  const int local = blockIdx.x >> 3;
-  const int sl = local / a.ntiles;
-  const int ntile = local - sl * a.ntiles;
-  const int slot = sl * 8 + (blockIdx.x & 7);
-  if (slot >= a.nslots) return;
-  int mt = 0;
-  const int ef = find_mtile<kF8BM>(a.offsets, a.E, slot, mt);
-  if (ef < 0) return;  // uniform over the workgroup
-  const int e = __builtin_amdgcn_readfirstlane(ef);
-  mt = __builtin_amdgcn_readfirstlane(mt);
-  const int row0 = a.offsets[e] + mt * kF8BM;
-  const int mrows = min(kF8BM, a.offsets[e + 1] - row0);
-  const int n0 = ntile * kF8BN;
-  const int steps = (a.K + kF8BK - 1) / kF8BK;  // K % 64 == 0: the last slice may be half
+  const int nt = build_items(a, sm.pre, sm.it, kF8BN, kF8GThreads, tid, wave, lane);
+  if (nt == 0) return;  // uniform
+  const int steps = (a.K + kF8BK - 1) / kF8BK;  // K % 64 == 0: the last slice of an item may be half
   const int ktail = a.K - (steps - 1) * kF8BK;  // k in the last slice
 
-  // loaders (buffer loads; fixed vector offsets, the slice in the scalar
-  // offset; chunks past K in a half last slice load as zero)
+  // loaders (buffer loads; the item-dependent vector offsets formed once per
+  // item, the slice in the scalar offset; chunks past K in a half last slice
+  // load as zero; slices past the last item load nothing)
   const bool aload = kF8AThreads == kF8GThreads || tid < kF8AThreads;  // uniform per wave
   const int act_rows = a.fc1 ? a.rows / a.topk : a.rows;
   const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
       uniform_ptr(a.act), (short)0, (int)((uint32_t)act_rows * (uint32_t)a.K * 2u), 0x00020000);
   int ar[kF8ALoads], aq[kF8ALoads];
-  uint32_t avoff[kF8ALoads];
+  uint32_t atail[kF8ALoads];
 #pragma unroll
   for (int i = 0; i < kF8ALoads; ++i) {
     const int c = tid + i * kF8AThreads;
     ar[i] = c / kF8Units;
     aq[i] = c % kF8Units;
-    avoff[i] = kF8OutOfRange;
-    if (aload && ar[i] < mrows) {
-      const int p = row0 + ar[i];
-      const int src = a.fc1 ? (a.p2e[p] / a.topk) : p;
-      avoff[i] = (uint32_t)src * (uint32_t)a.K * 2u + (uint32_t)(aq[i] * 16);
-    }
+    atail[i] = aq[i] * 8 >= ktail ? kF8OutOfRange : 0u;
   }
   const int cb = tid / kF8LPC, bq = tid % kF8LPC;  // columns cb + j * kF8CPP; 16 bytes bq of the slice
-  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      uniform_ptr(a.w + (size_t)e * a.N * a.K), (short)0, (int)((uint32_t)a.N * (uint32_t)a.K), 0x00020000);
-  uint32_t bvoff[kF8BLoads];
+  const uint32_t btail = bq * 16 >= ktail ? kF8OutOfRange : 0u;
+  int lt = 0, lks = 0, e = 0;
+  uint32_t avoff[kF8ALoads], bvoff[kF8BLoads];
 #pragma unroll
-  for (int j = 0; j < kF8BLoads; ++j) {
-    const int col = n0 + cb + kF8CPP * j;
-    bvoff[j] = col < a.N ? (uint32_t)col * (uint32_t)a.K + (uint32_t)(bq * 16) : kF8OutOfRange;
-  }
+  for (int i = 0; i < kF8ALoads; ++i) avoff[i] = kF8OutOfRange;
+#pragma unroll
+  for (int j = 0; j < kF8BLoads; ++j) bvoff[j] = kF8OutOfRange;
   // Every thread issues the same loads for every slice, also past the last
-  // one (out-of-range offsets: no memory access, zeros), so the compiler's
-  // wait counts at the pipeline's join points stay exact.
-  auto load_slice = [&](int s, F8SliceRegs &r) {
-    const int k0 = s * kF8BK;
-    const bool dead = s >= steps;                         // uniform
-    const bool half = s == steps - 1 && ktail < kF8BK;    // uniform
-    const uint32_t kill = dead ? kF8OutOfRange : 0u;
+  // one, with no branch around a load, so the compiler's wait counts at the
+  // pipeline's join points stay exact.
+  auto load_slice = [&](F8SliceRegs &r) {
+    const bool dead = lt >= nt;  // uniform
+    if (lks == 0 && !dead) {     // uniform
+      e = __builtin_amdgcn_readfirstlane(sm.it.item[lt][0]);
+      const int n0 = __builtin_amdgcn_readfirstlane(sm.it.item[lt][3]);
+#pragma unroll
+      for (int i = 0; i < kF8ALoads; ++i) {
+        const int srow = aload ? sm.it.src[lt][ar[i]] : -1;
+        avoff[i] = srow >= 0 ? (uint32_t)srow * (uint32_t)a.K * 2u + (uint32_t)(aq[i] * 16) : kF8OutOfRange;
+      }
+#pragma unroll
+      for (int j = 0; j < kF8BLoads; ++j) {
+        const int col = n0 + cb + kF8CPP * j;
+        bvoff[j] = col < a.N ? (uint32_t)col * (uint32_t)a.K + (uint32_t)(bq * 16) : kF8OutOfRange;
+      }
+    }
+    const int k0 = lks * kF8BK;
+    const uint32_t kill = dead ? kF8OutOfRange : 0u;                      // uniform
+    const uint32_t halfm = (lks == steps - 1 && ktail < kF8BK) ? ~0u : 0u;  // uniform
     const int ao = __builtin_amdgcn_readfirstlane(k0 * 2), bo = __builtin_amdgcn_readfirstlane(k0);
 #pragma unroll
-    for (int i = 0; i < kF8ALoads; ++i) {
-      const uint32_t off = (half && aq[i] * 8 >= ktail) ? kF8OutOfRange : avoff[i];
-      r.A[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(arsrc, off | kill, ao, 0));
-    }
-    const uint32_t bmask = ((half && bq * 16 >= ktail) ? kF8OutOfRange : 0u) | kill;
+    for (int i = 0; i < kF8ALoads; ++i)
+      r.A[i] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(arsrc, avoff[i] | kill | (atail[i] & halfm), ao, 0));
+    const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(a.w + (size_t)e * a.N * a.K), (short)0, (int)((uint32_t)a.N * (uint32_t)a.K), 0x00020000);
 #pragma unroll
     for (int j = 0; j < kF8BLoads; ++j)
-      r.B[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, bvoff[j] | bmask, bo, 2));
+      r.B[j] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, bvoff[j] | kill | (btail & halfm), bo, 2));
+    if (++lks == steps) {
+      lks = 0;
+      ++lt;
+    }
   };
   auto store_slice = [&](int buf, const F8SliceRegs &r) {
     if (aload) {
@@ -318,8 +324,16 @@ __global__ __launch_bounds__(kF8GThreads) __attribute__((amdgpu_waves_per_eu(kF8
 
   // MFMA roles: lane (lk, li) -> column li of a 16-column tile, k 8 lk .. +7 of a 32-k group
   const int li = lane & 15, lk = lane >> 4;
-  const int live = (mrows + 15) >> 4;
-  const bool wave_cols = n0 + wave * 32 < a.N;  // uniform (N % 32 == 0)
+  // the item being computed: (ct, cks) is its next slice
+  int ct = 0, cks = 0;
+  int c_live = 0, c_row0 = 0, c_mrows = 0, c_n0 = 0;
+  auto load_citem = [&]() {
+    c_row0 = __builtin_amdgcn_readfirstlane(sm.it.item[ct][1]);
+    c_mrows = __builtin_amdgcn_readfirstlane(sm.it.item[ct][2]);
+    c_n0 = __builtin_amdgcn_readfirstlane(sm.it.item[ct][3]);
+    c_live = (c_mrows + 15) >> 4;  // 16-row sub-tiles holding routed rows
+  };
+  load_citem();
   f32x4_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -327,7 +341,7 @@ __global__ __launch_bounds__(kF8GThreads) __attribute__((amdgpu_waves_per_eu(kF8
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   auto compute_slice = [&](int buf) {
-    if (!wave_cols) return;
+    if (c_n0 + wave * 32 >= a.N) return;  // uniform (N % 32 == 0): this wave's columns do not exist
 #pragma unroll
     for (int kg = 0; kg < kF8BK / 32; ++kg) {
       const int unit = kg * 4 + lk;  // 8-k unit of the slice
@@ -340,7 +354,7 @@ __global__ __launch_bounds__(kF8GThreads) __attribute__((amdgpu_waves_per_eu(kF8
       }
 #pragma unroll
       for (int ms = 0; ms < 4; ++ms) {
-        if (ms >= live) break;  // uniform
+        if (ms >= c_live) break;  // uniform
         const int r = ms * 16 + li;
         const bf16x8_t av = __builtin_bit_cast(bf16x8_t, sm.a[buf][r][unit ^ (r & (kF8Units - 1))]);
         acc[ms][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[0], acc[ms][0], 0, 0, 0);
@@ -349,47 +363,69 @@ __global__ __launch_bounds__(kF8GThreads) __attribute__((amdgpu_waves_per_eu(kF8
     }
   };
 
+  // epilogue of the item being computed (lane holds rows 4 lk + i, column li
+  // of each 16-column tile; no global load: one issued behind the next
+  // item's slice loads would wait for all of them); then the accumulators
+  // restart for the next item
+  auto finish_item = [&]() {
+    if (c_n0 + wave * 32 < a.N) {  // uniform
+      const float gs = sm.it.gsc[ct];
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms) {
+        if (ms >= c_live) break;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int col = c_n0 + wave * 32 + t * 16 + li;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = ms * 16 + lk * 4 + i;
+            const float u = gs * acc[ms][t][i];
+            if (a.fc1 && !a.concat) {
+              const float partner = __uint_as_float(dpp_u32<kDppXor1>(__float_as_uint(u)));
+              if (r < c_mrows && (lane & 1) == 0)
+                a.out_bf16[(size_t)(c_row0 + r) * (a.N >> 1) + (col >> 1)] =
+                    (uint16_t)bf16_rne(swiglu(u, partner, a.alpha, a.beta, a.limit));
+            } else if (r < c_mrows) {
+              a.out_f32[(size_t)(c_row0 + r) * a.N + col] = u;  // FC2 y, or FC1 u for the concatenated layout
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (++ct < nt) load_citem();
+  };
+  auto advance_compute = [&]() {
+    if (++cks == steps) {  // uniform: the item's last slice is done
+      cks = 0;
+      finish_item();
+    }
+  };
+
   F8SliceRegs r0, r1;
-  load_slice(0, r0);
+  load_slice(r0);
   // slice 0's loads stay ahead of slice 1's: the loop waits for the older
   // register set only (memory returns in issue order)
   __builtin_amdgcn_sched_barrier(0);
-  load_slice(1, r1);
+  load_slice(r1);
+  const int total = nt * steps;
   // One exit, at the bottom: a break between the halves makes the compiler
   // wait for both register sets at the top of the loop.
-  for (int s = 0; s < steps; s += 2) {
+  for (int s = 0; s < total; s += 2) {
     store_slice(0, r0);
-    load_slice(s + 2, r0);
+    load_slice(r0);
     __syncthreads();
     compute_slice(0);
+    advance_compute();
     store_slice(1, r1);
-    load_slice(s + 3, r1);
+    load_slice(r1);
     __syncthreads();
-    if (s + 1 < steps) compute_slice(1);
-  }
-
-  // epilogue: lane holds rows 4 lk + i, column li of each 16-column tile
-  if (!wave_cols) return;
-  const float gs = a.gscale[e];
-#pragma unroll
-  for (int ms = 0; ms < 4; ++ms) {
-    if (ms >= live) break;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int col = n0 + wave * 32 + t * 16 + li;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = ms * 16 + lk * 4 + i;
-        const float u = gs * acc[ms][t][i];
-        if (a.fc1 && !a.concat) {
-          const float partner = __uint_as_float(dpp_u32<kDppXor1>(__float_as_uint(u)));
-          if (r < mrows && (lane & 1) == 0)
-            a.out_bf16[(size_t)(row0 + r) * (a.N >> 1) + (col >> 1)] =
-                (uint16_t)bf16_rne(swiglu(u, partner, a.alpha, a.beta, a.limit));
-        } else if (r < mrows) {
-          a.out_f32[(size_t)(row0 + r) * a.N + col] = u;
-        }
-      }
+    if (s + 1 < total) {
+      compute_slice(1);
+      advance_compute();
     }
   }
 }
@@ -398,9 +434,11 @@ hipError_t launch_fp8_grouped(GemvArgs &a, void *ws, hipStream_t s) {
   const int erows = a.rows < a.E ? a.rows : a.E;
   a.nslots = (a.rows + kF8BM - 1) / kF8BM + erows;  // worst-case (expert, m tile) count
   a.ntiles = (a.N + kF8BN - 1) / kF8BN;
-  const dim3 grid((unsigned)((a.nslots + 7) / 8 * 8 * a.ntiles));
+  unsigned grid = 0;
+  const hipError_t gerr = grouped_grid(a, &grid);
+  if (gerr != hipSuccess) return gerr;
   if (a.concat) a.out_f32 = (float *)ws;
-  fp8_grouped_kernel<<<grid, kF8GThreads, 0, s>>>(a);
+  fp8_grouped_kernel<<<dim3(grid), kF8GThreads, 0, s>>>(a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !a.concat) return err;
   a.partials = (float *)ws;

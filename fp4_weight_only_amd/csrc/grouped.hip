@@ -49,9 +49,7 @@
 //   n tiles of one m tile land on one XCD (its activation rows stay in that
 //   L2).  Each slice's loads are branch-free (item-dependent offsets formed
 //   once per item) so the compiler waits for exactly the older register set.
-#include "device_common.h"
-#include "qmoe_internal.h"
-#include "qmoe.h"
+#include "grouped_sched.h"
 
 namespace qmoe {
 
@@ -71,19 +69,15 @@ constexpr int kAChunks = kBK / 8;    // 16-byte chunks per activation row of a s
 constexpr int kBRow = kBN / 2;       // packed bytes per weight row of a slice (two 128-byte lines)
 constexpr uint32_t kGOutOfRange = 0x80000000u;
 
-constexpr int kMaxItems = 32;        // work items per workgroup (LDS tables)
-constexpr int kClasses = 4;          // m-tile classes: 16-row sub-tiles holding routed rows
-constexpr int kPreE = QMOE_MAX_EXPERTS;
+static_assert(kBM == kGBM, "m tile of the item lists");
 
 struct GroupedSmem {
   u32x4_t a[2][kBM][kAChunks];      // activations, chunk c of row r at c ^ (r & 15)
   uint8_t b[2][kBK][kBRow];         // packed codes, 8-byte unit u of row r at u ^ (r & 31)
   uint8_t sc[2][kBK / 16][kBN + 16];  // block scales of the slice (B = 32 uses 4 rows); the pad
                                       // puts neighbouring block rows on other banks
-  int32_t pre[kClasses][kPreE + 1];   // per class (4, 3, 2, 1): its slots in the experts before e
-  int32_t item[kMaxItems][4];         // this workgroup's items in order: expert, first row, rows, first column
-  int32_t src[kMaxItems][kBM];        // activation row of each m-tile row, -1 past the expert's rows
-  float gsc[kMaxItems];               // the item's global scale (1 without one)
+  GroupedPre pre;                     // set-up only
+  GroupedItems it;                    // this workgroup's items
 };
 
 // One slice's global loads for one thread.
@@ -127,67 +121,6 @@ __device__ __forceinline__ bf16x8_t decode_operand(uint32_t d, uint32_t sbyte) {
   return __builtin_bit_cast(bf16x8_t, o);
 }
 
-// ---- work items --------------------------------------------------------------
-// A slot is one (expert, 64-row m tile); its class is the number of 16-row
-// sub-tiles holding routed rows (1..4), which sets its MFMA and LDS work.  An
-// expert with R rows has R / 64 full tiles (class 4) and, when R % 64 != 0, one
-// tile of class ceil((R % 64) / 16).  Slots are ordered by class, heaviest
-// first (experts ascending within a class); a work item is (slot, n tile).
-// pre[w][e] counts the class-(4 - w) slots of the experts before e.
-__device__ __forceinline__ void class_prefix(const int32_t *__restrict__ off, int E, GroupedSmem &sm, int wave,
-                                             int lane) {
-  if (wave >= kClasses) return;  // uniform
-  const int c = kClasses - wave;
-  int o[5];
-#pragma unroll
-  for (int i = 0; i < 5; ++i) {
-    const int e = 4 * lane + i;
-    o[i] = (e <= E) ? off[e] : 0;
-  }
-  int cnt[4], sum = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int R = (4 * lane + i < E) ? o[i + 1] - o[i] : 0;
-    cnt[i] = (((R & (kBM - 1)) + 15) >> 4) == c ? 1 : 0;
-    if (c == kClasses) cnt[i] += R / kBM;
-    sum += cnt[i];
-  }
-  int incl = sum;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int v = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += v;
-  }
-  int run = incl - sum;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    sm.pre[wave][4 * lane + i] = run;
-    run += cnt[i];
-  }
-  if (lane == 63) sm.pre[wave][kPreE] = run;
-}
-
-// Slot q of the class order -> expert and m tile.
-__device__ __forceinline__ void slot_of(const int32_t *__restrict__ off, int E, const GroupedSmem &sm, int q, int &e,
-                                        int &mt) {
-  int w = 0, base = 0;
-  while (w < kClasses - 1 && q >= base + sm.pre[w][kPreE]) {
-    base += sm.pre[w][kPreE];
-    ++w;
-  }
-  const int u = q - base;
-  int lo = 0, hi = E;  // pre[w][lo] <= u < pre[w][hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (sm.pre[w][mid] <= u)
-      lo = mid;
-    else
-      hi = mid;
-  }
-  e = lo;
-  mt = (w == 0) ? u - sm.pre[0][lo] : (off[lo + 1] - off[lo]) / kBM;
-}
-
 // Persistent grouped GEMM: G workgroups (one per CU or as many as the item
 // tables need), workgroup g takes the items at positions g, 2G - 1 - g,
 // 2G + g, ... of the class order (a snake over the rounds, so the heavy
@@ -201,58 +134,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = lane_id();
-  const int G = gridDim.x;
-  const int g = blockIdx.x;
-  const int NT = a.ntiles;
-
   // ---- this workgroup's items -------------------------------------------------
-  class_prefix(a.offsets, a.E, sm, wave, lane);
-  __syncthreads();
-  int S = 0;
-#pragma unroll
-  for (int w = 0; w < kClasses; ++w) S += sm.pre[w][kPreE];
-  const int NI = S * NT;
-  int nt = 0;
-  while (nt < kMaxItems) {
-    const int j = nt * G + ((nt & 1) ? G - 1 - g : g);
-    if (j >= NI) break;
-    ++nt;
-  }
+  const int nt = build_items(a, sm.pre, sm.it, kBN, kThreads, tid, wave, lane);
   if (nt == 0) return;  // uniform
-  // The items of one slot sit 8 positions apart (blocks of 8 slots x NT
-  // tiles), so they run on one XCD and share its L2 copy of the activation
-  // rows.  Workgroups start their lists at an offset set by the XCD, so at
-  // any time each XCD works on a different mix of classes.
-  const int rot = ((g & 7) * nt) >> 3;
-  if (tid < nt) {
-    const int t = tid;
-    const int j = t * G + ((t & 1) ? G - 1 - g : g);
-    const int bsz = 8 * NT;
-    const int b = j / bsz;
-    const int p = j - b * bsz;
-    const int sb = min(8, S - 8 * b);
-    const int q = 8 * b + p % sb;
-    const int ntile = p / sb;
-    int e, mt;
-    slot_of(a.offsets, a.E, sm, q, e, mt);
-    const int row0 = a.offsets[e] + mt * kBM;
-    int tt = t - rot;
-    if (tt < 0) tt += nt;
-    sm.item[tt][0] = e;
-    sm.item[tt][1] = row0;
-    sm.item[tt][2] = min(kBM, a.offsets[e + 1] - row0);
-    sm.item[tt][3] = ntile * kBN;
-    sm.gsc[tt] = a.gscale ? a.gscale[e] : 1.0f;
-  }
-  __syncthreads();
-  for (int x = tid; x < nt * kBM; x += kThreads) {
-    const int t = x / kBM, r = x - (x / kBM) * kBM;
-    const int row0 = sm.item[t][1], mrows = sm.item[t][2];
-    int src = -1;
-    if (r < mrows) src = a.fc1 ? a.p2e[row0 + r] / a.topk : row0 + r;
-    sm.src[t][r] = src;
-  }
-  __syncthreads();
 
   const int steps = (a.K + kBK - 1) / kBK;
   const bool ragged = (a.K % kBK) != 0;  // the last slice of an item holds 64 valid k rows
@@ -308,11 +192,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   auto load_slice = [&](Regs &r) {
     const bool dead = lt >= nt;  // uniform
     if (lks == 0 && !dead) {     // uniform
-      e = __builtin_amdgcn_readfirstlane(sm.item[lt][0]);
-      const int n0 = __builtin_amdgcn_readfirstlane(sm.item[lt][3]);
+      e = __builtin_amdgcn_readfirstlane(sm.it.item[lt][0]);
+      const int n0 = __builtin_amdgcn_readfirstlane(sm.it.item[lt][3]);
 #pragma unroll
       for (int i = 0; i < kALoads; ++i) {
-        const int srow = sm.src[lt][ra[i]];
+        const int srow = sm.it.src[lt][ra[i]];
         avoff[i] = srow >= 0 ? (uint32_t)srow * (uint32_t)a.K * 2u + (uint32_t)(aq * 16) : kGOutOfRange;
       }
       // a partial last tile (N % 512 != 0) reads nothing past N
@@ -386,9 +270,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   // the epilogue makes no global load: one issued behind the next item's
   // slice loads would wait for all of them
   auto load_citem = [&]() {
-    c_row0 = __builtin_amdgcn_readfirstlane(sm.item[ct][1]);
-    c_mrows = __builtin_amdgcn_readfirstlane(sm.item[ct][2]);
-    c_n0 = __builtin_amdgcn_readfirstlane(sm.item[ct][3]);
+    c_row0 = __builtin_amdgcn_readfirstlane(sm.it.item[ct][1]);
+    c_mrows = __builtin_amdgcn_readfirstlane(sm.it.item[ct][2]);
+    c_n0 = __builtin_amdgcn_readfirstlane(sm.it.item[ct][3]);
     c_live = (c_mrows + 15) >> 4;  // 16-row sub-tiles holding routed rows
   };
   load_citem();
@@ -444,7 +328,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   // column lane%16 of each tile; then the accumulators restart for the next
   auto finish_item = [&]() {
     if (c_n0 + wave * 16 * kCT < a.N) {  // uniform
-      const float gs = sm.gsc[ct];
+      const float gs = sm.it.gsc[ct];
 #pragma unroll
       for (int ms = 0; ms < 4; ++ms) {
         if (ms >= c_live) break;
@@ -518,20 +402,13 @@ hipError_t launch_grouped(GemvArgs &a, int fmt, hipStream_t s) {
   const int erows = a.rows < a.E ? a.rows : a.E;
   a.nslots = (a.rows + kBM - 1) / kBM + erows;  // worst-case (expert, m tile) count
   a.ntiles = (a.N + kBN - 1) / kBN;  // N % 128 == 0: a partial last tile (whole 16 kCT-column waves)
-  // one workgroup per CU, more when a workgroup's item table would overflow
-  int dev = 0, cus = 0;
-  hipError_t err = hipGetDevice(&dev);
-  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  unsigned grid = 0;
+  const hipError_t err = grouped_grid(a, &grid);
   if (err != hipSuccess) return err;
-  if (cus < 1) return hipErrorInvalidConfiguration;
-  const long items = (long)a.nslots * a.ntiles;
-  long grid = (cus + 7) / 8 * 8;
-  const long need = (items + kMaxItems - 1) / kMaxItems;
-  if (grid < need) grid = (need + 7) / 8 * 8;
   if (fmt == 0)
-    grouped_gemm_kernel<0><<<dim3((unsigned)grid), kThreads, 0, s>>>(a);
+    grouped_gemm_kernel<0><<<dim3(grid), kThreads, 0, s>>>(a);
   else
-    grouped_gemm_kernel<1><<<dim3((unsigned)grid), kThreads, 0, s>>>(a);
+    grouped_gemm_kernel<1><<<dim3(grid), kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
