@@ -9,11 +9,13 @@
 // float32 y.  Same outputs as the decode GEMV.
 //
 // gfx950 design:
-// * Work item = (expert, 64-row m tile, 512-column n tile); a workgroup of
-//   16 waves steps through K in 128-k slices.  Wave w owns columns 32w..32w+31
-//   (two 16-column MFMA tiles) for every live 16-row sub-tile of the m tile,
-//   with v_mfma_f32_16x16x32_bf16.  Most experts of a prefill batch hold a
-//   handful of rows, so the cost is streaming and decoding weights.
+// * Work item = (expert, 64-row m tile, 512-column n tile), K in 128-k
+//   slices.  A workgroup has two wave groups: four loader waves move each
+//   slice from memory into LDS, eight consumer waves compute; consumer wave w
+//   owns columns 64w..64w+63 (four 16-column MFMA tiles) for every live
+//   16-row sub-tile of the m tile, with v_mfma_f32_16x16x32_bf16.  Most
+//   experts of a prefill batch hold a handful of rows, so the cost is
+//   streaming and decoding weights.
 // * Weights stay packed in LDS, copied as loaded: 128 k rows x 256 bytes per
 //   slice (sixteen lanes load a row's two 128-byte lines; 8-byte units
 //   XOR-swizzled by row in LDS).  gfx950's 4-bit transpose read
@@ -32,12 +34,17 @@
 // * Activations: 64 rows x 128 k bf16 per slice (rows gathered through the
 //   permutation for FC1), 16-byte chunks XOR-swizzled by row so the operand
 //   reads are conflict free.
-// * Pipeline: global loads two slices ahead in registers (up to 52 KB per
-//   workgroup per slice), LDS double buffered, one barrier per slice; one
-//   workgroup (16 waves, at most 128 VGPRs each) per CU.  The 512-column
-//   tile halves the activation re-reads of the n tiles (measured against 256
-//   columns on 8 waves).  16-row sub-tiles with no routed rows are skipped.
-//   No weight element is decoded or read from LDS by more than one wave.
+// * Pipeline: the loaders keep two slices of loads in flight in registers
+//   (52 KB per workgroup per slice at most) and store each slice into one of
+//   two LDS buffers; the groups hand slices over through per-buffer counts
+//   in LDS (no workgroup barrier in the loop), so the loaders' stores and
+//   waits overlap the consumers' reads, conversions and MFMAs.  With every
+//   wave doing both in turn (one barrier per slice), the kernel was bound by
+//   its in-CU work per slice rather than by HBM.  One workgroup (12 waves,
+//   at most 168 VGPRs each) per CU.  The 512-column tile halves the
+//   activation re-reads of the n tiles (measured against 256 columns).
+//   16-row sub-tiles with no routed rows are skipped.  No weight element is
+//   decoded or read from LDS by more than one wave.
 // * Persistent work items: one workgroup per CU takes a fixed list of
 //   (expert, 64-row m tile, n tile) items and streams their slices as one
 //   sequence, so the next item's first loads are in flight while the
@@ -58,16 +65,20 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kBM = 64, kBN = 512, kBK = 128;
-constexpr int kCT = 2;                     // 16-column MFMA tiles per wave
-constexpr int kWaves = kBN / (16 * kCT);   // wave w owns columns 16 kCT w .. 16 kCT (w + 1) - 1
-constexpr int kThreads = kWaves * 64;
-constexpr int kALoads = kBM * (kBK / 8) / kThreads;   // 16-byte activation chunks per thread per slice
-constexpr int kBLoads = kBK * 16 / kThreads;          // 16-byte weight chunks per thread per slice
-constexpr int kBRowStep = kThreads / 16;              // k rows between a thread's weight chunks
-static_assert(kALoads >= 1 && kBLoads >= 1 && kBN % (16 * kCT) == 0, "tile shape");
+constexpr int kCT = 4;                      // 16-column MFMA tiles per consumer wave
+constexpr int kCWaves = kBN / (16 * kCT);   // consumer wave w owns columns 16 kCT w .. 16 kCT (w + 1) - 1
+constexpr int kLWaves = 4;                  // loader waves
+constexpr int kThreads = (kCWaves + kLWaves) * 64;
+constexpr int kLThreads = kLWaves * 64;
+constexpr int kALoads = kBM * (kBK / 8) / kLThreads;  // 16-byte activation chunks per loader thread per slice
+constexpr int kBLoads = kBK * 16 / kLThreads;         // 16-byte weight chunks per loader thread per slice
+constexpr int kARowStep = kLThreads / 16;             // rows between a loader thread's activation chunks
+constexpr int kBRowStep = kLThreads / 16;             // k rows between a loader thread's weight chunks
+static_assert(kALoads >= 1 && kBLoads >= 1 && kBN % (16 * kCT) == 0 && kCWaves == 8, "tile shape");
 constexpr int kAChunks = kBK / 8;    // 16-byte chunks per activation row of a slice
 constexpr int kBRow = kBN / 2;       // packed bytes per weight row of a slice (two 128-byte lines)
 constexpr uint32_t kGOutOfRange = 0x80000000u;
+constexpr int kMaxPolls = 1 << 22;   // bound of every wait on the other wave group (a fault, not a slow load)
 
 static_assert(kBM == kGBM, "m tile of the item lists");
 
@@ -78,15 +89,42 @@ struct GroupedSmem {
                                       // puts neighbouring block rows on other banks
   GroupedPre pre;                     // set-up only
   GroupedItems it;                    // this workgroup's items
+  uint32_t ready[2];                  // per buffer: loader-wave stores of its slices (4 per slice)
+  uint32_t done[2];                   // per buffer: consumer-wave reads of its slices (8 per slice)
+  uint32_t abort;                     // set when a wait ran past its bound
 };
 
-// One slice's global loads for one thread.
+// One slice's global loads for one loader thread.
 template <int NS>
 struct SliceRegs {
   u32x4_t A[kALoads];
   u32x4_t B[kBLoads];
   uint32_t S[NS];
 };
+
+// The wave groups' counters, addressed as LDS: through a generic pointer the
+// compiler would make them flat accesses, which it also waits for with the
+// global-load counter (a loader's wait would then drain its loads).
+typedef __attribute__((address_space(3))) volatile uint32_t lds_cnt_t;
+__device__ __forceinline__ lds_cnt_t *lds_cnt(uint32_t &x) { return (lds_cnt_t *)&x; }
+
+// Waits (the calling lane polling LDS, sleeping between polls) until
+// *c >= target; past the poll bound it sets *abort and returns false.  One
+// loop with one exit and nothing else in it: other forms (a second exit, an
+// asm statement) made the compiler's waits for the loader's in-flight loads
+// conservative (they waited for the next slice's loads too).
+__device__ __forceinline__ bool wait_count(lds_cnt_t *c, uint32_t target, lds_cnt_t *abort) {
+  uint32_t polls = 0;
+  while (*c < target && polls < (uint32_t)kMaxPolls) {
+    __builtin_amdgcn_s_sleep(1);
+    ++polls;
+  }
+  if (polls >= (uint32_t)kMaxPolls) {
+    *abort = 1u;
+    return false;
+  }
+  return true;
+}
 
 // MFMA B operand of one lane: 8 consecutive k codes of its column (one
 // dword, low nibble first), decoded to bf16 with the block scale.  The
@@ -128,7 +166,7 @@ __device__ __forceinline__ bf16x8_t decode_operand(uint32_t d, uint32_t sbyte) {
 // loads for the next item's first slices are in flight while the current
 // item finishes and writes its tile.
 template <int FMT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4))) void grouped_gemm_kernel(GemvArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void grouped_gemm_kernel(GemvArgs a) {
   constexpr int B = (FMT == 0) ? 16 : 32;
   __shared__ __attribute__((aligned(16))) GroupedSmem sm;
   const int tid = threadIdx.x;
@@ -140,135 +178,169 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 
   const int steps = (a.K + kBK - 1) / kBK;
   const bool ragged = (a.K % kBK) != 0;  // the last slice of an item holds 64 valid k rows
-  const uint32_t rowbytes = (uint32_t)(a.N >> 1);
-  const int KB = a.K / B;
+  const int total = nt * steps;
+  if (tid == 0) {
+    sm.ready[0] = sm.ready[1] = 0u;
+    sm.done[0] = sm.done[1] = 0u;
+    sm.abort = 0u;
+  }
+  __syncthreads();
 
-  // ---- loader roles ----------------------------------------------------------
-  // Every load is a buffer load; rows and columns outside the data, and
-  // slices past the last item, get an out-of-range vector offset (reads
-  // return 0, no memory access).  A ragged last slice (K % 128 == 64) is only
-  // read for its first 64 k.
-  // activations: thread -> 16-byte chunk aq (8 k) of m-tile rows ra[i]
-  const int aq = tid & 15;
-  int ra[kALoads];
+  // Two wave groups, no workgroup barrier in the loop: four loader waves
+  // move each slice from memory into an LDS buffer (two buffers) and count
+  // it in the buffer's ready count; eight consumer waves wait for that count,
+  // read, convert and multiply the slice, and count their reads in the
+  // buffer's done count, which frees the buffer for the loaders.  So the
+  // stores, the waits and the compute of different slices overlap instead of
+  // alternating in step.  The counts are per buffer: a wave cannot count a
+  // buffer's next slice before the other group has passed it, so a count of
+  // (waves x uses) means every wave is through; one count over both buffers
+  // could be reached while a wave two slices behind still reads.
+  if (wave >= kCWaves) {
+    // ---- loaders ---------------------------------------------------------------
+    const int lt_id = tid - kCWaves * 64;
+    const uint32_t rowbytes = (uint32_t)(a.N >> 1);
+    const int KB = a.K / B;
+    // activations: thread -> 16-byte chunk aq (8 k) of m-tile rows ra[i]
+    const int aq = lt_id & 15;
+    int ra[kALoads];
 #pragma unroll
-  for (int i = 0; i < kALoads; ++i) ra[i] = (tid >> 4) + i * (kThreads / 16);
-  const int act_rows = a.fc1 ? a.rows / a.topk : a.rows;
-  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
-      uniform_ptr(a.act), (short)0, (int)((uint32_t)act_rows * (uint32_t)a.K * 2u), 0x00020000);
-  // weights: thread -> 16 bytes bq of k rows rb + j * kBRowStep; sixteen
-  // lanes read a row's 256 bytes (two 128-byte lines)
-  const int rb = tid >> 4;
-  const int bq = tid & 15;
-
-  // Loads are issued for the slice sequence of all items in order; (lt, lks)
-  // is the next slice to load.  Every thread issues the same loads for every
-  // slice, also past the last one, so the compiler's wait counts at the
-  // pipeline's join points stay exact.  Offsets that are uniform go through
-  // readfirstlane: in a vector register they would force a readfirstlane
-  // loop around each load.
-  // The item-dependent part of the offsets is formed once per item, when
-  // the loader reaches the item's first slice; a slice's loads then differ
-  // only by uniform masks, so the load sequence has no branches (a branch
-  // around a load leaves the compiler's wait counts conservative, and the
-  // pipeline's waits would then include the next slice's first loads).
-  // Out-of-range offsets stay out of range when a row step is added.
-  constexpr int kSBlocks = kBK / B;
-  constexpr int kSLoads = (kSBlocks * (kBN / 4) + kThreads - 1) / kThreads;
-  const int sq = tid & 127;  // scales: thread -> 4 columns sq of block rows sb[i]
-  uint32_t btail[kBLoads], stail[kSLoads];  // rows past the first 64 k of a ragged slice
+    for (int i = 0; i < kALoads; ++i) ra[i] = (lt_id >> 4) + i * kARowStep;
+    const int act_rows = a.fc1 ? a.rows / a.topk : a.rows;
+    const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(a.act), (short)0, (int)((uint32_t)act_rows * (uint32_t)a.K * 2u), 0x00020000);
+    // weights: thread -> 16 bytes bq of k rows rb + j * kBRowStep; sixteen
+    // lanes read a row's 256 bytes (two 128-byte lines)
+    const int rb = lt_id >> 4;
+    const int bq = lt_id & 15;
+    constexpr int kSBlocks = kBK / B;
+    constexpr int kSLoads = (kSBlocks * (kBN / 4) + kLThreads - 1) / kLThreads;
+    const int sq = lt_id & 127;  // scales: thread -> 4 columns sq of block rows sb[i]
+    uint32_t btail[kBLoads], stail[kSLoads];  // rows past the first 64 k of a ragged slice
 #pragma unroll
-  for (int j = 0; j < kBLoads; ++j) btail[j] = (rb + j * kBRowStep >= kBK / 2) ? kGOutOfRange : 0u;
-#pragma unroll
-  for (int i = 0; i < kSLoads; ++i) stail[i] = ((tid >> 7) + i * (kThreads / 128) >= kSBlocks / 2) ? kGOutOfRange : 0u;
-  int lt = 0, lks = 0;
-  int e = 0;
-  uint32_t avoff[kALoads], boff = kGOutOfRange, soff[kSLoads];
-#pragma unroll
-  for (int i = 0; i < kALoads; ++i) avoff[i] = kGOutOfRange;
-#pragma unroll
-  for (int i = 0; i < kSLoads; ++i) soff[i] = kGOutOfRange;
-  using Regs = SliceRegs<kSLoads>;
-  auto load_slice = [&](Regs &r) {
-    const bool dead = lt >= nt;  // uniform
-    if (lks == 0 && !dead) {     // uniform
-      e = __builtin_amdgcn_readfirstlane(sm.it.item[lt][0]);
-      const int n0 = __builtin_amdgcn_readfirstlane(sm.it.item[lt][3]);
-#pragma unroll
-      for (int i = 0; i < kALoads; ++i) {
-        const int srow = sm.it.src[lt][ra[i]];
-        avoff[i] = srow >= 0 ? (uint32_t)srow * (uint32_t)a.K * 2u + (uint32_t)(aq * 16) : kGOutOfRange;
-      }
-      // a partial last tile (N % 512 != 0) reads nothing past N
-      boff = n0 + 32 * bq + 32 <= a.N ? (uint32_t)rb * rowbytes + (uint32_t)(n0 >> 1) + (uint32_t)(bq * 16)
-                                      : kGOutOfRange;
-#pragma unroll
-      for (int i = 0; i < kSLoads; ++i) {
-        const int sb = (tid >> 7) + i * (kThreads / 128);
-        soff[i] = (n0 + sq * 4 + 4 <= a.N && sb < kSBlocks) ? (uint32_t)sb * (uint32_t)a.N + (uint32_t)(n0 + sq * 4)
-                                                           : kGOutOfRange;
-      }
-    }
-    const int k0 = lks * kBK;
-    const uint32_t tailm = (ragged && lks + 1 == steps) ? ~0u : 0u;  // uniform
-    const uint32_t kill = dead ? kGOutOfRange : 0u;                  // uniform
-    const int ao = __builtin_amdgcn_readfirstlane(k0 * 2);
-#pragma unroll
-    for (int i = 0; i < kALoads; ++i) r.A[i] = __builtin_amdgcn_raw_buffer_load_b128(arsrc, avoff[i] | kill, ao, 0);
-    const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
-        uniform_ptr(a.w + (size_t)e * a.K * rowbytes), (short)0, (int)((uint32_t)a.K * rowbytes), 0x00020000);
-    const int so = __builtin_amdgcn_readfirstlane((int)((uint32_t)k0 * rowbytes));
-#pragma unroll
-    for (int j = 0; j < kBLoads; ++j)
-      r.B[j] = __builtin_amdgcn_raw_buffer_load_b128(
-          wrsrc, (boff + (uint32_t)(j * kBRowStep) * rowbytes) | kill | (btail[j] & tailm), so, 2);
-    const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
-        uniform_ptr(a.scales + (size_t)e * KB * a.N), (short)0, (int)((uint32_t)KB * a.N), 0x00020000);
-    const int sso = __builtin_amdgcn_readfirstlane((int)((uint32_t)(k0 / B) * (uint32_t)a.N));
+    for (int j = 0; j < kBLoads; ++j) btail[j] = (rb + j * kBRowStep >= kBK / 2) ? kGOutOfRange : 0u;
 #pragma unroll
     for (int i = 0; i < kSLoads; ++i)
-      r.S[i] = __builtin_amdgcn_raw_buffer_load_b32(srsrc, soff[i] | kill | (stail[i] & tailm), sso, 0);
-    if (++lks == steps) {
-      lks = 0;
-      ++lt;
+      stail[i] = ((lt_id >> 7) + i * (kLThreads / 128) >= kSBlocks / 2) ? kGOutOfRange : 0u;
+    // The item-dependent part of the offsets is formed once per item; a
+    // slice's loads then differ only by uniform masks, so the load sequence
+    // has no branches (a branch around a load leaves the compiler's wait
+    // counts conservative).  Out-of-range offsets stay out of range when a
+    // row step is added.
+    int lt = 0, lks = 0;
+    int e = 0;
+    uint32_t avoff[kALoads], boff = kGOutOfRange, soff[kSLoads];
+#pragma unroll
+    for (int i = 0; i < kALoads; ++i) avoff[i] = kGOutOfRange;
+#pragma unroll
+    for (int i = 0; i < kSLoads; ++i) soff[i] = kGOutOfRange;
+    using Regs = SliceRegs<kSLoads>;
+    auto load_slice = [&](Regs &r) {
+      const bool dead = lt >= nt;  // uniform
+      if (lks == 0 && !dead) {     // uniform
+        e = __builtin_amdgcn_readfirstlane(sm.it.item[lt][0]);
+        const int n0 = __builtin_amdgcn_readfirstlane(sm.it.item[lt][3]);
+#pragma unroll
+        for (int i = 0; i < kALoads; ++i) {
+          const int srow = sm.it.src[lt][ra[i]];
+          avoff[i] = srow >= 0 ? (uint32_t)srow * (uint32_t)a.K * 2u + (uint32_t)(aq * 16) : kGOutOfRange;
+        }
+        // a partial last tile (N % 512 != 0) reads nothing past N
+        boff = n0 + 32 * bq + 32 <= a.N ? (uint32_t)rb * rowbytes + (uint32_t)(n0 >> 1) + (uint32_t)(bq * 16)
+                                        : kGOutOfRange;
+#pragma unroll
+        for (int i = 0; i < kSLoads; ++i) {
+          const int sb = (lt_id >> 7) + i * (kLThreads / 128);
+          soff[i] = (n0 + sq * 4 + 4 <= a.N && sb < kSBlocks) ? (uint32_t)sb * (uint32_t)a.N + (uint32_t)(n0 + sq * 4)
+                                                             : kGOutOfRange;
+        }
+      }
+      const int k0 = lks * kBK;
+      const uint32_t tailm = (ragged && lks + 1 == steps) ? ~0u : 0u;  // uniform
+      const uint32_t kill = dead ? kGOutOfRange : 0u;                  // uniform
+      const int ao = __builtin_amdgcn_readfirstlane(k0 * 2);
+#pragma unroll
+      for (int i = 0; i < kALoads; ++i) r.A[i] = __builtin_amdgcn_raw_buffer_load_b128(arsrc, avoff[i] | kill, ao, 0);
+      const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+          uniform_ptr(a.w + (size_t)e * a.K * rowbytes), (short)0, (int)((uint32_t)a.K * rowbytes), 0x00020000);
+      const int so = __builtin_amdgcn_readfirstlane((int)((uint32_t)k0 * rowbytes));
+#pragma unroll
+      for (int j = 0; j < kBLoads; ++j)
+        r.B[j] = __builtin_amdgcn_raw_buffer_load_b128(
+            wrsrc, (boff + (uint32_t)(j * kBRowStep) * rowbytes) | kill | (btail[j] & tailm), so, 2);
+      const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
+          uniform_ptr(a.scales + (size_t)e * KB * a.N), (short)0, (int)((uint32_t)KB * a.N), 0x00020000);
+      const int sso = __builtin_amdgcn_readfirstlane((int)((uint32_t)(k0 / B) * (uint32_t)a.N));
+#pragma unroll
+      for (int i = 0; i < kSLoads; ++i)
+        r.S[i] = __builtin_amdgcn_raw_buffer_load_b32(srsrc, soff[i] | kill | (stail[i] & tailm), sso, 0);
+      if (++lks == steps) {
+        lks = 0;
+        ++lt;
+      }
+    };
+    // LDS positions of this thread's stores (unit u of weight row r sits at
+    // u ^ (r & 31): the two 8-byte halves of a loaded chunk land separately;
+    // the transpose reads of lane groups 16 rows apart then hit opposite bank
+    // halves)
+    int bpos[kBLoads][2];
+#pragma unroll
+    for (int j = 0; j < kBLoads; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) bpos[j][h] = 8 * ((2 * bq + h) ^ ((rb + j * kBRowStep) & 31));
+    auto store_slice = [&](int buf, const Regs &r) {
+#pragma unroll
+      for (int i = 0; i < kALoads; ++i) sm.a[buf][ra[i]][aq ^ (ra[i] & 15)] = r.A[i];
+#pragma unroll
+      for (int j = 0; j < kBLoads; ++j) {
+        const int row = rb + j * kBRowStep;
+        *(u32x2_t *)&sm.b[buf][row][bpos[j][0]] = u32x2_t{r.B[j].x, r.B[j].y};
+        *(u32x2_t *)&sm.b[buf][row][bpos[j][1]] = u32x2_t{r.B[j].z, r.B[j].w};
+      }
+#pragma unroll
+      for (int i = 0; i < kSLoads; ++i) {
+        const int sb = (lt_id >> 7) + i * (kLThreads / 128);
+        if (sb < kSBlocks) *(uint32_t *)&sm.sc[buf][sb][sq * 4] = r.S[i];
+      }
+    };
+    // slice s: wait until every consumer wave is done with slice s - 2 (the
+    // buffer's previous slice, its (s / 2)-th use), store, count
+    // (A wait past its bound lets the loader go on: the results are then
+    // wrong but every wave still ends.  Control flow that depends on the wait's
+    // outcome made the compiler's waits for the in-flight loads conservative.)
+    auto put = [&](int s, int buf, Regs &r) {
+      if (s >= 2 && (lane == 0)) (void)wait_count(lds_cnt(sm.done[buf]), (uint32_t)(kCWaves * (s >> 1)), lds_cnt(sm.abort));
+      asm volatile("" ::: "memory");
+      store_slice(buf, r);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's stores are in LDS
+      if (lane == 0) __hip_atomic_fetch_add(lds_cnt(sm.ready[buf]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    Regs r0, r1;
+    load_slice(r0);
+    // slice 0's loads stay ahead of slice 1's: each store waits for the older
+    // register set only (memory returns in issue order)
+    __builtin_amdgcn_sched_barrier(0);
+    load_slice(r1);
+    // One exit, at the bottom: a break between the halves makes the compiler
+    // wait for both register sets at the top of the loop.
+    for (int s = 0; s < total; s += 2) {
+      put(s, 0, r0);
+      load_slice(r0);
+      if (s + 1 < total) put(s + 1, 1, r1);
+      load_slice(r1);
     }
-  };
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    return;
+  }
 
-  // LDS positions of this thread's stores (unit u of weight row r sits at
-  // u ^ (r & 31): the two 8-byte halves of a loaded chunk land separately;
-  // the transpose reads of lane groups 16 rows apart then hit opposite bank
-  // halves)
-  int bpos[kBLoads][2];
-#pragma unroll
-  for (int j = 0; j < kBLoads; ++j)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) bpos[j][h] = 8 * ((2 * bq + h) ^ ((rb + j * kBRowStep) & 31));
-
-  auto store_slice = [&](int buf, const Regs &r) {
-#pragma unroll
-    for (int i = 0; i < kALoads; ++i) sm.a[buf][ra[i]][aq ^ (ra[i] & 15)] = r.A[i];
-#pragma unroll
-    for (int j = 0; j < kBLoads; ++j) {
-      const int row = rb + j * kBRowStep;
-      *(u32x2_t *)&sm.b[buf][row][bpos[j][0]] = u32x2_t{r.B[j].x, r.B[j].y};
-      *(u32x2_t *)&sm.b[buf][row][bpos[j][1]] = u32x2_t{r.B[j].z, r.B[j].w};
-    }
-#pragma unroll
-    for (int i = 0; i < kSLoads; ++i) {
-      const int sb = (tid >> 7) + i * (kThreads / 128);
-      if (sb < kSBlocks) *(uint32_t *)&sm.sc[buf][sb][sq * 4] = r.S[i];
-    }
-  };
-
-  // ---- MFMA roles: wave w owns units T = kCT w + t of a packed row (16
+  // ---- consumers: wave w owns units T = kCT w + t of a packed row (16
   // columns each; the row swizzle permutes the row's 32 units) ---------------
   const int li = lane & 15;
   const int lk = lane >> 4;
   // the item being computed: (ct, cks) is its next slice
   int ct = 0, cks = 0;
   int c_live = 0, c_row0 = 0, c_mrows = 0, c_n0 = 0;
-  // the epilogue makes no global load: one issued behind the next item's
-  // slice loads would wait for all of them
+  // the epilogue makes no global load
   auto load_citem = [&]() {
     c_row0 = __builtin_amdgcn_readfirstlane(sm.it.item[ct][1]);
     c_mrows = __builtin_amdgcn_readfirstlane(sm.it.item[ct][2]);
@@ -357,36 +429,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       for (int j = 0; j < kCT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (++ct < nt) load_citem();
   };
-  auto advance_compute = [&]() {
+
+  // slice s: wait until the four loader waves have stored it, compute,
+  // count this wave's reads done (they have returned: lgkmcnt 0).  Unrolled
+  // by two so each buffer's LDS offsets are constants.
+  auto take = [&](int s, int buf) {
+    bool ok = true;
+    if (lane == 0) ok = wait_count(lds_cnt(sm.ready[buf]), (uint32_t)(kLWaves * ((s >> 1) + 1)), lds_cnt(sm.abort));
+    ok = __builtin_amdgcn_readfirstlane((int)ok) != 0;
+    if (!ok) return false;  // uniform: a wait ran past its bound
+    asm volatile("" ::: "memory");
+    compute_slice(buf);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (lane == 0) __hip_atomic_fetch_add(lds_cnt(sm.done[buf]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     if (++cks == steps) {  // uniform: the item's last slice is done
       cks = 0;
       finish_item();
     }
+    return true;
   };
-
-  // ---- pipeline: loads two slices ahead in registers, LDS double buffered ----
-  Regs r0, r1;
-  load_slice(r0);
-  // slice 0's loads stay ahead of slice 1's: the loop waits for the older
-  // register set only (memory returns in issue order)
-  __builtin_amdgcn_sched_barrier(0);
-  load_slice(r1);
-  const int total = nt * steps;
-  // One exit, at the bottom: a break between the halves makes the compiler
-  // wait for both register sets at the top of the loop.
   for (int s = 0; s < total; s += 2) {
-    store_slice(0, r0);
-    load_slice(r0);
-    __syncthreads();
-    compute_slice(0);
-    advance_compute();
-    store_slice(1, r1);
-    load_slice(r1);
-    __syncthreads();
-    if (s + 1 < total) {
-      compute_slice(1);
-      advance_compute();
-    }
+    if (!take(s, 0)) break;
+    if (s + 1 < total && !take(s + 1, 1)) break;
   }
 }
 
