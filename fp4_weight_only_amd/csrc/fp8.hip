@@ -202,16 +202,18 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kF8BM = 64;
 constexpr int kF8BK = 128;                          // k per slice: one 128-byte line of a column
-constexpr int kF8GWaves = 8;
-constexpr int kF8BN = kF8GWaves * 32;               // columns per work item
-constexpr int kF8GThreads = kF8GWaves * 64;
+constexpr int kF8CWaves = 8;                        // consumer waves, 32 columns each
+constexpr int kF8LWaves = 4;                        // loader waves
+constexpr int kF8BN = kF8CWaves * 32;               // columns per work item
+constexpr int kF8GThreads = (kF8CWaves + kF8LWaves) * 64;
+constexpr int kF8LThreads = kF8LWaves * 64;
 constexpr int kF8Units = kF8BK / 8;                 // 8-k units per slice (B: 8 bytes, A: 16 bytes)
-constexpr int kF8ALoads = (kF8BM * kF8Units + kF8GThreads - 1) / kF8GThreads;  // 16-byte A loads per thread
-constexpr int kF8AThreads = kF8BM * kF8Units / kF8ALoads;                   // threads that load A
+constexpr int kF8ALoads = kF8BM * kF8Units / kF8LThreads;  // 16-byte A loads per loader thread
 constexpr int kF8LPC = kF8BK / 16;                  // lanes per column (16 bytes each)
-constexpr int kF8CPP = kF8GThreads / kF8LPC;        // columns per load pass
-constexpr int kF8BLoads = kF8BN / kF8CPP;           // 16-byte B loads per thread
-static_assert(kF8AThreads % 64 == 0 && kF8BN % kF8CPP == 0 && (kF8Units & (kF8Units - 1)) == 0, "tile shape");
+constexpr int kF8CPP = kF8LThreads / kF8LPC;        // columns per load pass
+constexpr int kF8BLoads = kF8BN / kF8CPP;           // 16-byte B loads per loader thread
+static_assert(kF8ALoads * kF8LThreads == kF8BM * kF8Units && kF8BN % kF8CPP == 0 &&
+                  (kF8Units & (kF8Units - 1)) == 0, "tile shape");
 static_assert(kF8BM == kGBM, "m tile of the item lists");
 
 struct F8GroupedSmem {
@@ -219,6 +221,9 @@ struct F8GroupedSmem {
   uint8_t b[2][kF8BN][kF8BK];       // weight bytes, 8-byte unit u of column n at u ^ (n % units)
   GroupedPre pre;                   // set-up only
   GroupedItems it;                  // this workgroup's items
+  uint32_t ready[2];                // per buffer: loader-wave stores of its slices (4 per slice)
+  uint32_t done[2];                 // per buffer: consumer-wave reads of its slices (8 per slice)
+  uint32_t abort;                   // set when a wait ran past its bound
 };
 
 struct F8SliceRegs {
@@ -235,8 +240,7 @@ __device__ __forceinline__ bf16x8_t fp8_operand(u32x2_t d) {
   return __builtin_bit_cast(bf16x8_t, o);
 }
 
-__global__ __launch_bounds__(kF8GThreads) __attribute__((amdgpu_waves_per_eu(kF8GWaves / 4))) void fp8_grouped_kernel(
-    GemvArgs a) {
+__global__ __launch_bounds__(kF8GThreads) __attribute__((amdgpu_waves_per_eu(3))) void fp8_grouped_kernel(GemvArgs a) {
   __shared__ __attribute__((aligned(16))) F8GroupedSmem sm;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -246,83 +250,119 @@ __global__ __launch_bounds__(kF8GThreads) __attribute__((amdgpu_waves_per_eu(kF8
   if (nt == 0) return;  // uniform
   const int steps = (a.K + kF8BK - 1) / kF8BK;  // K % 64 == 0: the last slice of an item may be half
   const int ktail = a.K - (steps - 1) * kF8BK;  // k in the last slice
-
-  // loaders (buffer loads; the item-dependent vector offsets formed once per
-  // item, the slice in the scalar offset; chunks past K in a half last slice
-  // load as zero; slices past the last item load nothing)
-  const bool aload = kF8AThreads == kF8GThreads || tid < kF8AThreads;  // uniform per wave
-  const int act_rows = a.fc1 ? a.rows / a.topk : a.rows;
-  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
-      uniform_ptr(a.act), (short)0, (int)((uint32_t)act_rows * (uint32_t)a.K * 2u), 0x00020000);
-  int ar[kF8ALoads], aq[kF8ALoads];
-  uint32_t atail[kF8ALoads];
-#pragma unroll
-  for (int i = 0; i < kF8ALoads; ++i) {
-    const int c = tid + i * kF8AThreads;
-    ar[i] = c / kF8Units;
-    aq[i] = c % kF8Units;
-    atail[i] = aq[i] * 8 >= ktail ? kF8OutOfRange : 0u;
+  const int total = nt * steps;
+  if (tid == 0) {
+    sm.ready[0] = sm.ready[1] = 0u;
+    sm.done[0] = sm.done[1] = 0u;
+    sm.abort = 0u;
   }
-  const int cb = tid / kF8LPC, bq = tid % kF8LPC;  // columns cb + j * kF8CPP; 16 bytes bq of the slice
-  const uint32_t btail = bq * 16 >= ktail ? kF8OutOfRange : 0u;
-  int lt = 0, lks = 0, e = 0;
-  uint32_t avoff[kF8ALoads], bvoff[kF8BLoads];
+  __syncthreads();
+
+  // Loader and consumer wave groups hand slices over through per-buffer
+  // counts in LDS, as on the FP4 path (grouped.hip).
+  if (wave >= kF8CWaves) {
+    // ---- loaders (buffer loads; the item-dependent vector offsets formed once
+    // per item, the slice in the scalar offset; chunks past K in a half last
+    // slice load as zero; slices past the last item load nothing) -------------
+    const int lt_id = tid - kF8CWaves * 64;
+    const int act_rows = a.fc1 ? a.rows / a.topk : a.rows;
+    const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(a.act), (short)0, (int)((uint32_t)act_rows * (uint32_t)a.K * 2u), 0x00020000);
+    int ar[kF8ALoads], aq[kF8ALoads];
+    uint32_t atail[kF8ALoads];
 #pragma unroll
-  for (int i = 0; i < kF8ALoads; ++i) avoff[i] = kF8OutOfRange;
-#pragma unroll
-  for (int j = 0; j < kF8BLoads; ++j) bvoff[j] = kF8OutOfRange;
-  // Every thread issues the same loads for every slice, also past the last
-  // one, with no branch around a load, so the compiler's wait counts at the
-  // pipeline's join points stay exact.
-  auto load_slice = [&](F8SliceRegs &r) {
-    const bool dead = lt >= nt;  // uniform
-    if (lks == 0 && !dead) {     // uniform
-      e = __builtin_amdgcn_readfirstlane(sm.it.item[lt][0]);
-      const int n0 = __builtin_amdgcn_readfirstlane(sm.it.item[lt][3]);
-#pragma unroll
-      for (int i = 0; i < kF8ALoads; ++i) {
-        const int srow = aload ? sm.it.src[lt][ar[i]] : -1;
-        avoff[i] = srow >= 0 ? (uint32_t)srow * (uint32_t)a.K * 2u + (uint32_t)(aq[i] * 16) : kF8OutOfRange;
-      }
-#pragma unroll
-      for (int j = 0; j < kF8BLoads; ++j) {
-        const int col = n0 + cb + kF8CPP * j;
-        bvoff[j] = col < a.N ? (uint32_t)col * (uint32_t)a.K + (uint32_t)(bq * 16) : kF8OutOfRange;
-      }
+    for (int i = 0; i < kF8ALoads; ++i) {
+      const int c = lt_id + i * kF8LThreads;
+      ar[i] = c / kF8Units;
+      aq[i] = c % kF8Units;
+      atail[i] = aq[i] * 8 >= ktail ? kF8OutOfRange : 0u;
     }
-    const int k0 = lks * kF8BK;
-    const uint32_t kill = dead ? kF8OutOfRange : 0u;                      // uniform
-    const uint32_t halfm = (lks == steps - 1 && ktail < kF8BK) ? ~0u : 0u;  // uniform
-    const int ao = __builtin_amdgcn_readfirstlane(k0 * 2), bo = __builtin_amdgcn_readfirstlane(k0);
+    const int cb = lt_id / kF8LPC, bq = lt_id % kF8LPC;  // columns cb + j * kF8CPP; 16 bytes bq of the slice
+    const uint32_t btail = bq * 16 >= ktail ? kF8OutOfRange : 0u;
+    int lt = 0, lks = 0, e = 0;
+    uint32_t avoff[kF8ALoads], bvoff[kF8BLoads];
 #pragma unroll
-    for (int i = 0; i < kF8ALoads; ++i)
-      r.A[i] = __builtin_bit_cast(
-          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(arsrc, avoff[i] | kill | (atail[i] & halfm), ao, 0));
-    const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
-        uniform_ptr(a.w + (size_t)e * a.N * a.K), (short)0, (int)((uint32_t)a.N * (uint32_t)a.K), 0x00020000);
+    for (int i = 0; i < kF8ALoads; ++i) avoff[i] = kF8OutOfRange;
 #pragma unroll
-    for (int j = 0; j < kF8BLoads; ++j)
-      r.B[j] = __builtin_bit_cast(
-          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, bvoff[j] | kill | (btail & halfm), bo, 2));
-    if (++lks == steps) {
-      lks = 0;
-      ++lt;
-    }
-  };
-  auto store_slice = [&](int buf, const F8SliceRegs &r) {
-    if (aload) {
+    for (int j = 0; j < kF8BLoads; ++j) bvoff[j] = kF8OutOfRange;
+    // Every loader thread issues the same loads for every slice, also past
+    // the last one, with no branch around a load, so the compiler's wait
+    // counts stay exact.
+    auto load_slice = [&](F8SliceRegs &r) {
+      const bool dead = lt >= nt;  // uniform
+      if (lks == 0 && !dead) {     // uniform
+        e = __builtin_amdgcn_readfirstlane(sm.it.item[lt][0]);
+        const int n0 = __builtin_amdgcn_readfirstlane(sm.it.item[lt][3]);
+#pragma unroll
+        for (int i = 0; i < kF8ALoads; ++i) {
+          const int srow = sm.it.src[lt][ar[i]];
+          avoff[i] = srow >= 0 ? (uint32_t)srow * (uint32_t)a.K * 2u + (uint32_t)(aq[i] * 16) : kF8OutOfRange;
+        }
+#pragma unroll
+        for (int j = 0; j < kF8BLoads; ++j) {
+          const int col = n0 + cb + kF8CPP * j;
+          bvoff[j] = col < a.N ? (uint32_t)col * (uint32_t)a.K + (uint32_t)(bq * 16) : kF8OutOfRange;
+        }
+      }
+      const int k0 = lks * kF8BK;
+      const uint32_t kill = dead ? kF8OutOfRange : 0u;                      // uniform
+      const uint32_t halfm = (lks == steps - 1 && ktail < kF8BK) ? ~0u : 0u;  // uniform
+      const int ao = __builtin_amdgcn_readfirstlane(k0 * 2), bo = __builtin_amdgcn_readfirstlane(k0);
+#pragma unroll
+      for (int i = 0; i < kF8ALoads; ++i)
+        r.A[i] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(arsrc, avoff[i] | kill | (atail[i] & halfm), ao, 0));
+      const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+          uniform_ptr(a.w + (size_t)e * a.N * a.K), (short)0, (int)((uint32_t)a.N * (uint32_t)a.K), 0x00020000);
+#pragma unroll
+      for (int j = 0; j < kF8BLoads; ++j)
+        r.B[j] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, bvoff[j] | kill | (btail & halfm), bo, 2));
+      if (++lks == steps) {
+        lks = 0;
+        ++lt;
+      }
+    };
+    auto store_slice = [&](int buf, const F8SliceRegs &r) {
 #pragma unroll
       for (int i = 0; i < kF8ALoads; ++i) sm.a[buf][ar[i]][aq[i] ^ (ar[i] & (kF8Units - 1))] = r.A[i];
-    }
 #pragma unroll
-    for (int j = 0; j < kF8BLoads; ++j) {
-      const int n = cb + kF8CPP * j;
-      *(u32x2_t *)&sm.b[buf][n][8 * ((2 * bq) ^ (n & (kF8Units - 1)))] = u32x2_t{r.B[j].x, r.B[j].y};
-      *(u32x2_t *)&sm.b[buf][n][8 * ((2 * bq + 1) ^ (n & (kF8Units - 1)))] = u32x2_t{r.B[j].z, r.B[j].w};
+      for (int j = 0; j < kF8BLoads; ++j) {
+        const int n = cb + kF8CPP * j;
+        *(u32x2_t *)&sm.b[buf][n][8 * ((2 * bq) ^ (n & (kF8Units - 1)))] = u32x2_t{r.B[j].x, r.B[j].y};
+        *(u32x2_t *)&sm.b[buf][n][8 * ((2 * bq + 1) ^ (n & (kF8Units - 1)))] = u32x2_t{r.B[j].z, r.B[j].w};
+      }
+    };
+    // slice s: wait until every consumer wave is done with slice s - 2 (the
+    // buffer's previous slice, its (s / 2)-th use), store, count.  A wait past
+    // its bound lets the loader go on (results then wrong, every wave ends).
+    auto put = [&](int s, int buf, F8SliceRegs &r) {
+      if (s >= 2 && (lane == 0)) (void)wait_count(lds_cnt(sm.done[buf]), (uint32_t)(kF8CWaves * (s >> 1)), lds_cnt(sm.abort));
+      asm volatile("" ::: "memory");
+      store_slice(buf, r);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's stores are in LDS
+      if (lane == 0) __hip_atomic_fetch_add(lds_cnt(sm.ready[buf]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    F8SliceRegs r0, r1;
+    load_slice(r0);
+    // slice 0's loads stay ahead of slice 1's: each store waits for the older
+    // register set only (memory returns in issue order)
+    __builtin_amdgcn_sched_barrier(0);
+    load_slice(r1);
+    // One exit, at the bottom: a break between the halves makes the compiler
+    // wait for both register sets at the top of the loop.
+    for (int s = 0; s < total; s += 2) {
+      put(s, 0, r0);
+      load_slice(r0);
+      if (s + 1 < total) put(s + 1, 1, r1);
+      load_slice(r1);
     }
-  };
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    return;
+  }
 
-  // MFMA roles: lane (lk, li) -> column li of a 16-column tile, k 8 lk .. +7 of a 32-k group
+  // ---- consumers: lane (lk, li) -> column li of a 16-column tile, k 8 lk .. +7
+  // of a 32-k group; wave w owns columns 32w..32w+31 ---------------------------
   const int li = lane & 15, lk = lane >> 4;
   // the item being computed: (ct, cks) is its next slice
   int ct = 0, cks = 0;
@@ -364,9 +404,7 @@ __global__ __launch_bounds__(kF8GThreads) __attribute__((amdgpu_waves_per_eu(kF8
   };
 
   // epilogue of the item being computed (lane holds rows 4 lk + i, column li
-  // of each 16-column tile; no global load: one issued behind the next
-  // item's slice loads would wait for all of them); then the accumulators
-  // restart for the next item
+  // of each 16-column tile; no global load); then the accumulators restart
   auto finish_item = [&]() {
     if (c_n0 + wave * 32 < a.N) {  // uniform
       const float gs = sm.it.gsc[ct];
@@ -398,35 +436,28 @@ __global__ __launch_bounds__(kF8GThreads) __attribute__((amdgpu_waves_per_eu(kF8
       for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (++ct < nt) load_citem();
   };
-  auto advance_compute = [&]() {
+
+  // slice s: wait until the four loader waves have stored it, compute, count
+  // this wave's reads done (they have returned: lgkmcnt 0).  Unrolled by two
+  // so each buffer's LDS offsets are constants.
+  auto take = [&](int s, int buf) {
+    bool ok = true;
+    if (lane == 0) ok = wait_count(lds_cnt(sm.ready[buf]), (uint32_t)(kF8LWaves * ((s >> 1) + 1)), lds_cnt(sm.abort));
+    ok = __builtin_amdgcn_readfirstlane((int)ok) != 0;
+    if (!ok) return false;  // uniform: a wait ran past its bound
+    asm volatile("" ::: "memory");
+    compute_slice(buf);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (lane == 0) __hip_atomic_fetch_add(lds_cnt(sm.done[buf]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     if (++cks == steps) {  // uniform: the item's last slice is done
       cks = 0;
       finish_item();
     }
+    return true;
   };
-
-  F8SliceRegs r0, r1;
-  load_slice(r0);
-  // slice 0's loads stay ahead of slice 1's: the loop waits for the older
-  // register set only (memory returns in issue order)
-  __builtin_amdgcn_sched_barrier(0);
-  load_slice(r1);
-  const int total = nt * steps;
-  // One exit, at the bottom: a break between the halves makes the compiler
-  // wait for both register sets at the top of the loop.
   for (int s = 0; s < total; s += 2) {
-    store_slice(0, r0);
-    load_slice(r0);
-    __syncthreads();
-    compute_slice(0);
-    advance_compute();
-    store_slice(1, r1);
-    load_slice(r1);
-    __syncthreads();
-    if (s + 1 < total) {
-      compute_slice(1);
-      advance_compute();
-    }
+    if (!take(s, 0)) break;
+    if (s + 1 < total && !take(s + 1, 1)) break;
   }
 }
 

@@ -78,7 +78,6 @@ static_assert(kALoads >= 1 && kBLoads >= 1 && kBN % (16 * kCT) == 0 && kCWaves =
 constexpr int kAChunks = kBK / 8;    // 16-byte chunks per activation row of a slice
 constexpr int kBRow = kBN / 2;       // packed bytes per weight row of a slice (two 128-byte lines)
 constexpr uint32_t kGOutOfRange = 0x80000000u;
-constexpr int kMaxPolls = 1 << 22;   // bound of every wait on the other wave group (a fault, not a slow load)
 
 static_assert(kBM == kGBM, "m tile of the item lists");
 
@@ -101,30 +100,6 @@ struct SliceRegs {
   u32x4_t B[kBLoads];
   uint32_t S[NS];
 };
-
-// The wave groups' counters, addressed as LDS: through a generic pointer the
-// compiler would make them flat accesses, which it also waits for with the
-// global-load counter (a loader's wait would then drain its loads).
-typedef __attribute__((address_space(3))) volatile uint32_t lds_cnt_t;
-__device__ __forceinline__ lds_cnt_t *lds_cnt(uint32_t &x) { return (lds_cnt_t *)&x; }
-
-// Waits (the calling lane polling LDS, sleeping between polls) until
-// *c >= target; past the poll bound it sets *abort and returns false.  One
-// loop with one exit and nothing else in it: other forms (a second exit, an
-// asm statement) made the compiler's waits for the loader's in-flight loads
-// conservative (they waited for the next slice's loads too).
-__device__ __forceinline__ bool wait_count(lds_cnt_t *c, uint32_t target, lds_cnt_t *abort) {
-  uint32_t polls = 0;
-  while (*c < target && polls < (uint32_t)kMaxPolls) {
-    __builtin_amdgcn_s_sleep(1);
-    ++polls;
-  }
-  if (polls >= (uint32_t)kMaxPolls) {
-    *abort = 1u;
-    return false;
-  }
-  return true;
-}
 
 // MFMA B operand of one lane: 8 consecutive k codes of its column (one
 // dword, low nibble first), decoded to bf16 with the block scale.  The

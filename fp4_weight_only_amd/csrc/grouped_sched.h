@@ -142,6 +142,34 @@ __device__ __forceinline__ int build_items(const GemvArgs &a, GroupedPre &pre, G
   return nt;
 }
 
+// ---- hand-off between the loader and consumer wave groups -------------------
+constexpr int kMaxPolls = 1 << 22;  // bound of every wait on the other wave group (a fault, not a slow load)
+
+// The wave groups' counters, addressed as LDS: through a generic pointer the
+// compiler would make them flat accesses, which it also waits for with the
+// global-load counter (a loader's wait would then drain its loads).
+typedef __attribute__((address_space(3))) volatile uint32_t lds_cnt_t;
+__device__ __forceinline__ lds_cnt_t *lds_cnt(uint32_t &x) { return (lds_cnt_t *)&x; }
+
+// Waits (the calling lane polling LDS, sleeping between polls) until
+// *c >= target; past the poll bound it sets *abort and returns false.  One
+// loop with one exit and nothing else in it; a loader ignores the result:
+// control flow that depends on it made the compiler's waits for the
+// loader's in-flight loads conservative (they waited for the next slice's
+// loads too).
+__device__ __forceinline__ bool wait_count(lds_cnt_t *c, uint32_t target, lds_cnt_t *abort) {
+  uint32_t polls = 0;
+  while (*c < target && polls < (uint32_t)kMaxPolls) {
+    __builtin_amdgcn_s_sleep(1);
+    ++polls;
+  }
+  if (polls >= (uint32_t)kMaxPolls) {
+    *abort = 1u;
+    return false;
+  }
+  return true;
+}
+
 // Grid of a persistent grouped GEMM: one workgroup per CU (a multiple of 8,
 // the XCD count), more when a workgroup's item table would overflow; a.nslots
 // and a.ntiles set (the worst-case item count is their product).
