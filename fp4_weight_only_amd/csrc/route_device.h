@@ -46,10 +46,17 @@ constexpr uint32_t kNoExpert = 0xFFFFu;  // padding / consumed slot: loses every
 __device__ __forceinline__ void topk_token(const float *__restrict__ row, const float *__restrict__ rw, int E, int k,
                                            int lane, int &sel, float &wsel) {
   uint32_t kv[4], ex[4];
+  // all four loads unconditional (a lane past E reads expert E - 1 and
+  // drops it), so they are in flight together: written as conditional
+  // loads, each sat in its own branch with a wait behind it, four memory
+  // round trips in a row
+  float lv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lv[i] = row[min(lane + 64 * i, E - 1)];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
-    kv[i] = (e < E) ? ord_key(row[e]) : 0u;
+    kv[i] = (e < E) ? ord_key(lv[i]) : 0u;
     ex[i] = (e < E) ? (uint32_t)e : kNoExpert;
   }
   auto order = [&](int a, int b) {  // slot a before slot b
