@@ -1004,15 +1004,23 @@ def fill_pattern(t, pat):
 
 
 # The same layers against the C++ oracle (plain single-threaded float64,
-# written independently of the numpy oracle): the full decode, MTP-verify
-# and FP8 layers, a grouped-path batch, the prefill layer on sampled columns
-# and the full standalone dequant.
+# written independently of the numpy oracle): the full decode, MTP-verify,
+# MXFP4 decode and FP8 layers, a grouped-path batch, the prefill layer on
+# sampled columns and the full standalone dequant.
 CPP_LAYERS = [synth.TINY, synth.DECODE, synth.MTP4, synth.MTP8, synth.FP8_MTP4, GROUPED[0], GROUPED[3]]
 
 
 @pytest.mark.parametrize("cfg", CPP_LAYERS, ids=lambda c: c.name)
 def test_layer_against_cpp_oracle(cfg):
     check_layer(synth.layer_inputs(cfg), orc="cpp")
+
+
+@pytest.mark.timeout(600)
+def test_layer_mxfp4_decode_full_against_cpp_oracle():
+    """The 8-token MXFP4 decode layer (E=256, hidden 4096, intermediate 2048,
+    64 rows) on the GEMV path, every column of h, y and out, against the C++
+    oracle (about a minute of single-threaded float64 on the host)."""
+    check_layer(synth.layer_inputs(synth.MX_DECODE), orc="cpp")
 
 
 def test_prefill_full_sampled_against_cpp_oracle():
