@@ -530,7 +530,7 @@ __device__ __forceinline__ void run_item(const LayerArgs &a, S &sm, const ItemIn
 // already ran, or to another resident workgroup whose earlier items are FC1
 // items (no wait) or FC2 items of earlier slots (by induction, they finish).
 template <int FMT, int MRMAX>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void fp4_layer_kernel(LayerArgs a) {
+__device__ __forceinline__ void layer_body(const LayerArgs &a) {
   __shared__ __attribute__((aligned(16))) LayerSmem<MRMAX> sm;
   const int tid0 = threadIdx.x;
 
@@ -571,6 +571,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   if (blockIdx.x == 0) write_routing(a, sm, tid0);
 }
 
+// The kernel at four workgroups per CU (128 VGPRs) and at three (168 VGPRs).
+template <int FMT, int MRMAX>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void fp4_layer_kernel(LayerArgs a) {
+  layer_body<FMT, MRMAX>(a);
+}
+template <int FMT, int MRMAX>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void fp4_layer_kernel_w3(LayerArgs a) {
+  layer_body<FMT, MRMAX>(a);
+}
+
 // Two-row passes up to four tokens: at four tokens the hot experts' four
 // rows then take two slots (their weights are read twice, 1.8 MB each) and
 // the longest items shorten (layer 27.4 -> 26.9 us on MI355X); one-row
@@ -589,16 +599,27 @@ namespace {
 
 typedef void (*LayerKernel)(LayerArgs);
 
-LayerKernel layer_kernel(int fmt, int mr) {
-  if (fmt == 0) return mr == 1 ? fp4_layer_kernel<0, 1> : (mr == 2 ? fp4_layer_kernel<0, 2> : fp4_layer_kernel<0, 4>);
-  return mr == 1 ? fp4_layer_kernel<1, 1> : (mr == 2 ? fp4_layer_kernel<1, 2> : fp4_layer_kernel<1, 4>);
+// Workgroups per CU (waves per SIMD): four (128 VGPRs) at one token and at
+// four, three (168 VGPRs: resident slots given up for register room) at two
+// or three tokens and from five on, as measured on MI355X (NVFP4 E=256,
+// H=2048, I=768: T=2 layer 21.7 -> 20.5 us, T=8 40.9 -> 39.8 us; T=4 the
+// same 26.9 us either way).
+template <int FMT>
+LayerKernel layer_kernel_fmt(int mr, int T) {
+  if (mr == 1) return fp4_layer_kernel<FMT, 1>;
+  if (mr == 2) return T == 4 ? fp4_layer_kernel<FMT, 2> : fp4_layer_kernel_w3<FMT, 2>;
+  return fp4_layer_kernel_w3<FMT, 4>;
+}
+
+LayerKernel layer_kernel(int fmt, int mr, int T) {
+  return fmt == 0 ? layer_kernel_fmt<0>(mr, T) : layer_kernel_fmt<1>(mr, T);
 }
 
 }  // namespace
 
 hipError_t launch_fp4_layer(const LayerArgs &a, int fmt, hipStream_t s) {
   const int mr = layer_rows_per_pass(a.T);
-  LayerKernel kern = layer_kernel(fmt, mr);
+  LayerKernel kern = layer_kernel(fmt, mr, a.T);
   // no more workgroups than fit on the chip at once: an FC2 item waits only
   // for items of workgroups that are resident
   int dev = 0, cus = 0, per_cu = 0;

@@ -63,14 +63,14 @@ class MoELayer:
                                  and qmoe_fp4_resolve_path(T, k, w1, path) == QMOE_PATH_GEMV)
         self.ws_layer = (alloc_layer_workspace(layer_persistent_workspace_bytes(T, k, w1, w2, act), dev)
                          if self.layer_persistent else None)
-        # run(fused=True) takes the one-launch layer at two to four tokens,
-        # where it measured faster than the multi-launch calls (NVFP4 E=256,
-        # H=2048, I=768, same box: T=2 22.0 vs 23.7 us, T=4 27.6 vs 30.2); at
-        # T=1 the three launches with routing inside FC1 measured 17.45
-        # against 18.19 us (four repetitions each, one box), and at T=8 the
-        # one-launch layer's three rounds of resident workgroups 42.4 against
-        # 41.3 us
-        self.one_launch = self.layer_persistent and 2 <= T <= 4
+        # run(fused=True) takes the one-launch layer at two to eight tokens of
+        # a hidden size up to 2048, where it measured faster than the
+        # multi-launch calls (NVFP4 E=256, H=2048, I=768, one box: T=2 20.5
+        # vs 23.4 us, T=4 26.9 vs 28.9, T=8 39.8 vs 40.6); at T=1 the three
+        # launches with routing inside FC1 measured 17.0 against 17.2-18.3
+        # us, and at hidden size 4096 (MXFP4 T=8) the multi-launch calls 182
+        # against 233 us
+        self.one_launch = self.layer_persistent and 2 <= T <= 8 and H <= 2048
         if not self.fp8 and R <= GEMV_MAX_ROWS:  # route_fc1() is callable
             need = max(need, fc_workspace_bytes(4, T, k, w1, path, act))
         self.decode_layer_callable = fits
