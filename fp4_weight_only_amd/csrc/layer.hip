@@ -571,22 +571,20 @@ __device__ __forceinline__ void layer_body(const LayerArgs &a) {
   if (blockIdx.x == 0) write_routing(a, sm, tid0);
 }
 
-// The kernel at four workgroups per CU (128 VGPRs) and at three (168 VGPRs).
+// Three workgroups per CU (168 VGPRs): with four (128 VGPRs) the body
+// spilled and ran slower at every token count measured on MI355X (NVFP4
+// E=256, H=2048, I=768: T=1 17.4 -> 16.5 us, T=2 21.7 -> 20.5, T=4 26.8 ->
+// 25.6 with four-row passes, T=8 40.9 -> 39.8).
 template <int FMT, int MRMAX>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void fp4_layer_kernel(LayerArgs a) {
-  layer_body<FMT, MRMAX>(a);
-}
-template <int FMT, int MRMAX>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void fp4_layer_kernel_w3(LayerArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void fp4_layer_kernel(LayerArgs a) {
   layer_body<FMT, MRMAX>(a);
 }
 
-// Two-row passes up to four tokens: at four tokens the hot experts' four
-// rows then take two slots (their weights are read twice, 1.8 MB each) and
-// the longest items shorten (layer 27.4 -> 26.9 us on MI355X); one-row
-// passes there took 30.7 us, two-row passes at eight tokens 44.1 against
-// 42.0 us.
-int layer_rows_per_pass(int T) { return T <= 1 ? 1 : (T <= 4 ? 2 : 4); }
+// Rows per pass: one at one token, two at two, else four (an expert holds at
+// most T rows).  At four tokens four-row passes (the hot experts' weights
+// read once) ran 25.6 us against 27.3 us for two-row passes (MI355X, three
+// workgroups per CU).
+int layer_rows_per_pass(int T) { return T <= 1 ? 1 : (T <= 2 ? 2 : 4); }
 
 int layer_max_items(const LayerArgs &a) {
   const int mr = layer_rows_per_pass(a.T);
@@ -599,27 +597,18 @@ namespace {
 
 typedef void (*LayerKernel)(LayerArgs);
 
-// Workgroups per CU (waves per SIMD): four (128 VGPRs) at one token and at
-// four, three (168 VGPRs: resident slots given up for register room) at two
-// or three tokens and from five on, as measured on MI355X (NVFP4 E=256,
-// H=2048, I=768: T=2 layer 21.7 -> 20.5 us, T=8 40.9 -> 39.8 us; T=4 the
-// same 26.9 us either way).
 template <int FMT>
-LayerKernel layer_kernel_fmt(int mr, int T) {
-  if (mr == 1) return fp4_layer_kernel<FMT, 1>;
-  if (mr == 2) return T == 4 ? fp4_layer_kernel<FMT, 2> : fp4_layer_kernel_w3<FMT, 2>;
-  return fp4_layer_kernel_w3<FMT, 4>;
+LayerKernel layer_kernel_fmt(int mr) {
+  return mr == 1 ? fp4_layer_kernel<FMT, 1> : (mr == 2 ? fp4_layer_kernel<FMT, 2> : fp4_layer_kernel<FMT, 4>);
 }
 
-LayerKernel layer_kernel(int fmt, int mr, int T) {
-  return fmt == 0 ? layer_kernel_fmt<0>(mr, T) : layer_kernel_fmt<1>(mr, T);
-}
+LayerKernel layer_kernel(int fmt, int mr) { return fmt == 0 ? layer_kernel_fmt<0>(mr) : layer_kernel_fmt<1>(mr); }
 
 }  // namespace
 
 hipError_t launch_fp4_layer(const LayerArgs &a, int fmt, hipStream_t s) {
   const int mr = layer_rows_per_pass(a.T);
-  LayerKernel kern = layer_kernel(fmt, mr, a.T);
+  LayerKernel kern = layer_kernel(fmt, mr);
   // no more workgroups than fit on the chip at once: an FC2 item waits only
   // for items of workgroups that are resident
   int dev = 0, cus = 0, per_cu = 0;

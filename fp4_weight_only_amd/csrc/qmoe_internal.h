@@ -86,7 +86,7 @@ constexpr int kLayerMaxTiles2 = 64;    // H <= 16384
 constexpr int kLayerSyncStride = 16;   // int32 per counter: one 64-byte segment each
 constexpr size_t kLayerSyncBytes =
     (size_t)(2 + kLayerMaxTiles2 + 64 * kLayerMaxHChunks) * kLayerSyncStride * sizeof(int32_t);
-// rows per workgroup pass of the layer (1 for one token, 2 up to 4 tokens, else 4)
+// rows per workgroup pass of the layer (1 for one token, 2 for two, else 4)
 int layer_rows_per_pass(int T);
 // upper bound of the work items of one call (every slot live)
 int layer_max_items(const LayerArgs &a);

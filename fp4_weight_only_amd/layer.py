@@ -63,14 +63,13 @@ class MoELayer:
                                  and qmoe_fp4_resolve_path(T, k, w1, path) == QMOE_PATH_GEMV)
         self.ws_layer = (alloc_layer_workspace(layer_persistent_workspace_bytes(T, k, w1, w2, act), dev)
                          if self.layer_persistent else None)
-        # run(fused=True) takes the one-launch layer at two to eight tokens of
-        # a hidden size up to 2048, where it measured faster than the
-        # multi-launch calls (NVFP4 E=256, H=2048, I=768, one box: T=2 20.5
-        # vs 23.4 us, T=4 26.9 vs 28.9, T=8 39.8 vs 40.6); at T=1 the three
-        # launches with routing inside FC1 measured 17.0 against 17.2-18.3
-        # us, and at hidden size 4096 (MXFP4 T=8) the multi-launch calls 182
-        # against 233 us
-        self.one_launch = self.layer_persistent and 2 <= T <= 8 and H <= 2048
+        # run(fused=True) takes the one-launch layer up to eight tokens of a
+        # hidden size up to 2048, where it measured faster than the
+        # multi-launch calls (NVFP4 E=256, H=2048, I=768, one box: T=1 16.5
+        # vs 17.0 us, T=2 20.5 vs 23.4, T=4 25.6 vs 28.9, T=8 39.8 vs 40.6);
+        # at hidden size 4096 (MXFP4 T=8) the multi-launch calls 182 against
+        # 233 us
+        self.one_launch = self.layer_persistent and T <= 8 and H <= 2048
         if not self.fp8 and R <= GEMV_MAX_ROWS:  # route_fc1() is callable
             need = max(need, fc_workspace_bytes(4, T, k, w1, path, act))
         self.decode_layer_callable = fits
