@@ -19,8 +19,10 @@
 // * Decode: a nibble zip and gfx950's FP4 -> bf16 conversion turn two k rows
 //   of a lane's 8 columns into 8 K-paired bf16x2 registers (twelve VALU
 //   instructions per 16 codes, no table, no branch); v_dot2c_f32_bf16 multiplies a K pair of
-//   activations by a K pair of weights.  Products are summed per scale block
-//   and the block scale is applied once per (row, column, block).
+//   activations by a K pair of weights (one NVFP4 row), or 4x4x4 bf16 MFMA
+//   blocks take four k of a column for up to four rows (several rows, and
+//   one MXFP4 row).  Products are summed per scale block and the block scale
+//   is applied once per (row, column, block).
 // * Split-K inside the workgroup: the two halves of a wave add through a
 //   lane swap, then the W waves through LDS, in a fixed order.  When K spans
 //   several chunks each workgroup writes g * partial to the workspace and a

@@ -206,12 +206,16 @@ __device__ __forceinline__ void lane_mfma_group(Smem<MRMAX> &sm, const uint32_t 
   }
 }
 
-// One pass over mr <= MRMAX staged rows starting at r0: one row on the dot2
-// path, two to four on the matrix cores.
+// One pass over mr <= MRMAX staged rows starting at r0: two to four rows on
+// the matrix cores; one row on the dot2 path for NVFP4 and on the matrix
+// cores for MXFP4 (a quarter of each 4x4x4 block used, the dot products off
+// the VALU: the MXFP4 hidden-4096 decode layer, whose GEMV is VALU-bound,
+// 182.7 -> 169.8 us on MI355X; the NVFP4 single-launch layers, bound by
+// each item's latency, ran 0.3-0.5 us slower that way).
 template <int FMT, int MRMAX>
 __device__ __forceinline__ void lane_pass(Smem<MRMAX> &sm, const uint32_t (&A)[kGemvLaneK], const u32x2_t (&SB)[2],
                                           int g, int wave, int lane, int r0, int mr) {
-  if (MRMAX == 1 || mr == 1) {
+  if (FMT == 0 && (MRMAX == 1 || mr == 1)) {
     lane_dot<FMT, 1, MRMAX>(sm, A, SB, g, wave, lane, r0);
   } else {
     lane_mfma_group<FMT, MRMAX, 0>(sm, A, SB, g, wave, lane, r0, mr);
