@@ -81,7 +81,7 @@ def parse():
     ap.add_argument("--workload", default="mtp4", choices=LAYER_WORKLOADS + ("dequant", "fp8_dequant"))
     ap.add_argument("--layer-call", default="auto", choices=("auto", "multi", "one"),
                     help="decode layer: auto = the library's default (one kernel launch, "
-                         "qmoe_fp4_moe_layer_persistent, two to eight tokens at hidden size <= 2048), multi = the multi-launch calls, "
+                         "qmoe_fp4_moe_layer_persistent, up to four tokens at hidden size <= 2048), multi = the multi-launch calls, "
                          "one = one launch wherever the shape allows")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true",

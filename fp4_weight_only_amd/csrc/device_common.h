@@ -91,6 +91,21 @@ constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowMirror = 0x140;
 
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active): a
+// Hillis-Steele scan inside each 16-lane row (row shifts by 1, 2, 4, 8;
+// lanes shifted in from outside the row read 0), then the last lane of row
+// 0 is added to rows 1 and 3 and the last lane of row 1 to rows 2 and 3
+// (row broadcasts; rows masked off add 0).
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 // Finds the expert holding the s-th non-empty row range, with its first row
 // and row count.  Every lane gets the same answer; returns -1 if fewer than
 // s+1 experts have rows.
@@ -135,9 +150,11 @@ __device__ __forceinline__ int find_slot_expert(const int32_t *__restrict__ off,
 // group's first row and row count (every lane the same answer), or -1 when
 // s is past the last group.  A lane covers experts 4*lane .. 4*lane + 3
 // (E <= 256); a wave prefix sum of the per-lane group counts locates s.
+// G is a power of two (the pass sizes 1, 2 and 4).
 __device__ __forceinline__ int find_slot_group(const int32_t *__restrict__ off, int E, int s, int G, int &row0,
                                                int &m) {
   const int lane = lane_id();
+  const int gsh = __builtin_ctz((unsigned)G);
   int o[5];
 #pragma unroll
   for (int i = 0; i < 5; ++i) {
@@ -148,15 +165,10 @@ __device__ __forceinline__ int find_slot_group(const int32_t *__restrict__ off, 
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     cnt[i] = (4 * lane + i < E) ? o[i + 1] - o[i] : 0;
-    grp[i] = (cnt[i] + G - 1) / G;
+    grp[i] = (cnt[i] + G - 1) >> gsh;
     local += grp[i];
   }
-  int incl = local;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int v = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += v;
-  }
+  const int incl = wave_inclusive_sum(local);
   int found = -1, r0 = 0, rc = 0;
   int run = incl - local;
 #pragma unroll

@@ -77,7 +77,7 @@ struct RouteSmem {
 // the later calls.
 __device__ __forceinline__ void route_prologue(const GemvArgs &a, RouteSmem &rs, int W, int wave, int lane) {
   const int E = a.E, k = a.topk, T = a.route_T, R = a.rows;
-  const bool writer = blockIdx.x == 0;
+  const bool writer = blockIdx.x == 0 && blockIdx.y == 0;
   for (int t = wave; t < T; t += W) {  // wave-uniform
     int sel;
     float wsel;
@@ -184,11 +184,12 @@ __global__ __launch_bounds__(max_waves<MRMAX>() * 64) __attribute__((amdgpu_wave
   const int W = a.waves;
   const int KC = W * kGemvWaveK;
 
-  // Work item: XCD-aware decode of the linear workgroup id.
-  const int L = blockIdx.x;
-  const int j = L >> 3;
-  const int item = (j / a.nchunks) * 8 + (L & 7);
-  const int kc = j % a.nchunks;
+  // Work item: XCD-aware grid (x = k chunk * 8 + XCD, y = group of 8
+  // items); the linear dispatch order (x fastest) deals consecutive
+  // workgroups round-robin over the 8 XCDs, so item 8y + x % 8 runs on XCD
+  // x % 8 with all its k chunks.
+  const int kc = (int)blockIdx.x >> 3;
+  const int item = (int)blockIdx.y * 8 + ((int)blockIdx.x & 7);
   if (item >= a.nslots * a.ntiles) return;
   const int slot = item / a.ntiles;
   const int tile = item - slot * a.ntiles;
@@ -320,7 +321,7 @@ __global__ __launch_bounds__(max_waves<MRMAX>() * 64) __attribute__((amdgpu_wave
     }
     lds_barrier();
 
-    lane_pass<FMT, MRMAX>(sm, A, SB, g, wave, lane, 0, mr);
+    lane_pass<FMT, MRMAX, false>(sm, A, SB, g, wave, lane, 0, mr);
     lds_barrier();
 
     // ---- reduce the W waves (fixed order); one thread per column ------------
@@ -448,7 +449,7 @@ void gemv_plan(GemvArgs &a, int max_rows_per_expert, void *ws) {
   // An expert that may hold more rows than a pass is dealt out over several
   // slots of at most a pass each (workgroups of equal length; no pass loop).
   // Slots needed: sum_e ceil(m_e / G) <= (rows + min(E, rows) * (G - 1)) / G.
-  const int mr = rows_per_pass(max_rows_per_expert);
+  const int mr = rows_per_pass(max_rows_per_expert);  // 1, 2 or 4: find_slot_group takes a power of two
   const int nexp = a.rows < a.E ? a.rows : a.E;
   a.split_rows = max_rows_per_expert > mr ? mr : 0;
   a.nslots = a.split_rows ? (a.rows + nexp * (mr - 1)) / mr : nexp;
@@ -459,7 +460,7 @@ void gemv_plan(GemvArgs &a, int max_rows_per_expert, void *ws) {
 
 hipError_t launch_fp4_gemv(const GemvArgs &a, int fmt, int max_rows_per_expert, hipStream_t s) {
   const int items = a.nslots * a.ntiles;
-  const dim3 grid((unsigned)(((items + 7) / 8) * 8 * a.nchunks));
+  const dim3 grid((unsigned)(8 * a.nchunks), (unsigned)((items + 7) / 8));
   const dim3 block((unsigned)(a.waves * 64));
   // one pass of at most mr rows per workgroup: an expert holding more rows
   // (a token selects an expert at most once, so at most max_rows_per_expert)

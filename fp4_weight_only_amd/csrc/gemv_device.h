@@ -149,21 +149,27 @@ __device__ __forceinline__ void e2m1_kpair_cvt_half(uint32_t a, uint32_t b, uint
 // Two to four staged rows r0 .. r0 + mr - 1 through the matrix cores, over
 // the same lane layout as lane_dot: 4x4x4 bf16 blocks, sixteen per
 // instruction.  Block b is lanes 4b .. 4b + 3; lane 4b + i brings activation
-// row r0 + i (zeros past mr) and lane 4b + j one of its own weight columns,
+// row r0 + i and lane 4b + j one of its own weight columns,
 // each over a k quad (4 of the lane's 32 k rows); the result is the lane's
 // column for all four rows.  Per column and scale block the k quads
 // accumulate in fp32 from +0, and the block scale multiplies the block sum
 // into the lane's running sum (fma), the dot2 path's order of operations.
 // Columns go in two groups of four to bound the live accumulators.
-template <int FMT, int MRMAX, int GRP>
+// MASKX: lanes past the mr rows read zeros (a masked read per k quad);
+// otherwise they read a staged row, which is as good: a block's output row i
+// depends on activation row i alone, and rows past mr are never stored.  The
+// per-call GEMV reads unmasked (MXFP4 hidden-4096 T=8 layer 170.8 -> 164.5 us
+// with the shift-based slot lookup); the single-launch layer keeps the
+// masked read (T=4 25.7 against 26.5 us unmasked).
+template <int FMT, int MRMAX, int GRP, bool MASKX>
 __device__ __forceinline__ void lane_mfma_group(Smem<MRMAX> &sm, const uint32_t (&A)[kGemvLaneK],
                                                 const u32x2_t (&SB)[2], int g, int wave, int lane, int r0, int mr) {
   constexpr int B = (FMT == 0) ? 16 : 32;
   constexpr int NBLK = kGemvLaneK / B;
   constexpr int QPB = B / 4;  // k quads per scale block
   const int i = lane & 3;
-  const bool xon = i < mr;
-  const uint16_t *xrow = &sm.xs[xon ? r0 + i : 0][g * kGemvLaneK];
+  const bool xon = !MASKX || i < mr;
+  const uint16_t *xrow = &sm.xs[MASKX ? (xon ? r0 + i : 0) : (r0 + i < MRMAX ? r0 + i : MRMAX - 1)][g * kGemvLaneK];
   float acc[4][4];
 #pragma unroll
   for (int c = 0; c < 4; ++c)
@@ -212,14 +218,14 @@ __device__ __forceinline__ void lane_mfma_group(Smem<MRMAX> &sm, const uint32_t 
 // the VALU: the MXFP4 hidden-4096 decode layer, whose GEMV is VALU-bound,
 // 182.7 -> 169.8 us on MI355X; the NVFP4 single-launch layers, bound by
 // each item's latency, ran 0.3-0.5 us slower that way).
-template <int FMT, int MRMAX>
+template <int FMT, int MRMAX, bool MASKX = true>
 __device__ __forceinline__ void lane_pass(Smem<MRMAX> &sm, const uint32_t (&A)[kGemvLaneK], const u32x2_t (&SB)[2],
                                           int g, int wave, int lane, int r0, int mr) {
   if (FMT == 0 && (MRMAX == 1 || mr == 1)) {
     lane_dot<FMT, 1, MRMAX>(sm, A, SB, g, wave, lane, r0);
   } else {
-    lane_mfma_group<FMT, MRMAX, 0>(sm, A, SB, g, wave, lane, r0, mr);
-    lane_mfma_group<FMT, MRMAX, 1>(sm, A, SB, g, wave, lane, r0, mr);
+    lane_mfma_group<FMT, MRMAX, 0, MASKX>(sm, A, SB, g, wave, lane, r0, mr);
+    lane_mfma_group<FMT, MRMAX, 1, MASKX>(sm, A, SB, g, wave, lane, r0, mr);
   }
 }
 

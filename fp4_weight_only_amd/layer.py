@@ -63,13 +63,14 @@ class MoELayer:
                                  and qmoe_fp4_resolve_path(T, k, w1, path) == QMOE_PATH_GEMV)
         self.ws_layer = (alloc_layer_workspace(layer_persistent_workspace_bytes(T, k, w1, w2, act), dev)
                          if self.layer_persistent else None)
-        # run(fused=True) takes the one-launch layer up to eight tokens of a
+        # run(fused=True) takes the one-launch layer up to four tokens of a
         # hidden size up to 2048, where it measured faster than the
-        # multi-launch calls (NVFP4 E=256, H=2048, I=768, one box: T=1 16.5
-        # vs 17.0 us, T=2 20.5 vs 23.4, T=4 25.6 vs 28.9, T=8 39.8 vs 40.6);
-        # at hidden size 4096 (MXFP4 T=8) the multi-launch calls 182 against
-        # 233 us
-        self.one_launch = self.layer_persistent and T <= 8 and H <= 2048
+        # multi-launch calls (NVFP4 E=256, H=2048, I=768, one box: T=1 16.4
+        # vs 16.7 us, T=2 20.5 vs 23.4, T=4 25.6 vs 28.6); from five tokens
+        # the multi-launch calls are faster (T=5 32.8 vs 35.0, T=6 34.3 vs
+        # 35.0, T=7 36.9 vs 37.7, T=8 38.3 vs 39.8); at hidden size 4096
+        # (MXFP4 T=8) the multi-launch calls 164 against 233 us
+        self.one_launch = self.layer_persistent and T <= 4 and H <= 2048
         if not self.fp8 and R <= GEMV_MAX_ROWS:  # route_fc1() is callable
             need = max(need, fc_workspace_bytes(4, T, k, w1, path, act))
         self.decode_layer_callable = fits

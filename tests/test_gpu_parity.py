@@ -35,6 +35,9 @@ SMALL = [
     synth.shrink(synth.MX_DECODE, E=40, T=8, k=8, H=544, I=160, seed=3),      # MXFP4, ragged
     synth.shrink(synth.DECODE, E=16, T=64, k=1, H=256, I=64, seed=4),         # m up to 64 per expert
     synth.shrink(synth.MX_DECODE, E=4, T=16, k=4, H=1024, I=512, seed=5),     # every expert has 16 rows
+    # two k chunks per GEMV workgroup (five chunks: the last pair has one)
+    synth.shrink(synth.DECODE, E=16, T=1, k=4, H=1184, I=1040, seed=40),      # one NVFP4 row; FC2's K tail inside a lane
+    synth.shrink(synth.MX_DECODE, E=24, T=8, k=8, H=1184, I=1056, seed=41),   # MXFP4, FC1 and FC2 in five chunks
     synth.shrink(synth.MTP4, E=32, T=2, k=8, H=512, I=192, seed=26),          # T=2: one two-row pass
     synth.shrink(synth.MTP4, E=32, T=3, k=8, H=512, I=192, seed=27),          # T=3: 3-row experts over two-row slots (2 + 1)
 ]
@@ -632,7 +635,10 @@ def test_layer_decode_equals_separate_calls(cfg, mode, route_in_fc1):
 
 
 PERSISTENT = LAYER_DECODE + [synth.MTP8, synth.shrink(synth.MX_DECODE, E=32, T=8, k=8, H=1024, I=512, seed=28),
-                             synth.shrink(synth.MTP4, E=64, T=6, k=8, H=2304, I=1280, seed=29)]
+                             synth.shrink(synth.MTP4, E=64, T=6, k=8, H=2304, I=1280, seed=29),
+                             # separate FC1 calls on the two-chunk GEMV, five k chunks
+                             synth.shrink(synth.MX_DECODE, E=24, T=8, k=8, H=1184, I=1024, seed=42),
+                             synth.shrink(synth.DECODE, E=16, T=1, k=4, H=1184, I=256, seed=43)]
 
 
 @pytest.mark.parametrize("mode", ["softmax", "router_weights", "gptoss_concat"])
