@@ -36,6 +36,15 @@ __device__ __forceinline__ void decode_scales(u32x2_t sb, float (&sc)[8]) {
 }
 
 
+// Lower + upper half-wave sums of two values at once: v_permlane32_swap
+// exchanges lanes 32..63 of a with lanes 0..31 of b, so lanes 0..31 end up
+// with a's lower + upper halves and lanes 32..63 with b's (both sums taken
+// lower half first, as a lane swap with __shfl_xor would give).
+__device__ __forceinline__ float half_sum_pair(float a, float b) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
 template <int MRMAX>
 struct Smem {
   uint16_t xs[MRMAX][kMaxChunkK];                 // activations of the chunk
@@ -119,15 +128,15 @@ __device__ __forceinline__ void lane_dot(Smem<MRMAX> &sm, const uint32_t (&A)[kG
       for (int c = 0; c < 8; ++c) acc[r][c] = fmaf(sc[c], bs[r][c], acc[r][c]);
   }
   const int nl = lane & 31;
+  // columns c and c + 4 paired: lanes 0..31 store columns 0..3 of their
+  // eight, lanes 32..63 columns 4..7
+  const int half = lane >> 5;
 #pragma unroll
   for (int r = 0; r < MR; ++r) {
+    float v[4];
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-      acc[r][c] = acc[r][c] + __shfl_xor(acc[r][c], 32);  // lower half + upper half, same order in every lane pair
-    if (lane < 32) {
-      *(float4 *)&sm.red[wave][r0 + r][nl * 8] = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
-      *(float4 *)&sm.red[wave][r0 + r][nl * 8 + 4] = make_float4(acc[r][4], acc[r][5], acc[r][6], acc[r][7]);
-    }
+    for (int c = 0; c < 4; ++c) v[c] = half_sum_pair(acc[r][c], acc[r][c + 4]);
+    *(float4 *)&sm.red[wave][r0 + r][nl * 8 + 4 * half] = make_float4(v[0], v[1], v[2], v[3]);
   }
 }
 
@@ -201,13 +210,33 @@ __device__ __forceinline__ void lane_mfma_group(Smem<MRMAX> &sm, const uint32_t 
       for (int r = 0; r < 4; ++r) acc[c][r] = fmaf(sc[4 * GRP + c], bacc[c][r], acc[c][r]);
   }
   const int nl = lane & 31;
+  if constexpr (FMT == 0) {
+    // rows rp and rp + 1 paired: lanes 0..31 store row rp, lanes 32..63 row
+    // rp + 1 (NVFP4 T=4 single-launch layer 25.7 -> 25.4 us, T=8 separate
+    // calls 38.5 -> 37.8 us)
+    const int half = lane >> 5;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    if (r < mr) {  // uniform
+    for (int rp = 0; rp < 4; rp += 2) {
+      if (rp < mr) {  // uniform
+        float v[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[c][r] = acc[c][r] + __shfl_xor(acc[c][r], 32);  // lower half + upper half
-      if (lane < 32)
-        *(float4 *)&sm.red[wave][r0 + r][nl * 8 + 4 * GRP] = make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
+        for (int c = 0; c < 4; ++c) v[c] = half_sum_pair(acc[c][rp], acc[c][rp + 1]);
+        const int r = rp + half;
+        if (r < mr)
+          *(float4 *)&sm.red[wave][r0 + r][nl * 8 + 4 * GRP] = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    }
+  } else {
+    // MXFP4: a lane swap per value (the paired form measured slower here:
+    // hidden-4096 T=8 layer 164.3 -> 165.9 us)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (r < mr) {  // uniform
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c][r] = acc[c][r] + __shfl_xor(acc[c][r], 32);  // lower half + upper half
+        if (lane < 32)
+          *(float4 *)&sm.red[wave][r0 + r][nl * 8 + 4 * GRP] = make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
+      }
     }
   }
 }
