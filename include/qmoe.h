@@ -37,12 +37,17 @@
  *   qmoe_fp4_weights and qmoe_swiglu are host structs whose members point to
  *   device memory.  Every device pointer must be 16-byte aligned
  *   (QMOE_EALIGN otherwise).  The caller owns every buffer; the library
- *   allocates nothing, keeps no state between calls and never synchronises.
+ *   allocates nothing, keeps no state between calls (the allocation-free
+ *   layer call aside: its split-K sums live in a file-scope device array)
+ *   and never synchronises.
  * - Work is enqueued on `stream` (a hipStream_t; 0 is the null stream) and is
  *   asynchronous.  All argument checks run on the host before any launch; a
  *   failed check returns its status and enqueues nothing.  QMOE_ELAUNCH
- *   reports a launch error; device faults surface at the caller's next
- *   synchronisation.
+ *   reports a launch error; a call made of several launches (the layer
+ *   calls, the fused FC2 + finalize, the concatenated-SwiGLU grouped FC1,
+ *   any GEMV call with a split-K epilogue) may already have enqueued its
+ *   earlier launches when a later one fails, and its outputs are then
+ *   undefined.  Device faults surface at the caller's next synchronisation.
  * - bf16 values are passed as their 16-bit patterns (uint16_t).
  *
  * Data layouts
