@@ -55,6 +55,13 @@ qmoe_status check_fc(const qmoe_fp4_weights *w, int32_t T, int32_t k, const void
   return QMOE_OK;
 }
 
+// The GEMV grid's y dimension counts groups of eight (slot, column tile)
+// items, at most 64 slots: within 65535 for up to 8191 column tiles.
+constexpr int kGemvMaxColumnTiles = 8191;
+inline bool gemv_grid_fits(const qmoe_fp4_weights *w) {
+  return (w->N + kGemvTileN - 1) / kGemvTileN <= kGemvMaxColumnTiles;
+}
+
 // Resolves AUTO and checks the row window and tile shape of each path.
 // AUTO follows the decode GEMV's 64-row window: the GEMV up to 64 expanded
 // rows, the grouped MFMA GEMM (the dense contraction of prefill) above.  The
@@ -65,7 +72,7 @@ qmoe_status resolve_path(qmoe_path path, int32_t rows, int32_t max_rows_per_expe
   (void)max_rows_per_expert;
   qmoe_path p = path;
   if (p == QMOE_PATH_AUTO) p = rows <= QMOE_GEMV_MAX_ROWS ? QMOE_PATH_GEMV : QMOE_PATH_GROUPED;
-  if (p == QMOE_PATH_GEMV && rows > QMOE_GEMV_MAX_ROWS) return QMOE_EUNSUPPORTED;
+  if (p == QMOE_PATH_GEMV && (rows > QMOE_GEMV_MAX_ROWS || !gemv_grid_fits(w))) return QMOE_EUNSUPPORTED;
   if (p == QMOE_PATH_GROUPED && (w->K % 64 != 0 || w->N % 128 != 0)) return QMOE_EUNSUPPORTED;
   // buffer resources address the activations of a call in 32 bits
   if (p == QMOE_PATH_GROUPED && (int64_t)rows * w->K * 2 >= ((int64_t)1 << 31)) return QMOE_EUNSUPPORTED;
@@ -293,7 +300,7 @@ qmoe_status qmoe_fp4_route_fc1_swiglu(const float *logits, const float *router_w
       !aligned16(topk_w) || !aligned16(perm_to_expanded) || !aligned16(expanded_to_perm))
     return QMOE_EALIGN;
   // the maps of one call are ranked by one wave
-  if (sh.rows > QMOE_GEMV_MAX_ROWS) return QMOE_EUNSUPPORTED;
+  if (sh.rows > QMOE_GEMV_MAX_ROWS || !gemv_grid_fits(w1)) return QMOE_EUNSUPPORTED;
   GemvArgs a = {};
   a.act = x;
   a.topk = k;
@@ -448,6 +455,7 @@ qmoe_status layer_decode(const float *logits, const float *router_weights, const
       !aligned16(topk_w) || !aligned16(perm_to_expanded) || !aligned16(expanded_to_perm))
     return QMOE_EALIGN;
   if (sh.rows > QMOE_GEMV_MAX_ROWS || w2->N % 32 != 0 || w2->N % 8 != 0) return QMOE_EUNSUPPORTED;
+  if (!gemv_grid_fits(w1) || !gemv_grid_fits(w2)) return QMOE_EUNSUPPORTED;
   const int32_t fusion = act ? act->fusion : QMOE_SWIGLU_INTERLEAVED;
   if (fusion != 0 && fusion != QMOE_SWIGLU_INTERLEAVED && fusion != QMOE_SWIGLU_CONCAT) return QMOE_EINVAL;
   // workspace: FC1's split-K partials (u, g applied), then FC2's

@@ -134,6 +134,8 @@ typedef struct {
 
 #define QMOE_MAX_EXPERTS 256
 #define QMOE_MAX_TOPK 8
+/* the GEMV path: at most 64 expanded rows and N <= 8191 * 256 = 2,096,896
+ * output columns (QMOE_EUNSUPPORTED otherwise) */
 #define QMOE_GEMV_MAX_ROWS 64
 
 /*

@@ -169,6 +169,10 @@ def test_auto_path_rule(q):
     assert resolved(8, 8, 768, 2048, G) == (q.QMOE_OK, G)           # explicit grouped inside the window
     assert resolved(9, 8, 2048, 1536, V)[0] == q.QMOE_EUNSUPPORTED  # past the GEMV window
     assert resolved(8, 8, 784, 2048, G)[0] == q.QMOE_EUNSUPPORTED   # K % 64
+    # the GEMV grid holds at most 8191 column tiles of 256 (N <= 2,096,896)
+    assert resolved(8, 8, 32, 8191 * 256, V) == (q.QMOE_OK, V)
+    assert resolved(8, 8, 32, 8191 * 256 + 32, V)[0] == q.QMOE_EUNSUPPORTED
+    assert resolved(8, 8, 32, 8191 * 256 + 32)[0] == q.QMOE_EUNSUPPORTED  # AUTO in the GEMV window
     assert q.lib.qmoe_fp4_resolve_path(1, 1, ctypes.byref(weights(q)), AU, None) == q.QMOE_EINVAL
     assert size(8, 8, 768, 2048, G) != size(8, 8, 768, 2048, V)
     assert size(8, 8, 768, 2048, AU) == size(8, 8, 768, 2048, V)
